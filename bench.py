@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of attention-aware INT2 KV caching on one MI355X.
+
+One step = the whole hot path over one batch: the demote of the oldest recent token (rotate,
+clip, quantise, pack into the INT2 history, new token into the BF16 recent window) followed by
+decode attention (query rotation, BF16 sink/recent split, INT2 history split-K, log-sum-exp merge
+with the R_V^T un-rotation).
+
+Workload (default): a Qwen3-8B-shaped attention layer, 32 query heads / 8 KV heads, head_dim 128,
+batch 1, 100,000 tokens of context (64 BF16 sink + 256 BF16 recent + 99,680 INT2 history, group
+128, bf16 scale/zero), K/V drawn with heavy outlier channels, rotations from the eigenbases of
+synthetic calibration covariances, history pages a seeded permutation of the pool.
+
+Inputs are resident in HBM before timing. Every timed step reads a different copy of the cache
+(the copies together exceed the 256 MB Infinity Cache), so each step's bytes come from HBM.
+Steps are captured in a HIP graph and replayed; HIP events recorded by the library around its
+kernels time the dominant kernel (the INT2 history split) within the same timed region.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X published HBM3E bandwidth
+PAGE = 16
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--context", type=int, default=100_000)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0: enough for >= 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurement")
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter scaling reference)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- inputs
+def workload_inputs(w, batch, context, seed_offset=0, fast=False):
+    """K/V (bf16 device tensors [B, Hkv, T, d]) and q, drawn with the workload's channel law.
+    fast=True draws on the GPU (values differ from the numpy draws; shapes and laws do not)."""
+    import torch
+    import synth
+    hkv, d = w.num_kv_heads, w.head_dim
+    K = torch.empty((batch, hkv, context, d), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    g = torch.Generator(device="cuda")
+    for b in range(batch):
+        for kv in range(hkv):
+            sk = torch.from_numpy(synth.channel_scales(w, "chan_k", kv)).float().cuda()
+            sv = torch.from_numpy(synth.channel_scales(w, "chan_v", kv)).float().cuda()
+            if fast:
+                g.manual_seed(w.seed * 1_000_003 + b * 1009 + kv + seed_offset)
+                K[b, kv] = (torch.randn((context, d), generator=g, device="cuda") * sk).bfloat16()
+                V[b, kv] = (torch.randn((context, d), generator=g, device="cuda") * sv).bfloat16()
+            else:
+                ks, vs = synth.kv_slice(w, b, kv, context)
+                K[b, kv] = torch.from_numpy(ks).cuda().bfloat16()
+                V[b, kv] = torch.from_numpy(vs).cuda().bfloat16()
+    q = np.stack([synth.decode_query(w, b % w.batch) for b in range(batch)])
+    return K, V, torch.from_numpy(q).cuda().bfloat16()
+
+
+def rotations(w):
+    """R_K, R_V [Hkv, d, d] fp32 from the product calibration (offline step)."""
+    import torch
+    import synth
+    from bit_rotated_kv_amd import calib
+    rk, rv = [], []
+    for kv in range(w.num_kv_heads):
+        qc = torch.from_numpy(synth.calibration_queries(w, kv))
+        kc, vc = synth.calibration_context(w, kv)
+        rk.append(calib.rotation(calib.eigvecs_descending(calib.query_covariance(qc))))
+        cs = calib.value_covariance(qc[:, :1024], torch.from_numpy(kc), torch.from_numpy(vc), 1.0 / math.sqrt(w.head_dim))
+        rv.append(calib.rotation(calib.eigvecs_descending(cs)))
+    return torch.stack(rk).cuda(), torch.stack(rv).cuda()
+
+
+# ---------------------------------------------------------------- INT2 path
+class Int2Setup:
+    def __init__(self, w, batch, context, copies, steps_total, fast_inputs):
+        import torch
+        import bit_rotated_kv_amd as brk
+        import synth
+        self.w, self.batch, self.context = w, batch, context
+        t0 = context - 1                                   # cache before the first step's append
+        visits = steps_total // copies + 2
+        self.max_seq = context + visits
+        hist_pages = (self.max_seq - 320 + PAGE - 1) // PAGE
+        order = synth.page_permutation(w.seed, batch * hist_pages)
+        K, V, q = workload_inputs(w, batch, context, fast=fast_inputs)
+        self.q = q
+        self.rk, self.rv = rotations(w)
+        base = brk.allocate_cache(w.num_q_heads, w.num_kv_heads, w.head_dim, batch, self.max_seq,
+                                  pages2_per_request=hist_pages, page_order2=order)
+        self.layout = base.layout
+        base.seq_len.fill_(t0)
+        Kp = torch.zeros((batch, w.num_kv_heads, self.max_seq, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        Vp = torch.zeros_like(Kp)
+        Kp[:, :, :context] = K
+        Vp[:, :, :context] = V
+        brk.kv_prefill(self.layout, base.seq_len, Kp, Vp, self.rk, self.rv, base.pool, base.page_table, base.window)
+        torch.cuda.synchronize()
+        self.new_k = Kp[:, :, t0].contiguous()
+        self.new_v = Vp[:, :, t0].contiguous()
+        del Kp, Vp, K, V
+        self.page_table = base.page_table
+        self.pools = [base.pool] + [base.pool.clone() for _ in range(copies - 1)]
+        self.windows = [base.window] + [base.window.clone() for _ in range(copies - 1)]
+        self.lens = [[base.seq_len.clone(), torch.empty_like(base.seq_len)] for _ in range(copies)]
+        self.parity = [0] * copies
+        self.ws = torch.zeros(brk.decode_workspace_bytes(self.layout, batch, self.max_seq), dtype=torch.uint8,
+                              device="cuda")
+        self.out = torch.empty((batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        self.copies = copies
+        torch.cuda.synchronize()
+
+    def step(self, i, events=None):
+        import bit_rotated_kv_amd as brk
+        c = i % self.copies
+        par = self.parity[c]
+        sin, sout = self.lens[c][par], self.lens[c][1 - par]
+        brk.kv_demote(self.layout, sin, self.new_k, self.new_v, self.rk, self.rv, self.pools[c], self.page_table,
+                      self.windows[c], seq_len_out=sout)
+        brk.decode_attn(self.layout, self.q, sout, self.windows[c], self.pools[c], self.page_table, self.rk,
+                        self.rv, self.ws, self.max_seq, out=self.out, events=events)
+        self.parity[c] = 1 - par
+
+    def bytes_per_step(self):
+        """Algorithmic HBM bytes of one step (INT2 history at ~context, BF16 window, demote)."""
+        w = self.w
+        d, hkv = w.head_dim, w.num_kv_heads
+        hist = self.context - 320
+        int2 = self.batch * hkv * hist * (2 * (d * 2 // 8) + 8)          # K,V codes + (s,z) x2
+        bf16 = self.batch * hkv * 320 * 2 * d * 2                        # sink + recent K,V
+        demote = self.batch * hkv * (2 * 2 * d * 2 + (2 * (d * 2 // 8) + 8))   # read old + write new token, pack
+        return int2, bf16, demote
+
+
+def time_int2(setup, steps, warmup, eager):
+    """Returns (ms per step, mean kernel intervals [prologue, split, merge] in ms, launch mode).
+
+    Step time: the K steps captured in one HIP graph and replayed (no host work inside the timed
+    region). Kernel intervals: K more steps launched eagerly behind a GPU-side sleep, so every
+    launch is already queued when the GPU reaches it; the library's events then bracket kernels."""
+    import torch
+    for i in range(warmup):
+        setup.step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mode = "eager"
+    base = warmup
+    if not eager:
+        try:
+            parity0 = list(setup.parity)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    setup.step(base + i)
+            setup.parity = parity0          # capture did not run the steps
+            mode = "graph"
+        except Exception as ex:             # capture unsupported: fall back to eager launches
+            print(f"graph capture failed ({ex}); timing eager launches", file=sys.stderr)
+            setup.parity = parity0
+    torch.cuda.synchronize()
+    if mode == "graph":
+        start.record()
+        g.replay()
+        stop.record()
+        for i in range(steps):
+            setup.parity[(base + i) % setup.copies] ^= 1
+    else:
+        torch.cuda._sleep(int(5e7))
+        start.record()
+        for i in range(steps):
+            setup.step(base + i)
+        stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    base += steps
+    # kernel intervals
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(1e8))
+    for i in range(steps):
+        setup.step(base + i, events=evs[i])
+    torch.cuda.synchronize()
+    k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
+    return ms, k.mean(axis=0), mode
+
+
+# ---------------------------------------------------------------- BF16 baseline
+def time_bf16(w, batch, context, steps, warmup, fast_inputs):
+    import torch
+    import bit_rotated_kv_amd as brk
+    import synth
+    L = brk.make_layout(w.num_q_heads, w.num_kv_heads, w.head_dim)
+    npg = (context + PAGE - 1) // PAGE
+    page_bytes = brk.page_bytes(L, 16)
+    copies = max(2, math.ceil(1.0e9 / (batch * npg * page_bytes)))
+    K, V, q = workload_inputs(w, batch, context, seed_offset=7, fast=True)
+    order = synth.page_permutation(w.seed + 1, batch * npg)
+    pt = torch.from_numpy(order.reshape(batch, npg).astype(np.int32)).cuda()
+    seq = torch.full((batch,), context, dtype=torch.int32, device="cuda")
+    pages = []
+    for _ in range(copies):
+        pg = torch.empty(batch * npg * page_bytes, dtype=torch.uint8, device="cuda")
+        brk.bf16_fill(L, seq, K, V, pg, batch * npg, pt)
+        pages.append(pg)
+    del K, V
+    ws = torch.zeros(brk.bf16_decode_workspace_bytes(L, batch, context), dtype=torch.uint8, device="cuda")
+    out = torch.empty((batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        brk.bf16_decode_attn(L, q, seq, pages[i % copies], batch * npg, pt, ws, context, out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nbytes = batch * w.num_kv_heads * context * 2 * w.head_dim * 2
+    return ms, nbytes
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(w, context, kv_heads=8):
+    """The oracle's decode attention for `kv_heads` of the workload's KV heads (their query
+    groups) at full context, timed on the host; scaled to GB/s of the step's algorithmic bytes."""
+    import oracle
+    import synth
+    import threadpoolctl
+    w1 = w
+    rk, rv = [], []
+    for kv in range(kv_heads):
+        qc = synth.calibration_queries(w, kv)
+        kc, vc = synth.calibration_context(w, kv)
+        rk.append(oracle.rotation_fp32(oracle.compose_rotation(oracle.eigenbasis(oracle.query_covariance(qc)))))
+        rv.append(oracle.rotation_fp32(oracle.compose_rotation(oracle.eigenbasis(
+            oracle.score_weighted_value_covariance(qc[:, :1024], kc, vc, 1.0 / math.sqrt(w.head_dim))))))
+    rk, rv = np.stack(rk)[:kv_heads], np.stack(rv)[:kv_heads]
+    K = np.stack([synth.kv_slice(w1, 0, kv, context)[0] for kv in range(kv_heads)])
+    V = np.stack([synth.kv_slice(w1, 0, kv, context)[1] for kv in range(kv_heads)])
+    cache = oracle.OracleCache.from_prefix(K, V, rk, rv, w.group_size)      # untimed: the prefill
+    q = synth.decode_query(w, 0)[:kv_heads * w.gqa]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    times = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.decode_attention(cache, q)
+        times.append(time.perf_counter() - t)
+    sec = float(np.median(times))
+    d = w.head_dim
+    nbytes = kv_heads * ((context - 320) * (2 * (d * 2 // 8) + 8) + 320 * 2 * d * 2)
+    return {"value": round(nbytes / sec / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle decode attention of {kv_heads} of {w.num_kv_heads} KV heads ({kv_heads * w.gqa} query "
+                      f"heads), full {context}-token context, median of 3 runs of {sec:.2f} s; bytes counted as "
+                      f"the GPU metric's (INT2 history + BF16 window) for that share",
+            "seconds": round(sec, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    torch.manual_seed(0)
+    w = synth.workload(2)
+    batch, context = args.batch, args.context
+    int2_bytes_est = batch * w.num_kv_heads * (context - 320) * 72
+    copies = args.copies or max(2, math.ceil(1.0e9 / int2_bytes_est))
+    t_setup = time.time()
+    log(f"setting up INT2 cache: batch {batch}, context {context}, {copies} copies")
+    setup = Int2Setup(w, batch, context, copies, args.steps + args.warmup, fast_inputs=False)
+    setup_s = time.time() - t_setup
+    log(f"setup done in {setup_s:.1f} s; timing {args.steps} steps")
+    ms, kern, mode = time_int2(setup, args.steps, args.warmup, args.eager)
+    int2, bf16, demote = setup.bytes_per_step()
+    step_bytes = int2 + bf16 + demote
+    split_ms = float(kern[1])
+    achieved = (int2 + bf16) / (split_ms * 1e-3) / 1e9
+    result = {
+        "metric": "INT2-KV decode attn: us/step + achieved HBM GB/s at 100K ctx, bs 1 and 32",
+        "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "tokens_per_s": round(batch / (ms * 1e-3), 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int2+bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded; Qwen3-8B-shaped layer, outlier channels, covariance-eigenbasis rotations)",
+        "config": {"workload": f"qwen3-8b-layer decode, batch {batch}, context {context}, 32q/8kv heads, d 128, "
+                               f"64 sink + 256 recent BF16, INT2 history group 128, paged 16, demote in step",
+                   "global_batch": batch, "seq_len": context, "parallelism": "single GPU",
+                   "cache_copies": copies, "launch": mode},
+        "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
+        "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
+                      "merge": round(float(kern[2]), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "split_kernel<128,4> (BF16 window + INT2 history split-K, one launch)",
+                     "bytes_per_launch": int2 + bf16},
+        "setup_s": round(setup_s, 1),
+    }
+    del setup
+    torch.cuda.empty_cache()
+    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (prologue, split, merge) us: "
+        f"{', '.join(f'{x * 1e3:.2f}' for x in kern)}")
+    if not args.no_bf16:
+        log("timing the BF16 baseline")
+        bms, bbytes = time_bf16(w, batch, context, args.steps, args.warmup, True)
+        dec_ms = float(sum(kern))
+        result["bf16_baseline"] = {"ms_per_step": round(bms, 5), "GB_per_s": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                                   "bytes": bbytes, "speedup_step": round(bms / ms, 3),
+                                   "speedup_decode_only": round(bms / dec_ms, 3)}
+        torch.cuda.empty_cache()
+    if not args.no_bs32:
+        log("batch-32 companion measurement")
+        w32 = synth.workload(3)
+        c32 = 32_768
+        est = 32 * 8 * (c32 - 320) * 72
+        s32 = Int2Setup(w32, 32, c32, max(2, math.ceil(1.0e9 / est)), args.steps + args.warmup, fast_inputs=True)
+        ms32, k32, mode32 = time_int2(s32, args.steps, args.warmup, args.eager)
+        i2, b2, d2 = s32.bytes_per_step()
+        result["bs32"] = {"workload": "paged batch 32 x 32,768 tokens, demote in step", "ms_per_step": round(ms32, 5),
+                          "us_per_step": round(ms32 * 1e3, 2), "GB_per_s": round((i2 + b2 + d2) / (ms32 * 1e-3) / 1e9, 1),
+                          "tokens_per_s": round(32 / (ms32 * 1e-3), 1),
+                          "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
+                          "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "kernel_ms": [round(float(x), 5) for x in k32]}
+        del s32
+        torch.cuda.empty_cache()
+        if not args.no_bf16:
+            bms32, bb32 = time_bf16(w32, 32, c32, args.steps, args.warmup, True)
+            result["bs32"]["bf16_baseline_ms"] = round(bms32, 5)
+            result["bs32"]["speedup_step"] = round(bms32 / ms32, 3)
+            torch.cuda.empty_cache()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(w, context)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,377 @@
+// C ABI of the OSCAR gfx950 library (declared and documented in include/oscar.h): host-side
+// validation, workspace planning and kernel launches. Nothing here touches device memory.
+#include <math.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace oscar;
+
+namespace {
+
+constexpr int kTargetWorkgroups = 1536;  // ~6 per CU on 256 CUs
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+oscar_status_t check_layout(const oscar_layout_t* L) {
+  if (!L) return OSCAR_ERR_INVALID_ARG;
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0 || L->num_q_heads % L->num_kv_heads) return OSCAR_ERR_INVALID_ARG;
+  if (L->head_dim <= 0 || L->group_size <= 0 || L->head_dim % L->group_size) return OSCAR_ERR_INVALID_ARG;
+  if (L->sink_len < 0 || L->recent_len <= 0 || L->page_size <= 0) return OSCAR_ERR_INVALID_ARG;
+  if (L->mixed != 0 && L->mixed != 1) return OSCAR_ERR_INVALID_ARG;
+  if (L->pool_pages < 0) return OSCAR_ERR_INVALID_ARG;
+  if (L->mixed && (L->int4_page_offset < 0 || L->int4_page_offset > L->pool_pages)) return OSCAR_ERR_INVALID_ARG;
+  const float clips[4] = {L->clip_k, L->clip_v, L->clip_k4, L->clip_v4};
+  for (float c : clips)
+    if (!(c > 0.0f && c <= 1.0f)) return OSCAR_ERR_INVALID_ARG;
+  const int gq = L->num_q_heads / L->num_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8) return OSCAR_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return OSCAR_ERR_UNSUPPORTED;
+  if (L->group_size != L->head_dim) return OSCAR_ERR_UNSUPPORTED;
+  if (L->page_size != kPage) return OSCAR_ERR_UNSUPPORTED;
+  if (L->sink_len % kPage || L->recent_len % kPage || L->sink_len > 256 || L->recent_len > 1024)
+    return OSCAR_ERR_UNSUPPORTED;
+  return OSCAR_OK;
+}
+
+Dims make_dims(const oscar_layout_t* L, int batch, int max_seq_len, int pt_stride) {
+  Dims d;
+  d.batch = batch;
+  d.hq = L->num_q_heads;
+  d.hkv = L->num_kv_heads;
+  d.gq = L->num_q_heads / L->num_kv_heads;
+  d.d = L->head_dim;
+  d.sink = L->sink_len;
+  d.recent = L->recent_len;
+  d.wpages = (L->sink_len + L->recent_len) / kPage;
+  d.mixed = L->mixed;
+  d.off4 = L->mixed ? L->int4_page_offset : L->pool_pages;
+  d.pool_pages = L->pool_pages;
+  d.max_seq_len = max_seq_len;
+  d.pt_stride = pt_stride;
+  return d;
+}
+
+int choose_ppw(int64_t total_pages) {
+  int64_t p = (total_pages + 4LL * kTargetWorkgroups - 1) / (4LL * kTargetWorkgroups);
+  if (p < 1) p = 1;
+  if (p > 64) p = 64;
+  return (int)p;
+}
+
+struct DecodePlan {
+  int ppw, s2, s4, nwin, ns;
+  size_t off_q, off_qsc, off_po, off_pl, total;
+};
+
+DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len) {
+  DecodePlan p;
+  int hist = max_seq_len - L->sink_len - L->recent_len;
+  if (hist < 0) hist = 0;
+  const int hp = (hist + kPage - 1) / kPage;
+  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * hp);
+  p.s2 = (hp + 4 * p.ppw - 1) / (4 * p.ppw);
+  p.s4 = L->mixed ? p.s2 : 0;
+  p.nwin = ((L->sink_len + L->recent_len) / kPage + 3) / 4;
+  while (p.s2 + p.s4 > kMaxSlots && p.ppw < 64) {
+    p.ppw = p.ppw * 2 > 64 ? 64 : p.ppw * 2;
+    p.s2 = (hp + 4 * p.ppw - 1) / (4 * p.ppw);
+    p.s4 = L->mixed ? p.s2 : 0;
+  }
+  p.ns = p.nwin + p.s2 + p.s4;
+  const size_t bhq = (size_t)batch * L->num_q_heads;
+  const int gq = L->num_q_heads / L->num_kv_heads;
+  p.off_q = kAlign;
+  p.off_qsc = p.off_q + 4 * align_up(bhq * L->head_dim * 2);
+  p.off_po = p.off_qsc + align_up(bhq * 16);
+  const size_t nsl = (size_t)batch * L->num_kv_heads * p.ns * gq;
+  p.off_pl = p.off_po + align_up(nsl * L->head_dim * 4);
+  p.total = p.off_pl + align_up(nsl * 4);
+  return p;
+}
+
+struct Bf16Plan {
+  int ppw, s;
+  size_t off_po, off_pl, total;
+};
+
+Bf16Plan plan_bf16(const oscar_layout_t* L, int batch, int max_seq_len) {
+  Bf16Plan p;
+  const int pages = (max_seq_len + kPage - 1) / kPage;
+  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * pages);
+  p.s = (pages + 4 * p.ppw - 1) / (4 * p.ppw);
+  // fewer splits when the merge could not hold them all
+  while (p.s > kMaxSlots && p.ppw < 64) {
+    p.ppw *= 2;
+    p.s = (pages + 4 * p.ppw - 1) / (4 * p.ppw);
+  }
+  if (p.s < 1) p.s = 1;
+  const int gq = L->num_q_heads / L->num_kv_heads;
+  const size_t nsl = (size_t)batch * L->num_kv_heads * p.s * gq;
+  p.off_po = kAlign;
+  p.off_pl = p.off_po + align_up(nsl * L->head_dim * 4);
+  p.total = p.off_pl + align_up(nsl * 4);
+  return p;
+}
+
+size_t page_bytes(const oscar_layout_t* L, int bits) {
+  if (bits == 16) return (size_t)L->num_kv_heads * bf16_page_head_bytes(L->head_dim);
+  return (size_t)L->num_kv_heads * qpage_head_bytes(L->head_dim, bits);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(oscar_status_t s) {
+  switch (s) {
+    case OSCAR_OK: return "OSCAR_OK";
+    case OSCAR_ERR_INVALID_ARG: return "OSCAR_ERR_INVALID_ARG";
+    case OSCAR_ERR_UNSUPPORTED: return "OSCAR_ERR_UNSUPPORTED";
+    case OSCAR_ERR_WORKSPACE: return "OSCAR_ERR_WORKSPACE";
+    case OSCAR_ERR_LAUNCH: return "OSCAR_ERR_LAUNCH";
+  }
+  return "OSCAR_ERR_UNKNOWN";
+}
+
+const char* oscar_version(void) { return "oscar-mi355x 0.1.0 gfx950"; }
+
+size_t oscar_page_bytes(const oscar_layout_t* L, int32_t bits) {
+  if (check_layout(L) != OSCAR_OK || (bits != 2 && bits != 4 && bits != 16)) return 0;
+  return page_bytes(L, bits);
+}
+
+size_t oscar_window_bytes(const oscar_layout_t* L, int32_t batch) {
+  if (check_layout(L) != OSCAR_OK || batch < 0) return 0;
+  return (size_t)batch * L->num_kv_heads * ((L->sink_len + L->recent_len) / kPage) * bf16_page_head_bytes(L->head_dim);
+}
+
+size_t oscar_pool_bytes(const oscar_layout_t* L) {
+  if (check_layout(L) != OSCAR_OK) return 0;
+  if (!L->mixed) return (size_t)L->pool_pages * page_bytes(L, 2);
+  return (size_t)L->int4_page_offset * page_bytes(L, 2) + (size_t)(L->pool_pages - L->int4_page_offset) * page_bytes(L, 4);
+}
+
+oscar_status_t oscar_quantize_pack(int64_t rows, int32_t dim, int32_t group, int32_t bits, float clip, const float* x,
+                                   uint8_t* codes, uint16_t* scale_zero, hipStream_t stream) {
+  if (rows < 0 || dim <= 0 || group <= 0 || dim % group) return OSCAR_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 4) return OSCAR_ERR_INVALID_ARG;
+  if (group % (8 / bits)) return OSCAR_ERR_INVALID_ARG;
+  if (!(clip > 0.0f && clip <= 1.0f)) return OSCAR_ERR_INVALID_ARG;
+  if (dim > 1024) return OSCAR_ERR_UNSUPPORTED;
+  if (rows == 0) return OSCAR_OK;
+  if (!x || !codes || !scale_zero) return OSCAR_ERR_INVALID_ARG;
+  return launch_quantize_pack(rows, dim, group, bits, clip, x, codes, scale_zero, stream) == hipSuccess
+             ? OSCAR_OK
+             : OSCAR_ERR_LAUNCH;
+}
+
+oscar_status_t oscar_kv_prefill(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
+                                const void* k, const void* v, const uint8_t* token_bits, const float* rot_k,
+                                const float* rot_v, void* pool, const int32_t* page_table, const int32_t* page_table4,
+                                int32_t pt_stride, void* window, int32_t* n_int4_out, hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || pt_stride < 0) return OSCAR_ERR_INVALID_ARG;
+  if (batch == 0) return OSCAR_OK;
+  if (!seq_len || !k || !v || !rot_k || !rot_v || !window) return OSCAR_ERR_INVALID_ARG;
+  const int hist_max = max_seq_len - L->sink_len - L->recent_len;
+  if (hist_max > 0) {
+    if (!pool || !page_table || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
+    if (L->mixed && !page_table4) return OSCAR_ERR_INVALID_ARG;
+  }
+  CacheWriteArgs a{};
+  a.dm = make_dims(L, batch, max_seq_len, pt_stride);
+  a.seq_len = seq_len;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bits = L->mixed ? token_bits : nullptr;
+  a.rot_k = rot_k;
+  a.rot_v = rot_v;
+  a.clip_k = L->clip_k;
+  a.clip_v = L->clip_v;
+  a.clip_k4 = L->clip_k4;
+  a.clip_v4 = L->clip_v4;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.pt2 = page_table;
+  a.pt4 = page_table4;
+  a.window = static_cast<uint8_t*>(window);
+  a.n_int4_out = n_int4_out;
+  return launch_prefill(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+}
+
+oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int32_t* seq_len, const int32_t* n_int4,
+                               const void* new_k, const void* new_v, const uint8_t* demote_bits, const float* rot_k,
+                               const float* rot_v, void* pool, const int32_t* page_table, const int32_t* page_table4,
+                               int32_t pt_stride, void* window, int32_t* seq_len_out, int32_t* n_int4_out,
+                               hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
+  if (batch == 0) return OSCAR_OK;
+  if (!seq_len || !new_k || !new_v || !rot_k || !rot_v || !pool || !page_table || !window) return OSCAR_ERR_INVALID_ARG;
+  if (L->mixed && !page_table4) return OSCAR_ERR_INVALID_ARG;
+  if (seq_len_out && (const void*)seq_len_out == (const void*)seq_len) return OSCAR_ERR_INVALID_ARG;
+  if (n_int4_out && n_int4 && (const void*)n_int4_out == (const void*)n_int4) return OSCAR_ERR_INVALID_ARG;
+  CacheWriteArgs a{};
+  a.dm = make_dims(L, batch, 0, pt_stride);
+  a.seq_len = seq_len;
+  a.n_int4 = n_int4;
+  a.k = static_cast<const uint16_t*>(new_k);
+  a.v = static_cast<const uint16_t*>(new_v);
+  a.bits = L->mixed ? demote_bits : nullptr;
+  a.rot_k = rot_k;
+  a.rot_v = rot_v;
+  a.clip_k = L->clip_k;
+  a.clip_v = L->clip_v;
+  a.clip_k4 = L->clip_k4;
+  a.clip_v4 = L->clip_v4;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.pt2 = page_table;
+  a.pt4 = page_table4;
+  a.window = static_cast<uint8_t*>(window);
+  a.seq_len_out = seq_len_out;
+  a.n_int4_out = n_int4_out;
+  return launch_demote(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len) {
+  if (check_layout(L) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
+  return plan_decode(L, batch, max_seq_len).total;
+}
+
+static oscar_status_t decode_impl(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
+                                  const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
+                                  const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                  const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
+                                  size_t workspace_bytes, float* out, hipEvent_t* events, hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || pt_stride < 0 || !(softmax_scale >= 0.0f)) return OSCAR_ERR_INVALID_ARG;
+  if (batch == 0) return OSCAR_OK;
+  if (!q || !seq_len || !window || !rot_k || !rot_v || !out) return OSCAR_ERR_INVALID_ARG;
+  const int hist_max = max_seq_len - L->sink_len - L->recent_len;
+  if (hist_max > 0) {
+    if (!pool || !page_table || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
+    if (L->mixed && !page_table4) return OSCAR_ERR_INVALID_ARG;
+  }
+  const DecodePlan p = plan_decode(L, batch, max_seq_len);
+  if (p.s2 + p.s4 > kMaxSlots) return OSCAR_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < p.total) return OSCAR_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t qbytes = align_up((size_t)batch * L->num_q_heads * L->head_dim * 2);
+  DecodeArgs a{};
+  a.dm = make_dims(L, batch, max_seq_len, pt_stride);
+  a.q = static_cast<const uint16_t*>(q);
+  a.seq_len = seq_len;
+  a.n_int4 = L->mixed ? n_int4 : nullptr;
+  a.window = static_cast<const uint8_t*>(window);
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.pt2 = page_table;
+  a.pt4 = page_table4;
+  a.rot_k = rot_k;
+  a.rot_v = rot_v;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)L->head_dim);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.out = out;
+  a.ws.flags = reinterpret_cast<uint32_t*>(ws);
+  a.ws.qh2 = reinterpret_cast<uint16_t*>(ws + p.off_q);
+  a.ws.ql2 = reinterpret_cast<uint16_t*>(ws + p.off_q + qbytes);
+  a.ws.qh4 = reinterpret_cast<uint16_t*>(ws + p.off_q + 2 * qbytes);
+  a.ws.ql4 = reinterpret_cast<uint16_t*>(ws + p.off_q + 3 * qbytes);
+  a.ws.qsc = reinterpret_cast<float*>(ws + p.off_qsc);
+  a.ws.part_o = reinterpret_cast<float*>(ws + p.off_po);
+  a.ws.part_lse = reinterpret_cast<float*>(ws + p.off_pl);
+  a.ws.ns = p.ns;
+  a.ws.nwin = p.nwin;
+  a.ws.s2 = p.s2;
+  a.ws.s4 = p.s4;
+  a.ws.ppw = p.ppw;
+  a.events = events;
+  return launch_decode(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+}
+
+oscar_status_t oscar_decode_attn(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
+                                 const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
+                                 const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                 const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, float* out, hipStream_t stream) {
+  return decode_impl(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
+                     rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, nullptr, stream);
+}
+
+oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len,
+                                          const void* q, const int32_t* seq_len, const int32_t* n_int4,
+                                          const void* window, const void* pool, const int32_t* page_table,
+                                          const int32_t* page_table4, int32_t pt_stride, const float* rot_k,
+                                          const float* rot_v, float softmax_scale, void* workspace,
+                                          size_t workspace_bytes, float* out, hipEvent_t* events, int32_t n_events,
+                                          hipStream_t stream) {
+  if (!events || n_events < 4) return OSCAR_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return OSCAR_ERR_INVALID_ARG;
+  return decode_impl(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
+                     rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, events, stream);
+}
+
+oscar_status_t oscar_bf16_fill(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
+                               const void* k, const void* v, void* pages, int64_t num_pages,
+                               const int32_t* page_table, int32_t pt_stride, hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || num_pages < 0) return OSCAR_ERR_INVALID_ARG;
+  if (batch == 0 || max_seq_len == 0) return OSCAR_OK;
+  if (!seq_len || !k || !v || !pages || !page_table) return OSCAR_ERR_INVALID_ARG;
+  if (pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
+  Bf16Args a{};
+  a.dm = make_dims(L, batch, max_seq_len, pt_stride);
+  a.dm.pool_pages = num_pages;
+  a.seq_len = seq_len;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.pages = static_cast<uint8_t*>(pages);
+  a.pt = page_table;
+  return launch_bf16_fill(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+}
+
+size_t oscar_bf16_decode_workspace_bytes(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len) {
+  if (check_layout(L) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
+  return plan_bf16(L, batch, max_seq_len).total;
+}
+
+oscar_status_t oscar_bf16_decode_attn(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
+                                      const int32_t* seq_len, const void* pages, int64_t num_pages,
+                                      const int32_t* page_table, int32_t pt_stride, float softmax_scale,
+                                      void* workspace, size_t workspace_bytes, float* out, hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || num_pages < 0 || pt_stride < 0 || !(softmax_scale >= 0.0f))
+    return OSCAR_ERR_INVALID_ARG;
+  if (batch == 0) return OSCAR_OK;
+  if (!q || !seq_len || !pages || !page_table || !out) return OSCAR_ERR_INVALID_ARG;
+  if (pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
+  const Bf16Plan p = plan_bf16(L, batch, max_seq_len);
+  if (p.s > kMaxSlots) return OSCAR_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < p.total) return OSCAR_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  Bf16Args a{};
+  a.dm = make_dims(L, batch, max_seq_len, pt_stride);
+  a.dm.pool_pages = num_pages;
+  a.q = static_cast<const uint16_t*>(q);
+  a.seq_len = seq_len;
+  a.pages = static_cast<uint8_t*>(const_cast<void*>(pages));
+  a.pt = page_table;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)L->head_dim);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.out = out;
+  a.flags = reinterpret_cast<uint32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(ws + p.off_po);
+  a.part_lse = reinterpret_cast<float*>(ws + p.off_pl);
+  a.s = p.s;
+  a.ppw = p.ppw;
+  return launch_bf16_decode(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+}
+
+}  // extern "C"

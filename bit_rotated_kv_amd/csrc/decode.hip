@@ -1,0 +1,915 @@
+// Decode attention over the three-segment cache (OSCAR overview page, method paragraph: the INT2
+// kernel unpacks codes, restores scale/zero and accumulates in floating point, the BF16 kernel
+// handles sink/recent, an online-softmax merge combines them; news article: keys stored as x.R_K,
+// values as v.R_V). TriAxialKV reading note, section 4: bitwidth-homogeneous splits (INT2 pages,
+// INT4 pages) merged by log-sum-exp.
+//
+// Kernels of one decode call, in stream order:
+//   q_prologue   q' = (q . R_K) * scale * log2(e) per query head, split into fp16 high/low
+//                matrix-core operands scaled per channel for the code unpacking below
+//   split        one launch, three homogeneous roles by workgroup index: BF16 window pages
+//                (sink + recent), INT2 history pages, INT4 history pages (mixed caches); each
+//                workgroup = 4 wavefronts and writes one (o, lse) partial per query head
+//   merge        per query head: LSE-merge the history partials (rotated basis), apply R_V^T,
+//                LSE-merge with the BF16 window partials, write the fp32 output
+//
+// Matrix-core mapping (v_mfma_f32_16x16x32_f16 for QK^T, v_mfma_f32_16x16x16_f16 for PV; BF16
+// variants for the window): the 16 tokens of a page on the M rows of QK^T, the query heads of the
+// GQA group on the N columns. The QK^T result layout (lane l holds tokens 4*(l/16)+r of head
+// l%16) is exactly the A-operand layout of PV (rows = heads, k = tokens), so the softmax weights
+// never leave their lanes. Codes reach the matrix cores as fp16 subnormals: masking a code c at
+// bit p of a half-word gives the fp16 value c * 2^(p-24); the 2^(24-p) factor is folded into the
+// query operand (keys) or applied once to the accumulator (values). Query and softmax weights are
+// split into high + low fp16 parts (~22 significant bits); the pair sits in spare rows (PV) or in
+// a second MFMA (QK^T). Each wavefront keeps the next page's loads in flight while it computes
+// the current one, with all its page ids fetched by one vector load up front.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace oscar {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kHistPipe = 4;   // history pages in the per-wave load ring
+constexpr int kBf16Pipe = 2;   // BF16 pages in the per-wave load ring (8 KB each)
+
+__device__ __forceinline__ float4_t mfma32_f16(const u32x4_t& a, const half8_t& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma16_f16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
+  const u32x2_t av = {a0, a1}, bv = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), __builtin_bit_cast(half4_t, bv), c,
+                                               0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma32_bf16(const u32x4_t& a, const u32x4_t& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma16_bf16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
+  const u32x2_t av = {a0, a1}, bv = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, av), __builtin_bit_cast(short4_t, bv),
+                                                   c, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t row_shr_or_zero(uint32_t v) {
+  if constexpr (N >= 16) return 0u;
+  else return dpp_row_shr<N>(v);
+}
+
+// ------------------------------------------------------------------ split bookkeeping
+struct HistCounts {
+  int T, hist, n2, n4;
+};
+__device__ inline HistCounts hist_counts(const DecodeArgs& a, int b) {
+  HistCounts c;
+  int T = a.seq_len[b];
+  T = T < 0 ? 0 : (T > a.dm.max_seq_len ? a.dm.max_seq_len : T);
+  c.T = T;
+  c.hist = max(0, T - a.dm.sink - a.dm.recent);
+  int n4 = (a.dm.mixed && a.n_int4) ? a.n_int4[b] : 0;
+  n4 = n4 < 0 ? 0 : (n4 > c.hist ? c.hist : n4);
+  c.n4 = n4;
+  c.n2 = c.hist - n4;
+  return c;
+}
+
+// ------------------------------------------------------------------ query prologue
+// One workgroup per (kv-head, request). Thread (j, part) holds its part of column j of R_K in
+// registers (all loads issued together) and forms the partial dot products of every query head
+// of the group.
+template <int D>
+__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
+  constexpr int NP = 256 / D;      // parts of a column
+  constexpr int RP = D / NP;       // rows per part
+  __shared__ float qs[8][D];
+  __shared__ float part_s[NP][8][D];
+  __shared__ float qr[8][D];
+  const Dims& dm = a.dm;
+  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int gq = dm.gq;
+  const size_t row0 = (size_t)b * dm.hq + (size_t)kv * gq;
+  const int j = tid % D, part = tid / D;
+  float rc[RP];
+  const float* rot = a.rot_k + (size_t)kv * D * D;
+#pragma unroll
+  for (int i = 0; i < RP; ++i) rc[i] = rot[(part * RP + i) * D + j];
+  for (int idx = tid; idx < gq * D; idx += 256) qs[idx / D][idx % D] = bf16_bits_to_f32(a.q[row0 * D + idx]);
+  __syncthreads();
+  for (int h = 0; h < gq; ++h) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) acc = fmaf(qs[h][part * RP + i], rc[i], acc);
+    part_s[part][h][j] = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < gq * D; idx += 256) {
+    const int h = idx / D, jj = idx % D;
+    float s = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) s += part_s[p][h][jj];
+    qr[h][jj] = s * a.scale_log2e;
+  }
+  __syncthreads();
+  for (int h = wave; h < gq; h += 4) {
+    const size_t qi = row0 + h;
+    float sum = 0.0f, m2 = 0.0f, m4 = 0.0f;
+    for (int jj = lane; jj < D; jj += kWave) {
+      const float v = qr[h][jj];
+      const int m = (jj % 8) / 2;
+      sum += v;
+      m2 = fmaxf(m2, ldexpf(fabsf(v), 24 - 2 * m));
+      m4 = fmaxf(m4, ldexpf(fabsf(v), 24 - 4 * (m % 2)));
+    }
+    sum = wave_sum(sum);
+    m2 = wave_max(m2);
+    m4 = wave_max(m4);
+    int e2 = 0, e4 = 0;
+    if (m2 > 0.0f) { frexpf(m2, &e2); e2 -= 15; }
+    if (m4 > 0.0f) { frexpf(m4, &e4); e4 -= 15; }
+    for (int jj = lane; jj < D; jj += kWave) {
+      const float v = qr[h][jj];
+      const int m = (jj % 8) / 2;
+      const float q2 = ldexpf(v, 24 - 2 * m - e2);
+      const uint32_t h2 = f32_to_f16_bits(q2);
+      a.ws.qh2[qi * D + jj] = (uint16_t)h2;
+      a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(q2 - f16_bits_to_f32(h2));
+      if (dm.mixed) {
+        const float q4 = ldexpf(v, 24 - 4 * (m % 2) - e4);
+        const uint32_t h4 = f32_to_f16_bits(q4);
+        a.ws.qh4[qi * D + jj] = (uint16_t)h4;
+        a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(q4 - f16_bits_to_f32(h4));
+      }
+    }
+    if (lane == 0) {
+      a.ws.qsc[qi * 4 + 0] = sum;
+      a.ws.qsc[qi * 4 + 1] = ldexpf(1.0f, e2);
+      a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e4);
+      a.ws.qsc[qi * 4 + 3] = 0.0f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ per-wave softmax state
+template <int D, int GQ>
+struct WaveState {
+  float m_run, l_part, z_part;
+  float4_t o[D / 16];
+  __device__ void init() {
+    m_run = kNegInf;
+    l_part = 0.0f;
+    z_part = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) o[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+};
+
+// Online-softmax update for one page given the 4 logits of this lane (tokens 4g+r of head
+// h = lane%16); returns the 4 probabilities. Rescales only when the page max exceeds the running
+// max by more than 8 (log2 units), so probabilities stay below 2^8.
+template <int D, int GQ>
+__device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float lg[4], float p[4], int lane) {
+  const int h = lane % 16, g = lane / 16;
+  float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const bool need = (h < GQ) && (mx > st.m_run + 8.0f);
+  if (__any(need)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = (st.m_run == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.l_part *= alpha;
+    st.z_part *= alpha;
+    st.m_run = m_new;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, (4 * g + r) % GQ, kWave);
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) st.o[nb][r] *= ar;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = (h < GQ && lg[r] != kNegInf) ? __builtin_amdgcn_exp2f(lg[r] - st.m_run) : 0.0f;
+}
+
+// Writes the wave's state to LDS and merges the 4 waves of the workgroup into one partial
+// (o normalised, lse in log2 units). VSH_BITS selects the value-code scale restore.
+template <int D, int GQ, int VSH_BITS, bool REDIST = false>
+__device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
+                                float* part_o, float* part_lse) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, h = lane % 16;
+  float l_tot = st.l_part, z_tot = st.z_part;
+  if constexpr (REDIST) {
+    // lanes c, c+GQ, ... of a row share a head: fold them first
+#pragma unroll
+    for (int o = GQ; o < 16; o <<= 1) {
+      l_tot += __shfl_xor(l_tot, o, kWave);
+      z_tot += __shfl_xor(z_tot, o, kWave);
+    }
+  }
+  l_tot += __shfl_xor(l_tot, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  z_tot += __shfl_xor(z_tot, 16, kWave);
+  z_tot += __shfl_xor(z_tot, 32, kWave);
+  if (g == 0 && h < GQ) {
+    st_lds[wave][0][h] = st.m_run;
+    st_lds[wave][1][h] = l_tot;
+    st_lds[wave][2][h] = z_tot;
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
+    }
+  __syncthreads();
+  for (int idx = tid; idx < GQ * D; idx += 256) {
+    const int hh = idx / D, ch = idx % D, nb = ch / 16;
+    float M = kNegInf;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, st_lds[w][0][hh]);
+    float L = 0.0f, Z = 0.0f, O = 0.0f;
+    if (M != kNegInf) {
+      for (int w = 0; w < 4; ++w) {
+        const float mw = st_lds[w][0][hh];
+        if (mw == kNegInf) continue;
+        const float aw = exp2f(mw - M);
+        L += aw * st_lds[w][1][hh];
+        Z += aw * st_lds[w][2][hh];
+        O += aw * (o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch]);
+      }
+    }
+    float vscale = 1.0f;
+    if (VSH_BITS == 2) vscale = ldexpf(1.0f, 24 - 2 * (nb % 4));
+    if (VSH_BITS == 4) vscale = ldexpf(1.0f, 24 - 4 * (nb % 2));
+    const bool empty = (M == kNegInf) || !(L > 0.0f);
+    part_o[hh * D + ch] = empty ? 0.0f : (O * vscale + Z) / L;
+    if (ch == 0) part_lse[hh] = empty ? kNegInf : M + log2f(L);
+  }
+}
+
+// ------------------------------------------------------------------ page pipeline
+// Runs proc(buf, pg) for pg in [wp0, wp1) while the loads of the next NB-1 pages are in flight.
+// Buffers are indexed by compile-time constants (the ring is fully unrolled), and every load is
+// issued unconditionally -- out-of-range prefetches read a fixed dummy page-head that stays in
+// cache -- so the compiler waits exactly for the buffer about to be used.
+template <int NB, typename Page, typename LoadF, typename ProcF>
+__device__ __forceinline__ void page_pipeline(int wp0, int wp1, LoadF&& load, ProcF&& proc) {
+  Page buf[NB];
+  bool ok[NB];
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k) ok[k] = load(buf[k], wp0 + k);
+  for (int pg = wp0; pg < wp1; pg += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
+      if (pg + k < wp1) proc(buf[k], ok[k], pg + k);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ BF16 page-heads
+template <int D>
+struct Bf16Page {
+  u32x4_t ka[D / 32];  // key lane chunk: 8 bf16 per k-step
+  u32x4_t va[D / 32];  // value lane chunk: two 16-channel blocks per uint4
+};
+
+template <int D>
+__device__ __forceinline__ void load_bf16_page(Bf16Page<D>& pr, const uint8_t* ph, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) pr.ka[kk] = *reinterpret_cast<const u32x4_t*>(ph + lane * (D / 2) + 16 * kk);
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) pr.va[j] = *reinterpret_cast<const u32x4_t*>(ph + 32 * D + lane * (D / 2) + 16 * j);
+}
+
+template <int D, int GQ>
+__device__ __forceinline__ void process_bf16_page(WaveState<D, GQ>& st, const Bf16Page<D>& pr, const u32x4_t* bq,
+                                                  const bool valid[4], float sl2e, int lane) {
+  const int h = lane % 16;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) acc = mfma32_bf16(pr.ka[kk], bq[kk], acc);
+  float lg[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lg[r] = valid[r] ? acc[r] * sl2e : kNegInf;
+  float p[4];
+  softmax_page<D, GQ>(st, lg, p, lane);
+  st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hb[r] = f32_to_bf16_bits(p[r]);
+    lb[r] = f32_to_bf16_bits(p[r] - bf16_bits_to_f32(hb[r]));
+  }
+  const uint32_t l01 = lb[0] | (lb[1] << 16), l23 = lb[2] | (lb[3] << 16);
+  const uint32_t s01 = row_shr_or_zero<GQ>(l01), s23 = row_shr_or_zero<GQ>(l23);
+  const uint32_t a01 = h < GQ ? (hb[0] | (hb[1] << 16)) : (h < 2 * GQ ? s01 : 0u);
+  const uint32_t a23 = h < GQ ? (hb[2] | (hb[3] << 16)) : (h < 2 * GQ ? s23 : 0u);
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    const u32x4_t& v = pr.va[nb / 2];
+    const uint32_t b0 = (nb & 1) ? v[2] : v[0];
+    const uint32_t b1 = (nb & 1) ? v[3] : v[1];
+    st.o[nb] = mfma16_bf16(a01, a23, b0, b1, st.o[nb]);
+  }
+}
+
+template <int D, int GQ>
+__device__ __forceinline__ void load_bf16_query(u32x4_t* bq, const uint16_t* q, size_t qrow_base, int lane) {
+  const int g = lane / 16, h = lane % 16;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    bq[kk] = u32x4_t{0, 0, 0, 0};
+    if (h < GQ) bq[kk] = *reinterpret_cast<const u32x4_t*>(q + (qrow_base + h) * D + 32 * kk + 8 * g);
+  }
+}
+
+// Window role: workgroup wi of (b, kv) covers window pages 4*wi .. 4*wi+3, one per wavefront.
+template <int D, int GQ>
+__device__ void window_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8]) {
+  const Dims& dm = a.dm;
+  const int nw = a.ws.nwin;
+  const int wi = idx % nw, bk = idx / nw, kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
+  int T = a.seq_len[b];
+  T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
+  u32x4_t bq[D / 32];
+  load_bf16_query<D, GQ>(bq, a.q, (size_t)b * dm.hq + (size_t)kv * GQ, lane);
+  WaveState<D, GQ> st;
+  st.init();
+  const int pg = 4 * wi + wave;
+  if (pg < dm.wpages) {
+    const uint8_t* ph = a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + pg) * bf16_page_head_bytes(D);
+    Bf16Page<D> pr;
+    load_bf16_page<D>(pr, ph, lane);
+    bool valid[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * g + r;
+      if (pg < dm.sink / kPage) {
+        valid[r] = kPage * pg + t < T;
+      } else if (T <= dm.sink) {
+        valid[r] = false;
+      } else {
+        const int sl = kPage * (pg - dm.sink / kPage) + t;
+        int back = (T - 1 - sl) % dm.recent;
+        if (back < 0) back += dm.recent;
+        valid[r] = T - 1 - back >= dm.sink;
+      }
+    }
+    process_bf16_page<D, GQ>(st, pr, bq, valid, a.scale_log2e, lane);
+  }
+  const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + wi;
+  workgroup_merge<D, GQ, 16>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D, a.ws.part_lse + pbase * GQ);
+}
+
+// ------------------------------------------------------------------ INT2 / INT4 history pages
+// For GQA widths 4 and 8 the QK^T result is redistributed with DPP so that every lane owns whole
+// (token, head) logits (1 per lane at GQ 4, 2 at GQ 8); each lane then loads only its own tokens'
+// scale/zero and the softmax arithmetic runs on all 64 lanes. The PV operand is gathered back
+// with DPP. Widths 1 and 2 keep the QK^T result layout (4 tokens per lane on the first GQ lanes
+// of each row).
+template <int GQ>
+struct Redist {
+  static constexpr bool on = GQ == 4 || GQ == 8;
+  static constexpr int per_lane = GQ == 8 ? 2 : 1;   // logits per lane when redistributed
+  static constexpr int meta_words = GQ == 4 ? 2 : (GQ == 8 ? 4 : 8);
+};
+
+template <int BITS, int D, int GQ>
+struct QPage {
+  static constexpr int CW = D * BITS / 128;  // 32-bit words of one lane-chunk part
+  uint32_t kw[CW], vw[CW];
+  uint32_t mt[Redist<GQ>::meta_words];
+};
+
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, const uint8_t* ph, int lane) {
+  constexpr int CW = QPage<BITS, D, GQ>::CW;
+  const int g = lane / 16, c = lane % 16;
+  if constexpr (CW == 1) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(ph + lane * 8);
+    pr.kw[0] = v[0];
+    pr.vw[0] = v[1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2 * CW / 4; ++j) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ph + lane * 8 * CW + 16 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = 4 * j + e;
+        if (w < CW) pr.kw[w] = v[e];
+        else pr.vw[w - CW] = v[e];
+      }
+    }
+  }
+  const uint8_t* meta = ph + 4 * D * BITS;
+  if constexpr (GQ == 4) {
+    const u32x2_t m = *reinterpret_cast<const u32x2_t*>(meta + 8 * (4 * g + c / 4));
+    pr.mt[0] = m[0];
+    pr.mt[1] = m[1];
+  } else if constexpr (GQ == 8) {
+    const u32x4_t m = *reinterpret_cast<const u32x4_t*>(meta + 8 * (4 * g + 2 * (c / 8)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr.mt[e] = m[e];
+  } else {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(meta + 32 * g);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(meta + 32 * g + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pr.mt[e] = a[e];
+      pr.mt[4 + e] = b[e];
+    }
+  }
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// fp16 high part in the low half, fp16 low part (W - high) in the high half
+__device__ __forceinline__ uint32_t split_f16(float w) {
+  const uint32_t h = f32_to_f16_bits(w);
+  return h | (f32_to_f16_bits(w - f16_bits_to_f32(h)) << 16);
+}
+
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const half8_t* bhi, const half8_t* blo) {
+  constexpr int NKK = D / 32;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4_t av;
+    if constexpr (BITS == 2) {
+      const uint32_t w = (kk & 1) ? (pr.kw[kk / 2] >> 8) : pr.kw[kk / 2];
+      av[0] = w & 0x00030003u;
+      av[1] = w & 0x000C000Cu;
+      av[2] = w & 0x00300030u;
+      av[3] = w & 0x00C000C0u;
+    } else {
+      const uint32_t w = pr.kw[kk], w1 = pr.kw[kk] >> 8;
+      av[0] = w & 0x000F000Fu;
+      av[1] = w & 0x00F000F0u;
+      av[2] = w1 & 0x000F000Fu;
+      av[3] = w1 & 0x00F000F0u;
+    }
+    acc = mfma32_f16(av, bhi[kk], acc);
+    acc = mfma32_f16(av, blo[kk], acc);
+  }
+  return acc;
+}
+
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void pv_page(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, uint32_t a01,
+                                        uint32_t a23) {
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    uint32_t b0, b1;
+    if constexpr (BITS == 2) {
+      const uint32_t w = pr.vw[nb / 4];
+      const uint32_t mask = 0x00030003u << (2 * (nb % 4));
+      b0 = w & mask;
+      b1 = (w >> 8) & mask;
+    } else {
+      const uint32_t w = pr.vw[nb / 2];
+      const uint32_t mask = 0x000F000Fu << (4 * (nb % 2));
+      b0 = w & mask;
+      b1 = (w >> 8) & mask;
+    }
+    st.o[nb] = mfma16_f16(a01, a23, b0, b1, st.o[nb]);
+  }
+}
+
+// Rescale of the PV accumulators by alpha of each row's head. Row 4*g+r of the accumulators is
+// head (4g+r) mod GQ (rows GQ..2GQ-1 hold the low parts of heads 0..GQ-1); alpha of head hh is
+// read from a lane that owns hh.
+template <int D, int GQ>
+__device__ __forceinline__ void rescale_rows(WaveState<D, GQ>& st, float alpha, int lane) {
+  const int g = lane / 16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float ar;
+    if constexpr (GQ == 8) {
+      const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), r));
+      const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 + r));
+      ar = (g & 1) ? a1 : a0;
+    } else if constexpr (GQ == 4) {
+      ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), r));
+    } else {
+      ar = __shfl(alpha, (4 * g + r) % GQ, kWave);
+    }
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[nb][r] *= ar;
+  }
+}
+
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, const half8_t* bhi,
+                                              const half8_t* blo, float sigma, float esc, int slot0, int ntok,
+                                              int lane) {
+  const int g = lane / 16, c = lane % 16;
+  const float4_t acc = qk_page<BITS, D, GQ>(pr, bhi, blo);
+  if constexpr (GQ == 4) {
+    float x = acc[0];
+    x = dpp_row_shr_into<4, 0x2>(x, acc[1]);
+    x = dpp_row_shr_into<8, 0x4>(x, acc[2]);
+    x = dpp_row_shr_into<12, 0x8>(x, acc[3]);
+    const float lg = slot0 + 4 * g + c / 4 < ntok ? fmaf(lo_bf16(pr.mt[0]), x * esc, hi_bf16(pr.mt[0]) * sigma) : kNegInf;
+    float mx = fmaxf(lg, dpp_row_ror<4>(lg));
+    mx = fmaxf(mx, dpp_row_ror<8>(mx));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    if (__any(mx > st.m_run + 8.0f)) {
+      const float m_new = fmaxf(st.m_run, mx);
+      const float alpha = st.m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+      st.l_part *= alpha;
+      st.z_part *= alpha;
+      st.m_run = m_new;
+      rescale_rows<D, GQ>(st, alpha, lane);
+    }
+    const float p = lg == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg - st.m_run);
+    st.l_part += p;
+    st.z_part = fmaf(p, hi_bf16(pr.mt[1]), st.z_part);
+    const uint32_t P = split_f16(p * lo_bf16(pr.mt[1]));
+    const uint32_t S4 = dpp_row_shl<4>(P), S8 = dpp_row_shl<8>(P), S12 = dpp_row_shl<12>(P);
+    const uint32_t R4 = dpp_row_shr<4>(P);
+    const uint32_t a01 = c < 4 ? pack_lo16(P, S4) : (c < 8 ? pack_hi16(R4, P) : 0u);
+    const uint32_t a23 = c < 4 ? pack_lo16(S8, S12) : (c < 8 ? pack_hi16(S4, S8) : 0u);
+    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+  } else if constexpr (GQ == 8) {
+    float x0 = acc[0], x1 = acc[1];
+    x0 = dpp_row_shr_into<8, 0xC>(x0, acc[2]);
+    x1 = dpp_row_shr_into<8, 0xC>(x1, acc[3]);
+    const int t0 = slot0 + 4 * g + 2 * (c / 8);
+    const float lg0 = t0 < ntok ? fmaf(lo_bf16(pr.mt[0]), x0 * esc, hi_bf16(pr.mt[0]) * sigma) : kNegInf;
+    const float lg1 = t0 + 1 < ntok ? fmaf(lo_bf16(pr.mt[2]), x1 * esc, hi_bf16(pr.mt[2]) * sigma) : kNegInf;
+    float mx = fmaxf(lg0, lg1);
+    mx = fmaxf(mx, dpp_row_ror<8>(mx));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    if (__any(mx > st.m_run + 8.0f)) {
+      const float m_new = fmaxf(st.m_run, mx);
+      const float alpha = st.m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+      st.l_part *= alpha;
+      st.z_part *= alpha;
+      st.m_run = m_new;
+      rescale_rows<D, GQ>(st, alpha, lane);
+    }
+    const float p0 = lg0 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg0 - st.m_run);
+    const float p1 = lg1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg1 - st.m_run);
+    st.l_part += p0 + p1;
+    st.z_part = fmaf(p0, hi_bf16(pr.mt[1]), fmaf(p1, hi_bf16(pr.mt[3]), st.z_part));
+    const uint32_t q0 = split_f16(p0 * lo_bf16(pr.mt[1]));
+    const uint32_t q1 = split_f16(p1 * lo_bf16(pr.mt[3]));
+    const uint32_t P0 = pack_lo16(q0, q1);   // high parts of both tokens
+    const uint32_t L0 = pack_hi16(q0, q1);   // low parts of both tokens
+    const uint32_t a01 = c < 8 ? P0 : dpp_row_shr<8>(L0);
+    const uint32_t a23 = c < 8 ? dpp_row_shl<8>(P0) : L0;
+    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+  } else {
+    float lg[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      lg[r] = slot0 + 4 * g + r < ntok ? fmaf(lo_bf16(pr.mt[2 * r]), acc[r] * esc, hi_bf16(pr.mt[2 * r]) * sigma)
+                                       : kNegInf;
+    float p[4];
+    softmax_page<D, GQ>(st, lg, p, lane);
+    float W[4];
+    float lsum = 0.0f, zsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      W[r] = p[r] * lo_bf16(pr.mt[2 * r + 1]);
+      lsum += p[r];
+      zsum = fmaf(p[r], hi_bf16(pr.mt[2 * r + 1]), zsum);
+    }
+    st.l_part += lsum;
+    st.z_part += zsum;
+    const uint32_t q0 = split_f16(W[0]), q1 = split_f16(W[1]), q2 = split_f16(W[2]), q3 = split_f16(W[3]);
+    const uint32_t s01 = row_shr_or_zero<GQ>(pack_hi16(q0, q1)), s23 = row_shr_or_zero<GQ>(pack_hi16(q2, q3));
+    const uint32_t a01 = c < GQ ? pack_lo16(q0, q1) : (c < 2 * GQ ? s01 : 0u);
+    const uint32_t a23 = c < GQ ? pack_lo16(q2, q3) : (c < 2 * GQ ? s23 : 0u);
+    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+  }
+}
+
+template <int BITS, int D, int GQ>
+__device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8]) {
+  constexpr int NKK = D / 32;
+  const Dims& dm = a.dm;
+  const int S = BITS == 2 ? a.ws.s2 : a.ws.s4;
+  const int s = idx % S;
+  const int bk = idx / S;
+  const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  const HistCounts hc = hist_counts(a, b);
+  const int ntok = BITS == 2 ? hc.n2 : hc.n4;
+  const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
+  const int ppw = a.ws.ppw;
+  const int pg_begin = s * 4 * ppw;
+  if (pg_begin >= npages) return;  // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid % kWave, g = lane / 16, c = lane % 16;
+  const int wave = uniform(tid / kWave);
+  const int wp0 = uniform(pg_begin + wave * ppw);
+  const int wp1 = uniform(min(wp0 + ppw, npages));
+
+  const uint16_t* qh = BITS == 2 ? a.ws.qh2 : a.ws.qh4;
+  const uint16_t* ql = BITS == 2 ? a.ws.ql2 : a.ws.ql4;
+  const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
+  const size_t qrow = qbase + (c < GQ ? c : 0);
+  half8_t bhi[NKK], blo[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4_t vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
+    if (c < GQ) {
+      vh = *reinterpret_cast<const u32x4_t*>(qh + qrow * D + 32 * kk + 8 * g);
+      vl = *reinterpret_cast<const u32x4_t*>(ql + qrow * D + 32 * kk + 8 * g);
+    }
+    bhi[kk] = __builtin_bit_cast(half8_t, vh);
+    blo[kk] = __builtin_bit_cast(half8_t, vl);
+  }
+  // head whose logits this lane owns: c % GQ when redistributed, c (if < GQ) otherwise
+  const int hl = Redist<GQ>::on ? c % GQ : c;
+  const bool hl_ok = Redist<GQ>::on || c < GQ;
+  const float sigma = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 0] : 0.0f;
+  const float esc = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + (BITS == 2 ? 1 : 2)] : 0.0f;
+
+  WaveState<D, GQ> st;
+  st.init();
+  const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
+  const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
+  // page ids of this wavefront's range: one vector load, then read lane by lane
+  const int my_pid = (wp0 + lane < wp1) ? pt[wp0 + lane] : -1;
+  if (dm.pool_pages > 0) {
+    const uint8_t* dummy = a.pool;  // page-head 0 of the arena: target of out-of-range prefetches
+    page_pipeline<kHistPipe, QPage<BITS, D, GQ>>(
+        wp0, wp1,
+        [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
+          const int64_t page = pg < wp1 ? (int64_t)__builtin_amdgcn_readlane(my_pid, pg - wp0) : -1;
+          const bool valid = page >= 0 && page < dm.pool_pages && (BITS == 2 ? page < off4 : page >= off4);
+          load_qpage<BITS, D, GQ>(pr, valid ? page_head_addr(a.pool, page, kv, dm.hkv, D, off4) : dummy, lane);
+          return valid;
+        },
+        [&](const QPage<BITS, D, GQ>& pr, bool valid, int pg) {
+          if (valid) {
+            process_qpage<BITS, D, GQ>(st, pr, bhi, blo, sigma, esc, pg * kPage, ntok, lane);
+          } else if (lane == 0) {
+            atomicOr(a.ws.flags, 1u);
+          }
+        });
+  } else if (lane == 0) {
+    atomicOr(a.ws.flags, 1u);
+  }
+  const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
+  const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + slot;
+  workgroup_merge<D, GQ, BITS, Redist<GQ>::on>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
+                                                a.ws.part_lse + pbase * GQ);
+}
+
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
+  __shared__ float o_lds[4][2 * GQ][D];
+  __shared__ float st_lds[4][3][8];
+  const int n_win = a.dm.batch * a.dm.hkv * a.ws.nwin;
+  const int n_int2 = a.dm.batch * a.dm.hkv * a.ws.s2;
+  const int bid = blockIdx.x;
+  if (bid < n_win) {
+    window_role<D, GQ>(a, bid, o_lds, st_lds);
+  } else if (bid < n_win + n_int2) {
+    hist_role<2, D, GQ>(a, bid - n_win, o_lds, st_lds);
+  } else {
+    hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds);
+  }
+}
+
+// ------------------------------------------------------------------ BF16 baseline split
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void bf16_paged_split_kernel(Bf16Args a) {
+  __shared__ float o_lds[4][2 * GQ][D];
+  __shared__ float st_lds[4][3][8];
+  const Dims& dm = a.dm;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
+  const int s = blockIdx.x % a.s;
+  const int bk = blockIdx.x / a.s;
+  const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  int T = a.seq_len[b];
+  T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
+  const int npages = min((T + kPage - 1) / kPage, dm.pt_stride);
+  const int pg0 = s * 4 * a.ppw;
+  if (pg0 >= npages) return;
+  const int wp0 = pg0 + wave * a.ppw;
+  const int wp1 = min(wp0 + a.ppw, npages);
+  u32x4_t bq[D / 32];
+  load_bf16_query<D, GQ>(bq, a.q, (size_t)b * dm.hq + (size_t)kv * GQ, lane);
+  WaveState<D, GQ> st;
+  st.init();
+  const int my_pid = (wp0 + lane < wp1) ? a.pt[(size_t)b * dm.pt_stride + wp0 + lane] : -1;
+  const int64_t pbytes = bf16_page_head_bytes(D);
+  if (dm.pool_pages > 0) {
+    page_pipeline<kBf16Pipe, Bf16Page<D>>(
+        wp0, wp1,
+        [&](Bf16Page<D>& pr, int pg) -> bool {
+          const int64_t page = pg < wp1 ? (int64_t)__builtin_amdgcn_readlane(my_pid, pg - wp0) : -1;
+          const bool valid = page >= 0 && page < dm.pool_pages;
+          load_bf16_page<D>(pr, a.pages + (valid ? (page * dm.hkv + kv) * pbytes : 0), lane);
+          return valid;
+        },
+        [&](const Bf16Page<D>& pr, bool valid, int pg) {
+          if (valid) {
+            bool tv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tv[r] = kPage * pg + 4 * g + r < T;
+            process_bf16_page<D, GQ>(st, pr, bq, tv, a.scale_log2e, lane);
+          } else if (lane == 0) {
+            atomicOr(a.flags, 1u);
+          }
+        });
+  } else if (lane == 0) {
+    atomicOr(a.flags, 1u);
+  }
+  const size_t pbase = ((size_t)b * dm.hkv + kv) * a.s + s;
+  workgroup_merge<D, GQ, 16>(st, o_lds, st_lds, a.part_o + pbase * GQ * D, a.part_lse + pbase * GQ);
+}
+
+// ------------------------------------------------------------------ merge
+// LSE-merge of n partial slots (slot i at slot_of(i)) for one query head into o[D] and its lse.
+// All lse values are fetched first; the weighted sum then issues independent float4 loads.
+template <int D>
+__device__ void merge_slots(const float* po, const float* pl, size_t sbase, int gq, int hh, int n, int first, int n_a,
+                            int base_b, float* wl, float* red, float (*acc_s)[D], float* o_out, float* lse_out) {
+  constexpr int C4 = D / 4;          // float4 columns
+  constexpr int NG = 256 / C4;       // slot groups
+  const int tid = threadIdx.x;
+  auto slot_of = [&](int i) { return i < n_a ? first + i : base_b + (i - n_a); };
+  float m = kNegInf;
+  for (int i = tid; i < n; i += 256) {
+    const float l = pl[(sbase + slot_of(i)) * gq + hh];
+    wl[i] = l;
+    m = fmaxf(m, l);
+  }
+  red[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float ws = 0.0f;
+  for (int i = tid; i < n; i += 256) {
+    const float w = (M == kNegInf || wl[i] == kNegInf) ? 0.0f : exp2f(wl[i] - M);
+    wl[i] = w;
+    ws += w;
+  }
+  red[tid] = ws;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float W = red[0];
+  const int c4 = tid % C4, grp = tid / C4;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int i = grp; i < n; i += NG) {
+    const float w = wl[i];
+    const float4 v = *reinterpret_cast<const float4*>(po + ((sbase + slot_of(i)) * gq + hh) * D + 4 * c4);
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  acc_s[grp][4 * c4 + 0] = acc.x;
+  acc_s[grp][4 * c4 + 1] = acc.y;
+  acc_s[grp][4 * c4 + 2] = acc.z;
+  acc_s[grp][4 * c4 + 3] = acc.w;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.0f;
+    for (int gg = 0; gg < NG; ++gg) o += acc_s[gg][tid];
+    o_out[tid] = W > 0.0f ? o / W : 0.0f;
+  }
+  if (tid == 0) *lse_out = (M == kNegInf || !(W > 0.0f)) ? kNegInf : M + log2f(W);
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  constexpr int NP = 256 / D;
+  constexpr int RP = D / NP;
+  __shared__ float wl[kMaxSlots];
+  __shared__ float red[256];
+  __shared__ float acc_s[256 / (D / 4)][D];
+  __shared__ float orot[D], obf[D];
+  __shared__ float part_s[NP][D];
+  __shared__ float lse_s[2];
+  const Dims& dm = a.dm;
+  const int hq_i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int gq = dm.gq, kv = hq_i / gq, hh = hq_i % gq;
+  const HistCounts hc = hist_counts(a, b);
+  const int ppwg = 4 * a.ws.ppw;
+  const int n_a = (min((hc.n2 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
+  const int n_b = (min((hc.n4 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
+  const size_t sbase = ((size_t)b * dm.hkv + kv) * a.ws.ns;
+  // R_V row slices for the un-rotation, loaded while the partials are merged
+  const int j = tid % D, part = tid / D;
+  float rr[RP];
+  const float* rv = a.rot_v + ((size_t)kv * D + j) * D + part * RP;
+#pragma unroll
+  for (int i = 0; i < RP; i += 4) {
+    const float4 r4 = *reinterpret_cast<const float4*>(rv + i);
+    rr[i] = r4.x;
+    rr[i + 1] = r4.y;
+    rr[i + 2] = r4.z;
+    rr[i + 3] = r4.w;
+  }
+  merge_slots<D>(a.ws.part_o, a.ws.part_lse, sbase, gq, hh, n_a + n_b, a.ws.nwin, n_a, a.ws.nwin + a.ws.s2, wl, red,
+                 acc_s, orot, &lse_s[0]);
+  merge_slots<D>(a.ws.part_o, a.ws.part_lse, sbase, gq, hh, a.ws.nwin, 0, a.ws.nwin, 0, wl, red, acc_s, obf,
+                 &lse_s[1]);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RP; ++i) s = fmaf(orot[part * RP + i], rr[i], s);
+  part_s[part][j] = s;
+  __syncthreads();
+  if (tid < D) {
+    float oh = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) oh += part_s[p][tid];
+    const float lseA = lse_s[0], lseB = lse_s[1];
+    const float MM = fmaxf(lseA, lseB);
+    float o = 0.0f;
+    if (MM != kNegInf) {
+      const float wa = lseA == kNegInf ? 0.0f : exp2f(lseA - MM);
+      const float wb = lseB == kNegInf ? 0.0f : exp2f(lseB - MM);
+      o = (wa * oh + wb * obf[tid]) / (wa + wb);
+    }
+    a.out[((size_t)b * dm.hq + hq_i) * D + tid] = o;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bf16_merge_kernel(Bf16Args a) {
+  __shared__ float wl[kMaxSlots];
+  __shared__ float red[256];
+  __shared__ float acc_s[256 / (D / 4)][D];
+  __shared__ float o_s[D];
+  __shared__ float lse_s[1];
+  const Dims& dm = a.dm;
+  const int hq_i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int gq = dm.gq, kv = hq_i / gq, hh = hq_i % gq;
+  int T = a.seq_len[b];
+  T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
+  const int n = (min((T + kPage - 1) / kPage, dm.pt_stride) + 4 * a.ppw - 1) / (4 * a.ppw);
+  const size_t sbase = ((size_t)b * dm.hkv + kv) * a.s;
+  merge_slots<D>(a.part_o, a.part_lse, sbase, gq, hh, n, 0, n, 0, wl, red, acc_s, o_s, &lse_s[0]);
+  if (tid < D) a.out[((size_t)b * dm.hq + hq_i) * D + tid] = o_s[tid];
+}
+
+// ------------------------------------------------------------------ launchers
+template <int D, int GQ>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const Dims& dm = a.dm;
+  auto mark = [&](int i) {
+    if (a.events) (void)hipEventRecord(a.events[i], stream);
+  };
+  mark(0);
+  hipLaunchKernelGGL(q_prologue_kernel<D>, dim3(dm.hkv, dm.batch), dim3(256), 0, stream, a);
+  mark(1);
+  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
+  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(256), 0, stream, a);
+  mark(2);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(dm.hq, dm.batch), dim3(256), 0, stream, a);
+  mark(3);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.dm.batch == 0) return hipSuccess;
+  const int d = a.dm.d, gq = a.dm.gq;
+#define OSCAR_DISPATCH(DD, GG) \
+  if (d == DD && gq == GG) return launch_decode_t<DD, GG>(a, stream);
+  OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
+  OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
+#undef OSCAR_DISPATCH
+  return hipErrorInvalidValue;
+}
+
+template <int D, int GQ>
+static hipError_t launch_bf16_decode_t(const Bf16Args& b, hipStream_t stream) {
+  hipLaunchKernelGGL((bf16_paged_split_kernel<D, GQ>), dim3(b.dm.batch * b.dm.hkv * b.s), dim3(256), 0, stream, b);
+  hipLaunchKernelGGL((bf16_merge_kernel<D>), dim3(b.dm.hq, b.dm.batch), dim3(256), 0, stream, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_decode(const Bf16Args& b, hipStream_t stream) {
+  if (b.dm.batch == 0) return hipSuccess;
+  const int d = b.dm.d, gq = b.dm.gq;
+#define OSCAR_DISPATCH(DD, GG) \
+  if (d == DD && gq == GG) return launch_bf16_decode_t<DD, GG>(b, stream);
+  OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
+  OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
+#undef OSCAR_DISPATCH
+  return hipErrorInvalidValue;
+}
+
+}  // namespace oscar

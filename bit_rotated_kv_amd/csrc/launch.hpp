@@ -1,0 +1,97 @@
+// Host-side launchers of the OSCAR kernels and the parameter blocks they take. The C ABI in
+// api.hip validates arguments and calls these; they only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+// Cache geometry shared by every kernel.
+struct Dims {
+  int batch, hq, hkv, gq, d, sink, recent, wpages;  // wpages = (sink + recent) / 16
+  int mixed;
+  int64_t off4;        // first INT4 page id (mixed) / pool_pages (INT2 only)
+  int64_t pool_pages;  // valid page ids are [0, pool_pages)
+  int max_seq_len;
+  int pt_stride;
+};
+
+// Workspace carve-up of oscar_decode_attn (all device pointers).
+struct DecodeWs {
+  uint32_t* flags;         // [64]; word 0 bit 0: skipped page id
+  uint16_t* qh2;           // [B][Hq][d] fp16: rotated, scaled query (INT2 operand, high part)
+  uint16_t* ql2;           // low part
+  uint16_t* qh4;           // INT4 operand high/low parts (mixed caches)
+  uint16_t* ql4;
+  float* qsc;              // [B][Hq][4]: {sum_j q'_j, 2^E2, 2^E4, 0}
+  float* part_o;           // [B][Hkv][NS][gq][d]
+  float* part_lse;         // [B][Hkv][NS][gq]  (log2 units)
+  int ns;                  // slots per (b, kv): nwin (BF16 window) + S2 (INT2) + S4 (INT4)
+  int nwin;                // window workgroups per (b, kv): ceil(window pages / 4)
+  int s2, s4;              // split slots per width
+  int ppw;                 // pages per wavefront in a history split (4 waves per split), <= 64
+};
+
+constexpr int kMaxSlots = 3200;  // partial slots per (request, kv-head) the merge holds in LDS
+
+struct DecodeArgs {
+  Dims dm;
+  const uint16_t* q;         // [B][Hq][d] bf16
+  const int32_t* seq_len;
+  const int32_t* n_int4;     // may be null
+  const uint8_t* window;
+  const uint8_t* pool;
+  const int32_t* pt2;
+  const int32_t* pt4;
+  const float* rot_k;
+  const float* rot_v;
+  float scale_log2e;         // softmax scale * log2(e)
+  float* out;                // [B][Hq][d] fp32
+  DecodeWs ws;
+  hipEvent_t* events;        // host: optional, 4 events recorded around the kernels
+};
+
+struct CacheWriteArgs {
+  Dims dm;
+  const int32_t* seq_len;
+  const int32_t* n_int4;
+  const uint16_t* k;         // prefill: [B][Hkv][max_seq_len][d]; demote: [B][Hkv][d]
+  const uint16_t* v;
+  const uint8_t* bits;       // prefill: [B][max_seq_len]; demote: [B]; may be null
+  const float* rot_k;
+  const float* rot_v;
+  float clip_k, clip_v, clip_k4, clip_v4;
+  uint8_t* pool;
+  const int32_t* pt2;
+  const int32_t* pt4;
+  uint8_t* window;
+  int32_t* seq_len_out;
+  int32_t* n_int4_out;
+};
+
+struct Bf16Args {
+  Dims dm;                   // pool_pages = number of BF16 pages
+  const uint16_t* q;
+  const int32_t* seq_len;
+  const uint16_t* k;         // fill: [B][Hkv][max_seq_len][d]
+  const uint16_t* v;
+  uint8_t* pages;
+  const int32_t* pt;
+  float scale_log2e;
+  float* out;
+  float* part_o;             // [B][Hkv][S][gq][d]
+  float* part_lse;           // [B][Hkv][S][gq]
+  uint32_t* flags;
+  int s, ppw;
+};
+
+hipError_t launch_quantize_pack(int64_t rows, int dim, int group, int bits, float clip, const float* x,
+                                uint8_t* codes, uint16_t* sz, hipStream_t stream);
+hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_demote(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_bf16_fill(const Bf16Args& a, hipStream_t stream);
+hipError_t launch_bf16_decode(const Bf16Args& a, hipStream_t stream);
+
+}  // namespace oscar

@@ -1,0 +1,200 @@
+"""Torch-facing wrappers of the C ABI (include/oscar.h), one per entry point, same names.
+
+Each wrapper checks dtypes/devices/shapes, passes device pointers and the current HIP stream,
+and raises on a non-OK status. No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+from ctypes import c_void_p
+from typing import Optional
+
+import torch
+
+from ._lib import Layout, check, lib
+
+PAGE = 16
+
+
+def make_layout(num_q_heads: int, num_kv_heads: int, head_dim: int, group_size: Optional[int] = None,
+                sink_len: int = 64, recent_len: int = 256, mixed: bool = False, int4_page_offset: int = 0,
+                pool_pages: int = 0, clip_k: float = 0.96, clip_v: float = 0.92, clip_k4: float = 1.0,
+                clip_v4: float = 1.0) -> Layout:
+    return Layout(num_q_heads, num_kv_heads, head_dim, head_dim if group_size is None else group_size, sink_len,
+                  recent_len, PAGE, 1 if mixed else 0, int4_page_offset, pool_pages, clip_k, clip_v, clip_k4,
+                  clip_v4)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream():
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: Optional[torch.Tensor], dtype, name: str, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ref(layout: Layout):
+    import ctypes
+    return ctypes.byref(layout)
+
+
+# ---------------------------------------------------------------- sizes
+def page_bytes(layout: Layout, bits: int) -> int:
+    return int(lib().oscar_page_bytes(_ref(layout), bits))
+
+
+def window_bytes(layout: Layout, batch: int) -> int:
+    return int(lib().oscar_window_bytes(_ref(layout), batch))
+
+
+def pool_bytes(layout: Layout) -> int:
+    return int(lib().oscar_pool_bytes(_ref(layout)))
+
+
+def decode_workspace_bytes(layout: Layout, batch: int, max_seq_len: int) -> int:
+    return int(lib().oscar_decode_workspace_bytes(_ref(layout), batch, max_seq_len))
+
+
+def bf16_decode_workspace_bytes(layout: Layout, batch: int, max_seq_len: int) -> int:
+    return int(lib().oscar_bf16_decode_workspace_bytes(_ref(layout), batch, max_seq_len))
+
+
+# ---------------------------------------------------------------- entry points
+def quantize_pack(x: torch.Tensor, group: int, bits: int, clip: float, codes: Optional[torch.Tensor] = None,
+                  scale_zero: Optional[torch.Tensor] = None):
+    """x [rows, dim] fp32 -> (codes uint8 [rows, dim*bits/8], scale_zero int16 [rows, dim/group, 2] bf16 bits)."""
+    _need(x, torch.float32, "x")
+    rows, dim = x.shape
+    if codes is None:
+        codes = torch.empty((rows, dim * bits // 8), dtype=torch.uint8, device=x.device)
+    if scale_zero is None:
+        scale_zero = torch.empty((rows, dim // group, 2), dtype=torch.int16, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scale_zero, torch.int16, "scale_zero")
+    check(lib().oscar_quantize_pack(rows, dim, group, bits, clip, _p(x), _p(codes), _p(scale_zero), _stream()),
+          "oscar_quantize_pack")
+    return codes, scale_zero
+
+
+def kv_prefill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rot_k: torch.Tensor,
+               rot_v: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor, window: torch.Tensor,
+               token_bits: Optional[torch.Tensor] = None, page_table4: Optional[torch.Tensor] = None,
+               n_int4_out: Optional[torch.Tensor] = None):
+    """k, v [B, Hkv, max_seq_len, d] bf16; seq_len [B] int32; page tables [B, stride] int32."""
+    _need(seq_len, torch.int32, "seq_len")
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(rot_k, torch.float32, "rot_k")
+    _need(rot_v, torch.float32, "rot_v")
+    _need(pool, torch.uint8, "pool")
+    _need(page_table, torch.int32, "page_table")
+    _need(window, torch.uint8, "window")
+    _need(token_bits, torch.uint8, "token_bits", optional=True)
+    _need(page_table4, torch.int32, "page_table4", optional=True)
+    _need(n_int4_out, torch.int32, "n_int4_out", optional=True)
+    B, hkv, tmax, d = k.shape
+    check(lib().oscar_kv_prefill(_ref(layout), B, tmax, _p(seq_len), _p(k), _p(v), _p(token_bits), _p(rot_k),
+                                 _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                 _p(window), _p(n_int4_out), _stream()), "oscar_kv_prefill")
+
+
+def kv_demote(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, rot_k: torch.Tensor,
+              rot_v: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor, window: torch.Tensor,
+              n_int4: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
+              page_table4: Optional[torch.Tensor] = None, seq_len_out: Optional[torch.Tensor] = None,
+              n_int4_out: Optional[torch.Tensor] = None):
+    """One step's cache update. new_k, new_v [B, Hkv, d] bf16."""
+    _need(seq_len, torch.int32, "seq_len")
+    _need(new_k, torch.bfloat16, "new_k")
+    _need(new_v, torch.bfloat16, "new_v")
+    _need(rot_k, torch.float32, "rot_k")
+    _need(rot_v, torch.float32, "rot_v")
+    _need(pool, torch.uint8, "pool")
+    _need(page_table, torch.int32, "page_table")
+    _need(window, torch.uint8, "window")
+    for t, n in ((n_int4, "n_int4"), (page_table4, "page_table4"), (seq_len_out, "seq_len_out"),
+                 (n_int4_out, "n_int4_out")):
+        _need(t, torch.int32, n, optional=True)
+    _need(demote_bits, torch.uint8, "demote_bits", optional=True)
+    B = new_k.shape[0]
+    check(lib().oscar_kv_demote(_ref(layout), B, _p(seq_len), _p(n_int4), _p(new_k), _p(new_v), _p(demote_bits),
+                                _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                _p(window), _p(seq_len_out), _p(n_int4_out), _stream()), "oscar_kv_demote")
+
+
+def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: torch.Tensor, pool: torch.Tensor,
+                page_table: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, workspace: torch.Tensor,
+                max_seq_len: int, out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
+                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                events: Optional[list] = None) -> torch.Tensor:
+    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (6 torch.cuda.Event), calls the
+    timing variant, which records them around the kernels of the call."""
+    _need(q, torch.bfloat16, "q")
+    _need(seq_len, torch.int32, "seq_len")
+    _need(window, torch.uint8, "window")
+    _need(pool, torch.uint8, "pool")
+    _need(page_table, torch.int32, "page_table")
+    _need(rot_k, torch.float32, "rot_k")
+    _need(rot_v, torch.float32, "rot_v")
+    _need(workspace, torch.uint8, "workspace")
+    _need(n_int4, torch.int32, "n_int4", optional=True)
+    _need(page_table4, torch.int32, "page_table4", optional=True)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    B = q.shape[0]
+    if events is None:
+        check(lib().oscar_decode_attn(_ref(layout), B, max_seq_len, _p(q), _p(seq_len), _p(n_int4), _p(window),
+                                      _p(pool), _p(page_table), _p(page_table4), page_table.shape[1], _p(rot_k),
+                                      _p(rot_v), softmax_scale, _p(workspace), workspace.numel(), _p(out), _stream()),
+              "oscar_decode_attn")
+        return out
+    import ctypes
+    arr = (c_void_p * len(events))(*[c_void_p(e.cuda_event) for e in events])
+    check(lib().oscar_decode_attn_profiled(_ref(layout), B, max_seq_len, _p(q), _p(seq_len), _p(n_int4), _p(window),
+                                           _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                           _p(rot_k), _p(rot_v), softmax_scale, _p(workspace), workspace.numel(),
+                                           _p(out), ctypes.cast(arr, c_void_p), len(events), _stream()),
+          "oscar_decode_attn_profiled")
+    return out
+
+
+def bf16_fill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pages: torch.Tensor,
+              num_pages: int, page_table: torch.Tensor):
+    _need(seq_len, torch.int32, "seq_len")
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(pages, torch.uint8, "pages")
+    _need(page_table, torch.int32, "page_table")
+    B, hkv, tmax, d = k.shape
+    check(lib().oscar_bf16_fill(_ref(layout), B, tmax, _p(seq_len), _p(k), _p(v), _p(pages), num_pages,
+                                _p(page_table), page_table.shape[1], _stream()), "oscar_bf16_fill")
+
+
+def bf16_decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, pages: torch.Tensor, num_pages: int,
+                     page_table: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
+                     out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0) -> torch.Tensor:
+    _need(q, torch.bfloat16, "q")
+    _need(seq_len, torch.int32, "seq_len")
+    _need(pages, torch.uint8, "pages")
+    _need(page_table, torch.int32, "page_table")
+    _need(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    check(lib().oscar_bf16_decode_attn(_ref(layout), q.shape[0], max_seq_len, _p(q), _p(seq_len), _p(pages),
+                                       num_pages, _p(page_table), page_table.shape[1], softmax_scale, _p(workspace),
+                                       workspace.numel(), _p(out), _stream()), "oscar_bf16_decode_attn")
+    return out

@@ -1,0 +1,243 @@
+/*
+ * oscar.h -- C ABI of the MI355X (gfx950) library for attention-aware INT2 KV caching.
+ *
+ * The method (OSCAR, as described by the "Together AI open-sources OSCAR" article, the OSCAR
+ * overview page and the OSCAR study note): per request the KV cache holds a BF16 sink (first
+ * 64 tokens), a BF16 recent window (last 256 tokens, current token included) and, between
+ * them, a history whose keys and values are rotated by R = U . H_Had . P_br, clipped,
+ * group-quantised to INT2 (4 codes per byte, per-group scale and zero) and paged. Decode
+ * attention runs the BF16 and INT2 segments in separate kernels and merges them with an
+ * online-softmax (log-sum-exp) combine. A demote kernel moves the oldest recent token into
+ * the history each step. A TriAxialKV-style mixed history (TriAxialKV reading note,
+ * section 4) adds an INT4 page pool above an address offset and decodes it in
+ * bitwidth-homogeneous splits.
+ *
+ * General contract
+ *  - Every pointer argument named *_host is host memory; every other pointer is device memory
+ *    on the current HIP device. The caller allocates and owns every buffer. The library never
+ *    allocates device memory, never synchronises the stream and keeps no global state.
+ *  - All work is enqueued asynchronously on `stream` (0 = the default stream).
+ *  - Arguments are validated on the host (scalars, null pointers, sizes); on a validation error
+ *    nothing is enqueued and a negative status is returned. Device-resident values (lengths,
+ *    page ids) are not read by the host: lengths above max_seq_len are clamped, and page ids
+ *    outside [0, pool_pages) are skipped (their tokens contribute nothing) and flagged in the
+ *    workspace error word (decode) -- they never cause an out-of-bounds access.
+ *  - A launch failure reported by HIP returns OSCAR_ERR_LAUNCH.
+ *  - Row-vector convention: a key row x is stored rotated as x . R; R is row-major [d][d] fp32.
+ *
+ * Fixed values of this build: page_size 16 tokens; head_dim 64 or 128; group_size == head_dim
+ * in the paged kernels (any divisor of head_dim in oscar_quantize_pack); Hq/Hkv in {1,2,4,8};
+ * sink_len and recent_len multiples of 16 with sink_len <= 256, 16 <= recent_len <= 1024.
+ *
+ * ---------------------------------------------------------------------------------------------
+ * Data layouts (all little-endian; "bf16" = IEEE bfloat16 bit pattern)
+ *
+ * History page ("page-head" = one page of one kv-head; a page holds 16 token slots).
+ *   INT2 page-head, d = head_dim: 64 lane chunks of (K: d/16 bytes, then V: d/16 bytes), then
+ *   16 x 8 bytes of metadata. Total 4*d*2 + 128 bytes (1152 at d = 128, 640 at d = 64).
+ *   INT4 page-head: 64 lane chunks of (K: d/8 bytes, V: d/8 bytes), then 128 bytes of
+ *   metadata. Total 4*d*4 + 128 bytes (2176 at d = 128).
+ *   A page = num_kv_heads consecutive page-heads. Page id p < int4_page_offset is an INT2 page
+ *   at pool + p*P2; page id p >= int4_page_offset is an INT4 page at
+ *   pool + int4_page_offset*P2 + (p - int4_page_offset)*P4 (P2, P4 = page bytes). A single
+ *   compare of the id decides the width, as in the TriAxialKV dual pool.
+ *   Metadata of token slot t (0..15): bf16 {sK, zK, sV, zV} at byte 8*t of the metadata block,
+ *   where (s, z) are the group's scale and zero: x_hat = s*code + z (rotated basis).
+ *   Codes are 32-bit little-endian words inside each lane chunk (word a = bytes 4a..4a+3):
+ *   INT2 key of slot t, channel ch:  kk = ch/32, g = (ch%32)/8, m = (ch%8)/2, hf = ch%2;
+ *       lane L = 16*g + t, word a = kk/2, bit 8*(kk%2) + 2*m + 16*hf.
+ *   INT2 value of slot t, channel ch: nb = ch/16, c = ch%16, g = t/4, m = (t%4)/2, hf = t%2;
+ *       lane L = 16*g + c, word a = nb/4, bit 2*(nb%4) + 8*m + 16*hf.
+ *   INT4 key of slot t, channel ch:  kk = ch/32, g = (ch%32)/8, m = (ch%8)/2, hf = ch%2;
+ *       lane L = 16*g + t, word a = kk, bit 4*m + 16*hf.
+ *   INT4 value of slot t, channel ch: nb = ch/16, c = ch%16, g = t/4, m = (t%4)/2, hf = t%2;
+ *       lane L = 16*g + c, word a = nb/2, bit 4*(nb%2) + 8*m + 16*hf.
+ *   (These orders put the codes each matrix-core lane needs into its own 16-byte load.)
+ *
+ * BF16 page-head (sink/recent window, and the full-BF16 baseline cache): 16 tokens of K then V.
+ *   K element (t, ch) at bf16 index ((g*16 + t)*(d/32) + kk)*8 + i with kk = ch/32,
+ *       g = (ch%32)/8, i = ch%8.
+ *   V element (t, ch) at bf16 index 16*d + ((g*16 + c)*(d/16) + nb)*4 + r with nb = ch/16,
+ *       c = ch%16, g = t/4, r = t%4.
+ *   64*d bytes per page-head (8192 at d = 128).
+ *
+ * Window (BF16 sink + recent of a batch): [batch][num_kv_heads][W pages][BF16 page-head] with
+ *   W = (sink_len + recent_len)/16. Position p < sink_len lives in window page p/16, slot p%16.
+ *   Position p >= sink_len lives in ring slot s = p % recent_len: window page
+ *   sink_len/16 + s/16, slot s%16. With T tokens in cache the recent window is
+ *   [max(sink_len, T - recent_len), T) and the history is [sink_len, T - recent_len).
+ *
+ * Cache state per request b: seq_len[b] = T (tokens in cache, current token included) and,
+ *   for a mixed cache, n_int4[b] = number of history tokens stored at 4 bits. History slot k of
+ *   width w lives in page table[b*pt_stride + k/16] (INT2: page_table, INT4: page_table4),
+ *   slot k%16. INT2 history count = max(0, T - sink_len - recent_len) - n_int4[b].
+ * ---------------------------------------------------------------------------------------------
+ */
+#ifndef OSCAR_H_
+#define OSCAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID_ARG = -1, /* null pointer, out-of-range scalar, inconsistent sizes      */
+  OSCAR_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d=96)    */
+  OSCAR_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required            */
+  OSCAR_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError after the launch)  */
+} oscar_status_t;
+
+/* Shape and policy of one attention layer's cache. */
+typedef struct oscar_layout {
+  int32_t num_q_heads;      /* Hq                                                            */
+  int32_t num_kv_heads;     /* Hkv; query head h reads kv-head h / (Hq/Hkv)                  */
+  int32_t head_dim;         /* d: 64 or 128                                                  */
+  int32_t group_size;       /* quantisation group along head_dim (== head_dim when paged)    */
+  int32_t sink_len;         /* BF16 sink tokens (64)                                         */
+  int32_t recent_len;       /* BF16 recent window tokens (256)                               */
+  int32_t page_size;        /* tokens per page: must be 16                                   */
+  int32_t mixed;            /* 0: INT2 history only; 1: INT2 + INT4 pools                    */
+  int64_t int4_page_offset; /* mixed: page ids >= this are INT4 pages                        */
+  int64_t pool_pages;       /* number of valid page ids in the pool arena                    */
+  float clip_k, clip_v;     /* INT2 clip ratios c_K, c_V (study note, case 2: 0.96, 0.92)    */
+  float clip_k4, clip_v4;   /* INT4 clip ratios (1.0: no clipping)                           */
+} oscar_layout_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* oscar_status_string(oscar_status_t status);
+
+/* Library version string. */
+const char* oscar_version(void);
+
+/* Byte sizes of the layouts above; 0 if the layout is invalid. */
+size_t oscar_page_bytes(const oscar_layout_t* layout, int32_t bits);   /* bits: 2, 4 or 16 */
+size_t oscar_window_bytes(const oscar_layout_t* layout, int32_t batch);
+size_t oscar_pool_bytes(const oscar_layout_t* layout);                  /* whole arena        */
+
+/*
+ * Group quantise already-rotated fp32 rows (the bit-exact parity surface; OSCAR overview page,
+ * method paragraph; clip constants from the study note, case 2).
+ *   x           [rows][dim] fp32 (device)
+ *   codes       [rows][dim*bits/8] bytes, canonical order: code i of a row at byte i/(8/bits),
+ *               bits (i%(8/bits))*bits (LSB first)
+ *   scale_zero  [rows][dim/group][2] bf16 patterns (s, z)
+ * Per group: lo = clip*min, hi = clip*max (fp32), s = bf16(fp32(hi-lo)/(2^bits-1)),
+ * z = bf16(lo), code = clamp(rint_even(fp32(fp32(clamp(x,lo,hi) - z)/s)), 0, 2^bits-1), and all
+ * codes 0 when s == 0. bits in {2, 4}; group divides dim; dim <= 1024; 0 < clip <= 1.
+ */
+oscar_status_t oscar_quantize_pack(int64_t rows, int32_t dim, int32_t group, int32_t bits,
+                                   float clip, const float* x, uint8_t* codes,
+                                   uint16_t* scale_zero, hipStream_t stream);
+
+/*
+ * Build the cache of a batch from full prefixes (prefill): writes the sink and recent windows
+ * into `window` and rotates (K by rot_k, V by rot_v), clips, quantises and packs every history
+ * token into its page (OSCAR overview page, method paragraph; news article, cache layout).
+ *   seq_len      [batch] int32, T of each request (<= max_seq_len)
+ *   k, v         [batch][Hkv][max_seq_len][d] bf16, positions 0..T-1 used
+ *   token_bits   [batch][max_seq_len] uint8 (2 or 4), width of each history token (mixed
+ *                caches only; NULL = all INT2). INT2 and INT4 tokens take consecutive slots
+ *                of their own page tables in position order.
+ *   rot_k, rot_v [Hkv][d][d] fp32
+ *   page_table   [batch][pt_stride] int32 INT2 history pages; page_table4 the INT4 pages
+ *                (mixed only, else may be NULL)
+ *   n_int4_out   [batch] int32 written with the INT4 history count (may be NULL)
+ */
+oscar_status_t oscar_kv_prefill(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                const int32_t* seq_len, const void* k, const void* v,
+                                const uint8_t* token_bits, const float* rot_k, const float* rot_v,
+                                void* pool, const int32_t* page_table, const int32_t* page_table4,
+                                int32_t pt_stride, void* window, int32_t* n_int4_out,
+                                hipStream_t stream);
+
+/*
+ * One decode step's cache update for every request (OSCAR overview page, method paragraph;
+ * study note, SGLang case): with T = seq_len[b], if T >= sink_len + recent_len the oldest recent
+ * token (position T - recent_len) is read from the window, rotated, clipped, quantised, packed
+ * into the next history slot of its width (demote_bits[b], 2 if NULL) and the new token
+ * (new_k/new_v [batch][Hkv][d] bf16) is written into the freed recent slot; otherwise the new
+ * token is written at position T of the window. seq_len_out[b] = T + 1 and
+ * n_int4_out[b] = n_int4[b] + (width == 4) are written when the pointers are not NULL; they
+ * must not alias seq_len / n_int4. n_int4 may be NULL for an INT2-only cache.
+ */
+oscar_status_t oscar_kv_demote(const oscar_layout_t* layout, int32_t batch, const int32_t* seq_len,
+                               const int32_t* n_int4, const void* new_k, const void* new_v,
+                               const uint8_t* demote_bits, const float* rot_k, const float* rot_v,
+                               void* pool, const int32_t* page_table, const int32_t* page_table4,
+                               int32_t pt_stride, void* window, int32_t* seq_len_out,
+                               int32_t* n_int4_out, hipStream_t stream);
+
+/* Workspace bytes oscar_decode_attn needs for this batch and length bound. */
+size_t oscar_decode_workspace_bytes(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len);
+
+/*
+ * Decode attention over the three-segment cache (OSCAR overview page, method paragraph; news
+ * article, key/value rotations): for query head h of request b, logits are
+ * softmax_scale*q.k over the BF16 sink/recent tokens and softmax_scale*(q.R_K).x_hat over
+ * history tokens; one softmax over all of them; out = sum_BF16 p v + (sum_hist p x_hat_V).R_V^T.
+ * Computed as bitwidth-homogeneous splits (BF16 / INT2 / INT4 pages) with fp32 accumulation,
+ * merged by log-sum-exp.
+ *   q          [batch][Hq][d] bf16
+ *   out        [batch][Hq][d] fp32
+ *   softmax_scale 0 -> 1/sqrt(d)
+ *   workspace  >= oscar_decode_workspace_bytes(); word 0 (uint32) is OR-ed with 1 when a page
+ *              id outside [0, pool_pages) was skipped. Contents are scratch between calls.
+ */
+oscar_status_t oscar_decode_attn(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                 const void* q, const int32_t* seq_len, const int32_t* n_int4,
+                                 const void* window, const void* pool, const int32_t* page_table,
+                                 const int32_t* page_table4, int32_t pt_stride,
+                                 const float* rot_k, const float* rot_v, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, float* out,
+                                 hipStream_t stream);
+
+/*
+ * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..3]
+ * (n_events >= 4, all created by the caller) before the query prologue, after it, after the split
+ * kernel (BF16 window, INT2 and INT4 history pages in one launch) and after the merge. Intervals
+ * between consecutive events time each kernel of the call.
+ */
+oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                          const void* q, const int32_t* seq_len, const int32_t* n_int4,
+                                          const void* window, const void* pool, const int32_t* page_table,
+                                          const int32_t* page_table4, int32_t pt_stride, const float* rot_k,
+                                          const float* rot_v, float softmax_scale, void* workspace,
+                                          size_t workspace_bytes, float* out, hipEvent_t* events,
+                                          int32_t n_events, hipStream_t stream);
+
+/*
+ * In-house BF16 baseline: the full context of each request in BF16 pages (BF16 page-head
+ * layout; page = Hkv page-heads, page ids index `pages`). Writes every position of k/v
+ * ([batch][Hkv][max_seq_len][d] bf16, T = seq_len[b]) into the pages of `page_table`.
+ */
+oscar_status_t oscar_bf16_fill(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                               const int32_t* seq_len, const void* k, const void* v, void* pages,
+                               int64_t num_pages, const int32_t* page_table, int32_t pt_stride,
+                               hipStream_t stream);
+
+/* Workspace bytes for oscar_bf16_decode_attn. */
+size_t oscar_bf16_decode_workspace_bytes(const oscar_layout_t* layout, int32_t batch,
+                                         int32_t max_seq_len);
+
+/*
+ * In-house BF16 decode attention (the speed-up denominator): plain softmax(scale q K^T) V over
+ * all T tokens of each request from a full-BF16 paged cache, split-K with a log-sum-exp merge.
+ * Same q/out/workspace conventions as oscar_decode_attn; ids outside [0, num_pages) skipped.
+ */
+oscar_status_t oscar_bf16_decode_attn(const oscar_layout_t* layout, int32_t batch,
+                                      int32_t max_seq_len, const void* q, const int32_t* seq_len,
+                                      const void* pages, int64_t num_pages,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      float softmax_scale, void* workspace, size_t workspace_bytes,
+                                      float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H_ */

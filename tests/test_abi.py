@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every function include/oscar.h declares, and validates its
+arguments on the host (no device work: every call here returns before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_rotated_kv_amd as brk
+from bit_rotated_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from bit_rotated_kv_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("oscar_kv_demote", "oscar_decode_attn", "oscar_quantize_pack", "oscar_kv_prefill",
+              "oscar_bf16_decode_attn", "oscar_decode_workspace_bytes", "oscar_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    assert set(declared_functions()) <= set(_lib._SIGS)
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert brk.status_string(code) == name
+    assert brk.status_string(7) == "OSCAR_ERR_UNKNOWN"
+    assert b"gfx950" in lib.oscar_version()
+
+
+def test_layout_struct_size():
+    assert ctypes.sizeof(_lib.Layout) == 64
+
+
+def layout(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, pool_pages=100)
+    base.update(kw)
+    return brk.make_layout(**base)
+
+
+def test_sizes(lib):
+    L = layout()
+    assert brk.page_bytes(L, 2) == 8 * 1152
+    assert brk.page_bytes(L, 4) == 8 * 2176
+    assert brk.page_bytes(L, 16) == 8 * 8192
+    assert brk.window_bytes(L, 3) == 3 * 8 * 20 * 8192
+    assert brk.pool_bytes(L) == 100 * 8 * 1152
+    M = layout(mixed=True, int4_page_offset=60)
+    assert brk.pool_bytes(M) == 60 * 8 * 1152 + 40 * 8 * 2176
+    assert brk.page_bytes(layout(head_dim=64, num_q_heads=2, num_kv_heads=1), 2) == 640
+    # workspace grows with context and is 0 for invalid layouts
+    assert brk.decode_workspace_bytes(L, 1, 100_000) > brk.decode_workspace_bytes(L, 1, 1000) > 0
+    assert brk.decode_workspace_bytes(layout(head_dim=96), 1, 1000) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -2), (dict(num_q_heads=24, num_kv_heads=8), -2), (dict(num_q_heads=30), -1),
+    (dict(group_size=64), -2), (dict(group_size=48), -1), (dict(clip_k=0.0), -1), (dict(clip_v=1.5), -1),
+    (dict(sink_len=72), -2), (dict(recent_len=0), -1), (dict(mixed=1, int4_page_offset=200), -1),
+    (dict(num_q_heads=64, num_kv_heads=4), -2),
+])
+def test_invalid_layouts_rejected(lib, kw, code):
+    L = layout(**kw)
+    r = lib.oscar_decode_attn(ctypes.byref(L), 1, 1000, 1, 1, None, 1, 1, 1, None, 100, 1, 1, 0.0, 1, 1 << 30, 1,
+                              None)
+    assert r == code
+    r = lib.oscar_kv_demote(ctypes.byref(L), 1, 1, None, 1, 1, None, 1, 1, 1, 1, None, 100, 1, None, None, None)
+    assert r == code
+
+
+def test_decode_argument_checks(lib):
+    L = ctypes.byref(layout())
+    ok_ptr = 1
+    # null q
+    assert lib.oscar_decode_attn(L, 1, 1000, None, ok_ptr, None, ok_ptr, ok_ptr, ok_ptr, None, 100, ok_ptr, ok_ptr,
+                                 0.0, ok_ptr, 1 << 30, ok_ptr, None) == -1
+    # empty page table although the length bound has a history
+    assert lib.oscar_decode_attn(L, 1, 100_000, ok_ptr, ok_ptr, None, ok_ptr, ok_ptr, ok_ptr, None, 0, ok_ptr,
+                                 ok_ptr, 0.0, ok_ptr, 1 << 30, ok_ptr, None) == -1
+    # workspace too small
+    assert lib.oscar_decode_attn(L, 1, 1000, ok_ptr, ok_ptr, None, ok_ptr, ok_ptr, ok_ptr, None, 100, ok_ptr, ok_ptr,
+                                 0.0, ok_ptr, 16, ok_ptr, None) == -3
+    # negative softmax scale
+    assert lib.oscar_decode_attn(L, 1, 1000, ok_ptr, ok_ptr, None, ok_ptr, ok_ptr, ok_ptr, None, 100, ok_ptr, ok_ptr,
+                                 -1.0, ok_ptr, 1 << 30, ok_ptr, None) == -1
+    # batch 0 is a no-op
+    assert lib.oscar_decode_attn(L, 0, 1000, None, None, None, None, None, None, None, 0, None, None, 0.0, None, 0,
+                                 None, None) == 0
+    # mixed cache without INT4 page table
+    M = ctypes.byref(layout(mixed=True, int4_page_offset=50))
+    assert lib.oscar_decode_attn(M, 1, 1000, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None, 100, ok_ptr,
+                                 ok_ptr, 0.0, ok_ptr, 1 << 30, ok_ptr, None) == -1
+
+
+def test_demote_argument_checks(lib):
+    L = ctypes.byref(layout())
+    p = 1
+    # aliasing seq_len and seq_len_out
+    assert lib.oscar_kv_demote(L, 2, 5, None, p, p, None, p, p, p, p, None, 10, p, 5, None, None) == -1
+    assert lib.oscar_kv_demote(L, 2, None, None, p, p, None, p, p, p, p, None, 10, p, None, None, None) == -1
+
+
+def test_quantize_pack_argument_checks(lib):
+    q = lib.oscar_quantize_pack
+    assert q(-1, 128, 128, 2, 0.96, 1, 1, 1, None) == -1
+    assert q(4, 128, 48, 2, 0.96, 1, 1, 1, None) == -1      # group does not divide dim
+    assert q(4, 128, 128, 3, 0.96, 1, 1, 1, None) == -1     # bits
+    assert q(4, 6, 6, 2, 0.96, 1, 1, 1, None) == -1         # group not a multiple of codes per byte
+    assert q(4, 128, 128, 2, 0.0, 1, 1, 1, None) == -1      # clip
+    assert q(4, 2048, 128, 2, 0.96, 1, 1, 1, None) == -2    # dim beyond this build
+    assert q(4, 128, 128, 2, 0.96, None, 1, 1, None) == -1  # null x
+    assert q(0, 128, 128, 2, 0.96, None, None, None, None) == 0
+
+
+def test_bf16_argument_checks(lib):
+    L = ctypes.byref(layout())
+    assert lib.oscar_bf16_decode_attn(L, 1, 1000, None, 1, 1, 10, 1, 100, 0.0, 1, 1 << 30, 1, None) == -1
+    assert lib.oscar_bf16_decode_attn(L, 1, 1000, 1, 1, 1, 10, 1, 100, 0.0, 1, 8, 1, None) == -3
+    assert lib.oscar_bf16_fill(L, 1, 1000, 1, 1, 1, 1, 10, 1, 0, None) == -1   # empty page table
