@@ -20,6 +20,7 @@ ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for every HIP object (-packed-fp32-ops).
 HIPFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-ffp-contract=fast-honor-pragmas",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
 
 

@@ -36,6 +36,11 @@ __device__ inline const uint8_t* page_head_addr(const uint8_t* pool, int64_t pag
   return pool + off4 * p2 + (page - off4) * p4 + (int64_t)kv * qpage_head_bytes(d, 4);
 }
 
+// Pointer into global memory (address space 1): loads through it are global loads, also where
+// the address was assembled from scalar registers.
+template <typename T>
+using GPtr = const __attribute__((address_space(1))) T*;
+
 // ------------------------------------------------------------------ number formats
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -84,12 +89,27 @@ __device__ __forceinline__ uint32_t dpp_row_shl(uint32_t v) {
   static_assert(N >= 1 && N <= 15, "row shift 1..15");
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xF, 0xF, false);
 }
-// DPP row shift right writing only the lanes of the 4-lane banks in BANKS (others keep old).
+// DPP move with a bank mask: lanes of the 4-lane banks set in BANKS receive src from the lane
+// that CTRL selects; the other lanes keep old. Selecting by bank mask keeps the move
+// unconditional: a data-dependent select around a DPP move may be turned into a branch, and a
+// DPP move executed under a narrowed exec mask reads inactive source lanes as invalid.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ uint32_t dpp_into(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANKS, false);
+}
 template <int N, int BANKS>
-__device__ __forceinline__ float dpp_row_shr_into(float old, float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
-                                                               __builtin_bit_cast(int, v), 0x110 + N, 0xF, BANKS,
-                                                               false));
+__device__ __forceinline__ uint32_t dpp_row_shr_into(uint32_t old, uint32_t src) {
+  static_assert(N >= 1 && N <= 15, "row shift 1..15");
+  return dpp_into<0x110 + N, BANKS>(old, src);
+}
+template <int N, int BANKS>
+__device__ __forceinline__ uint32_t dpp_row_shl_into(uint32_t old, uint32_t src) {
+  static_assert(N >= 1 && N <= 15, "row shift 1..15");
+  return dpp_into<0x100 + N, BANKS>(old, src);
+}
+template <int N, int BANKS>
+__device__ __forceinline__ float dpp_row_shr_into(float old, float src) {
+  return __uint_as_float(dpp_row_shr_into<N, BANKS>(__float_as_uint(old), __float_as_uint(src)));
 }
 // DPP row rotate right by N lanes inside each 16-lane row.
 template <int N>

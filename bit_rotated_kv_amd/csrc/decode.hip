@@ -153,10 +153,11 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------ per-wave softmax state
 template <int D, int GQ>
 struct WaveState {
-  float m_run, l_part, z_part;
+  float m_run, m_thr, l_part, z_part;  // m_thr = m_run + 8: a logit above it triggers a rescale
   float4_t o[D / 16];
   __device__ void init() {
     m_run = kNegInf;
+    m_thr = kNegInf;
     l_part = 0.0f;
     z_part = 0.0f;
 #pragma unroll
@@ -383,18 +384,18 @@ struct QPage {
   uint32_t mt[Redist<GQ>::meta_words];
 };
 
-template <int BITS, int D, int GQ>
-__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, const uint8_t* ph, int lane) {
+template <int BITS, int D, int GQ, typename Ptr>
+__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, Ptr ph, int lane) {
   constexpr int CW = QPage<BITS, D, GQ>::CW;
   const int g = lane / 16, c = lane % 16;
   if constexpr (CW == 1) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(ph + lane * 8);
+    const u32x2_t v = *reinterpret_cast<GPtr<u32x2_t>>(ph + lane * 8);
     pr.kw[0] = v[0];
     pr.vw[0] = v[1];
   } else {
 #pragma unroll
     for (int j = 0; j < 2 * CW / 4; ++j) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ph + lane * 8 * CW + 16 * j);
+      const u32x4_t v = *reinterpret_cast<GPtr<u32x4_t>>(ph + lane * 8 * CW + 16 * j);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * j + e;
@@ -403,18 +404,18 @@ __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, const uint8_t
       }
     }
   }
-  const uint8_t* meta = ph + 4 * D * BITS;
+  const auto meta = ph + 4 * D * BITS;
   if constexpr (GQ == 4) {
-    const u32x2_t m = *reinterpret_cast<const u32x2_t*>(meta + 8 * (4 * g + c / 4));
+    const u32x2_t m = *reinterpret_cast<GPtr<u32x2_t>>(meta + 8 * (4 * g + c / 4));
     pr.mt[0] = m[0];
     pr.mt[1] = m[1];
   } else if constexpr (GQ == 8) {
-    const u32x4_t m = *reinterpret_cast<const u32x4_t*>(meta + 8 * (4 * g + 2 * (c / 8)));
+    const u32x4_t m = *reinterpret_cast<GPtr<u32x4_t>>(meta + 8 * (4 * g + 2 * (c / 8)));
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr.mt[e] = m[e];
   } else {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(meta + 32 * g);
-    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(meta + 32 * g + 16);
+    const u32x4_t a = *reinterpret_cast<GPtr<u32x4_t>>(meta + 32 * g);
+    const u32x4_t b = *reinterpret_cast<GPtr<u32x4_t>>(meta + 32 * g + 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pr.mt[e] = a[e];
@@ -504,10 +505,37 @@ __device__ __forceinline__ void rescale_rows(WaveState<D, GQ>& st, float alpha, 
   }
 }
 
+// Online softmax over redistributed logits (NL per lane, all of head lane%GQ). No page maximum
+// is formed on the common path: probabilities are taken against the running maximum, and only
+// when some logit exceeds it by more than 8 (log2 units) is the maximum rebuilt across the lanes
+// of each head and the state rescaled, so every probability stays below 2^8.
+template <int D, int GQ, int NL>
+__device__ __forceinline__ void redist_softmax(WaveState<D, GQ>& st, const float (&lg)[NL], float (&p)[NL], int lane) {
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) over |= lg[i] > st.m_thr;
+  if (__any(over)) {
+    float mx = lg[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mx = fmaxf(mx, lg[i]);
+#pragma unroll
+    for (int o = GQ; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 while m_run is -inf
+    st.l_part *= alpha;
+    st.z_part *= alpha;
+    st.m_run = m_new;
+    st.m_thr = m_new + 8.0f;
+    rescale_rows<D, GQ>(st, alpha, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);  // 0 for -inf logits
+}
+
 template <int BITS, int D, int GQ>
 __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, const half8_t* bhi,
-                                              const half8_t* blo, float sigma, float esc, int slot0, int ntok,
-                                              int lane) {
+                                              const half8_t* blo, float sigma, float esc, uint32_t psel,
+                                              int slot0, int ntok, int lane) {
   const int g = lane / 16, c = lane % 16;
   const float4_t acc = qk_page<BITS, D, GQ>(pr, bhi, blo);
   if constexpr (GQ == 4) {
@@ -515,57 +543,43 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     x = dpp_row_shr_into<4, 0x2>(x, acc[1]);
     x = dpp_row_shr_into<8, 0x4>(x, acc[2]);
     x = dpp_row_shr_into<12, 0x8>(x, acc[3]);
-    const float lg = slot0 + 4 * g + c / 4 < ntok ? fmaf(lo_bf16(pr.mt[0]), x * esc, hi_bf16(pr.mt[0]) * sigma) : kNegInf;
-    float mx = fmaxf(lg, dpp_row_ror<4>(lg));
-    mx = fmaxf(mx, dpp_row_ror<8>(mx));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (__any(mx > st.m_run + 8.0f)) {
-      const float m_new = fmaxf(st.m_run, mx);
-      const float alpha = st.m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-      st.l_part *= alpha;
-      st.z_part *= alpha;
-      st.m_run = m_new;
-      rescale_rows<D, GQ>(st, alpha, lane);
-    }
-    const float p = lg == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg - st.m_run);
-    st.l_part += p;
-    st.z_part = fmaf(p, hi_bf16(pr.mt[1]), st.z_part);
-    const uint32_t P = split_f16(p * lo_bf16(pr.mt[1]));
-    const uint32_t S4 = dpp_row_shl<4>(P), S8 = dpp_row_shl<8>(P), S12 = dpp_row_shl<12>(P);
-    const uint32_t R4 = dpp_row_shr<4>(P);
-    const uint32_t a01 = c < 4 ? pack_lo16(P, S4) : (c < 8 ? pack_hi16(R4, P) : 0u);
-    const uint32_t a23 = c < 4 ? pack_lo16(S8, S12) : (c < 8 ? pack_hi16(S4, S8) : 0u);
+    float lg[1] = {fmaf(lo_bf16(pr.mt[0]), x * esc, hi_bf16(pr.mt[0]) * sigma)};
+    lg[0] = slot0 + 4 * g + c / 4 < ntok ? lg[0] : kNegInf;
+    float p[1];
+    redist_softmax<D, GQ, 1>(st, lg, p, lane);
+    st.l_part += p[0];
+    st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), st.z_part);
+    // A operand of the PV product: row c < 4 holds the fp16 high parts of head c for tokens
+    // 4g..4g+3 (lanes c, c+4, c+8, c+12), row 4 + c the low parts (lanes c, c+4, c+8, c+12 seen
+    // from row 4 + c: offsets -4, 0, +4, +8); rows 8..15 are zero (selector bytes 0x0C).
+    const uint32_t P = split_f16(p[0] * lo_bf16(pr.mt[1]));
+    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(0u, P), P);
+    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(0u, P), P);
+    const uint32_t v8 = dpp_row_shl<8>(P);
+    const uint32_t a01 = __builtin_amdgcn_perm(y, P, psel);
+    const uint32_t a23 = __builtin_amdgcn_perm(u, v8, psel);
     pv_page<BITS, D, GQ>(st, pr, a01, a23);
   } else if constexpr (GQ == 8) {
     float x0 = acc[0], x1 = acc[1];
     x0 = dpp_row_shr_into<8, 0xC>(x0, acc[2]);
     x1 = dpp_row_shr_into<8, 0xC>(x1, acc[3]);
     const int t0 = slot0 + 4 * g + 2 * (c / 8);
-    const float lg0 = t0 < ntok ? fmaf(lo_bf16(pr.mt[0]), x0 * esc, hi_bf16(pr.mt[0]) * sigma) : kNegInf;
-    const float lg1 = t0 + 1 < ntok ? fmaf(lo_bf16(pr.mt[2]), x1 * esc, hi_bf16(pr.mt[2]) * sigma) : kNegInf;
-    float mx = fmaxf(lg0, lg1);
-    mx = fmaxf(mx, dpp_row_ror<8>(mx));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (__any(mx > st.m_run + 8.0f)) {
-      const float m_new = fmaxf(st.m_run, mx);
-      const float alpha = st.m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-      st.l_part *= alpha;
-      st.z_part *= alpha;
-      st.m_run = m_new;
-      rescale_rows<D, GQ>(st, alpha, lane);
-    }
-    const float p0 = lg0 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg0 - st.m_run);
-    const float p1 = lg1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(lg1 - st.m_run);
-    st.l_part += p0 + p1;
-    st.z_part = fmaf(p0, hi_bf16(pr.mt[1]), fmaf(p1, hi_bf16(pr.mt[3]), st.z_part));
-    const uint32_t q0 = split_f16(p0 * lo_bf16(pr.mt[1]));
-    const uint32_t q1 = split_f16(p1 * lo_bf16(pr.mt[3]));
+    float lg[2] = {fmaf(lo_bf16(pr.mt[0]), x0 * esc, hi_bf16(pr.mt[0]) * sigma),
+                   fmaf(lo_bf16(pr.mt[2]), x1 * esc, hi_bf16(pr.mt[2]) * sigma)};
+    lg[0] = t0 < ntok ? lg[0] : kNegInf;
+    lg[1] = t0 + 1 < ntok ? lg[1] : kNegInf;
+    float p[2];
+    redist_softmax<D, GQ, 2>(st, lg, p, lane);
+    st.l_part += p[0] + p[1];
+    st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), fmaf(p[1], hi_bf16(pr.mt[3]), st.z_part));
+    const uint32_t q0 = split_f16(p[0] * lo_bf16(pr.mt[1]));
+    const uint32_t q1 = split_f16(p[1] * lo_bf16(pr.mt[3]));
     const uint32_t P0 = pack_lo16(q0, q1);   // high parts of both tokens
     const uint32_t L0 = pack_hi16(q0, q1);   // low parts of both tokens
-    const uint32_t a01 = c < 8 ? P0 : dpp_row_shr<8>(L0);
-    const uint32_t a23 = c < 8 ? dpp_row_shl<8>(P0) : L0;
+    // row c < 8: high parts of head c, tokens 4g, 4g+1 (own) and 4g+2, 4g+3 (lane c+8);
+    // row c >= 8: low parts of head c-8, tokens 4g, 4g+1 (lane c-8) and 4g+2, 4g+3 (own)
+    const uint32_t a01 = dpp_row_shr_into<8, 0xC>(P0, L0);
+    const uint32_t a23 = dpp_row_shl_into<8, 0x3>(L0, P0);
     pv_page<BITS, D, GQ>(st, pr, a01, a23);
   } else {
     float lg[4];
@@ -633,25 +647,34 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const float sigma = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 0] : 0.0f;
   const float esc = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + (BITS == 2 ? 1 : 2)] : 0.0f;
 
+  // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
+  // hi/hi halves on lanes 4..7, zero elsewhere)
+  const uint32_t psel = c < 4 ? 0x05040100u : (c < 8 ? 0x03020706u : 0x0C0C0C0Cu);
   WaveState<D, GQ> st;
   st.init();
   const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
   const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
-  // page ids of this wavefront's range: one vector load, then read lane by lane
-  const int my_pid = (wp0 + lane < wp1) ? pt[wp0 + lane] : -1;
+  // Page-head addresses of this wavefront's range (at most 64 pages): lane i resolves page wp0+i
+  // with one vector load; ids outside the pool or of the other width are invalid and point at
+  // page-head 0 of the arena, which also serves the prefetches past the range.
+  const int64_t page = (wp0 + lane < wp1) ? (int64_t)pt[wp0 + lane] : -1;
+  const bool page_ok = page >= 0 && page < dm.pool_pages && (BITS == 2 ? page < off4 : page >= off4);
+  const uint64_t my_addr = (uint64_t)(page_ok ? page_head_addr(a.pool, page, kv, dm.hkv, D, off4) : a.pool);
+  const uint64_t valid_mask = __ballot(page_ok);
+  const uint32_t addr_lo = (uint32_t)my_addr, addr_hi = (uint32_t)(my_addr >> 32);
   if (dm.pool_pages > 0) {
-    const uint8_t* dummy = a.pool;  // page-head 0 of the arena: target of out-of-range prefetches
     page_pipeline<kHistPipe, QPage<BITS, D, GQ>>(
         wp0, wp1,
         [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
-          const int64_t page = pg < wp1 ? (int64_t)__builtin_amdgcn_readlane(my_pid, pg - wp0) : -1;
-          const bool valid = page >= 0 && page < dm.pool_pages && (BITS == 2 ? page < off4 : page >= off4);
-          load_qpage<BITS, D, GQ>(pr, valid ? page_head_addr(a.pool, page, kv, dm.hkv, D, off4) : dummy, lane);
-          return valid;
+          const int li = min(pg - wp0, kWave - 1);
+          const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
+                              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, li) << 32);
+          load_qpage<BITS, D, GQ>(pr, reinterpret_cast<GPtr<uint8_t>>(ad), lane);
+          return pg < wp1 && ((valid_mask >> li) & 1u);
         },
         [&](const QPage<BITS, D, GQ>& pr, bool valid, int pg) {
           if (valid) {
-            process_qpage<BITS, D, GQ>(st, pr, bhi, blo, sigma, esc, pg * kPage, ntok, lane);
+            process_qpage<BITS, D, GQ>(st, pr, bhi, blo, sigma, esc, psel, pg * kPage, ntok, lane);
           } else if (lane == 0) {
             atomicOr(a.ws.flags, 1u);
           }
