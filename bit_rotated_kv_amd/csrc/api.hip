@@ -10,7 +10,11 @@ using namespace oscar;
 
 namespace {
 
-constexpr int kTargetWorkgroups = 1536;  // ~6 per CU on 256 CUs
+#ifndef OSCAR_TARGET_WORKGROUPS
+#define OSCAR_TARGET_WORKGROUPS 512
+#endif
+// history workgroups a decode aims for (pages per wavefront are sized from it, 1..64)
+constexpr int kTargetWorkgroups = OSCAR_TARGET_WORKGROUPS;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

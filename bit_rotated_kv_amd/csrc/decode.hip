@@ -74,79 +74,77 @@ __device__ inline HistCounts hist_counts(const DecodeArgs& a, int b) {
 }
 
 // ------------------------------------------------------------------ query prologue
-// One workgroup per (kv-head, request). Thread (j, part) holds its part of column j of R_K in
-// registers (all loads issued together) and forms the partial dot products of every query head
-// of the group.
+// One workgroup per (query head, request): q_rot = q R_K, then the fp16 hi/lo operands of the
+// history products. Thread (j, part) holds its part of column j of R_K in registers (all loads
+// issued together) and forms one partial dot product; the parts are summed through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
   constexpr int NP = 256 / D;      // parts of a column
   constexpr int RP = D / NP;       // rows per part
-  __shared__ float qs[8][D];
-  __shared__ float part_s[NP][8][D];
-  __shared__ float qr[8][D];
+  __shared__ float qs[D];
+  __shared__ float part_s[NP][D];
+  __shared__ float red[4][3];
   const Dims& dm = a.dm;
-  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int gq = dm.gq;
-  const size_t row0 = (size_t)b * dm.hq + (size_t)kv * gq;
+  const int hq_i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int kv = hq_i / dm.gq;
+  const size_t qi = (size_t)b * dm.hq + hq_i;
   const int j = tid % D, part = tid / D;
   float rc[RP];
   const float* rot = a.rot_k + (size_t)kv * D * D;
 #pragma unroll
   for (int i = 0; i < RP; ++i) rc[i] = rot[(part * RP + i) * D + j];
-  for (int idx = tid; idx < gq * D; idx += 256) qs[idx / D][idx % D] = bf16_bits_to_f32(a.q[row0 * D + idx]);
+  if (tid < D) qs[tid] = bf16_bits_to_f32(a.q[qi * D + tid]);
   __syncthreads();
-  for (int h = 0; h < gq; ++h) {
-    float acc = 0.0f;
+  float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RP; ++i) acc = fmaf(qs[h][part * RP + i], rc[i], acc);
-    part_s[part][h][j] = acc;
+  for (int i = 0; i < RP; ++i) acc = fmaf(qs[part * RP + i], rc[i], acc);
+  part_s[part][j] = acc;
+  __syncthreads();
+  // thread jj < D: rotated, log2-scaled query channel jj; per-head sum and the largest
+  // magnitudes the INT2 and INT4 operand scalings see
+  const int jj = tid;
+  float v = 0.0f, m2 = 0.0f, m4 = 0.0f;
+  if (jj < D) {
+    float sacc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) sacc += part_s[p][jj];
+    v = sacc * a.scale_log2e;
+    const int m = (jj % 8) / 2;
+    m2 = ldexpf(fabsf(v), 24 - 2 * m);
+    m4 = ldexpf(fabsf(v), 24 - 4 * (m % 2));
+  }
+  const float ws = wave_sum(v), wm2 = wave_max(m2), wm4 = wave_max(m4);
+  const int wave = tid / kWave, lane = tid % kWave;
+  if (lane == 0) {
+    red[wave][0] = ws;
+    red[wave][1] = wm2;
+    red[wave][2] = wm4;
   }
   __syncthreads();
-  for (int idx = tid; idx < gq * D; idx += 256) {
-    const int h = idx / D, jj = idx % D;
-    float s = 0.0f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) s += part_s[p][h][jj];
-    qr[h][jj] = s * a.scale_log2e;
+  const float sum = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+  const float mm2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
+  const float mm4 = fmaxf(fmaxf(red[0][2], red[1][2]), fmaxf(red[2][2], red[3][2]));
+  int e2 = 0, e4 = 0;
+  if (mm2 > 0.0f) { frexpf(mm2, &e2); e2 -= 15; }
+  if (mm4 > 0.0f) { frexpf(mm4, &e4); e4 -= 15; }
+  if (jj < D) {
+    const int m = (jj % 8) / 2;
+    const float q2 = ldexpf(v, 24 - 2 * m - e2);
+    const uint32_t h2 = f32_to_f16_bits(q2);
+    a.ws.qh2[qi * D + jj] = (uint16_t)h2;
+    a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(q2 - f16_bits_to_f32(h2));
+    if (dm.mixed) {
+      const float q4 = ldexpf(v, 24 - 4 * (m % 2) - e4);
+      const uint32_t h4 = f32_to_f16_bits(q4);
+      a.ws.qh4[qi * D + jj] = (uint16_t)h4;
+      a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(q4 - f16_bits_to_f32(h4));
+    }
   }
-  __syncthreads();
-  for (int h = wave; h < gq; h += 4) {
-    const size_t qi = row0 + h;
-    float sum = 0.0f, m2 = 0.0f, m4 = 0.0f;
-    for (int jj = lane; jj < D; jj += kWave) {
-      const float v = qr[h][jj];
-      const int m = (jj % 8) / 2;
-      sum += v;
-      m2 = fmaxf(m2, ldexpf(fabsf(v), 24 - 2 * m));
-      m4 = fmaxf(m4, ldexpf(fabsf(v), 24 - 4 * (m % 2)));
-    }
-    sum = wave_sum(sum);
-    m2 = wave_max(m2);
-    m4 = wave_max(m4);
-    int e2 = 0, e4 = 0;
-    if (m2 > 0.0f) { frexpf(m2, &e2); e2 -= 15; }
-    if (m4 > 0.0f) { frexpf(m4, &e4); e4 -= 15; }
-    for (int jj = lane; jj < D; jj += kWave) {
-      const float v = qr[h][jj];
-      const int m = (jj % 8) / 2;
-      const float q2 = ldexpf(v, 24 - 2 * m - e2);
-      const uint32_t h2 = f32_to_f16_bits(q2);
-      a.ws.qh2[qi * D + jj] = (uint16_t)h2;
-      a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(q2 - f16_bits_to_f32(h2));
-      if (dm.mixed) {
-        const float q4 = ldexpf(v, 24 - 4 * (m % 2) - e4);
-        const uint32_t h4 = f32_to_f16_bits(q4);
-        a.ws.qh4[qi * D + jj] = (uint16_t)h4;
-        a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(q4 - f16_bits_to_f32(h4));
-      }
-    }
-    if (lane == 0) {
-      a.ws.qsc[qi * 4 + 0] = sum;
-      a.ws.qsc[qi * 4 + 1] = ldexpf(1.0f, e2);
-      a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e4);
-      a.ws.qsc[qi * 4 + 3] = 0.0f;
-    }
+  if (tid == 0) {
+    a.ws.qsc[qi * 4 + 0] = sum;
+    a.ws.qsc[qi * 4 + 1] = ldexpf(1.0f, e2);
+    a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e4);
+    a.ws.qsc[qi * 4 + 3] = 0.0f;
   }
 }
 
@@ -692,8 +690,9 @@ template <int D, int GQ>
 __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
   __shared__ float o_lds[4][2 * GQ][D];
   __shared__ float st_lds[4][3][8];
-  const int n_win = a.dm.batch * a.dm.hkv * a.ws.nwin;
-  const int n_int2 = a.dm.batch * a.dm.hkv * a.ws.s2;
+  const int nwin = a.ws.nwin, s2 = a.ws.s2;
+  const int n_win = a.dm.batch * a.dm.hkv * nwin;
+  const int n_int2 = a.dm.batch * a.dm.hkv * s2;
   const int bid = blockIdx.x;
   if (bid < n_win) {
     window_role<D, GQ>(a, bid, o_lds, st_lds);
@@ -701,6 +700,121 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
     hist_role<2, D, GQ>(a, bid - n_win, o_lds, st_lds);
   } else {
     hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds);
+  }
+}
+
+// ------------------------------------------------------------------ merge
+// One 1024-thread workgroup per (request, kv-head) merges every partial of the group -- window
+// slots, INT2 and INT4 history slots -- for its GQ query heads. All slots of a head are weighted
+// against one common maximum (lse in log2 units); the history sum, in the rotated basis of the
+// values, is un-rotated with R_V^T (each R_V row read once per group) and added to the window sum.
+constexpr int kMergeThreads = 1024;
+
+template <int D, int GQ>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  constexpr int NT = kMergeThreads;
+  constexpr int NW = NT / kWave;      // wavefronts
+  constexpr int C4 = D / 4;           // float4 columns of a partial
+  constexpr int TPH = NT / GQ;        // threads per head
+  constexpr int NG = TPH / C4;        // slot groups per head
+  constexpr int NP = NT / D;          // parts of an R_V row
+  constexpr int RP = D / NP;
+  constexpr int WPH = NW / GQ;        // wavefronts per head in the max pass
+  __shared__ float m_s[NW];
+  __shared__ float4 acc_h[NG][GQ][C4], acc_w[NG][GQ][C4];
+  __shared__ float w_s[NG][GQ];
+  __shared__ float hsum[GQ][D];
+  __shared__ float part_s[NP][GQ][D];
+  const Dims& dm = a.dm;
+  const int bk = blockIdx.x, kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const HistCounts hc = hist_counts(a, b);
+  const int ppwg = 4 * a.ws.ppw;
+  const int nwin = a.ws.nwin;
+  const int n_a = (min((hc.n2 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
+  const int n_b = (min((hc.n4 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
+  const int n = nwin + n_a + n_b;
+  // merged index i -> slot: window [0, nwin), INT2 [nwin, nwin+n_a), INT4 after the s2 INT2 slots
+  const int skip = a.ws.s2 - n_a;
+  auto slot_of = [&](int i) { return i < nwin + n_a ? i : i + skip; };
+  const size_t sbase = (size_t)bk * a.ws.ns;
+  const float* pl = a.ws.part_lse + sbase * GQ;
+  const float* po = a.ws.part_o + sbase * GQ * D;
+  // R_V row slices for the un-rotation (loads in flight during the merge)
+  const int j = tid % D, part = tid / D;
+  float rr[RP];
+  const float* rv = a.rot_v + ((size_t)kv * D + j) * D + part * RP;
+#pragma unroll
+  for (int i = 0; i < RP; i += 4) {
+    const float4 r4 = *reinterpret_cast<const float4*>(rv + i);
+    rr[i] = r4.x;
+    rr[i + 1] = r4.y;
+    rr[i + 2] = r4.z;
+    rr[i + 3] = r4.w;
+  }
+  // per-head maximum of the slot lse values: WPH wavefronts per head
+  {
+    const int hh = wave % GQ, wk = wave / GQ;
+    float m = kNegInf;
+    for (int i = wk * kWave + lane; i < n; i += WPH * kWave) m = fmaxf(m, pl[slot_of(i) * GQ + hh]);
+    m = wave_max(m);
+    if (lane == 0) m_s[wave] = m;
+  }
+  __syncthreads();
+  const int hh = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
+  float M = kNegInf;
+#pragma unroll
+  for (int wk = 0; wk < WPH; ++wk) M = fmaxf(M, m_s[wk * GQ + hh]);
+  float4 ah = {0.0f, 0.0f, 0.0f, 0.0f}, aw = {0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+#pragma unroll 8
+  for (int i = grp; i < n; i += NG) {
+    const int sl = slot_of(i);
+    const float l = pl[sl * GQ + hh];
+    const float4 v = *reinterpret_cast<const float4*>(po + ((size_t)sl * GQ + hh) * D + 4 * c4);
+    const float w = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - M);  // 0 for empty slots
+    wsum += w;
+    const float wh = i < nwin ? 0.0f : w, ww = i < nwin ? w : 0.0f;
+    ah.x = fmaf(wh, v.x, ah.x);
+    ah.y = fmaf(wh, v.y, ah.y);
+    ah.z = fmaf(wh, v.z, ah.z);
+    ah.w = fmaf(wh, v.w, ah.w);
+    aw.x = fmaf(ww, v.x, aw.x);
+    aw.y = fmaf(ww, v.y, aw.y);
+    aw.z = fmaf(ww, v.z, aw.z);
+    aw.w = fmaf(ww, v.w, aw.w);
+  }
+  acc_h[grp][hh][c4] = ah;
+  acc_w[grp][hh][c4] = aw;
+  if (c4 == 0) w_s[grp][hh] = wsum;
+  __syncthreads();
+  for (int t = tid; t < GQ * D; t += NT) {
+    const int h2 = t / D, ch = t % D;
+    float hs = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) hs += reinterpret_cast<const float*>(&acc_h[gg][h2][0])[ch];
+    hsum[h2][ch] = hs;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h2 = 0; h2 < GQ; ++h2) {
+    float sacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) sacc = fmaf(hsum[h2][part * RP + i], rr[i], sacc);
+    part_s[part][h2][j] = sacc;
+  }
+  __syncthreads();
+  for (int t = tid; t < GQ * D; t += NT) {
+    const int h2 = t / D, ch = t % D;
+    float oh = 0.0f, ow = 0.0f, W = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) oh += part_s[p][h2][ch];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      ow += reinterpret_cast<const float*>(&acc_w[gg][h2][0])[ch];
+      W += w_s[gg][h2];
+    }
+    a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h2) * D + ch] = W > 0.0f ? (oh + ow) / W : 0.0f;
   }
 }
 
@@ -816,61 +930,6 @@ __device__ void merge_slots(const float* po, const float* pl, size_t sbase, int 
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-  constexpr int NP = 256 / D;
-  constexpr int RP = D / NP;
-  __shared__ float wl[kMaxSlots];
-  __shared__ float red[256];
-  __shared__ float acc_s[256 / (D / 4)][D];
-  __shared__ float orot[D], obf[D];
-  __shared__ float part_s[NP][D];
-  __shared__ float lse_s[2];
-  const Dims& dm = a.dm;
-  const int hq_i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int gq = dm.gq, kv = hq_i / gq, hh = hq_i % gq;
-  const HistCounts hc = hist_counts(a, b);
-  const int ppwg = 4 * a.ws.ppw;
-  const int n_a = (min((hc.n2 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
-  const int n_b = (min((hc.n4 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
-  const size_t sbase = ((size_t)b * dm.hkv + kv) * a.ws.ns;
-  // R_V row slices for the un-rotation, loaded while the partials are merged
-  const int j = tid % D, part = tid / D;
-  float rr[RP];
-  const float* rv = a.rot_v + ((size_t)kv * D + j) * D + part * RP;
-#pragma unroll
-  for (int i = 0; i < RP; i += 4) {
-    const float4 r4 = *reinterpret_cast<const float4*>(rv + i);
-    rr[i] = r4.x;
-    rr[i + 1] = r4.y;
-    rr[i + 2] = r4.z;
-    rr[i + 3] = r4.w;
-  }
-  merge_slots<D>(a.ws.part_o, a.ws.part_lse, sbase, gq, hh, n_a + n_b, a.ws.nwin, n_a, a.ws.nwin + a.ws.s2, wl, red,
-                 acc_s, orot, &lse_s[0]);
-  merge_slots<D>(a.ws.part_o, a.ws.part_lse, sbase, gq, hh, a.ws.nwin, 0, a.ws.nwin, 0, wl, red, acc_s, obf,
-                 &lse_s[1]);
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < RP; ++i) s = fmaf(orot[part * RP + i], rr[i], s);
-  part_s[part][j] = s;
-  __syncthreads();
-  if (tid < D) {
-    float oh = 0.0f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) oh += part_s[p][tid];
-    const float lseA = lse_s[0], lseB = lse_s[1];
-    const float MM = fmaxf(lseA, lseB);
-    float o = 0.0f;
-    if (MM != kNegInf) {
-      const float wa = lseA == kNegInf ? 0.0f : exp2f(lseA - MM);
-      const float wb = lseB == kNegInf ? 0.0f : exp2f(lseB - MM);
-      o = (wa * oh + wb * obf[tid]) / (wa + wb);
-    }
-    a.out[((size_t)b * dm.hq + hq_i) * D + tid] = o;
-  }
-}
-
-template <int D>
 __global__ __launch_bounds__(256) void bf16_merge_kernel(Bf16Args a) {
   __shared__ float wl[kMaxSlots];
   __shared__ float red[256];
@@ -896,12 +955,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     if (a.events) (void)hipEventRecord(a.events[i], stream);
   };
   mark(0);
-  hipLaunchKernelGGL(q_prologue_kernel<D>, dim3(dm.hkv, dm.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(q_prologue_kernel<D>, dim3(dm.hq, dm.batch), dim3(256), 0, stream, a);
   mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
   hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(256), 0, stream, a);
   mark(2);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(dm.hq, dm.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
   mark(3);
   return hipGetLastError();
 }

@@ -33,7 +33,7 @@ struct DecodeWs {
   int ppw;                 // pages per wavefront in a history split (4 waves per split), <= 64
 };
 
-constexpr int kMaxSlots = 3200;  // partial slots per (request, kv-head) the merge holds in LDS
+constexpr int kMaxSlots = 3200;  // history partial slots per (request, kv-head)
 
 struct DecodeArgs {
   Dims dm;

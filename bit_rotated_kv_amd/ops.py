@@ -139,7 +139,7 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
                 max_seq_len: int, out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
                 page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                 events: Optional[list] = None) -> torch.Tensor:
-    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (6 torch.cuda.Event), calls the
+    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (4 torch.cuda.Event), calls the
     timing variant, which records them around the kernels of the call."""
     _need(q, torch.bfloat16, "q")
     _need(seq_len, torch.int32, "seq_len")

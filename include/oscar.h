@@ -181,12 +181,14 @@ size_t oscar_decode_workspace_bytes(const oscar_layout_t* layout, int32_t batch,
  * softmax_scale*q.k over the BF16 sink/recent tokens and softmax_scale*(q.R_K).x_hat over
  * history tokens; one softmax over all of them; out = sum_BF16 p v + (sum_hist p x_hat_V).R_V^T.
  * Computed as bitwidth-homogeneous splits (BF16 / INT2 / INT4 pages) with fp32 accumulation,
- * merged by log-sum-exp.
+ * merged by log-sum-exp (one merge workgroup per request and kv-head).
  *   q          [batch][Hq][d] bf16
  *   out        [batch][Hq][d] fp32
  *   softmax_scale 0 -> 1/sqrt(d)
  *   workspace  >= oscar_decode_workspace_bytes(); word 0 (uint32) is OR-ed with 1 when a page
- *              id outside [0, pool_pages) was skipped. Contents are scratch between calls.
+ *              id outside [0, pool_pages) was skipped. Contents are scratch between calls; calls
+ *              that overlap in time must not share a workspace.
+ *   Page tables are read only at indices below pt_stride (longer histories are cut there).
  */
 oscar_status_t oscar_decode_attn(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                  const void* q, const int32_t* seq_len, const int32_t* n_int4,

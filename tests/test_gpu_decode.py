@@ -72,6 +72,26 @@ def test_decode_is_deterministic():
     assert np.array_equal(a, b)
 
 
+def test_decode_reuses_a_dirty_workspace():
+    """Every workspace byte the decode reads is written earlier in the same call: a workspace
+    holding garbage (error word aside) and reused call after call gives the fresh-workspace
+    result."""
+    p = P.make_problem(small(2, batch=3, num_q_heads=8, num_kv_heads=2, seq_lens=(2500, 400, 1300)),
+                       with_oracle=False)
+    cb, rk, rv = G.build_cache(p, oracle_written=False)
+    ref, _ = G.decode(p, cb, rk, rv)
+    ws = torch.full((brk.decode_workspace_bytes(cb.layout, p.w.batch, cb.max_seq_len),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    ws[:4] = 0
+    q = G.bf16_tensor(oracle.bf16_bits(p.q))
+    for _ in range(3):
+        out = brk.decode_attn(cb.layout, q, cb.seq_len, cb.window, cb.pool, cb.page_table, rk, rv, ws,
+                              cb.max_seq_len, n_int4=cb.n_int4, page_table4=cb.page_table4)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+    assert int(ws[:4].view(torch.int32).item()) == 0
+
+
 def test_decode_skips_out_of_range_page_ids():
     p = P.make_problem(small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)))
     cb, rk, rv = G.build_cache(p, oracle_written=True)
