@@ -29,7 +29,12 @@
 namespace oscar {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kHistPipe = 4;   // history pages in the per-wave load ring
+#ifndef OSCAR_HIST_PIPE2
+#define OSCAR_HIST_PIPE2 4
+#endif
+// history pages in the per-wave load ring (INT2 page-heads are 1152 B, INT4 2176 B at d = 128)
+constexpr int kHistPipe2 = OSCAR_HIST_PIPE2;
+constexpr int kHistPipe4 = 4;
 constexpr int kBf16Pipe = 2;   // BF16 pages in the per-wave load ring (8 KB each)
 
 __device__ __forceinline__ float4_t mfma32_f16(const u32x4_t& a, const half8_t& b, float4_t c) {
@@ -661,7 +666,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const uint64_t valid_mask = __ballot(page_ok);
   const uint32_t addr_lo = (uint32_t)my_addr, addr_hi = (uint32_t)(my_addr >> 32);
   if (dm.pool_pages > 0) {
-    page_pipeline<kHistPipe, QPage<BITS, D, GQ>>(
+    page_pipeline<BITS == 2 ? kHistPipe2 : kHistPipe4, QPage<BITS, D, GQ>>(
         wp0, wp1,
         [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
           const int li = min(pg - wp0, kWave - 1);
