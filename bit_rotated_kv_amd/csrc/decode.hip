@@ -105,9 +105,15 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
   for (int i = 0; i < RP; ++i) acc = fmaf(qs[part * RP + i], rc[i], acc);
   part_s[part][j] = acc;
   __syncthreads();
-  // thread jj < D: rotated, log2-scaled query channel jj; per-head sum and the largest
-  // magnitudes the INT2 and INT4 operand scalings see
+  // Thread jj < D holds the rotated, log2-scaled query channel v = q'_jj. The history products
+  // see v as fp16 operands scaled per code bit position p (the code c sits at bit p of its
+  // fp16 slot, i.e. has the value c*2^(p-24)): operand = v*2^(24-p-E) with one exponent E per
+  // head and width. v is split on a power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11):
+  // v_hi = Delta*rint(v/Delta) has at most 11 significant bits, so its operand is exact in
+  // fp16 and every partial sum of c*v_hi over a head is an exact fp32 multiple of Delta
+  // (|sum| <= 15 * 128 * 2^11 Delta < 2^24 Delta); v_lo = v - v_hi carries the rest.
   const int jj = tid;
+  const int wave = tid / kWave, lane = tid % kWave;
   float v = 0.0f, m2 = 0.0f, m4 = 0.0f;
   if (jj < D) {
     float sacc = 0.0f;
@@ -118,38 +124,47 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
     m2 = ldexpf(fabsf(v), 24 - 2 * m);
     m4 = ldexpf(fabsf(v), 24 - 4 * (m % 2));
   }
-  const float ws = wave_sum(v), wm2 = wave_max(m2), wm4 = wave_max(m4);
-  const int wave = tid / kWave, lane = tid % kWave;
-  if (lane == 0) {
-    red[wave][0] = ws;
-    red[wave][1] = wm2;
-    red[wave][2] = wm4;
+  {
+    const float wv = wave_max(fabsf(v)), wm2 = wave_max(m2), wm4 = wave_max(m4);
+    if (lane == 0) {
+      red[wave][0] = wv;
+      red[wave][1] = wm2;
+      red[wave][2] = wm4;
+    }
   }
   __syncthreads();
-  const float sum = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+  const float vmax = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
   const float mm2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
   const float mm4 = fmaxf(fmaxf(red[0][2], red[1][2]), fmaxf(red[2][2], red[3][2]));
-  int e2 = 0, e4 = 0;
+  int e2 = 0, e4 = 0, ev = 0;
   if (mm2 > 0.0f) { frexpf(mm2, &e2); e2 -= 15; }
   if (mm4 > 0.0f) { frexpf(mm4, &e4); e4 -= 15; }
+  if (vmax > 0.0f) frexpf(vmax, &ev);  // vmax < 2^ev
+  const float v_hi = ldexpf(rintf(ldexpf(v, 11 - ev)), ev - 11);
+  const float v_lo = v - v_hi;
+  {
+    const float uh = wave_sum(v_hi), ul = wave_sum(v_lo);
+    __syncthreads();
+    if (lane == 0) {
+      red[wave][0] = uh;
+      red[wave][1] = ul;
+    }
+  }
+  __syncthreads();
   if (jj < D) {
     const int m = (jj % 8) / 2;
-    const float q2 = ldexpf(v, 24 - 2 * m - e2);
-    const uint32_t h2 = f32_to_f16_bits(q2);
-    a.ws.qh2[qi * D + jj] = (uint16_t)h2;
-    a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(q2 - f16_bits_to_f32(h2));
+    a.ws.qh2[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_hi, 24 - 2 * m - e2));
+    a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_lo, 24 - 2 * m - e2));
     if (dm.mixed) {
-      const float q4 = ldexpf(v, 24 - 4 * (m % 2) - e4);
-      const uint32_t h4 = f32_to_f16_bits(q4);
-      a.ws.qh4[qi * D + jj] = (uint16_t)h4;
-      a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(q4 - f16_bits_to_f32(h4));
+      a.ws.qh4[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_hi, 24 - 4 * (m % 2) - e4));
+      a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_lo, 24 - 4 * (m % 2) - e4));
     }
   }
   if (tid == 0) {
-    a.ws.qsc[qi * 4 + 0] = sum;
-    a.ws.qsc[qi * 4 + 1] = ldexpf(1.0f, e2);
-    a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e4);
-    a.ws.qsc[qi * 4 + 3] = 0.0f;
+    a.ws.qsc[qi * 4 + 0] = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);  // sum v_hi (exact)
+    a.ws.qsc[qi * 4 + 1] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);  // sum v_lo
+    a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e2);
+    a.ws.qsc[qi * 4 + 3] = ldexpf(1.0f, e4);
   }
 }
 
@@ -438,8 +453,10 @@ __device__ __forceinline__ uint32_t split_f16(float w) {
   return h | (f32_to_f16_bits(w - f16_bits_to_f32(h)) << 16);
 }
 
+// QK^T of one page: rows = the 16 token slots, columns = query operand columns (high parts of
+// the GQ heads in columns 0..GQ-1, low parts in GQ..2GQ-1, so one product covers both parts).
 template <int BITS, int D, int GQ>
-__device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const half8_t* bhi, const half8_t* blo) {
+__device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const half8_t* bq) {
   constexpr int NKK = D / 32;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -458,10 +475,21 @@ __device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const 
       av[2] = w1 & 0x000F000Fu;
       av[3] = w1 & 0x00F000F0u;
     }
-    acc = mfma32_f16(av, bhi[kk], acc);
-    acc = mfma32_f16(av, blo[kk], acc);
+    acc = mfma32_f16(av, bq[kk], acc);
   }
   return acc;
+}
+
+// History logit s*X + z*U + (s*X_lo + z*U_lo) of one token and head, where X = sum c*v_hi and
+// U = sum v_hi are exact fp32 multiples of the query grid: the two large products are formed
+// without rounding error (fma residuals), so cancellation between them costs no precision.
+__device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl, float uh, float ul) {
+#pragma clang fp contract(off)
+  const float p1 = s * xh;
+  const float r1 = fmaf(s, xh, -p1);
+  const float p2 = z * uh;
+  const float r2 = fmaf(z, uh, -p2);
+  return (p1 + p2) + ((r1 + r2) + fmaf(s, xl, z * ul));
 }
 
 template <int BITS, int D, int GQ>
@@ -535,18 +563,25 @@ __device__ __forceinline__ void redist_softmax(WaveState<D, GQ>& st, const float
   for (int i = 0; i < NL; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);  // 0 for -inf logits
 }
 
+// Softmax and PV product of one page, given its QK^T result `acc`: column c < GQ holds the
+// high-part product of head c, column GQ + c the low-part product.
 template <int BITS, int D, int GQ>
-__device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, const half8_t* bhi,
-                                              const half8_t* blo, float sigma, float esc, uint32_t psel,
-                                              int slot0, int ntok, int lane) {
+__device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, float4_t acc,
+                                              float uh, float ul, float esc, uint32_t psel, int slot0, int ntok,
+                                              int lane) {
   const int g = lane / 16, c = lane % 16;
-  const float4_t acc = qk_page<BITS, D, GQ>(pr, bhi, blo);
   if constexpr (GQ == 4) {
-    float x = acc[0];
-    x = dpp_row_shr_into<4, 0x2>(x, acc[1]);
-    x = dpp_row_shr_into<8, 0x4>(x, acc[2]);
-    x = dpp_row_shr_into<12, 0x8>(x, acc[3]);
-    float lg[1] = {fmaf(lo_bf16(pr.mt[0]), x * esc, hi_bf16(pr.mt[0]) * sigma)};
+    // lane (g, c) takes token 4g + c/4 of head c%4: high part from column c%4, low part from
+    // column 4 + c%4 of item c/4
+    float xh = acc[0];
+    xh = dpp_row_shr_into<4, 0x2>(xh, acc[1]);
+    xh = dpp_row_shr_into<8, 0x4>(xh, acc[2]);
+    xh = dpp_row_shr_into<12, 0x8>(xh, acc[3]);
+    float xl = acc[1];
+    xl = __uint_as_float(dpp_row_shl_into<4, 0x1>(__float_as_uint(xl), __float_as_uint(acc[0])));
+    xl = dpp_row_shr_into<4, 0x4>(xl, acc[2]);
+    xl = dpp_row_shr_into<8, 0x8>(xl, acc[3]);
+    float lg[1] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh * esc, xl * esc, uh, ul)};
     lg[0] = slot0 + 4 * g + c / 4 < ntok ? lg[0] : kNegInf;
     float p[1];
     redist_softmax<D, GQ, 1>(st, lg, p, lane);
@@ -563,12 +598,15 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const uint32_t a23 = __builtin_amdgcn_perm(u, v8, psel);
     pv_page<BITS, D, GQ>(st, pr, a01, a23);
   } else if constexpr (GQ == 8) {
-    float x0 = acc[0], x1 = acc[1];
-    x0 = dpp_row_shr_into<8, 0xC>(x0, acc[2]);
-    x1 = dpp_row_shr_into<8, 0xC>(x1, acc[3]);
+    // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8; high parts from columns 0..7,
+    // low parts from columns 8..15
+    const float h0 = dpp_row_shr_into<8, 0xC>(acc[0], acc[2]);
+    const float h1 = dpp_row_shr_into<8, 0xC>(acc[1], acc[3]);
+    const float l0 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[2]), __float_as_uint(acc[0])));
+    const float l1 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[3]), __float_as_uint(acc[1])));
     const int t0 = slot0 + 4 * g + 2 * (c / 8);
-    float lg[2] = {fmaf(lo_bf16(pr.mt[0]), x0 * esc, hi_bf16(pr.mt[0]) * sigma),
-                   fmaf(lo_bf16(pr.mt[2]), x1 * esc, hi_bf16(pr.mt[2]) * sigma)};
+    float lg[2] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0 * esc, l0 * esc, uh, ul),
+                   hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1 * esc, l1 * esc, uh, ul)};
     lg[0] = t0 < ntok ? lg[0] : kNegInf;
     lg[1] = t0 + 1 < ntok ? lg[1] : kNegInf;
     float p[2];
@@ -587,9 +625,12 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
   } else {
     float lg[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      lg[r] = slot0 + 4 * g + r < ntok ? fmaf(lo_bf16(pr.mt[2 * r]), acc[r] * esc, hi_bf16(pr.mt[2 * r]) * sigma)
-                                       : kNegInf;
+    for (int r = 0; r < 4; ++r) {
+      const float xl = __uint_as_float(dpp_row_shl<GQ>(__float_as_uint(acc[r])));
+      lg[r] = slot0 + 4 * g + r < ntok
+                  ? hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r] * esc, xl * esc, uh, ul)
+                  : kNegInf;
+    }
     float p[4];
     softmax_page<D, GQ>(st, lg, p, lane);
     float W[4];
@@ -618,75 +659,94 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const int s = idx % S;
   const int bk = idx / S;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
-  const HistCounts hc = hist_counts(a, b);
-  const int ntok = BITS == 2 ? hc.n2 : hc.n4;
-  const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
   const int ppw = a.ws.ppw;
   const int pg_begin = s * 4 * ppw;
-  if (pg_begin >= npages) return;  // uniform over the workgroup
   const int tid = threadIdx.x, lane = tid % kWave, g = lane / 16, c = lane % 16;
   const int wave = uniform(tid / kWave);
   const int wp0 = uniform(pg_begin + wave * ppw);
-  const int wp1 = uniform(min(wp0 + ppw, npages));
+  const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
+  const size_t pbase = (size_t)bk * a.ws.ns + slot;
 
+  // Loads that do not depend on the request's length are issued first, side by side with it:
+  // the page ids of this wavefront's range (lane i: page wp0+i, bounded by the table stride),
+  // the query operands and their scales.
+  const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
+  const int pidx = wp0 + lane;
+  const int64_t page = (lane < ppw && pidx < dm.pt_stride) ? (int64_t)pt[pidx] : -1;
   const uint16_t* qh = BITS == 2 ? a.ws.qh2 : a.ws.qh4;
   const uint16_t* ql = BITS == 2 ? a.ws.ql2 : a.ws.ql4;
   const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
-  const size_t qrow = qbase + (c < GQ ? c : 0);
-  half8_t bhi[NKK], blo[NKK];
+  // query operand columns: high parts of the heads in columns c < GQ, low parts in GQ..2GQ-1
+  const size_t qrow = qbase + (c < GQ ? c : (c < 2 * GQ ? c - GQ : 0));
+  half8_t bq[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    u32x4_t vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-    if (c < GQ) {
-      vh = *reinterpret_cast<const u32x4_t*>(qh + qrow * D + 32 * kk + 8 * g);
-      vl = *reinterpret_cast<const u32x4_t*>(ql + qrow * D + 32 * kk + 8 * g);
-    }
-    bhi[kk] = __builtin_bit_cast(half8_t, vh);
-    blo[kk] = __builtin_bit_cast(half8_t, vl);
+    u32x4_t v = {0, 0, 0, 0};
+    if (c < 2 * GQ) v = *reinterpret_cast<const u32x4_t*>((c < GQ ? qh : ql) + qrow * D + 32 * kk + 8 * g);
+    bq[kk] = __builtin_bit_cast(half8_t, v);
   }
   // head whose logits this lane owns: c % GQ when redistributed, c (if < GQ) otherwise
   const int hl = Redist<GQ>::on ? c % GQ : c;
   const bool hl_ok = Redist<GQ>::on || c < GQ;
-  const float sigma = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 0] : 0.0f;
-  const float esc = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + (BITS == 2 ? 1 : 2)] : 0.0f;
+  const float uh = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 0] : 0.0f;
+  const float ul = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 1] : 0.0f;
+  const float esc = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + (BITS == 2 ? 2 : 3)] : 0.0f;
+  const HistCounts hc = hist_counts(a, b);
+  const int ntok = BITS == 2 ? hc.n2 : hc.n4;
+  const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
+  if (pg_begin >= npages) {  // uniform over the workgroup: an empty partial
+    if (tid < GQ) a.ws.part_lse[pbase * GQ + tid] = kNegInf;
+    return;
+  }
+  const int wp1 = uniform(min(wp0 + ppw, npages));
 
   // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
   // hi/hi halves on lanes 4..7, zero elsewhere)
   const uint32_t psel = c < 4 ? 0x05040100u : (c < 8 ? 0x03020706u : 0x0C0C0C0Cu);
   WaveState<D, GQ> st;
   st.init();
-  const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
   const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
-  // Page-head addresses of this wavefront's range (at most 64 pages): lane i resolves page wp0+i
-  // with one vector load; ids outside the pool or of the other width are invalid and point at
+  // Page-head addresses: ids outside the pool or of the other width are invalid and point at
   // page-head 0 of the arena, which also serves the prefetches past the range.
-  const int64_t page = (wp0 + lane < wp1) ? (int64_t)pt[wp0 + lane] : -1;
   const bool page_ok = page >= 0 && page < dm.pool_pages && (BITS == 2 ? page < off4 : page >= off4);
   const uint64_t my_addr = (uint64_t)(page_ok ? page_head_addr(a.pool, page, kv, dm.hkv, D, off4) : a.pool);
   const uint64_t valid_mask = __ballot(page_ok);
   const uint32_t addr_lo = (uint32_t)my_addr, addr_hi = (uint32_t)(my_addr >> 32);
   if (dm.pool_pages > 0) {
-    page_pipeline<BITS == 2 ? kHistPipe2 : kHistPipe4, QPage<BITS, D, GQ>>(
-        wp0, wp1,
-        [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
-          const int li = min(pg - wp0, kWave - 1);
-          const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
-                              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, li) << 32);
-          load_qpage<BITS, D, GQ>(pr, reinterpret_cast<GPtr<uint8_t>>(ad), lane);
-          return pg < wp1 && ((valid_mask >> li) & 1u);
-        },
-        [&](const QPage<BITS, D, GQ>& pr, bool valid, int pg) {
-          if (valid) {
-            process_qpage<BITS, D, GQ>(st, pr, bhi, blo, sigma, esc, psel, pg * kPage, ntok, lane);
+    // Load ring of NB page buffers (compile-time indices; prefetches past the range read the
+    // dummy page-head) with the QK^T product one page ahead: the matrix cores work on page k+1
+    // while the vector units run the softmax of page k.
+    constexpr int NB = BITS == 2 ? kHistPipe2 : kHistPipe4;
+    auto load = [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
+      const int li = min(pg - wp0, kWave - 1);
+      const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, li) << 32);
+      load_qpage<BITS, D, GQ>(pr, reinterpret_cast<GPtr<uint8_t>>(ad), lane);
+      return pg < wp1 && ((valid_mask >> li) & 1u);
+    };
+    QPage<BITS, D, GQ> buf[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) ok[k] = load(buf[k], wp0 + k);
+    float4_t acc = qk_page<BITS, D, GQ>(buf[0], bq);
+    for (int pg = wp0; pg < wp1; pg += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
+        if (pg + k < wp1) {
+          const float4_t acc_next = qk_page<BITS, D, GQ>(buf[(k + 1) % NB], bq);
+          if (ok[k]) {
+            process_qpage<BITS, D, GQ>(st, buf[k], acc, uh, ul, esc, psel, (pg + k) * kPage, ntok, lane);
           } else if (lane == 0) {
             atomicOr(a.ws.flags, 1u);
           }
-        });
-  } else if (lane == 0) {
+          acc = acc_next;
+        }
+      }
+    }
+  } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
-  const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
-  const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + slot;
   workgroup_merge<D, GQ, BITS, Redist<GQ>::on>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
                                                 a.ws.part_lse + pbase * GQ);
 }
@@ -709,40 +769,30 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 1024-thread workgroup per (request, kv-head) merges every partial of the group -- window
-// slots, INT2 and INT4 history slots -- for its GQ query heads. All slots of a head are weighted
-// against one common maximum (lse in log2 units); the history sum, in the rotated basis of the
-// values, is un-rotated with R_V^T (each R_V row read once per group) and added to the window sum.
+// One 1024-thread workgroup per (request, kv-head) merges every partial slot of the group --
+// window slots, INT2 and INT4 history slots; slots of splits past the history hold lse = -inf --
+// for its GQ query heads, in one pass: each thread folds its slots with a running maximum (lse in
+// log2 units), the threads' states are combined through LDS, the history sum (rotated basis of the
+// values) is un-rotated with R_V^T (each R_V row read once per group) and added to the window sum.
 constexpr int kMergeThreads = 1024;
 
 template <int D, int GQ>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   constexpr int NT = kMergeThreads;
-  constexpr int NW = NT / kWave;      // wavefronts
   constexpr int C4 = D / 4;           // float4 columns of a partial
   constexpr int TPH = NT / GQ;        // threads per head
   constexpr int NG = TPH / C4;        // slot groups per head
   constexpr int NP = NT / D;          // parts of an R_V row
   constexpr int RP = D / NP;
-  constexpr int WPH = NW / GQ;        // wavefronts per head in the max pass
-  __shared__ float m_s[NW];
   __shared__ float4 acc_h[NG][GQ][C4], acc_w[NG][GQ][C4];
-  __shared__ float w_s[NG][GQ];
+  __shared__ float m_s[NG][GQ], w_s[NG][GQ];
   __shared__ float hsum[GQ][D];
   __shared__ float part_s[NP][GQ][D];
   const Dims& dm = a.dm;
   const int bk = blockIdx.x, kv = bk % dm.hkv, b = bk / dm.hkv;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const HistCounts hc = hist_counts(a, b);
-  const int ppwg = 4 * a.ws.ppw;
-  const int nwin = a.ws.nwin;
-  const int n_a = (min((hc.n2 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
-  const int n_b = (min((hc.n4 + kPage - 1) / kPage, dm.pt_stride) + ppwg - 1) / ppwg;
-  const int n = nwin + n_a + n_b;
-  // merged index i -> slot: window [0, nwin), INT2 [nwin, nwin+n_a), INT4 after the s2 INT2 slots
-  const int skip = a.ws.s2 - n_a;
-  auto slot_of = [&](int i) { return i < nwin + n_a ? i : i + skip; };
-  const size_t sbase = (size_t)bk * a.ws.ns;
+  const int tid = threadIdx.x;
+  const int nwin = a.ws.nwin, n = a.ws.ns;
+  const size_t sbase = (size_t)bk * n;
   const float* pl = a.ws.part_lse + sbase * GQ;
   const float* po = a.ws.part_o + sbase * GQ * D;
   // R_V row slices for the un-rotation (loads in flight during the merge)
@@ -757,47 +807,47 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
     rr[i + 2] = r4.z;
     rr[i + 3] = r4.w;
   }
-  // per-head maximum of the slot lse values: WPH wavefronts per head
-  {
-    const int hh = wave % GQ, wk = wave / GQ;
-    float m = kNegInf;
-    for (int i = wk * kWave + lane; i < n; i += WPH * kWave) m = fmaxf(m, pl[slot_of(i) * GQ + hh]);
-    m = wave_max(m);
-    if (lane == 0) m_s[wave] = m;
-  }
-  __syncthreads();
   const int hh = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
-  float M = kNegInf;
-#pragma unroll
-  for (int wk = 0; wk < WPH; ++wk) M = fmaxf(M, m_s[wk * GQ + hh]);
+  float m = kNegInf, wsum = 0.0f;
   float4 ah = {0.0f, 0.0f, 0.0f, 0.0f}, aw = {0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
 #pragma unroll 8
   for (int i = grp; i < n; i += NG) {
-    const int sl = slot_of(i);
-    const float l = pl[sl * GQ + hh];
-    const float4 v = *reinterpret_cast<const float4*>(po + ((size_t)sl * GQ + hh) * D + 4 * c4);
-    const float w = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - M);  // 0 for empty slots
-    wsum += w;
+    const float l = pl[(size_t)i * GQ + hh];
+    float4 v = *reinterpret_cast<const float4*>(po + ((size_t)i * GQ + hh) * D + 4 * c4);
+    if (l == kNegInf) v = float4{0.0f, 0.0f, 0.0f, 0.0f};  // empty slot: its o is not written
+    const float m_new = fmaxf(m, l);
+    const float sc = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);   // 0 when m is -inf
+    const float w = l == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - m_new);
+    m = m_new;
+    wsum = fmaf(wsum, sc, w);
     const float wh = i < nwin ? 0.0f : w, ww = i < nwin ? w : 0.0f;
-    ah.x = fmaf(wh, v.x, ah.x);
-    ah.y = fmaf(wh, v.y, ah.y);
-    ah.z = fmaf(wh, v.z, ah.z);
-    ah.w = fmaf(wh, v.w, ah.w);
-    aw.x = fmaf(ww, v.x, aw.x);
-    aw.y = fmaf(ww, v.y, aw.y);
-    aw.z = fmaf(ww, v.z, aw.z);
-    aw.w = fmaf(ww, v.w, aw.w);
+    ah.x = fmaf(ah.x, sc, wh * v.x);
+    ah.y = fmaf(ah.y, sc, wh * v.y);
+    ah.z = fmaf(ah.z, sc, wh * v.z);
+    ah.w = fmaf(ah.w, sc, wh * v.w);
+    aw.x = fmaf(aw.x, sc, ww * v.x);
+    aw.y = fmaf(aw.y, sc, ww * v.y);
+    aw.z = fmaf(aw.z, sc, ww * v.z);
+    aw.w = fmaf(aw.w, sc, ww * v.w);
   }
   acc_h[grp][hh][c4] = ah;
   acc_w[grp][hh][c4] = aw;
-  if (c4 == 0) w_s[grp][hh] = wsum;
+  if (c4 == 0) {
+    m_s[grp][hh] = m;
+    w_s[grp][hh] = wsum;
+  }
   __syncthreads();
   for (int t = tid; t < GQ * D; t += NT) {
     const int h2 = t / D, ch = t % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg][h2]);
     float hs = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) hs += reinterpret_cast<const float*>(&acc_h[gg][h2][0])[ch];
+    for (int gg = 0; gg < NG; ++gg) {
+      const float e = m_s[gg][h2] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_s[gg][h2] - M);
+      hs = fmaf(e, reinterpret_cast<const float*>(&acc_h[gg][h2][0])[ch], hs);
+    }
     hsum[h2][ch] = hs;
   }
   __syncthreads();
@@ -811,13 +861,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   __syncthreads();
   for (int t = tid; t < GQ * D; t += NT) {
     const int h2 = t / D, ch = t % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg][h2]);
     float oh = 0.0f, ow = 0.0f, W = 0.0f;
 #pragma unroll
     for (int p = 0; p < NP; ++p) oh += part_s[p][h2][ch];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-      ow += reinterpret_cast<const float*>(&acc_w[gg][h2][0])[ch];
-      W += w_s[gg][h2];
+      const float e = m_s[gg][h2] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_s[gg][h2] - M);
+      ow = fmaf(e, reinterpret_cast<const float*>(&acc_w[gg][h2][0])[ch], ow);
+      W = fmaf(e, w_s[gg][h2], W);
     }
     a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h2) * D + ch] = W > 0.0f ? (oh + ow) / W : 0.0f;
   }
@@ -872,7 +926,7 @@ __global__ __launch_bounds__(256) void bf16_paged_split_kernel(Bf16Args a) {
   workgroup_merge<D, GQ, 16>(st, o_lds, st_lds, a.part_o + pbase * GQ * D, a.part_lse + pbase * GQ);
 }
 
-// ------------------------------------------------------------------ merge
+// ------------------------------------------------------------------ BF16 baseline merge
 // LSE-merge of n partial slots (slot i at slot_of(i)) for one query head into o[D] and its lse.
 // All lse values are fetched first; the weighted sum then issues independent float4 loads.
 template <int D>

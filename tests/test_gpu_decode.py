@@ -47,11 +47,11 @@ def test_decode_oracle_written_cache(prob):
     cb, rk, rv = G.build_cache(p, oracle_written=True)
     got, ws = G.decode(p, cb, rk, rv)
     worst, mab = G.check_close(got, ref, tag=name)
-    # Same codes on both sides: only fp32 accumulation separates them. The history logit is the
-    # dequant-folded s*(q.c) + z*sum(q); its two terms are ~10x the logit and cancel, so the
-    # matrix-core fp32 accumulation rounding shows up as ~1e-3 absolute logit error (~2e-4 of
-    # the output), held here to 1e-3, five times inside the 5e-3 bar.
-    assert worst <= 1e-3, f"{name}: {worst:.2e}"
+    # Same codes on both sides: only the kernels' fp32 arithmetic separates them. The history
+    # logit s*(q.c) + z*sum(q) is formed from exact grid sums with error-free products, so its
+    # error stays near fp32 rounding of the logit itself; held here to 1e-4, fifty times inside
+    # the 5e-3 bar.
+    assert worst <= 1e-4, f"{name}: {worst:.2e}"
     assert int(ws[:4].view(torch.int32).item()) == 0
     print(f"{name}: oracle-written worst rel-L2 {worst:.2e} max-abs {mab:.2e}")
 
