@@ -138,14 +138,20 @@ class Int2Setup:
         torch.cuda.synchronize()
 
     def step(self, i, events=None):
+        """One decode step on cache copy i % copies: the fused step entry point, or (with events)
+        the demote and the timed decode entry point, which launch the same split kernel."""
         import bit_rotated_kv_amd as brk
         c = i % self.copies
         par = self.parity[c]
         sin, sout = self.lens[c][par], self.lens[c][1 - par]
-        brk.kv_demote(self.layout, sin, self.new_k, self.new_v, self.rk, self.rv, self.pools[c], self.page_table,
-                      self.windows[c], seq_len_out=sout)
-        brk.decode_attn(self.layout, self.q, sout, self.windows[c], self.pools[c], self.page_table, self.rk,
-                        self.rv, self.ws, self.max_seq, out=self.out, events=events)
+        if events is None:
+            brk.decode_step(self.layout, sin, self.new_k, self.new_v, self.q, self.rk, self.rv, self.pools[c],
+                            self.page_table, self.windows[c], sout, self.ws, self.max_seq, out=self.out)
+        else:
+            brk.kv_demote(self.layout, sin, self.new_k, self.new_v, self.rk, self.rv, self.pools[c], self.page_table,
+                          self.windows[c], seq_len_out=sout)
+            brk.decode_attn(self.layout, self.q, sout, self.windows[c], self.pools[c], self.page_table, self.rk,
+                            self.rv, self.ws, self.max_seq, out=self.out, events=events)
         self.parity[c] = 1 - par
 
     def bytes_per_step(self):

@@ -206,11 +206,12 @@ oscar_status_t oscar_kv_prefill(const oscar_layout_t* L, int32_t batch, int32_t 
   return launch_prefill(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
 
-oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int32_t* seq_len, const int32_t* n_int4,
-                               const void* new_k, const void* new_v, const uint8_t* demote_bits, const float* rot_k,
-                               const float* rot_v, void* pool, const int32_t* page_table, const int32_t* page_table4,
-                               int32_t pt_stride, void* window, int32_t* seq_len_out, int32_t* n_int4_out,
-                               hipStream_t stream) {
+// Validates the demote arguments and fills `a`; batch == 0 is valid (nothing to do).
+static oscar_status_t build_demote(const oscar_layout_t* L, int32_t batch, const int32_t* seq_len,
+                                   const int32_t* n_int4, const void* new_k, const void* new_v,
+                                   const uint8_t* demote_bits, const float* rot_k, const float* rot_v, void* pool,
+                                   const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                   void* window, int32_t* seq_len_out, int32_t* n_int4_out, CacheWriteArgs* out) {
   oscar_status_t st = check_layout(L);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
@@ -238,6 +239,19 @@ oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int
   a.window = static_cast<uint8_t*>(window);
   a.seq_len_out = seq_len_out;
   a.n_int4_out = n_int4_out;
+  *out = a;
+  return OSCAR_OK;
+}
+
+oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int32_t* seq_len, const int32_t* n_int4,
+                               const void* new_k, const void* new_v, const uint8_t* demote_bits, const float* rot_k,
+                               const float* rot_v, void* pool, const int32_t* page_table, const int32_t* page_table4,
+                               int32_t pt_stride, void* window, int32_t* seq_len_out, int32_t* n_int4_out,
+                               hipStream_t stream) {
+  CacheWriteArgs a{};
+  const oscar_status_t st = build_demote(L, batch, seq_len, n_int4, new_k, new_v, demote_bits, rot_k, rot_v, pool,
+                                         page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, &a);
+  if (st != OSCAR_OK || batch == 0) return st;
   return launch_demote(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
 
@@ -246,11 +260,12 @@ size_t oscar_decode_workspace_bytes(const oscar_layout_t* L, int32_t batch, int3
   return plan_decode(L, batch, max_seq_len).total;
 }
 
-static oscar_status_t decode_impl(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
-                                  const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
-                                  const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
-                                  const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
-                                  size_t workspace_bytes, float* out, hipEvent_t* events, hipStream_t stream) {
+// Validates the decode arguments and fills `out`; batch == 0 is valid (nothing to do).
+static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
+                                   const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
+                                   const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                   const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, float* out, DecodeArgs* args) {
   oscar_status_t st = check_layout(L);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || max_seq_len < 0 || pt_stride < 0 || !(softmax_scale >= 0.0f)) return OSCAR_ERR_INVALID_ARG;
@@ -293,6 +308,20 @@ static oscar_status_t decode_impl(const oscar_layout_t* L, int32_t batch, int32_
   a.ws.s2 = p.s2;
   a.ws.s4 = p.s4;
   a.ws.ppw = p.ppw;
+  *args = a;
+  return OSCAR_OK;
+}
+
+static oscar_status_t decode_impl(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
+                                  const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
+                                  const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                  const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
+                                  size_t workspace_bytes, float* out, hipEvent_t* events, hipStream_t stream) {
+  DecodeArgs a{};
+  const oscar_status_t st = build_decode(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table,
+                                         page_table4, pt_stride, rot_k, rot_v, softmax_scale, workspace,
+                                         workspace_bytes, out, &a);
+  if (st != OSCAR_OK || batch == 0) return st;
   a.events = events;
   return launch_decode(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
@@ -318,6 +347,25 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* L, int32_t batch
     if (!events[i]) return OSCAR_ERR_INVALID_ARG;
   return decode_impl(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
                      rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, events, stream);
+}
+
+oscar_status_t oscar_decode_step(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
+                                 const int32_t* n_int4, const void* new_k, const void* new_v,
+                                 const uint8_t* demote_bits, const void* q, const float* rot_k, const float* rot_v,
+                                 void* pool, const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                 void* window, int32_t* seq_len_out, int32_t* n_int4_out, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, float* out, hipStream_t stream) {
+  if (!seq_len_out) return OSCAR_ERR_INVALID_ARG;
+  if (L && L->mixed && !n_int4_out) return OSCAR_ERR_INVALID_ARG;
+  CacheWriteArgs cw{};
+  oscar_status_t st = build_demote(L, batch, seq_len, n_int4, new_k, new_v, demote_bits, rot_k, rot_v, pool,
+                                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, &cw);
+  if (st != OSCAR_OK) return st;
+  DecodeArgs a{};
+  st = build_decode(L, batch, max_seq_len, q, seq_len_out, n_int4_out, window, pool, page_table, page_table4,
+                    pt_stride, rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, &a);
+  if (st != OSCAR_OK || batch == 0) return st;
+  return launch_step(cw, a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
 
 oscar_status_t oscar_bf16_fill(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,

@@ -25,6 +25,7 @@
 // the current one, with all its page ids fetched by one vector load up front.
 #include "common.hpp"
 #include "launch.hpp"
+#include "demote.hpp"
 
 namespace oscar {
 
@@ -83,14 +84,14 @@ __device__ inline HistCounts hist_counts(const DecodeArgs& a, int b) {
 // history products. Thread (j, part) holds its part of column j of R_K in registers (all loads
 // issued together) and forms one partial dot product; the parts are summed through LDS.
 template <int D>
-__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
+__device__ inline void q_prologue_block(const DecodeArgs& a, int hq_i, int b) {
   constexpr int NP = 256 / D;      // parts of a column
   constexpr int RP = D / NP;       // rows per part
   __shared__ float qs[D];
   __shared__ float part_s[NP][D];
   __shared__ float red[4][3];
   const Dims& dm = a.dm;
-  const int hq_i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int kv = hq_i / dm.gq;
   const size_t qi = (size_t)b * dm.hq + hq_i;
   const int j = tid % D, part = tid / D;
@@ -165,6 +166,25 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
     a.ws.qsc[qi * 4 + 1] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);  // sum v_lo
     a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e2);
     a.ws.qsc[qi * 4 + 3] = ldexpf(1.0f, e4);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
+  q_prologue_block<D>(a, blockIdx.x, blockIdx.y);
+}
+
+// First launch of a fused decode step: the demote workgroups (K/V x kv-head x request) and the
+// query prologue workgroups (query head x request) are independent and run side by side.
+template <int D>
+__global__ __launch_bounds__(256) void step_pre_kernel(CacheWriteArgs cw, DecodeArgs da) {
+  const int nd = 2 * cw.dm.hkv * cw.dm.batch;
+  const int bid = blockIdx.x;
+  if (bid < nd) {
+    demote_block<D>(cw, bid % 2, (bid / 2) % cw.dm.hkv, bid / (2 * cw.dm.hkv));
+  } else {
+    const int j = bid - nd;
+    q_prologue_block<D>(da, j % da.dm.hq, j / da.dm.hq);
   }
 }
 
@@ -784,6 +804,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   constexpr int NG = TPH / C4;        // slot groups per head
   constexpr int NP = NT / D;          // parts of an R_V row
   constexpr int RP = D / NP;
+  constexpr int RS = D + 1;           // padded LDS row of R_V (conflict-free column walks)
+  __shared__ float rv_s[D * RS];
   __shared__ float4 acc_h[NG][GQ][C4], acc_w[NG][GQ][C4];
   __shared__ float m_s[NG][GQ], w_s[NG][GQ];
   __shared__ float hsum[GQ][D];
@@ -795,17 +817,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   const size_t sbase = (size_t)bk * n;
   const float* pl = a.ws.part_lse + sbase * GQ;
   const float* po = a.ws.part_o + sbase * GQ * D;
-  // R_V row slices for the un-rotation (loads in flight during the merge)
-  const int j = tid % D, part = tid / D;
-  float rr[RP];
-  const float* rv = a.rot_v + ((size_t)kv * D + j) * D + part * RP;
+  // R_V of this kv-head staged in LDS with coalesced loads (consumed after the partials)
+  {
+    const float4* rv4 = reinterpret_cast<const float4*>(a.rot_v + (size_t)kv * D * D);
 #pragma unroll
-  for (int i = 0; i < RP; i += 4) {
-    const float4 r4 = *reinterpret_cast<const float4*>(rv + i);
-    rr[i] = r4.x;
-    rr[i + 1] = r4.y;
-    rr[i + 2] = r4.z;
-    rr[i + 3] = r4.w;
+    for (int k = 0; k < D * D / 4 / NT; ++k) {
+      const int e = tid + k * NT;           // float4 index
+      const float4 r4 = rv4[e];
+      const int row = (4 * e) / D, col = (4 * e) % D;
+      float* dst = rv_s + row * RS + col;
+      dst[0] = r4.x;
+      dst[1] = r4.y;
+      dst[2] = r4.z;
+      dst[3] = r4.w;
+    }
   }
   const int hh = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
   float m = kNegInf, wsum = 0.0f;
@@ -851,12 +876,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
     hsum[h2][ch] = hs;
   }
   __syncthreads();
+  // un-rotation: thread (j, part) forms its part of out[h][j] = sum_i hsum[h][i] R_V[j][i]
+  {
+    const int j = tid % D, part = tid / D;
+    const float* rrow = rv_s + j * RS + part * RP;
+    float acc[GQ];
 #pragma unroll
-  for (int h2 = 0; h2 < GQ; ++h2) {
-    float sacc = 0.0f;
+    for (int h2 = 0; h2 < GQ; ++h2) acc[h2] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RP; ++i) sacc = fmaf(hsum[h2][part * RP + i], rr[i], sacc);
-    part_s[part][h2][j] = sacc;
+    for (int i = 0; i < RP; ++i) {
+      const float rji = rrow[i];
+#pragma unroll
+      for (int h2 = 0; h2 < GQ; ++h2) acc[h2] = fmaf(hsum[h2][part * RP + i], rji, acc[h2]);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < GQ; ++h2) part_s[part][h2][j] = acc[h2];
   }
   __syncthreads();
   for (int t = tid; t < GQ * D; t += NT) {
@@ -1022,6 +1056,28 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
   mark(3);
   return hipGetLastError();
+}
+
+template <int D, int GQ>
+static hipError_t launch_step_t(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream) {
+  const Dims& dm = a.dm;
+  const int npre = 2 * dm.hkv * dm.batch + dm.hq * dm.batch;
+  hipLaunchKernelGGL(step_pre_kernel<D>, dim3(npre), dim3(256), 0, stream, cw, a);
+  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
+  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream) {
+  if (a.dm.batch == 0) return hipSuccess;
+  const int d = a.dm.d, gq = a.dm.gq;
+#define OSCAR_DISPATCH(DD, GG) \
+  if (d == DD && gq == GG) return launch_step_t<DD, GG>(cw, a, stream);
+  OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
+  OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
+#undef OSCAR_DISPATCH
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -91,6 +91,7 @@ hipError_t launch_quantize_pack(int64_t rows, int dim, int group, int bits, floa
 hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_demote(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_step(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bf16_fill(const Bf16Args& a, hipStream_t stream);
 hipError_t launch_bf16_decode(const Bf16Args& a, hipStream_t stream);
 

@@ -171,6 +171,38 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
     return out
 
 
+def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
+                rot_k: torch.Tensor, rot_v: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
+                window: torch.Tensor, seq_len_out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
+                out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
+                n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
+                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0) -> torch.Tensor:
+    """kv_demote followed by decode_attn over the updated cache, in one call (three kernels)."""
+    _need(seq_len, torch.int32, "seq_len")
+    _need(new_k, torch.bfloat16, "new_k")
+    _need(new_v, torch.bfloat16, "new_v")
+    _need(q, torch.bfloat16, "q")
+    _need(rot_k, torch.float32, "rot_k")
+    _need(rot_v, torch.float32, "rot_v")
+    _need(pool, torch.uint8, "pool")
+    _need(page_table, torch.int32, "page_table")
+    _need(window, torch.uint8, "window")
+    _need(seq_len_out, torch.int32, "seq_len_out")
+    _need(workspace, torch.uint8, "workspace")
+    for t, n in ((n_int4, "n_int4"), (n_int4_out, "n_int4_out"), (page_table4, "page_table4")):
+        _need(t, torch.int32, n, optional=True)
+    _need(demote_bits, torch.uint8, "demote_bits", optional=True)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    check(lib().oscar_decode_step(_ref(layout), q.shape[0], max_seq_len, _p(seq_len), _p(n_int4), _p(new_k),
+                                  _p(new_v), _p(demote_bits), _p(q), _p(rot_k), _p(rot_v), _p(pool), _p(page_table),
+                                  _p(page_table4), page_table.shape[1], _p(window), _p(seq_len_out), _p(n_int4_out),
+                                  softmax_scale, _p(workspace), workspace.numel(), _p(out), _stream()),
+          "oscar_decode_step")
+    return out
+
+
 def bf16_fill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pages: torch.Tensor,
               num_pages: int, page_table: torch.Tensor):
     _need(seq_len, torch.int32, "seq_len")

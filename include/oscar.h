@@ -213,6 +213,23 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t 
                                           int32_t n_events, hipStream_t stream);
 
 /*
+ * One whole decode step: oscar_kv_demote (new_k/new_v appended, the oldest recent token demoted)
+ * followed by oscar_decode_attn of q over the updated cache, reading the lengths the demote
+ * writes (seq_len_out, and n_int4_out for a mixed cache; both required here). Identical results
+ * to the two calls in sequence. The demote and the query rotation share one launch (they are
+ * independent), so a step is three kernels: demote + query prologue, split, merge. Arguments
+ * follow the two calls above; max_seq_len bounds the updated lengths (T + 1).
+ */
+oscar_status_t oscar_decode_step(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                 const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
+                                 const void* new_v, const uint8_t* demote_bits, const void* q,
+                                 const float* rot_k, const float* rot_v, void* pool,
+                                 const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                 void* window, int32_t* seq_len_out, int32_t* n_int4_out,
+                                 float softmax_scale, void* workspace, size_t workspace_bytes, float* out,
+                                 hipStream_t stream);
+
+/*
  * In-house BF16 baseline: the full context of each request in BF16 pages (BF16 page-head
  * layout; page = Hkv page-heads, page ids index `pages`). Writes every position of k/v
  * ([batch][Hkv][max_seq_len][d] bf16, T = seq_len[b]) into the pages of `page_table`.

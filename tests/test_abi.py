@@ -120,6 +120,22 @@ def test_demote_argument_checks(lib):
     assert lib.oscar_kv_demote(L, 2, None, None, p, p, None, p, p, p, p, None, 10, p, None, None, None) == -1
 
 
+def test_step_argument_checks(lib):
+    L = ctypes.byref(layout())
+    p = 1
+    st = lib.oscar_decode_step
+    # (layout, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
+    #  page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, scale, ws, ws_bytes, out, stream)
+    assert st(L, 1, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, None, None, 0.0, p, 1 << 30, p, None) == -1
+    assert st(L, 1, 1000, 5, None, p, p, None, p, p, p, p, p, None, 100, p, 5, None, 0.0, p, 1 << 30, p, None) == -1
+    assert st(L, 1, 1000, p, None, p, p, None, None, p, p, p, p, None, 100, p, 2, None, 0.0, p, 1 << 30, p, None) == -1
+    assert st(L, 1, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, 2, None, 0.0, p, 16, p, None) == -3
+    M = ctypes.byref(layout(mixed=True, int4_page_offset=50))
+    assert st(M, 1, 1000, p, p, p, p, None, p, p, p, p, p, p, 100, p, 2, None, 0.0, p, 1 << 30, p, None) == -1
+    assert st(L, 0, 1000, None, None, None, None, None, None, None, None, None, None, None, 100, None, 2, None, 0.0,
+              None, 0, None, None) == 0
+
+
 def test_quantize_pack_argument_checks(lib):
     q = lib.oscar_quantize_pack
     assert q(-1, 128, 128, 2, 0.96, 1, 1, 1, None) == -1
