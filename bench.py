@@ -263,6 +263,39 @@ def time_bf16(w, batch, context, steps, warmup, fast_inputs):
     return ms, nbytes
 
 
+# ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's HIP sources (file names and contents, sorted)."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "bit_rotated_kv_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per split launch from the committed counter summary, or None when the summary is
+    missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 # ---------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(w, context, kv_heads=8):
     """The oracle's decode attention for `kv_heads` of the workload's KV heads (their query
@@ -340,7 +373,7 @@ def main():
         "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
                       "merge": round(float(kern[2]), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                      "kernel": "split_kernel<128,4> (BF16 window + INT2 history split-K, one launch)",
                      "bytes_per_launch": int2 + bf16},
         "setup_s": round(setup_s, 1),
