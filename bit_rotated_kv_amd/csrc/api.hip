@@ -58,8 +58,8 @@ Dims make_dims(const oscar_layout_t* L, int batch, int max_seq_len, int pt_strid
   return d;
 }
 
-int choose_ppw(int64_t total_pages) {
-  int64_t p = (total_pages + 4LL * kTargetWorkgroups - 1) / (4LL * kTargetWorkgroups);
+int choose_ppw(int64_t total_pages, int waves, int64_t target = kTargetWorkgroups) {
+  int64_t p = (total_pages + (int64_t)waves * target - 1) / ((int64_t)waves * target);
   if (p < 1) p = 1;
   if (p > 64) p = 64;
   return (int)p;
@@ -75,13 +75,17 @@ DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len) {
   int hist = max_seq_len - L->sink_len - L->recent_len;
   if (hist < 0) hist = 0;
   const int hp = (hist + kPage - 1) / kPage;
-  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * hp);
-  p.s2 = (hp + 4 * p.ppw - 1) / (4 * p.ppw);
+  constexpr int W = kSplitWaves;
+  p.nwin = ((L->sink_len + L->recent_len) / kPage + W - 1) / W;
+  // history workgroups aim at what the window workgroups leave of the target
+  const int64_t nwin_all = (int64_t)batch * L->num_kv_heads * p.nwin;
+  const int64_t hist_target = nwin_all < kTargetWorkgroups / 2 ? kTargetWorkgroups - nwin_all : kTargetWorkgroups / 2;
+  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * hp, W, hist_target);
+  p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
   p.s4 = L->mixed ? p.s2 : 0;
-  p.nwin = ((L->sink_len + L->recent_len) / kPage + 3) / 4;
   while (p.s2 + p.s4 > kMaxSlots && p.ppw < 64) {
     p.ppw = p.ppw * 2 > 64 ? 64 : p.ppw * 2;
-    p.s2 = (hp + 4 * p.ppw - 1) / (4 * p.ppw);
+    p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
     p.s4 = L->mixed ? p.s2 : 0;
   }
   p.ns = p.nwin + p.s2 + p.s4;
@@ -104,7 +108,7 @@ struct Bf16Plan {
 Bf16Plan plan_bf16(const oscar_layout_t* L, int batch, int max_seq_len) {
   Bf16Plan p;
   const int pages = (max_seq_len + kPage - 1) / kPage;
-  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * pages);
+  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * pages, 4);
   p.s = (pages + 4 * p.ppw - 1) / (4 * p.ppw);
   // fewer splits when the merge could not hold them all
   while (p.s > kMaxSlots && p.ppw < 64) {

@@ -23,6 +23,8 @@
 // split into high + low fp16 parts (~22 significant bits); the pair sits in spare rows (PV) or in
 // a second MFMA (QK^T). Each wavefront keeps the next page's loads in flight while it computes
 // the current one, with all its page ids fetched by one vector load up front.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "demote.hpp"
@@ -232,7 +234,7 @@ __device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float l
 
 // Writes the wave's state to LDS and merges the 4 waves of the workgroup into one partial
 // (o normalised, lse in log2 units). VSH_BITS selects the value-code scale restore.
-template <int D, int GQ, int VSH_BITS, bool REDIST = false>
+template <int D, int GQ, int VSH_BITS, bool REDIST = false, int NW = 4>
 __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
                                 float* part_o, float* part_lse) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, h = lane % 16;
@@ -262,13 +264,13 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
       if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
     }
   __syncthreads();
-  for (int idx = tid; idx < GQ * D; idx += 256) {
+  for (int idx = tid; idx < GQ * D; idx += NW * kWave) {
     const int hh = idx / D, ch = idx % D, nb = ch / 16;
     float M = kNegInf;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, st_lds[w][0][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, st_lds[w][0][hh]);
     float L = 0.0f, Z = 0.0f, O = 0.0f;
     if (M != kNegInf) {
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float mw = st_lds[w][0][hh];
         if (mw == kNegInf) continue;
         const float aw = exp2f(mw - M);
@@ -376,7 +378,7 @@ __device__ void window_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ]
   load_bf16_query<D, GQ>(bq, a.q, (size_t)b * dm.hq + (size_t)kv * GQ, lane);
   WaveState<D, GQ> st;
   st.init();
-  const int pg = 4 * wi + wave;
+  const int pg = kSplitWaves * wi + wave;
   if (pg < dm.wpages) {
     const uint8_t* ph = a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + pg) * bf16_page_head_bytes(D);
     Bf16Page<D> pr;
@@ -399,7 +401,8 @@ __device__ void window_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ]
     process_bf16_page<D, GQ>(st, pr, bq, valid, a.scale_log2e, lane);
   }
   const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + wi;
-  workgroup_merge<D, GQ, 16>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D, a.ws.part_lse + pbase * GQ);
+  workgroup_merge<D, GQ, 16, false, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
+                                                 a.ws.part_lse + pbase * GQ);
 }
 
 // ------------------------------------------------------------------ INT2 / INT4 history pages
@@ -680,45 +683,44 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const int bk = idx / S;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int ppw = a.ws.ppw;
-  const int pg_begin = s * 4 * ppw;
+  const int pg_begin = s * kSplitWaves * ppw;
   const int tid = threadIdx.x, lane = tid % kWave, g = lane / 16, c = lane % 16;
   const int wave = uniform(tid / kWave);
   const int wp0 = uniform(pg_begin + wave * ppw);
   const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
   const size_t pbase = (size_t)bk * a.ws.ns + slot;
 
-  // Loads that do not depend on the request's length are issued first, side by side with it:
-  // the page ids of this wavefront's range (lane i: page wp0+i, bounded by the table stride),
-  // the query operands and their scales.
+  // Loads that do not depend on the request's length are issued first, branch-free and side by
+  // side with it: the page ids of this wavefront's range (lane i: page wp0+i; the index is clamped
+  // to the table stride, which is >= 1 whenever history splits exist), the query operands and
+  // their per-head constants.
   const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
   const int pidx = wp0 + lane;
-  const int64_t page = (lane < ppw && pidx < dm.pt_stride) ? (int64_t)pt[pidx] : -1;
+  const int32_t raw_page = pt[min(pidx, dm.pt_stride - 1)];
   const uint16_t* qh = BITS == 2 ? a.ws.qh2 : a.ws.qh4;
   const uint16_t* ql = BITS == 2 ? a.ws.ql2 : a.ws.ql4;
   const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
   // query operand columns: high parts of the heads in columns c < GQ, low parts in GQ..2GQ-1
-  const size_t qrow = qbase + (c < GQ ? c : (c < 2 * GQ ? c - GQ : 0));
-  half8_t bq[NKK];
+  const uint16_t* qsrc = (c < GQ ? qh : ql) + (qbase + c % GQ) * D + 8 * g;
+  u32x4_t qv[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    u32x4_t v = {0, 0, 0, 0};
-    if (c < 2 * GQ) v = *reinterpret_cast<const u32x4_t*>((c < GQ ? qh : ql) + qrow * D + 32 * kk + 8 * g);
-    bq[kk] = __builtin_bit_cast(half8_t, v);
-  }
-  // head whose logits this lane owns: c % GQ when redistributed, c (if < GQ) otherwise
-  const int hl = Redist<GQ>::on ? c % GQ : c;
-  const bool hl_ok = Redist<GQ>::on || c < GQ;
-  const float uh = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 0] : 0.0f;
-  const float ul = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + 1] : 0.0f;
-  const float esc = hl_ok ? a.ws.qsc[(qbase + hl) * 4 + (BITS == 2 ? 2 : 3)] : 0.0f;
+  for (int kk = 0; kk < NKK; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qsrc + 32 * kk);
+  // head whose logits this lane owns: c % GQ (lanes c >= GQ of the plain layout are unused)
+  const float4 qk_const = *reinterpret_cast<const float4*>(a.ws.qsc + (qbase + c % GQ) * 4);
   const HistCounts hc = hist_counts(a, b);
   const int ntok = BITS == 2 ? hc.n2 : hc.n4;
   const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
-  if (pg_begin >= npages) {  // uniform over the workgroup: an empty partial
-    if (tid < GQ) a.ws.part_lse[pbase * GQ + tid] = kNegInf;
-    return;
+  // a wavefront (or a whole workgroup) past the history processes no page and leaves an empty
+  // partial (lse = -inf)
+  const int wp1 = uniform(max(wp0, min(wp0 + ppw, npages)));
+  const int64_t page = (lane < ppw && pidx < dm.pt_stride) ? (int64_t)raw_page : -1;
+  half8_t bq[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x4_t z = {0, 0, 0, 0};
+    bq[kk] = __builtin_bit_cast(half8_t, c < 2 * GQ ? qv[kk] : z);
   }
-  const int wp1 = uniform(min(wp0 + ppw, npages));
+  const float uh = qk_const.x, ul = qk_const.y, esc = BITS == 2 ? qk_const.z : qk_const.w;
 
   // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
   // hi/hi halves on lanes 4..7, zero elsewhere)
@@ -748,6 +750,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     bool ok[NB];
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k) ok[k] = load(buf[k], wp0 + k);
+    __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the first product waits
     float4_t acc = qk_page<BITS, D, GQ>(buf[0], bq);
     for (int pg = wp0; pg < wp1; pg += NB) {
 #pragma unroll
@@ -767,14 +770,14 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
-  workgroup_merge<D, GQ, BITS, Redist<GQ>::on>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
-                                                a.ws.part_lse + pbase * GQ);
+  workgroup_merge<D, GQ, BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
+                                                             a.ws.part_lse + pbase * GQ);
 }
 
 template <int D, int GQ>
-__global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
-  __shared__ float o_lds[4][2 * GQ][D];
-  __shared__ float st_lds[4][3][8];
+__global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a) {
+  __shared__ float o_lds[kSplitWaves][2 * GQ][D];
+  __shared__ float st_lds[kSplitWaves][3][8];
   const int nwin = a.ws.nwin, s2 = a.ws.s2;
   const int n_win = a.dm.batch * a.dm.hkv * nwin;
   const int n_int2 = a.dm.batch * a.dm.hkv * s2;
@@ -795,6 +798,67 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
 // log2 units), the threads' states are combined through LDS, the history sum (rotated basis of the
 // values) is un-rotated with R_V^T (each R_V row read once per group) and added to the window sum.
 constexpr int kMergeThreads = 1024;
+
+struct MergeState {
+  float m, wsum;   // running maximum (log2) and weight sum
+  float4 ah, aw;   // weighted history / window sums of this thread's float4 column
+};
+struct MergeCtx {
+  const float* pl;     // lse of the group's slots [slot][GQ]
+  const float* po;     // o of the group's slots [slot][GQ][D]
+  const float* rv;     // R_V of the kv-head [D][D]
+  float* rv_s;         // LDS copy of R_V, padded rows
+  int n, nwin, grp, hh, c4, tid;
+};
+
+// Folds slots base + grp + k*NG (k < MS) into the thread's state; with `stage`, also copies R_V
+// into LDS between issuing the slot loads and consuming them.
+template <int D, int GQ, int MS, int NG, int RS, int NT>
+__device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, int base, bool stage) {
+  float lv[MS];
+  float4 vv[MS];
+#pragma unroll
+  for (int k = 0; k < MS; ++k) {
+    const int i = min(base + c.grp + k * NG, c.n - 1);
+    lv[k] = c.pl[(size_t)i * GQ + c.hh];
+    vv[k] = *reinterpret_cast<const float4*>(c.po + ((size_t)i * GQ + c.hh) * D + 4 * c.c4);
+  }
+  if (stage) {
+    const float4* rv4 = reinterpret_cast<const float4*>(c.rv);
+#pragma unroll
+    for (int k = 0; k < D * D / 4 / NT; ++k) {
+      const int e = c.tid + k * NT;           // float4 index
+      const float4 r4 = rv4[e];
+      float* dst = c.rv_s + ((4 * e) / D) * RS + (4 * e) % D;
+      dst[0] = r4.x;
+      dst[1] = r4.y;
+      dst[2] = r4.z;
+      dst[3] = r4.w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MS; ++k) {
+    const int i = base + c.grp + k * NG;
+    // empty slots (lse = -inf, o not written) and clamped duplicates weigh 0
+    const float l = i < c.n ? lv[k] : kNegInf;
+    const bool live = l != kNegInf;
+    const float m_new = fmaxf(st.m, l);
+    const float sc = st.m == m_new ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);   // 0 when m is -inf
+    const float w = live ? __builtin_amdgcn_exp2f(l - m_new) : 0.0f;
+    st.m = m_new;
+    st.wsum = fmaf(st.wsum, sc, w);
+    const float4 v = live ? vv[k] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float wh = i < c.nwin ? 0.0f : w, ww = i < c.nwin ? w : 0.0f;
+    st.ah.x = fmaf(st.ah.x, sc, wh * v.x);
+    st.ah.y = fmaf(st.ah.y, sc, wh * v.y);
+    st.ah.z = fmaf(st.ah.z, sc, wh * v.z);
+    st.ah.w = fmaf(st.ah.w, sc, wh * v.w);
+    st.aw.x = fmaf(st.aw.x, sc, ww * v.x);
+    st.aw.y = fmaf(st.aw.y, sc, ww * v.y);
+    st.aw.z = fmaf(st.aw.z, sc, ww * v.z);
+    st.aw.w = fmaf(st.aw.w, sc, ww * v.w);
+  }
+}
 
 template <int D, int GQ>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
@@ -817,44 +881,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   const size_t sbase = (size_t)bk * n;
   const float* pl = a.ws.part_lse + sbase * GQ;
   const float* po = a.ws.part_o + sbase * GQ * D;
-  // R_V of this kv-head staged in LDS with coalesced loads (consumed after the partials)
-  {
-    const float4* rv4 = reinterpret_cast<const float4*>(a.rot_v + (size_t)kv * D * D);
-#pragma unroll
-    for (int k = 0; k < D * D / 4 / NT; ++k) {
-      const int e = tid + k * NT;           // float4 index
-      const float4 r4 = rv4[e];
-      const int row = (4 * e) / D, col = (4 * e) % D;
-      float* dst = rv_s + row * RS + col;
-      dst[0] = r4.x;
-      dst[1] = r4.y;
-      dst[2] = r4.z;
-      dst[3] = r4.w;
-    }
-  }
   const int hh = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
-  float m = kNegInf, wsum = 0.0f;
-  float4 ah = {0.0f, 0.0f, 0.0f, 0.0f}, aw = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-  for (int i = grp; i < n; i += NG) {
-    const float l = pl[(size_t)i * GQ + hh];
-    float4 v = *reinterpret_cast<const float4*>(po + ((size_t)i * GQ + hh) * D + 4 * c4);
-    if (l == kNegInf) v = float4{0.0f, 0.0f, 0.0f, 0.0f};  // empty slot: its o is not written
-    const float m_new = fmaxf(m, l);
-    const float sc = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);   // 0 when m is -inf
-    const float w = l == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - m_new);
-    m = m_new;
-    wsum = fmaf(wsum, sc, w);
-    const float wh = i < nwin ? 0.0f : w, ww = i < nwin ? w : 0.0f;
-    ah.x = fmaf(ah.x, sc, wh * v.x);
-    ah.y = fmaf(ah.y, sc, wh * v.y);
-    ah.z = fmaf(ah.z, sc, wh * v.z);
-    ah.w = fmaf(ah.w, sc, wh * v.w);
-    aw.x = fmaf(aw.x, sc, ww * v.x);
-    aw.y = fmaf(aw.y, sc, ww * v.y);
-    aw.z = fmaf(aw.z, sc, ww * v.z);
-    aw.w = fmaf(aw.w, sc, ww * v.w);
+  // Slots are taken 4 or 8 at a time per thread: every load of a batch is issued (indices clamped
+  // to the last slot, so always in bounds) before any is consumed, and the first batch's loads
+  // share one round trip with the R_V staging.
+  MergeState ms_st{kNegInf, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  const MergeCtx mc{pl, po, a.rot_v + (size_t)kv * D * D, rv_s, n, nwin, grp, hh, c4, tid};
+  const int per_thread = (n + NG - 1) / NG;   // uniform
+  if (per_thread <= 4) {
+    merge_fold<D, GQ, 4, NG, RS, NT>(ms_st, mc, 0, true);
+  } else {
+    merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, 0, true);
+    for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, base, false);
   }
+  const float m = ms_st.m, wsum = ms_st.wsum;
+  const float4 ah = ms_st.ah, aw = ms_st.aw;
   acc_h[grp][hh][c4] = ah;
   acc_w[grp][hh][c4] = aw;
   if (c4 == 0) {
@@ -1051,7 +1092,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(q_prologue_kernel<D>, dim3(dm.hq, dm.batch), dim3(256), 0, stream, a);
   mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), 0, stream, a);
   mark(2);
   hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
   mark(3);
@@ -1064,7 +1105,7 @@ static hipError_t launch_step_t(const CacheWriteArgs& cw, const DecodeArgs& a, h
   const int npre = 2 * dm.hkv * dm.batch + dm.hq * dm.batch;
   hipLaunchKernelGGL(step_pre_kernel<D>, dim3(npre), dim3(256), 0, stream, cw, a);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), 0, stream, a);
   hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -34,6 +34,8 @@ struct DecodeWs {
 };
 
 constexpr int kMaxSlots = 3200;  // history partial slots per (request, kv-head)
+// wavefronts of a decode split workgroup (6 was measured slower than 4 at both batch sizes)
+constexpr int kSplitWaves = 4;
 
 struct DecodeArgs {
   Dims dm;
