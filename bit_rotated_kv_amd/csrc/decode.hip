@@ -613,10 +613,11 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     // A operand of the PV product: row c < 4 holds the fp16 high parts of head c for tokens
     // 4g..4g+3 (lanes c, c+4, c+8, c+12), row 4 + c the low parts (lanes c, c+4, c+8, c+12 seen
     // from row 4 + c: offsets -4, 0, +4, +8); rows 8..15 are zero (selector bytes 0x0C).
+    // (lanes 8..15 of y, u, v8 keep whatever they hold: the selector zeroes those rows)
     const uint32_t P = split_f16(p[0] * lo_bf16(pr.mt[1]));
-    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(0u, P), P);
-    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(0u, P), P);
-    const uint32_t v8 = dpp_row_shl<8>(P);
+    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(P, P), P);
+    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(P, P), P);
+    const uint32_t v8 = dpp_row_shl_into<8, 0x3>(P, P);
     const uint32_t a01 = __builtin_amdgcn_perm(y, P, psel);
     const uint32_t a23 = __builtin_amdgcn_perm(u, v8, psel);
     pv_page<BITS, D, GQ>(st, pr, a01, a23);
