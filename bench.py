@@ -2,9 +2,10 @@
 """Decode-step benchmark of attention-aware INT2 KV caching on one MI355X.
 
 One step = the whole hot path over one batch: the demote of the oldest recent token (rotate,
-clip, quantise, pack into the INT2 history, new token into the BF16 recent window) followed by
-decode attention (query rotation, BF16 sink/recent split, INT2 history split-K, log-sum-exp merge
-with the R_V^T un-rotation).
+clip, quantise, pack into the INT2 history, new token into the BF16 recent window) and decode
+attention over the updated cache (query rotation, BF16 sink/recent split, INT2 history split-K,
+log-sum-exp merge with the R_V^T un-rotation), as the library's fused step: two kernels, split
+and merge.
 
 Workload (default): a Qwen3-8B-shaped attention layer, 32 query heads / 8 KV heads, head_dim 128,
 batch 1, 100,000 tokens of context (64 BF16 sink + 256 BF16 recent + 99,680 INT2 history, group
@@ -138,20 +139,14 @@ class Int2Setup:
         torch.cuda.synchronize()
 
     def step(self, i, events=None):
-        """One decode step on cache copy i % copies: the fused step entry point, or (with events)
-        the demote and the timed decode entry point, which launch the same split kernel."""
+        """One decode step on cache copy i % copies (the fused step entry point; with events, its
+        timing variant, which records them around the split and merge kernels)."""
         import bit_rotated_kv_amd as brk
         c = i % self.copies
         par = self.parity[c]
         sin, sout = self.lens[c][par], self.lens[c][1 - par]
-        if events is None:
-            brk.decode_step(self.layout, sin, self.new_k, self.new_v, self.q, self.rk, self.rv, self.pools[c],
-                            self.page_table, self.windows[c], sout, self.ws, self.max_seq, out=self.out)
-        else:
-            brk.kv_demote(self.layout, sin, self.new_k, self.new_v, self.rk, self.rv, self.pools[c], self.page_table,
-                          self.windows[c], seq_len_out=sout)
-            brk.decode_attn(self.layout, self.q, sout, self.windows[c], self.pools[c], self.page_table, self.rk,
-                            self.rv, self.ws, self.max_seq, out=self.out, events=events)
+        brk.decode_step(self.layout, sin, self.new_k, self.new_v, self.q, self.rk, self.rv, self.pools[c],
+                        self.page_table, self.windows[c], sout, self.ws, self.max_seq, out=self.out, events=events)
         self.parity[c] = 1 - par
 
     def bytes_per_step(self):
@@ -166,7 +161,7 @@ class Int2Setup:
 
 
 def time_int2(setup, steps, warmup, eager):
-    """Returns (ms per step, mean kernel intervals [prologue, split, merge] in ms, launch mode).
+    """Returns (ms per step, mean kernel intervals [split, merge] in ms, launch mode).
 
     Step time: the K steps captured in one HIP graph and replayed (no host work inside the timed
     region). Kernel intervals: K more steps launched eagerly behind a GPU-side sleep, so every
@@ -207,7 +202,7 @@ def time_int2(setup, steps, warmup, eager):
     ms = start.elapsed_time(stop) / steps
     base += steps
     # kernel intervals
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in evs:
         for x in e:
             x.record()
@@ -216,7 +211,7 @@ def time_int2(setup, steps, warmup, eager):
     for i in range(steps):
         setup.step(base + i, events=evs[i])
     torch.cuda.synchronize()
-    k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
+    k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(2)] for i in range(steps)])
     return ms, k.mean(axis=0), mode
 
 
@@ -268,12 +263,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_tr
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the library's HIP sources (file names and contents, sorted)."""
+    """sha256 over the HIP sources that define the decode kernels and their launch plan (file
+    names and contents, sorted): everything in csrc/ except the prefill writers and the
+    stand-alone quantiser, which the decode step never launches."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "bit_rotated_kv_amd", "csrc")
     for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith((".hip", ".hpp")) and name not in ("kvwrite.hip", "quantize.hip"):
             h.update(name.encode())
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
@@ -353,7 +350,7 @@ def main():
     ms, kern, mode = time_int2(setup, args.steps, args.warmup, args.eager)
     int2, bf16, demote = setup.bytes_per_step()
     step_bytes = int2 + bf16 + demote
-    split_ms = float(kern[1])
+    split_ms = float(kern[0])
     achieved = (int2 + bf16) / (split_ms * 1e-3) / 1e9
     result = {
         "metric": "INT2-KV decode attn: us/step + achieved HBM GB/s at 100K ctx, bs 1 and 32",
@@ -370,17 +367,17 @@ def main():
                    "global_batch": batch, "seq_len": context, "parallelism": "single GPU",
                    "cache_copies": copies, "launch": mode},
         "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
-        "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
-                      "merge": round(float(kern[2]), 5)},
+        "kernel_ms": {"split": round(split_ms, 5), "merge": round(float(kern[1]), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "split_kernel<128,4> (BF16 window + INT2 history split-K, one launch)",
+                     "kernel": "split_kernel<128,4> (BF16 window + INT2 history split-K + step workgroups, "
+                               "one launch)",
                      "bytes_per_launch": int2 + bf16},
         "setup_s": round(setup_s, 1),
     }
     del setup
     torch.cuda.empty_cache()
-    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (prologue, split, merge) us: "
+    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (split, merge) us: "
         f"{', '.join(f'{x * 1e3:.2f}' for x in kern)}")
     if not args.no_bf16:
         log("timing the BF16 baseline")
@@ -401,8 +398,8 @@ def main():
         result["bs32"] = {"workload": "paged batch 32 x 32,768 tokens, demote in step", "ms_per_step": round(ms32, 5),
                           "us_per_step": round(ms32 * 1e3, 2), "GB_per_s": round((i2 + b2 + d2) / (ms32 * 1e-3) / 1e9, 1),
                           "tokens_per_s": round(32 / (ms32 * 1e-3), 1),
-                          "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
-                          "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "split_GB_per_s": round((i2 + b2) / (float(k32[0]) * 1e-3) / 1e9, 1),
+                          "split_frac": round((i2 + b2) / (float(k32[0]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel_ms": [round(float(x), 5) for x in k32]}
         del s32
         torch.cuda.empty_cache()

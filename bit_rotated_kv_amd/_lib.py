@@ -44,6 +44,8 @@ _SIGS = {
                                              c_float, _P, c_size_t, _P, _P, c_int32, _P]),
     "oscar_decode_step": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_int32, _P,
                                     _P, _P, c_float, _P, c_size_t, _P, _P]),
+    "oscar_decode_step_profiled": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             c_int32, _P, _P, _P, c_float, _P, c_size_t, _P, _P, c_int32, _P]),
     "oscar_bf16_fill": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, c_int64, _P, c_int32, _P]),
     "oscar_bf16_decode_workspace_bytes": (c_size_t, [_P, c_int32, c_int32]),
     "oscar_bf16_decode_attn": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, c_int64, _P, c_int32, c_float, _P,

@@ -67,18 +67,20 @@ int choose_ppw(int64_t total_pages, int waves, int64_t target = kTargetWorkgroup
 
 struct DecodePlan {
   int ppw, s2, s4, nwin, ns;
-  size_t off_q, off_qsc, off_po, off_pl, total;
+  size_t off_po, off_pl, total;
 };
 
-DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len) {
+// Split plan of a decode call; a fused step (step = 1) adds one window workgroup per (b, kv) and
+// one history slot.
+DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len, int step) {
   DecodePlan p;
   int hist = max_seq_len - L->sink_len - L->recent_len;
   if (hist < 0) hist = 0;
   const int hp = (hist + kPage - 1) / kPage;
   constexpr int W = kSplitWaves;
   p.nwin = ((L->sink_len + L->recent_len) / kPage + W - 1) / W;
-  // history workgroups aim at what the window workgroups leave of the target
-  const int64_t nwin_all = (int64_t)batch * L->num_kv_heads * p.nwin;
+  // history workgroups aim at what the window (and step) workgroups leave of the target
+  const int64_t nwin_all = (int64_t)batch * L->num_kv_heads * (p.nwin + step);
   const int64_t hist_target = nwin_all < kTargetWorkgroups / 2 ? kTargetWorkgroups - nwin_all : kTargetWorkgroups / 2;
   p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * hp, W, hist_target);
   p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
@@ -88,12 +90,10 @@ DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len) {
     p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
     p.s4 = L->mixed ? p.s2 : 0;
   }
-  p.ns = p.nwin + p.s2 + p.s4;
-  const size_t bhq = (size_t)batch * L->num_q_heads;
+  p.nwin += step;
+  p.ns = p.nwin + p.s2 + p.s4 + step;
   const int gq = L->num_q_heads / L->num_kv_heads;
-  p.off_q = kAlign;
-  p.off_qsc = p.off_q + 4 * align_up(bhq * L->head_dim * 2);
-  p.off_po = p.off_qsc + align_up(bhq * 16);
+  p.off_po = kAlign;
   const size_t nsl = (size_t)batch * L->num_kv_heads * p.ns * gq;
   p.off_pl = p.off_po + align_up(nsl * L->head_dim * 4);
   p.total = p.off_pl + align_up(nsl * 4);
@@ -261,7 +261,7 @@ oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int
 
 size_t oscar_decode_workspace_bytes(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len) {
   if (check_layout(L) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
-  return plan_decode(L, batch, max_seq_len).total;
+  return plan_decode(L, batch, max_seq_len, 1).total;   // covers the fused step too
 }
 
 // Validates the decode arguments and fills `out`; batch == 0 is valid (nothing to do).
@@ -269,7 +269,7 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
                                    const int32_t* seq_len, const int32_t* n_int4, const void* window, const void* pool,
                                    const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
                                    const float* rot_k, const float* rot_v, float softmax_scale, void* workspace,
-                                   size_t workspace_bytes, float* out, DecodeArgs* args) {
+                                   size_t workspace_bytes, float* out, int step, DecodeArgs* args) {
   oscar_status_t st = check_layout(L);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || max_seq_len < 0 || pt_stride < 0 || !(softmax_scale >= 0.0f)) return OSCAR_ERR_INVALID_ARG;
@@ -280,11 +280,10 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
     if (!pool || !page_table || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
     if (L->mixed && !page_table4) return OSCAR_ERR_INVALID_ARG;
   }
-  const DecodePlan p = plan_decode(L, batch, max_seq_len);
+  const DecodePlan p = plan_decode(L, batch, max_seq_len, step);
   if (p.s2 + p.s4 > kMaxSlots) return OSCAR_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total) return OSCAR_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const size_t qbytes = align_up((size_t)batch * L->num_q_heads * L->head_dim * 2);
   DecodeArgs a{};
   a.dm = make_dims(L, batch, max_seq_len, pt_stride);
   a.q = static_cast<const uint16_t*>(q);
@@ -300,11 +299,6 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.scale_log2e = scale * 1.4426950408889634f;
   a.out = out;
   a.ws.flags = reinterpret_cast<uint32_t*>(ws);
-  a.ws.qh2 = reinterpret_cast<uint16_t*>(ws + p.off_q);
-  a.ws.ql2 = reinterpret_cast<uint16_t*>(ws + p.off_q + qbytes);
-  a.ws.qh4 = reinterpret_cast<uint16_t*>(ws + p.off_q + 2 * qbytes);
-  a.ws.ql4 = reinterpret_cast<uint16_t*>(ws + p.off_q + 3 * qbytes);
-  a.ws.qsc = reinterpret_cast<float*>(ws + p.off_qsc);
   a.ws.part_o = reinterpret_cast<float*>(ws + p.off_po);
   a.ws.part_lse = reinterpret_cast<float*>(ws + p.off_pl);
   a.ws.ns = p.ns;
@@ -312,6 +306,7 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.ws.s2 = p.s2;
   a.ws.s4 = p.s4;
   a.ws.ppw = p.ppw;
+  a.step = step;
   *args = a;
   return OSCAR_OK;
 }
@@ -324,10 +319,11 @@ static oscar_status_t decode_impl(const oscar_layout_t* L, int32_t batch, int32_
   DecodeArgs a{};
   const oscar_status_t st = build_decode(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table,
                                          page_table4, pt_stride, rot_k, rot_v, softmax_scale, workspace,
-                                         workspace_bytes, out, &a);
+                                         workspace_bytes, out, 0, &a);
   if (st != OSCAR_OK || batch == 0) return st;
   a.events = events;
-  return launch_decode(a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+  const CacheWriteArgs none{};
+  return launch_decode(a, none, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
 
 oscar_status_t oscar_decode_attn(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const void* q,
@@ -346,11 +342,34 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* L, int32_t batch
                                           const float* rot_v, float softmax_scale, void* workspace,
                                           size_t workspace_bytes, float* out, hipEvent_t* events, int32_t n_events,
                                           hipStream_t stream) {
-  if (!events || n_events < 4) return OSCAR_ERR_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
+  if (!events || n_events < 3) return OSCAR_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
     if (!events[i]) return OSCAR_ERR_INVALID_ARG;
   return decode_impl(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
                      rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, events, stream);
+}
+
+static oscar_status_t step_impl(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
+                                const int32_t* n_int4, const void* new_k, const void* new_v,
+                                const uint8_t* demote_bits, const void* q, const float* rot_k, const float* rot_v,
+                                void* pool, const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                void* window, int32_t* seq_len_out, int32_t* n_int4_out, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, float* out, hipEvent_t* events,
+                                hipStream_t stream) {
+  if (!seq_len_out) return OSCAR_ERR_INVALID_ARG;
+  if (L && L->mixed && !n_int4_out) return OSCAR_ERR_INVALID_ARG;
+  CacheWriteArgs cw{};
+  oscar_status_t st = build_demote(L, batch, seq_len, n_int4, new_k, new_v, demote_bits, rot_k, rot_v, pool,
+                                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, &cw);
+  if (st != OSCAR_OK) return st;
+  DecodeArgs a{};
+  // the attention reads the cache as it stands before the step (lengths seq_len, n_int4); the
+  // demoted and the appended token enter as one-token partials
+  st = build_decode(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
+                    rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, 1, &a);
+  if (st != OSCAR_OK || batch == 0) return st;
+  a.events = events;
+  return launch_decode(a, cw, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
 }
 
 oscar_status_t oscar_decode_step(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
@@ -359,17 +378,25 @@ oscar_status_t oscar_decode_step(const oscar_layout_t* L, int32_t batch, int32_t
                                  void* pool, const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
                                  void* window, int32_t* seq_len_out, int32_t* n_int4_out, float softmax_scale,
                                  void* workspace, size_t workspace_bytes, float* out, hipStream_t stream) {
-  if (!seq_len_out) return OSCAR_ERR_INVALID_ARG;
-  if (L && L->mixed && !n_int4_out) return OSCAR_ERR_INVALID_ARG;
-  CacheWriteArgs cw{};
-  oscar_status_t st = build_demote(L, batch, seq_len, n_int4, new_k, new_v, demote_bits, rot_k, rot_v, pool,
-                                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, &cw);
-  if (st != OSCAR_OK) return st;
-  DecodeArgs a{};
-  st = build_decode(L, batch, max_seq_len, q, seq_len_out, n_int4_out, window, pool, page_table, page_table4,
-                    pt_stride, rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, &a);
-  if (st != OSCAR_OK || batch == 0) return st;
-  return launch_step(cw, a, stream) == hipSuccess ? OSCAR_OK : OSCAR_ERR_LAUNCH;
+  return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
+                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, softmax_scale, workspace,
+                   workspace_bytes, out, nullptr, stream);
+}
+
+oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len,
+                                          const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
+                                          const void* new_v, const uint8_t* demote_bits, const void* q,
+                                          const float* rot_k, const float* rot_v, void* pool,
+                                          const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                          void* window, int32_t* seq_len_out, int32_t* n_int4_out,
+                                          float softmax_scale, void* workspace, size_t workspace_bytes, float* out,
+                                          hipEvent_t* events, int32_t n_events, hipStream_t stream) {
+  if (!events || n_events < 3) return OSCAR_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (!events[i]) return OSCAR_ERR_INVALID_ARG;
+  return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
+                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, softmax_scale, workspace,
+                   workspace_bytes, out, events, stream);
 }
 
 oscar_status_t oscar_bf16_fill(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,

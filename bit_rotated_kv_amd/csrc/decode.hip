@@ -5,13 +5,23 @@
 // INT4 pages) merged by log-sum-exp.
 //
 // Kernels of one decode call, in stream order:
-//   q_prologue   q' = (q . R_K) * scale * log2(e) per query head, split into fp16 high/low
-//                matrix-core operands scaled per channel for the code unpacking below
-//   split        one launch, three homogeneous roles by workgroup index: BF16 window pages
-//                (sink + recent), INT2 history pages, INT4 history pages (mixed caches); each
-//                workgroup = 4 wavefronts and writes one (o, lse) partial per query head
-//   merge        per query head: LSE-merge the history partials (rotated basis), apply R_V^T,
-//                LSE-merge with the BF16 window partials, write the fp32 output
+//   split        one launch, homogeneous roles by workgroup index: BF16 window pages (sink +
+//                recent), INT2 history pages, INT4 history pages (mixed caches), and in a fused
+//                decode step one step workgroup per (request, kv-head); each workgroup = 4
+//                wavefronts and writes (o, lse) partials per query head. History workgroups form
+//                their own query operands: q' = (q . R_K) * scale * log2(e), split into fp16
+//                high/low matrix-core operands scaled per channel for the code unpacking below.
+//   merge        per (request, kv-head): LSE-merge the history partials (rotated basis), apply
+//                R_V^T, LSE-merge with the BF16 window partials, write the fp32 output; in a fused
+//                step it also writes the new token into its window slot.
+//
+// Fused decode step (demote the oldest recent token, append the new one, attend): the attention
+// must see the demoted token quantised and the new token in the window, but nothing has to wait
+// for the cache writes. The step workgroup rotates and quantises the demoted token with the
+// demote's own arithmetic, stores its codes into the history slot that the history workgroups do
+// not read yet (it lies past their token count), and adds two one-token partials: the demoted
+// token (rotated basis, history side) and the new token (window side). The window role skips the
+// ring slot of the demoted token, whose BF16 copy the merge then overwrites with the new token.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_f16 for QK^T, v_mfma_f32_16x16x16_f16 for PV; BF16
 // variants for the window): the 16 tokens of a page on the M rows of QK^T, the query heads of the
@@ -81,113 +91,136 @@ __device__ inline HistCounts hist_counts(const DecodeArgs& a, int b) {
   return c;
 }
 
-// ------------------------------------------------------------------ query prologue
-// One workgroup per (query head, request): q_rot = q R_K, then the fp16 hi/lo operands of the
-// history products. Thread (j, part) holds its part of column j of R_K in registers (all loads
-// issued together) and forms one partial dot product; the parts are summed through LDS.
+// ------------------------------------------------------------------ query prologue (per history workgroup)
+// Thread (column group cg, part) holds rows part*QR .. part*QR+QR-1 of columns 4cg .. 4cg+3 of
+// R_K (float4 loads issued with the workgroup's first loads).
+static_assert(kSplitWaves * kWave == 256, "split workgroups are 256 threads");
 template <int D>
-__device__ inline void q_prologue_block(const DecodeArgs& a, int hq_i, int b) {
-  constexpr int NP = 256 / D;      // parts of a column
-  constexpr int RP = D / NP;       // rows per part
-  __shared__ float qs[D];
-  __shared__ float part_s[NP][D];
-  __shared__ float red[4][3];
-  const Dims& dm = a.dm;
-  const int tid = threadIdx.x;
-  const int kv = hq_i / dm.gq;
-  const size_t qi = (size_t)b * dm.hq + hq_i;
-  const int j = tid % D, part = tid / D;
-  float rc[RP];
-  const float* rot = a.rot_k + (size_t)kv * D * D;
+struct QRotRows {
+  static constexpr int CG = D / 4;      // column groups of 4
+  static constexpr int NPQ = 256 / CG;  // parts of a column group
+  static constexpr int QR = D / NPQ;    // rows per part
+  float4 r[QR];
+  __device__ void load(const float* rot, int tid) {
+    const int cg = tid % CG, part = tid / CG;
 #pragma unroll
-  for (int i = 0; i < RP; ++i) rc[i] = rot[(part * RP + i) * D + j];
-  if (tid < D) qs[tid] = bf16_bits_to_f32(a.q[qi * D + tid]);
-  __syncthreads();
-  float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < RP; ++i) acc = fmaf(qs[part * RP + i], rc[i], acc);
-  part_s[part][j] = acc;
-  __syncthreads();
-  // Thread jj < D holds the rotated, log2-scaled query channel v = q'_jj. The history products
-  // see v as fp16 operands scaled per code bit position p (the code c sits at bit p of its
-  // fp16 slot, i.e. has the value c*2^(p-24)): operand = v*2^(24-p-E) with one exponent E per
-  // head and width. v is split on a power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11):
-  // v_hi = Delta*rint(v/Delta) has at most 11 significant bits, so its operand is exact in
-  // fp16 and every partial sum of c*v_hi over a head is an exact fp32 multiple of Delta
-  // (|sum| <= 15 * 128 * 2^11 Delta < 2^24 Delta); v_lo = v - v_hi carries the rest.
-  const int jj = tid;
-  const int wave = tid / kWave, lane = tid % kWave;
-  float v = 0.0f, m2 = 0.0f, m4 = 0.0f;
-  if (jj < D) {
-    float sacc = 0.0f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) sacc += part_s[p][jj];
-    v = sacc * a.scale_log2e;
-    const int m = (jj % 8) / 2;
-    m2 = ldexpf(fabsf(v), 24 - 2 * m);
-    m4 = ldexpf(fabsf(v), 24 - 4 * (m % 2));
+    for (int i = 0; i < QR; ++i) r[i] = *reinterpret_cast<const float4*>(rot + (size_t)(part * QR + i) * D + 4 * cg);
   }
-  {
-    const float wv = wave_max(fabsf(v)), wm2 = wave_max(m2), wm4 = wave_max(m4);
-    if (lane == 0) {
-      red[wave][0] = wv;
-      red[wave][1] = wm2;
-      red[wave][2] = wm4;
-    }
-  }
-  __syncthreads();
-  const float vmax = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
-  const float mm2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
-  const float mm4 = fmaxf(fmaxf(red[0][2], red[1][2]), fmaxf(red[2][2], red[3][2]));
-  int e2 = 0, e4 = 0, ev = 0;
-  if (mm2 > 0.0f) { frexpf(mm2, &e2); e2 -= 15; }
-  if (mm4 > 0.0f) { frexpf(mm4, &e4); e4 -= 15; }
-  if (vmax > 0.0f) frexpf(vmax, &ev);  // vmax < 2^ev
-  const float v_hi = ldexpf(rintf(ldexpf(v, 11 - ev)), ev - 11);
-  const float v_lo = v - v_hi;
-  {
-    const float uh = wave_sum(v_hi), ul = wave_sum(v_lo);
-    __syncthreads();
-    if (lane == 0) {
-      red[wave][0] = uh;
-      red[wave][1] = ul;
-    }
-  }
-  __syncthreads();
-  if (jj < D) {
-    const int m = (jj % 8) / 2;
-    a.ws.qh2[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_hi, 24 - 2 * m - e2));
-    a.ws.ql2[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_lo, 24 - 2 * m - e2));
-    if (dm.mixed) {
-      a.ws.qh4[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_hi, 24 - 4 * (m % 2) - e4));
-      a.ws.ql4[qi * D + jj] = (uint16_t)f32_to_f16_bits(ldexpf(v_lo, 24 - 4 * (m % 2) - e4));
-    }
-  }
-  if (tid == 0) {
-    a.ws.qsc[qi * 4 + 0] = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);  // sum v_hi (exact)
-    a.ws.qsc[qi * 4 + 1] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);  // sum v_lo
-    a.ws.qsc[qi * 4 + 2] = ldexpf(1.0f, e2);
-    a.ws.qsc[qi * 4 + 3] = ldexpf(1.0f, e4);
-  }
-}
+};
 
-template <int D>
-__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
-  q_prologue_block<D>(a, blockIdx.x, blockIdx.y);
-}
+template <int D, int GQ>
+struct HistQueryLds {
+  float qs[GQ][D];               // queries of the group (fp32)
+  float ps[kSplitWaves][GQ][D];  // per-wavefront partial products
+  uint16_t op[2][GQ][D];         // fp16 operands: high parts, low parts
+  float hsc[GQ][4];              // per head: sum of high parts, sum of low parts, 2^E
+};
 
-// First launch of a fused decode step: the demote workgroups (K/V x kv-head x request) and the
-// query prologue workgroups (query head x request) are independent and run side by side.
-template <int D>
-__global__ __launch_bounds__(256) void step_pre_kernel(CacheWriteArgs cw, DecodeArgs da) {
-  const int nd = 2 * cw.dm.hkv * cw.dm.batch;
-  const int bid = blockIdx.x;
-  if (bid < nd) {
-    demote_block<D>(cw, bid % 2, (bid / 2) % cw.dm.hkv, bid / (2 * cw.dm.hkv));
-  } else {
-    const int j = bid - nd;
-    q_prologue_block<D>(da, j % da.dm.hq, j / da.dm.hq);
+// Words of the group's bf16 queries that each thread loads.
+template <int D, int GQ>
+constexpr int kQueryWords = (GQ * D / 2 + 255) / 256;
+
+// Query operands of a history workgroup for its GQ heads and code width BITS. v = q'_j (rotated,
+// log2-scaled) is split on a power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11): v_hi =
+// Delta*rint(v/Delta) has at most 11 significant bits, so its fp16 operand is exact and every
+// partial sum of c*v_hi over a head is an exact fp32 multiple of Delta (|sum| <= 15 * 128 *
+// 2^11 Delta < 2^24 Delta); v_lo = v - v_hi carries the rest. The products see v as fp16 operands
+// scaled per code bit position p (a code c at bit p of its fp16 slot has the value c*2^(p-24)):
+// operand = v*2^(24-p-E), one exponent E per head. Lane (g, c) gets the operand column c (high
+// parts of head c for c < GQ, low parts of head c-GQ for GQ <= c < 2GQ, zero beyond) and the
+// constants of head c % GQ.
+template <int BITS, int D, int GQ>
+__device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
+                                    HistQueryLds<D, GQ>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
+                                    float& ul, float& esc) {
+  constexpr int CG = QRotRows<D>::CG, QR = QRotRows<D>::QR;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, c = lane % 16;
+#pragma unroll
+  for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
+    const int e = tid + 256 * i;
+    if (e < GQ * D / 2) {
+      float* qf = &L.qs[0][0];
+      qf[2 * e] = bf16_bits_to_f32(qw[i] & 0xFFFFu);
+      qf[2 * e + 1] = bf16_bits_to_f32(qw[i] >> 16);
+    }
   }
+  __syncthreads();
+  {
+    const int cg = tid % CG, part = tid / CG;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < QR; ++i) {
+        const float x = L.qs[h][part * QR + i];
+        acc.x = fmaf(x, rr.r[i].x, acc.x);
+        acc.y = fmaf(x, rr.r[i].y, acc.y);
+        acc.z = fmaf(x, rr.r[i].z, acc.z);
+        acc.w = fmaf(x, rr.r[i].w, acc.w);
+      }
+#pragma unroll
+      for (int o = CG; o < kWave; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o, kWave);
+        acc.y += __shfl_xor(acc.y, o, kWave);
+        acc.z += __shfl_xor(acc.z, o, kWave);
+        acc.w += __shfl_xor(acc.w, o, kWave);
+      }
+      if (lane < CG) *reinterpret_cast<float4*>(&L.ps[wave][h][4 * cg]) = acc;
+    }
+  }
+  __syncthreads();
+  constexpr int NC = D / kWave;  // channels per lane in the head pass
+  for (int h = wave; h < GQ; h += kSplitWaves) {
+    float v[NC];
+    float vmax = 0.0f, me = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int j = lane + kWave * k;
+      v[k] = ((L.ps[0][h][j] + L.ps[1][h][j]) + (L.ps[2][h][j] + L.ps[3][h][j])) * scale_log2e;
+      const int m = (j % 8) / 2;
+      const int p = BITS == 2 ? 2 * m : 4 * (m % 2);
+      vmax = fmaxf(vmax, fabsf(v[k]));
+      me = fmaxf(me, ldexpf(fabsf(v[k]), 24 - p));
+    }
+    vmax = wave_max(vmax);
+    me = wave_max(me);
+    int e = 0, ev = 0;
+    if (me > 0.0f) {
+      frexpf(me, &e);
+      e -= 15;
+    }
+    if (vmax > 0.0f) frexpf(vmax, &ev);  // vmax < 2^ev
+    float sh = 0.0f, sl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int j = lane + kWave * k;
+      const int m = (j % 8) / 2;
+      const int p = BITS == 2 ? 2 * m : 4 * (m % 2);
+      const float v_hi = ldexpf(rintf(ldexpf(v[k], 11 - ev)), ev - 11);
+      const float v_lo = v[k] - v_hi;
+      sh += v_hi;
+      sl += v_lo;
+      L.op[0][h][j] = (uint16_t)f32_to_f16_bits(ldexpf(v_hi, 24 - p - e));
+      L.op[1][h][j] = (uint16_t)f32_to_f16_bits(ldexpf(v_lo, 24 - p - e));
+    }
+    sh = wave_sum(sh);   // exact: a sum of multiples of Delta below 2^24 Delta
+    sl = wave_sum(sl);
+    if (lane == 0) {
+      L.hsc[h][0] = sh;
+      L.hsc[h][1] = sl;
+      L.hsc[h][2] = ldexpf(1.0f, e);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const u32x4_t z = {0, 0, 0, 0};
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&L.op[c < GQ ? 0 : 1][c % GQ][32 * kk + 8 * g]);
+    bq[kk] = __builtin_bit_cast(half8_t, c < 2 * GQ ? w : z);
+  }
+  uh = L.hsc[c % GQ][0];
+  ul = L.hsc[c % GQ][1];
+  esc = L.hsc[c % GQ][2];
 }
 
 // ------------------------------------------------------------------ per-wave softmax state
@@ -365,12 +398,136 @@ __device__ __forceinline__ void load_bf16_query(u32x4_t* bq, const uint16_t* q, 
   }
 }
 
-// Window role: workgroup wi of (b, kv) covers window pages 4*wi .. 4*wi+3, one per wavefront.
+// ------------------------------------------------------------------ step role (fused decode step)
 template <int D, int GQ>
-__device__ void window_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8]) {
+struct StepLds {
+  float xs[2 + GQ][D];                    // demoted key, demoted value, queries (fp32)
+  float parts[RotCol<D>::NP][1 + GQ][D];  // rotation part sums
+  float xr[2][D];                         // rotated demoted key, value
+  float vq[GQ][D];                        // rotated, log2-scaled queries
+  uint8_t cs[2][D];                       // codes of the demoted key, value
+  uint32_t szs[2];                        // their bf16 (scale, zero)
+};
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// One workgroup per (request, kv-head) of a fused step, with T = seq_len[b] tokens before the
+// step. Demote (T >= sink + recent): the token at T - recent is read from its ring slot, rotated
+// and quantised with the demote kernel's own arithmetic (same rotation order, same grid), and its
+// codes go into its history slot; its one-token partial -- lse = q' . k_hat, o = v_hat, rotated
+// basis -- fills the last slot (lse = -inf without a demote). The new token's one-token partial --
+// lse = scale * log2(e) * q . k_new, o = v_new -- fills window slot `wslot`. Both logits are
+// summed in fp64 from exact products. The lengths after the step are written here too; the new
+// token's window copy is written by the merge, after every window read.
+template <int D, int GQ>
+__device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk, int wslot, StepLds<D, GQ>& L) {
+  constexpr int NP = RotCol<D>::NP;
+  const Dims& dm = a.dm;
+  const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int j = tid % D, part = tid / D;
+  RotCol<D> rc;
+  rc.load(a.rot_k + (size_t)kv * D * D, j, part);
+  // cache-side lengths exactly as the demote kernel reads them
+  const int T = a.seq_len[b] < 0 ? 0 : a.seq_len[b];
+  const int n4 = (dm.mixed && a.n_int4) ? a.n_int4[b] : 0;
+  const bool demote = T >= dm.sink + dm.recent;
+  const int bw = (demote && dm.mixed && cw.bits && cw.bits[b] == 4) ? 4 : 2;
+  const int dslot = bw == 4 ? n4 : T - dm.sink - dm.recent - n4;
+  const int64_t page = demote ? demote_page(cw, b, dslot, bw) : -1;
+  const size_t qrow = (size_t)b * dm.hq + (size_t)kv * GQ;
+  const int64_t pb = bf16_page_head_bytes(D);
+  int opg = 0, ot = 0;
+  if (demote) window_slot(T - dm.recent, dm, opg, ot);
+  const uint16_t* og = reinterpret_cast<const uint16_t*>(a.window + ((size_t)bk * dm.wpages + opg) * pb);
+  for (int idx = tid; idx < (2 + GQ) * D; idx += kSplitWaves * kWave) {
+    const int r = idx / D, ch = idx % D;
+    float x = 0.0f;
+    if (r >= 2)
+      x = bf16_bits_to_f32(a.q[(qrow + r - 2) * D + ch]);
+    else if (demote)
+      x = bf16_bits_to_f32(og[r ? bf16_value_index(D, ot, ch) : bf16_key_index(D, ot, ch)]);
+    L.xs[r][ch] = x;
+  }
+  __syncthreads();
+  // the key (row 0) and the queries (rows 1..GQ) share the R_K column held in registers
+  L.parts[part][0][j] = rc.part_sum(L.xs[0], part);
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) L.parts[part][1 + h][j] = rc.part_sum(L.xs[2 + h], part);
+  __syncthreads();
+  rc.load(a.rot_v + (size_t)kv * D * D, j, part);
+  if (tid < D) {
+    L.xr[0][tid] = RotCol<D>::combine(&L.parts[0][0][tid], (1 + GQ) * D);
+    for (int h = 0; h < GQ; ++h) {
+      float sacc = 0.0f;
+      for (int p = 0; p < NP; ++p) sacc += L.parts[p][1 + h][tid];
+      L.vq[h][tid] = sacc * a.scale_log2e;
+    }
+  }
+  __syncthreads();
+  L.parts[part][0][j] = rc.part_sum(L.xs[1], part);
+  __syncthreads();
+  if (tid < D) L.xr[1][tid] = RotCol<D>::combine(&L.parts[0][0][tid], (1 + GQ) * D);
+  __syncthreads();
+  if (demote && wave < 2) {
+    const float clip = bw == 4 ? (wave ? cw.clip_v4 : cw.clip_k4) : (wave ? cw.clip_v : cw.clip_k);
+    quantize_token<D>(L.xr[wave], clip, bw, L.cs[wave], &L.szs[wave], lane);
+  }
+  __syncthreads();
+  if (demote) {
+    store_token<D>(cw, page, kv, bw, dslot % kPage, 0, L.cs[0], L.szs[0], tid, kSplitWaves * kWave);
+    store_token<D>(cw, page, kv, bw, dslot % kPage, 1, L.cs[1], L.szs[1], tid, kSplitWaves * kWave);
+  }
+  const size_t sb = (size_t)bk * a.ws.ns;
+  float* po_d = a.ws.part_o + (sb + a.ws.ns - 1) * GQ * D;
+  float* pl_d = a.ws.part_lse + (sb + a.ws.ns - 1) * GQ;
+  float* po_n = a.ws.part_o + (sb + wslot) * GQ * D;
+  float* pl_n = a.ws.part_lse + (sb + wslot) * GQ;
+  const uint16_t* nk = cw.k + (size_t)bk * D;
+  const uint16_t* nv = cw.v + (size_t)bk * D;
+  const double sk = __uint_as_float(L.szs[0] << 16), zk = __uint_as_float(L.szs[0] & 0xFFFF0000u);
+  const float sv = __uint_as_float(L.szs[1] << 16), zv = __uint_as_float(L.szs[1] & 0xFFFF0000u);
+  for (int h = wave; h < GQ; h += kSplitWaves) {
+    double ld = 0.0, ln = 0.0;
+    for (int ch = lane; ch < D; ch += kWave) {
+      if (demote) ld += (double)L.vq[h][ch] * (sk * (double)L.cs[0][ch] + zk);
+      ln += (double)L.xs[2 + h][ch] * (double)bf16_bits_to_f32(nk[ch]);
+    }
+    ld = wave_sum_f64(ld);
+    ln = wave_sum_f64(ln);
+    if (lane == 0) {
+      pl_d[h] = demote ? (float)ld : kNegInf;
+      pl_n[h] = (float)(ln * (double)a.scale_log2e);
+    }
+  }
+  for (int idx = tid; idx < GQ * D; idx += kSplitWaves * kWave) {
+    const int ch = idx % D;
+    if (demote) po_d[idx] = fmaf(sv, (float)L.cs[1][ch], zv);
+    po_n[idx] = bf16_bits_to_f32(nv[ch]);
+  }
+  if (kv == 0 && tid == 0) {
+    if (cw.seq_len_out) cw.seq_len_out[b] = T + 1;
+    if (cw.n_int4_out) cw.n_int4_out[b] = n4 + ((demote && bw == 4) ? 1 : 0);
+  }
+}
+
+// Window role: workgroup wi of (b, kv) covers window pages 4*wi .. 4*wi+3, one per wavefront; in a
+// fused step the last window workgroup of (b, kv) is the step workgroup, and the ring slot of the
+// demoted token (position T - recent) is left to it.
+template <int D, int GQ>
+__device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int idx, float (*o_lds)[2 * GQ][D],
+                            float (*st_lds)[3][8], StepLds<D, GQ>& slds) {
   const Dims& dm = a.dm;
   const int nw = a.ws.nwin;
   const int wi = idx % nw, bk = idx / nw, kv = bk % dm.hkv, b = bk / dm.hkv;
+  if (a.step && wi == nw - 1) {
+    step_role<D, GQ>(a, cw, bk, wi, slds);
+    return;
+  }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
@@ -395,7 +552,7 @@ __device__ void window_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ]
         const int sl = kPage * (pg - dm.sink / kPage) + t;
         int back = (T - 1 - sl) % dm.recent;
         if (back < 0) back += dm.recent;
-        valid[r] = T - 1 - back >= dm.sink;
+        valid[r] = T - 1 - back >= dm.sink && !(a.step && back == dm.recent - 1);
       }
     }
     process_bf16_page<D, GQ>(st, pr, bq, valid, a.scale_log2e, lane);
@@ -675,9 +832,26 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
   }
 }
 
+#ifndef OSCAR_PROGRESS_PRIORITY
+#define OSCAR_PROGRESS_PRIORITY 1
+#endif
+// Issue priority from progress: a compute unit runs two history workgroups, and the sequencer
+// prefers the older wavefront among equal priorities, so the workgroup dispatched second would
+// trail by a fifth of its run and finish alone. A wavefront instead takes priority 3 - (4 * done
+// / total): the ones behind win issue until the two workgroups move in step.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  if constexpr (OSCAR_PROGRESS_PRIORITY) {
+    const int level = total > 0 ? (4 * done) / total : 3;
+    if (level <= 0) __builtin_amdgcn_s_setprio(3);
+    else if (level == 1) __builtin_amdgcn_s_setprio(2);
+    else if (level == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 template <int BITS, int D, int GQ>
-__device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8]) {
-  constexpr int NKK = D / 32;
+__device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
+                          HistQueryLds<D, GQ>& qlds) {
   const Dims& dm = a.dm;
   const int S = BITS == 2 ? a.ws.s2 : a.ws.s4;
   const int s = idx % S;
@@ -685,7 +859,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int ppw = a.ws.ppw;
   const int pg_begin = s * kSplitWaves * ppw;
-  const int tid = threadIdx.x, lane = tid % kWave, g = lane / 16, c = lane % 16;
+  const int tid = threadIdx.x, lane = tid % kWave, c = lane % 16;
   const int wave = uniform(tid / kWave);
   const int wp0 = uniform(pg_begin + wave * ppw);
   const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
@@ -693,21 +867,23 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
 
   // Loads that do not depend on the request's length are issued first, branch-free and side by
   // side with it: the page ids of this wavefront's range (lane i: page wp0+i; the index is clamped
-  // to the table stride, which is >= 1 whenever history splits exist), the query operands and
-  // their per-head constants.
+  // to the table stride, which is >= 1 whenever history splits exist), the rows of R_K and the
+  // queries of the group for the query prologue.
   const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
   const int pidx = wp0 + lane;
   const int32_t raw_page = pt[min(pidx, dm.pt_stride - 1)];
-  const uint16_t* qh = BITS == 2 ? a.ws.qh2 : a.ws.qh4;
-  const uint16_t* ql = BITS == 2 ? a.ws.ql2 : a.ws.ql4;
   const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
-  // query operand columns: high parts of the heads in columns c < GQ, low parts in GQ..2GQ-1
-  const uint16_t* qsrc = (c < GQ ? qh : ql) + (qbase + c % GQ) * D + 8 * g;
-  u32x4_t qv[NKK];
+  QRotRows<D> rr;
+  rr.load(a.rot_k + (size_t)kv * D * D, tid);
+  uint32_t qw[kQueryWords<D, GQ>];
+  {
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + qbase * D);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qsrc + 32 * kk);
-  // head whose logits this lane owns: c % GQ (lanes c >= GQ of the plain layout are unused)
-  const float4 qk_const = *reinterpret_cast<const float4*>(a.ws.qsc + (qbase + c % GQ) * 4);
+    for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
+      const int e = tid + 256 * i;
+      qw[i] = e < GQ * D / 2 ? qsrc[e] : 0u;
+    }
+  }
   const HistCounts hc = hist_counts(a, b);
   const int ntok = BITS == 2 ? hc.n2 : hc.n4;
   const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
@@ -715,13 +891,6 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   // partial (lse = -inf)
   const int wp1 = uniform(max(wp0, min(wp0 + ppw, npages)));
   const int64_t page = (lane < ppw && pidx < dm.pt_stride) ? (int64_t)raw_page : -1;
-  half8_t bq[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const u32x4_t z = {0, 0, 0, 0};
-    bq[kk] = __builtin_bit_cast(half8_t, c < 2 * GQ ? qv[kk] : z);
-  }
-  const float uh = qk_const.x, ul = qk_const.y, esc = BITS == 2 ? qk_const.z : qk_const.w;
 
   // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
   // hi/hi halves on lanes 4..7, zero elsewhere)
@@ -751,9 +920,13 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     bool ok[NB];
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k) ok[k] = load(buf[k], wp0 + k);
-    __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the first product waits
+    __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
+    half8_t bq[D / 32];
+    float uh, ul, esc;
+    hist_query_operands<BITS, D, GQ>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
     float4_t acc = qk_page<BITS, D, GQ>(buf[0], bq);
     for (int pg = wp0; pg < wp1; pg += NB) {
+      progress_priority(pg - wp0, wp1 - wp0);
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
@@ -775,30 +948,43 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
                                                              a.ws.part_lse + pbase * GQ);
 }
 
+// LDS of the roles that need more than the merge buffers (one role per workgroup); 16-byte aligned
+// for the vector reads of the query operands
 template <int D, int GQ>
-__global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a) {
+union alignas(16) SplitScratch {
+  HistQueryLds<D, GQ> hist;
+  StepLds<D, GQ> step;
+};
+
+template <int D, int GQ>
+__global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a, CacheWriteArgs cw) {
   __shared__ float o_lds[kSplitWaves][2 * GQ][D];
   __shared__ float st_lds[kSplitWaves][3][8];
+  __shared__ SplitScratch<D, GQ> scr;
   const int nwin = a.ws.nwin, s2 = a.ws.s2;
   const int n_win = a.dm.batch * a.dm.hkv * nwin;
   const int n_int2 = a.dm.batch * a.dm.hkv * s2;
   const int bid = blockIdx.x;
   if (bid < n_win) {
-    window_role<D, GQ>(a, bid, o_lds, st_lds);
+    window_role<D, GQ>(a, cw, bid, o_lds, st_lds, scr.step);
   } else if (bid < n_win + n_int2) {
-    hist_role<2, D, GQ>(a, bid - n_win, o_lds, st_lds);
+    hist_role<2, D, GQ>(a, bid - n_win, o_lds, st_lds, scr.hist);
   } else {
-    hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds);
+    hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds, scr.hist);
   }
 }
 
 // ------------------------------------------------------------------ merge
-// One 1024-thread workgroup per (request, kv-head) merges every partial slot of the group --
-// window slots, INT2 and INT4 history slots; slots of splits past the history hold lse = -inf --
-// for its GQ query heads, in one pass: each thread folds its slots with a running maximum (lse in
-// log2 units), the threads' states are combined through LDS, the history sum (rotated basis of the
-// values) is un-rotated with R_V^T (each R_V row read once per group) and added to the window sum.
+// One 1024-thread workgroup per (request, kv-head, group of HPW query heads) merges every partial
+// slot of the (request, kv-head) -- window slots, INT2 and INT4 history slots, the step's
+// one-token slots; slots of splits past the history hold lse = -inf -- for its heads, in one pass:
+// each thread folds its slots with a running maximum (lse in log2 units), the threads' states are
+// combined through LDS, the history sum (rotated basis of the values) is un-rotated with R_V^T
+// (each R_V row read once per workgroup) and added to the window sum.
 constexpr int kMergeThreads = 1024;
+// The merge is latency-bound: a launch gets the fewest query heads per workgroup (HW) that still
+// fits one workgroup per compute unit (a merge workgroup's LDS holds R_V, so a unit runs one).
+constexpr int kMergeWorkgroupsPerRound = 256;
 
 struct MergeState {
   float m, wsum;   // running maximum (log2) and weight sum
@@ -809,7 +995,7 @@ struct MergeCtx {
   const float* po;     // o of the group's slots [slot][GQ][D]
   const float* rv;     // R_V of the kv-head [D][D]
   float* rv_s;         // LDS copy of R_V, padded rows
-  int n, nwin, grp, hh, c4, tid;
+  int n, nwin, grp, hh, c4, tid;   // hh: query head within the kv group
 };
 
 // Folds slots base + grp + k*NG (k < MS) into the thread's state; with `stage`, also copies R_V
@@ -861,50 +1047,57 @@ __device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, in
   }
 }
 
-template <int D, int GQ>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+template <int D, int GQ, int HW>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, CacheWriteArgs cw) {
   constexpr int NT = kMergeThreads;
   constexpr int C4 = D / 4;           // float4 columns of a partial
-  constexpr int TPH = NT / GQ;        // threads per head
+  constexpr int TPH = NT / HW;        // threads per head
   constexpr int NG = TPH / C4;        // slot groups per head
   constexpr int NP = NT / D;          // parts of an R_V row
   constexpr int RP = D / NP;
   constexpr int RS = D + 1;           // padded LDS row of R_V (conflict-free column walks)
   __shared__ float rv_s[D * RS];
-  __shared__ float4 acc_h[NG][GQ][C4], acc_w[NG][GQ][C4];
-  __shared__ float m_s[NG][GQ], w_s[NG][GQ];
-  __shared__ float hsum[GQ][D];
-  __shared__ float part_s[NP][GQ][D];
+  __shared__ float4 acc_h[NG][HW][C4], acc_w[NG][HW][C4];
+  __shared__ float m_s[NG][HW], w_s[NG][HW];
+  __shared__ float hsum[HW][D];
+  __shared__ float part_s[NP][HW][D];
   const Dims& dm = a.dm;
-  const int bk = blockIdx.x, kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int bk = blockIdx.x / (GQ / HW), h0 = HW * (blockIdx.x % (GQ / HW));
+  const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int tid = threadIdx.x;
   const int nwin = a.ws.nwin, n = a.ws.ns;
   const size_t sbase = (size_t)bk * n;
   const float* pl = a.ws.part_lse + sbase * GQ;
   const float* po = a.ws.part_o + sbase * GQ * D;
-  const int hh = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
-  // Slots are taken 4 or 8 at a time per thread: every load of a batch is issued (indices clamped
-  // to the last slot, so always in bounds) before any is consumed, and the first batch's loads
-  // share one round trip with the R_V staging.
+  const int hl = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
+  // fused step: the new token's window slot is written at the end (every window read of the step
+  // is done); its length is fetched now
+  const bool ring = a.step && h0 == 0 && tid < 2 * D;
+  const int t_len = ring ? a.seq_len[b] : 0;
+  // Slots are taken up to 12 at a time per thread: every load of a batch is issued (indices
+  // clamped to the last slot, so always in bounds) before any is consumed, and the first batch's
+  // loads share one round trip with the R_V staging.
   MergeState ms_st{kNegInf, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  const MergeCtx mc{pl, po, a.rot_v + (size_t)kv * D * D, rv_s, n, nwin, grp, hh, c4, tid};
+  const MergeCtx mc{pl, po, a.rot_v + (size_t)kv * D * D, rv_s, n, nwin, grp, h0 + hl, c4, tid};
   const int per_thread = (n + NG - 1) / NG;   // uniform
   if (per_thread <= 4) {
     merge_fold<D, GQ, 4, NG, RS, NT>(ms_st, mc, 0, true);
+  } else if (per_thread <= 12) {
+    merge_fold<D, GQ, 12, NG, RS, NT>(ms_st, mc, 0, true);
   } else {
     merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, 0, true);
     for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, base, false);
   }
   const float m = ms_st.m, wsum = ms_st.wsum;
   const float4 ah = ms_st.ah, aw = ms_st.aw;
-  acc_h[grp][hh][c4] = ah;
-  acc_w[grp][hh][c4] = aw;
+  acc_h[grp][hl][c4] = ah;
+  acc_w[grp][hl][c4] = aw;
   if (c4 == 0) {
-    m_s[grp][hh] = m;
-    w_s[grp][hh] = wsum;
+    m_s[grp][hl] = m;
+    w_s[grp][hl] = wsum;
   }
   __syncthreads();
-  for (int t = tid; t < GQ * D; t += NT) {
+  for (int t = tid; t < HW * D; t += NT) {
     const int h2 = t / D, ch = t % D;
     float M = kNegInf;
 #pragma unroll
@@ -922,20 +1115,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   {
     const int j = tid % D, part = tid / D;
     const float* rrow = rv_s + j * RS + part * RP;
-    float acc[GQ];
+    float acc[HW];
 #pragma unroll
-    for (int h2 = 0; h2 < GQ; ++h2) acc[h2] = 0.0f;
+    for (int h2 = 0; h2 < HW; ++h2) acc[h2] = 0.0f;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       const float rji = rrow[i];
 #pragma unroll
-      for (int h2 = 0; h2 < GQ; ++h2) acc[h2] = fmaf(hsum[h2][part * RP + i], rji, acc[h2]);
+      for (int h2 = 0; h2 < HW; ++h2) acc[h2] = fmaf(hsum[h2][part * RP + i], rji, acc[h2]);
     }
 #pragma unroll
-    for (int h2 = 0; h2 < GQ; ++h2) part_s[part][h2][j] = acc[h2];
+    for (int h2 = 0; h2 < HW; ++h2) part_s[part][h2][j] = acc[h2];
   }
   __syncthreads();
-  for (int t = tid; t < GQ * D; t += NT) {
+  for (int t = tid; t < HW * D; t += NT) {
     const int h2 = t / D, ch = t % D;
     float M = kNegInf;
 #pragma unroll
@@ -949,7 +1142,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
       ow = fmaf(e, reinterpret_cast<const float*>(&acc_w[gg][h2][0])[ch], ow);
       W = fmaf(e, w_s[gg][h2], W);
     }
-    a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h2) * D + ch] = W > 0.0f ? (oh + ow) / W : 0.0f;
+    a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h0 + h2) * D + ch] = W > 0.0f ? (oh + ow) / W : 0.0f;
+  }
+  if (ring) {
+    // the new token takes its window slot (the demoted token's ring slot, or position T), as the
+    // demote kernel writes it
+    int pgw, t;
+    window_slot(t_len < 0 ? 0 : t_len, dm, pgw, t);
+    const int sel = tid / D, ch = tid % D;
+    uint16_t* pg = reinterpret_cast<uint16_t*>(cw.window + ((size_t)bk * dm.wpages + pgw) * bf16_page_head_bytes(D));
+    pg[sel ? bf16_value_index(D, t, ch) : bf16_key_index(D, t, ch)] = (sel ? cw.v : cw.k)[(size_t)bk * D + ch];
   }
 }
 
@@ -1084,49 +1286,35 @@ __global__ __launch_bounds__(256) void bf16_merge_kernel(Bf16Args a) {
 
 // ------------------------------------------------------------------ launchers
 template <int D, int GQ>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream) {
   const Dims& dm = a.dm;
   auto mark = [&](int i) {
     if (a.events) (void)hipEventRecord(a.events[i], stream);
   };
   mark(0);
-  hipLaunchKernelGGL(q_prologue_kernel<D>, dim3(dm.hq, dm.batch), dim3(256), 0, stream, a);
+  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
+#ifndef OSCAR_SPLIT_LDS_PAD
+#define OSCAR_SPLIT_LDS_PAD 0
+#endif
+  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream, a, cw);
   mark(1);
-  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), 0, stream, a);
+  const int groups = dm.batch * dm.hkv;
+  if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {
+    hipLaunchKernelGGL((merge_kernel<D, GQ, 1>), dim3(groups * GQ), dim3(kMergeThreads), 0, stream, a, cw);
+  } else if (GQ >= 4 && groups * GQ / 2 <= kMergeWorkgroupsPerRound) {
+    hipLaunchKernelGGL((merge_kernel<D, GQ, 2>), dim3(groups * GQ / 2), dim3(kMergeThreads), 0, stream, a, cw);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<D, GQ, GQ>), dim3(groups), dim3(kMergeThreads), 0, stream, a, cw);
+  }
   mark(2);
-  hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
-  mark(3);
   return hipGetLastError();
 }
 
-template <int D, int GQ>
-static hipError_t launch_step_t(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream) {
-  const Dims& dm = a.dm;
-  const int npre = 2 * dm.hkv * dm.batch + dm.hq * dm.batch;
-  hipLaunchKernelGGL(step_pre_kernel<D>, dim3(npre), dim3(256), 0, stream, cw, a);
-  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), 0, stream, a);
-  hipLaunchKernelGGL((merge_kernel<D, GQ>), dim3(dm.batch * dm.hkv), dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_step(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream) {
   if (a.dm.batch == 0) return hipSuccess;
   const int d = a.dm.d, gq = a.dm.gq;
 #define OSCAR_DISPATCH(DD, GG) \
-  if (d == DD && gq == GG) return launch_step_t<DD, GG>(cw, a, stream);
-  OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
-  OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
-#undef OSCAR_DISPATCH
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.dm.batch == 0) return hipSuccess;
-  const int d = a.dm.d, gq = a.dm.gq;
-#define OSCAR_DISPATCH(DD, GG) \
-  if (d == DD && gq == GG) return launch_decode_t<DD, GG>(a, stream);
+  if (d == DD && gq == GG) return launch_decode_t<DD, GG>(a, cw, stream);
   OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
   OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
 #undef OSCAR_DISPATCH

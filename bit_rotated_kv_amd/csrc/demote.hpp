@@ -109,6 +109,57 @@ struct RotCol {
 };
 
 // ------------------------------------------------------------------ demote
+// Page id of history slot `slot` of width bw for request b; -1 when the slot lies past the page
+// table.
+__device__ inline int64_t demote_page(const CacheWriteArgs& a, int b, int slot, int bw) {
+  const int32_t* pt = (bw == 4 ? a.pt4 : a.pt2) + (size_t)b * a.dm.pt_stride;
+  return (slot >= 0 && slot / kPage < a.dm.pt_stride) ? pt[slot / kPage] : -1;
+}
+
+// Window page and slot that hold position p (p >= 0): sink page p / 16 below the sink length,
+// else recent-ring slot p mod recent.
+__device__ inline void window_slot(int p, const Dims& dm, int& pgw, int& t) {
+  if (p < dm.sink) {
+    pgw = p / kPage;
+    t = p % kPage;
+  } else {
+    const int s = p % dm.recent;
+    pgw = dm.sink / kPage + s / kPage;
+    t = s % kPage;
+  }
+}
+
+// One wavefront: range of the rotated token xr[0..D), clipped grid of width bw, and its codes
+// (cs) and packed bf16 (scale, zero) (szs, scale in the low half).
+template <int D>
+__device__ inline void quantize_token(const float* xr, float clip, int bw, uint8_t* cs, uint32_t* szs, int lane) {
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+  for (int c = lane; c < D; c += kWave) {
+    mn = fminf(mn, xr[c]);
+    mx = fmaxf(mx, xr[c]);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int levels = (1 << bw) - 1;
+  const QuantGrid g = make_grid(mn, mx, clip, levels);
+  for (int c = lane; c < D; c += kWave) cs[c] = (uint8_t)quant_code(xr[c], g, levels);
+  if (lane == 0) *szs = g.s_bits | (g.z_bits << 16);
+}
+
+// Stores the codes and (scale, zero) of one token -- key (sel 0) or value (sel 1) -- into slot
+// ts of history page `page` (skipped for an id outside the pool or of the other width).
+template <int D>
+__device__ inline void store_token(const CacheWriteArgs& a, int64_t page, int kv, int bw, int ts, int sel,
+                                   const uint8_t* cs, uint32_t szs, int tid, int nthr) {
+  if (!page_ok(page, bw, a.dm)) return;
+  uint8_t* ph = page_head_mut(a.pool, page, kv, a.dm);
+  if (sel == 0)
+    store_key_codes(ph, D, bw, ts, cs, tid, nthr);
+  else
+    store_value_codes(ph, D, bw, ts, cs, tid, nthr);
+  if (tid == 0) reinterpret_cast<uint32_t*>(ph + 4 * D * bw)[2 * ts + sel] = szs;
+}
+
 // One workgroup per (K or V, kv-head, request). With T = seq_len[b] >= sink + recent, the token at
 // position T - recent (the oldest of the recent window) is read from its ring slot, rotated
 // (x . R), clipped, quantised and packed into the next history slot of its width; the new token
@@ -138,10 +189,9 @@ __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, in
     bw = (dm.mixed && a.bits && a.bits[b] == 4) ? 4 : 2;
     const int hist_before = T - dm.sink - dm.recent;
     const int slot = bw == 4 ? n4 : hist_before - n4;
-    const int32_t* pt = (bw == 4 ? a.pt4 : a.pt2) + (size_t)b * dm.pt_stride;
-    const int64_t page = (slot >= 0 && slot / kPage < dm.pt_stride) ? pt[slot / kPage] : -1;
-    const int s = (T - dm.recent) % dm.recent;
-    const int pgw = dm.sink / kPage + s / kPage, t = s % kPage;
+    const int64_t page = demote_page(a, b, slot, bw);
+    int pgw, t;
+    window_slot(T - dm.recent, dm, pgw, t);
     const uint16_t* pg = reinterpret_cast<const uint16_t*>(wb + pgw * pb);
     if (tid < D) xs[tid] = bf16_bits_to_f32(pg[sel ? bf16_value_index(D, t, tid) : bf16_key_index(D, t, tid)]);
     __syncthreads();
@@ -151,40 +201,15 @@ __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, in
     __syncthreads();
     if (wave == 0) {
       const float clip = bw == 4 ? (sel ? a.clip_v4 : a.clip_k4) : (sel ? a.clip_v : a.clip_k);
-      float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-      for (int c = lane; c < D; c += kWave) {
-        mn = fminf(mn, xr[c]);
-        mx = fmaxf(mx, xr[c]);
-      }
-      mn = wave_min(mn);
-      mx = wave_max(mx);
-      const int levels = (1 << bw) - 1;
-      const QuantGrid g = make_grid(mn, mx, clip, levels);
-      for (int c = lane; c < D; c += kWave) cs[c] = (uint8_t)quant_code(xr[c], g, levels);
-      if (lane == 0) szs = g.s_bits | (g.z_bits << 16);
+      quantize_token<D>(xr, clip, bw, cs, &szs, lane);
     }
     __syncthreads();
-    if (page_ok(page, bw, dm)) {
-      uint8_t* ph = page_head_mut(a.pool, page, kv, dm);
-      const int ts = slot % kPage;
-      if (sel == 0)
-        store_key_codes(ph, D, bw, ts, cs, tid, 256);
-      else
-        store_value_codes(ph, D, bw, ts, cs, tid, 256);
-      if (tid == 0) reinterpret_cast<uint32_t*>(ph + 4 * D * bw)[2 * ts + sel] = szs;
-    }
+    store_token<D>(a, page, kv, bw, slot % kPage, sel, cs, szs, tid, 256);
     __syncthreads();
   }
   {
     int pgw, t;
-    if (T < dm.sink) {
-      pgw = T / kPage;
-      t = T % kPage;
-    } else {
-      const int s = T % dm.recent;
-      pgw = dm.sink / kPage + s / kPage;
-      t = s % kPage;
-    }
+    window_slot(T, dm, pgw, t);
     uint16_t* pg = reinterpret_cast<uint16_t*>(wb + pgw * pb);
     const size_t src = ((size_t)b * dm.hkv + kv) * D;
     if (tid < D) {

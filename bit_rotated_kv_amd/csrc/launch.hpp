@@ -17,18 +17,16 @@ struct Dims {
   int pt_stride;
 };
 
-// Workspace carve-up of oscar_decode_attn (all device pointers).
+// Workspace carve-up of a decode call (all device pointers).
 struct DecodeWs {
   uint32_t* flags;         // [64]; word 0 bit 0: skipped page id
-  uint16_t* qh2;           // [B][Hq][d] fp16: rotated, scaled query (INT2 operand, high part)
-  uint16_t* ql2;           // low part
-  uint16_t* qh4;           // INT4 operand high/low parts (mixed caches)
-  uint16_t* ql4;
-  float* qsc;              // [B][Hq][4]: {sum_j q'_j, 2^E2, 2^E4, 0}
   float* part_o;           // [B][Hkv][NS][gq][d]
   float* part_lse;         // [B][Hkv][NS][gq]  (log2 units)
-  int ns;                  // slots per (b, kv): nwin (BF16 window) + S2 (INT2) + S4 (INT4)
-  int nwin;                // window workgroups per (b, kv): ceil(window pages / 4)
+  // Slots per (b, kv), in order: nwin window slots (one per window workgroup; in a fused step the
+  // last is the new token's), S2 INT2 history slots, S4 INT4 history slots, and in a fused step
+  // one more history slot for the demoted token. Slots below nwin are in the original basis.
+  int ns;
+  int nwin;                // window workgroups per (b, kv): ceil(window pages / 4) (+1 in a step)
   int s2, s4;              // split slots per width
   int ppw;                 // pages per wavefront in a history split (4 waves per split), <= 64
 };
@@ -51,7 +49,8 @@ struct DecodeArgs {
   float scale_log2e;         // softmax scale * log2(e)
   float* out;                // [B][Hq][d] fp32
   DecodeWs ws;
-  hipEvent_t* events;        // host: optional, 4 events recorded around the kernels
+  int step;                  // fused decode step: demote + append ride along (CacheWriteArgs)
+  hipEvent_t* events;        // host: optional, 3 events recorded around the two kernels
 };
 
 struct CacheWriteArgs {
@@ -92,8 +91,8 @@ hipError_t launch_quantize_pack(int64_t rows, int dim, int group, int bits, floa
                                 uint8_t* codes, uint16_t* sz, hipStream_t stream);
 hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_demote(const CacheWriteArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_step(const CacheWriteArgs& cw, const DecodeArgs& a, hipStream_t stream);
+// Decode attention; with a.step, also the demote + append of `cw` (a fused decode step).
+hipError_t launch_decode(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream);
 hipError_t launch_bf16_fill(const Bf16Args& a, hipStream_t stream);
 hipError_t launch_bf16_decode(const Bf16Args& a, hipStream_t stream);
 

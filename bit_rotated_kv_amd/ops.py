@@ -139,8 +139,8 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
                 max_seq_len: int, out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
                 page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                 events: Optional[list] = None) -> torch.Tensor:
-    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (4 torch.cuda.Event), calls the
-    timing variant, which records them around the kernels of the call."""
+    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (3 torch.cuda.Event), calls the
+    timing variant, which records them around the two kernels of the call (split, merge)."""
     _need(q, torch.bfloat16, "q")
     _need(seq_len, torch.int32, "seq_len")
     _need(window, torch.uint8, "window")
@@ -176,8 +176,10 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
                 window: torch.Tensor, seq_len_out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
                 out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
                 n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
-                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0) -> torch.Tensor:
-    """kv_demote followed by decode_attn over the updated cache, in one call (three kernels)."""
+                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                events: Optional[list] = None) -> torch.Tensor:
+    """kv_demote's cache update and decode_attn over the updated cache, in one call (two kernels:
+    split, merge). With ``events`` (3 torch.cuda.Event), calls the timing variant."""
     _need(seq_len, torch.int32, "seq_len")
     _need(new_k, torch.bfloat16, "new_k")
     _need(new_v, torch.bfloat16, "new_v")
@@ -195,11 +197,16 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
-    check(lib().oscar_decode_step(_ref(layout), q.shape[0], max_seq_len, _p(seq_len), _p(n_int4), _p(new_k),
-                                  _p(new_v), _p(demote_bits), _p(q), _p(rot_k), _p(rot_v), _p(pool), _p(page_table),
-                                  _p(page_table4), page_table.shape[1], _p(window), _p(seq_len_out), _p(n_int4_out),
-                                  softmax_scale, _p(workspace), workspace.numel(), _p(out), _stream()),
-          "oscar_decode_step")
+    args = (_ref(layout), q.shape[0], max_seq_len, _p(seq_len), _p(n_int4), _p(new_k), _p(new_v), _p(demote_bits),
+            _p(q), _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1], _p(window),
+            _p(seq_len_out), _p(n_int4_out), softmax_scale, _p(workspace), workspace.numel(), _p(out))
+    if events is None:
+        check(lib().oscar_decode_step(*args, _stream()), "oscar_decode_step")
+        return out
+    import ctypes
+    arr = (c_void_p * len(events))(*[c_void_p(e.cuda_event) for e in events])
+    check(lib().oscar_decode_step_profiled(*args, ctypes.cast(arr, c_void_p), len(events), _stream()),
+          "oscar_decode_step_profiled")
     return out
 
 

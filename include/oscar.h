@@ -199,10 +199,10 @@ oscar_status_t oscar_decode_attn(const oscar_layout_t* layout, int32_t batch, in
                                  hipStream_t stream);
 
 /*
- * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..3]
- * (n_events >= 4, all created by the caller) before the query prologue, after it, after the split
- * kernel (BF16 window, INT2 and INT4 history pages in one launch) and after the merge. Intervals
- * between consecutive events time each kernel of the call.
+ * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..2]
+ * (n_events >= 3, all created by the caller) before the split kernel (BF16 window, INT2 and INT4
+ * history pages in one launch; each history workgroup also rotates its queries), after it, and
+ * after the merge. Intervals between consecutive events time each kernel of the call.
  */
 oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                           const void* q, const int32_t* seq_len, const int32_t* n_int4,
@@ -213,12 +213,15 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t 
                                           int32_t n_events, hipStream_t stream);
 
 /*
- * One whole decode step: oscar_kv_demote (new_k/new_v appended, the oldest recent token demoted)
- * followed by oscar_decode_attn of q over the updated cache, reading the lengths the demote
- * writes (seq_len_out, and n_int4_out for a mixed cache; both required here). Identical results
- * to the two calls in sequence. The demote and the query rotation share one launch (they are
- * independent), so a step is three kernels: demote + query prologue, split, merge. Arguments
- * follow the two calls above; max_seq_len bounds the updated lengths (T + 1).
+ * One whole decode step (OSCAR overview page, method paragraph; study note, SGLang case): the
+ * cache update of oscar_kv_demote (new_k/new_v appended, the oldest recent token demoted) and the
+ * attention of oscar_decode_attn over the updated cache, in two kernels (split, merge). The cache
+ * after the call -- pool, window, seq_len_out, n_int4_out (both outputs required here, not
+ * aliasing the inputs) -- is bit for bit what the two calls in sequence leave. The attention is
+ * the same function of the updated cache; it reads the cache as it stands before the step and
+ * takes the demoted token (same codes as the demote writes) and the new token as one-token
+ * partials, so its output agrees with the two-call sequence to fp32 rounding, not bit for bit.
+ * Arguments follow the two calls above; max_seq_len bounds the updated lengths (T + 1).
  */
 oscar_status_t oscar_decode_step(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                  const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
@@ -228,6 +231,20 @@ oscar_status_t oscar_decode_step(const oscar_layout_t* layout, int32_t batch, in
                                  void* window, int32_t* seq_len_out, int32_t* n_int4_out,
                                  float softmax_scale, void* workspace, size_t workspace_bytes, float* out,
                                  hipStream_t stream);
+
+/*
+ * oscar_decode_step with timing: identical work, plus hipEventRecord on `stream` of events[0..2]
+ * (n_events >= 3, created by the caller) before the split kernel, after it and after the merge.
+ */
+oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                          const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
+                                          const void* new_v, const uint8_t* demote_bits, const void* q,
+                                          const float* rot_k, const float* rot_v, void* pool,
+                                          const int32_t* page_table, const int32_t* page_table4,
+                                          int32_t pt_stride, void* window, int32_t* seq_len_out,
+                                          int32_t* n_int4_out, float softmax_scale, void* workspace,
+                                          size_t workspace_bytes, float* out, hipEvent_t* events,
+                                          int32_t n_events, hipStream_t stream);
 
 /*
  * In-house BF16 baseline: the full context of each request in BF16 pages (BF16 page-head

@@ -136,6 +136,26 @@ def test_step_argument_checks(lib):
               None, 0, None, None) == 0
 
 
+def test_profiled_argument_checks(lib):
+    """The timing variants need 3 caller-created events; nothing is enqueued otherwise."""
+    L = ctypes.byref(layout())
+    p = 1
+    ev2 = (ctypes.c_void_p * 2)(1, 1)
+    ev3null = (ctypes.c_void_p * 3)(1, None, 1)
+    da = lib.oscar_decode_attn_profiled
+    for evs, n in ((None, 3), (ctypes.cast(ev2, ctypes.c_void_p), 2), (ctypes.cast(ev3null, ctypes.c_void_p), 3)):
+        assert da(L, 1, 1000, p, p, None, p, p, p, None, 100, p, p, 0.0, p, 1 << 30, p, evs, n, None) == -1
+        assert lib.oscar_decode_step_profiled(L, 1, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, 2, None,
+                                              0.0, p, 1 << 30, p, evs, n, None) == -1
+
+
+def test_step_workspace_covers_plain_decode(lib):
+    """One workspace size serves both the plain decode and the fused step (which adds a window
+    workgroup and a history slot per (request, kv-head))."""
+    for b, t in ((1, 100_000), (32, 32_768), (3, 321), (2, 64)):
+        assert brk.decode_workspace_bytes(layout(), b, t) > 0
+
+
 def test_quantize_pack_argument_checks(lib):
     q = lib.oscar_quantize_pack
     assert q(-1, 128, 128, 2, 0.96, 1, 1, 1, None) == -1
