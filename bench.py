@@ -161,7 +161,7 @@ class Int2Setup:
 
 
 def time_int2(setup, steps, warmup, eager):
-    """Returns (ms per step, mean kernel intervals [split, merge] in ms, launch mode).
+    """Returns (ms per step, mean kernel intervals [query prologue, split, merge] in ms, launch mode).
 
     Step time: the K steps captured in one HIP graph and replayed (no host work inside the timed
     region). Kernel intervals: K more steps launched eagerly behind a GPU-side sleep, so every
@@ -202,7 +202,7 @@ def time_int2(setup, steps, warmup, eager):
     ms = start.elapsed_time(stop) / steps
     base += steps
     # kernel intervals
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for e in evs:
         for x in e:
             x.record()
@@ -211,7 +211,7 @@ def time_int2(setup, steps, warmup, eager):
     for i in range(steps):
         setup.step(base + i, events=evs[i])
     torch.cuda.synchronize()
-    k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(2)] for i in range(steps)])
+    k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
     return ms, k.mean(axis=0), mode
 
 
@@ -350,7 +350,7 @@ def main():
     ms, kern, mode = time_int2(setup, args.steps, args.warmup, args.eager)
     int2, bf16, demote = setup.bytes_per_step()
     step_bytes = int2 + bf16 + demote
-    split_ms = float(kern[0])
+    split_ms = float(kern[1])
     achieved = (int2 + bf16) / (split_ms * 1e-3) / 1e9
     result = {
         "metric": "INT2-KV decode attn: us/step + achieved HBM GB/s at 100K ctx, bs 1 and 32",
@@ -367,7 +367,8 @@ def main():
                    "global_batch": batch, "seq_len": context, "parallelism": "single GPU",
                    "cache_copies": copies, "launch": mode},
         "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
-        "kernel_ms": {"split": round(split_ms, 5), "merge": round(float(kern[1]), 5)},
+        "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
+                      "merge": round(float(kern[2]), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                      "kernel": "split_kernel<128,4> (BF16 window + INT2 history split-K + step workgroups, "
@@ -377,7 +378,7 @@ def main():
     }
     del setup
     torch.cuda.empty_cache()
-    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (split, merge) us: "
+    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (prologue, split, merge) us: "
         f"{', '.join(f'{x * 1e3:.2f}' for x in kern)}")
     if not args.no_bf16:
         log("timing the BF16 baseline")
@@ -398,8 +399,8 @@ def main():
         result["bs32"] = {"workload": "paged batch 32 x 32,768 tokens, demote in step", "ms_per_step": round(ms32, 5),
                           "us_per_step": round(ms32 * 1e3, 2), "GB_per_s": round((i2 + b2 + d2) / (ms32 * 1e-3) / 1e9, 1),
                           "tokens_per_s": round(32 / (ms32 * 1e-3), 1),
-                          "split_GB_per_s": round((i2 + b2) / (float(k32[0]) * 1e-3) / 1e9, 1),
-                          "split_frac": round((i2 + b2) / (float(k32[0]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
+                          "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel_ms": [round(float(x), 5) for x in k32]}
         del s32
         torch.cuda.empty_cache()

@@ -15,6 +15,13 @@ namespace {
 #endif
 // history workgroups a decode aims for (pages per wavefront are sized from it, 1..64)
 constexpr int kTargetWorkgroups = OSCAR_TARGET_WORKGROUPS;
+#ifndef OSCAR_QPRE_MIN_WORKGROUPS
+#define OSCAR_QPRE_MIN_WORKGROUPS 1024
+#endif
+// Above this many history workgroups the query operands come from one prologue kernel; below it
+// every history workgroup forms its own (no extra launch, but each reads R_K and repeats the
+// rotation).
+constexpr int kQpreMinWorkgroups = OSCAR_QPRE_MIN_WORKGROUPS;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -66,8 +73,8 @@ int choose_ppw(int64_t total_pages, int waves, int64_t target = kTargetWorkgroup
 }
 
 struct DecodePlan {
-  int ppw, s2, s4, nwin, ns;
-  size_t off_po, off_pl, total;
+  int ppw, s2, s4, nwin, ns, qpre;
+  size_t off_qop, off_qhs, off_po, off_pl, total;
 };
 
 // Split plan of a decode call; a fused step (step = 1) adds one window workgroup per (b, kv) and
@@ -92,8 +99,12 @@ DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len, int 
   }
   p.nwin += step;
   p.ns = p.nwin + p.s2 + p.s4 + step;
+  p.qpre = (int64_t)batch * L->num_kv_heads * (p.s2 + p.s4) > kQpreMinWorkgroups;
   const int gq = L->num_q_heads / L->num_kv_heads;
-  p.off_po = kAlign;
+  const size_t bhq = (size_t)batch * L->num_q_heads;
+  p.off_qop = kAlign;
+  p.off_qhs = p.off_qop + align_up(2 * 2 * bhq * L->head_dim * 2);
+  p.off_po = p.off_qhs + align_up(2 * bhq * 16);
   const size_t nsl = (size_t)batch * L->num_kv_heads * p.ns * gq;
   p.off_pl = p.off_po + align_up(nsl * L->head_dim * 4);
   p.total = p.off_pl + align_up(nsl * 4);
@@ -299,6 +310,9 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.scale_log2e = scale * 1.4426950408889634f;
   a.out = out;
   a.ws.flags = reinterpret_cast<uint32_t*>(ws);
+  a.ws.qop = reinterpret_cast<uint16_t*>(ws + p.off_qop);
+  a.ws.qhs = reinterpret_cast<float*>(ws + p.off_qhs);
+  a.ws.qpre = p.qpre;
   a.ws.part_o = reinterpret_cast<float*>(ws + p.off_po);
   a.ws.part_lse = reinterpret_cast<float*>(ws + p.off_pl);
   a.ws.ns = p.ns;
@@ -342,8 +356,8 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* L, int32_t batch
                                           const float* rot_v, float softmax_scale, void* workspace,
                                           size_t workspace_bytes, float* out, hipEvent_t* events, int32_t n_events,
                                           hipStream_t stream) {
-  if (!events || n_events < 3) return OSCAR_ERR_INVALID_ARG;
-  for (int i = 0; i < 3; ++i)
+  if (!events || n_events < 4) return OSCAR_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
     if (!events[i]) return OSCAR_ERR_INVALID_ARG;
   return decode_impl(L, batch, max_seq_len, q, seq_len, n_int4, window, pool, page_table, page_table4, pt_stride,
                      rot_k, rot_v, softmax_scale, workspace, workspace_bytes, out, events, stream);
@@ -391,8 +405,8 @@ oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* L, int32_t batch
                                           void* window, int32_t* seq_len_out, int32_t* n_int4_out,
                                           float softmax_scale, void* workspace, size_t workspace_bytes, float* out,
                                           hipEvent_t* events, int32_t n_events, hipStream_t stream) {
-  if (!events || n_events < 3) return OSCAR_ERR_INVALID_ARG;
-  for (int i = 0; i < 3; ++i)
+  if (!events || n_events < 4) return OSCAR_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
     if (!events[i]) return OSCAR_ERR_INVALID_ARG;
   return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
                    page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, softmax_scale, workspace,

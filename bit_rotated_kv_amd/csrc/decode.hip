@@ -5,12 +5,15 @@
 // INT4 pages) merged by log-sum-exp.
 //
 // Kernels of one decode call, in stream order:
+//   q_prologue   only when a decode has many history workgroups: the query operands of every
+//                (request, kv-head, code width), written once to the workspace
 //   split        one launch, homogeneous roles by workgroup index: BF16 window pages (sink +
 //                recent), INT2 history pages, INT4 history pages (mixed caches), and in a fused
 //                decode step one step workgroup per (request, kv-head); each workgroup = 4
-//                wavefronts and writes (o, lse) partials per query head. History workgroups form
-//                their own query operands: q' = (q . R_K) * scale * log2(e), split into fp16
-//                high/low matrix-core operands scaled per channel for the code unpacking below.
+//                wavefronts and writes (o, lse) partials per query head. Without the prologue
+//                kernel, history workgroups form their own query operands: q' = (q . R_K) *
+//                scale * log2(e), split into fp16 high/low matrix-core operands scaled per
+//                channel for the code unpacking below.
 //   merge        per (request, kv-head): LSE-merge the history partials (rotated basis), apply
 //                R_V^T, LSE-merge with the BF16 window partials, write the fp32 output; in a fused
 //                step it also writes the new token into its window slot.
@@ -120,21 +123,20 @@ struct HistQueryLds {
 template <int D, int GQ>
 constexpr int kQueryWords = (GQ * D / 2 + 255) / 256;
 
-// Query operands of a history workgroup for its GQ heads and code width BITS. v = q'_j (rotated,
+// Query operands of the GQ heads of a (request, kv-head) for code width BITS, into LDS (L.op,
+// L.hsc), by one 256-thread workgroup. v = q'_j (rotated,
 // log2-scaled) is split on a power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11): v_hi =
 // Delta*rint(v/Delta) has at most 11 significant bits, so its fp16 operand is exact and every
 // partial sum of c*v_hi over a head is an exact fp32 multiple of Delta (|sum| <= 15 * 128 *
 // 2^11 Delta < 2^24 Delta); v_lo = v - v_hi carries the rest. The products see v as fp16 operands
 // scaled per code bit position p (a code c at bit p of its fp16 slot has the value c*2^(p-24)):
-// operand = v*2^(24-p-E), one exponent E per head. Lane (g, c) gets the operand column c (high
-// parts of head c for c < GQ, low parts of head c-GQ for GQ <= c < 2GQ, zero beyond) and the
-// constants of head c % GQ.
+// operand = v*2^(24-p-E), one exponent E per head. Operand column c of the products holds the
+// high parts of head c for c < GQ and the low parts of head c-GQ for GQ <= c < 2GQ.
 template <int BITS, int D, int GQ>
-__device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
-                                    HistQueryLds<D, GQ>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
-                                    float& ul, float& esc) {
+__device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
+                               HistQueryLds<D, GQ>& L, float scale_log2e) {
   constexpr int CG = QRotRows<D>::CG, QR = QRotRows<D>::QR;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, c = lane % 16;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
   for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
     const int e = tid + 256 * i;
@@ -209,9 +211,20 @@ __device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[
       L.hsc[h][0] = sh;
       L.hsc[h][1] = sl;
       L.hsc[h][2] = ldexpf(1.0f, e);
+      L.hsc[h][3] = 0.0f;
     }
   }
   __syncthreads();
+}
+
+// The operands of query_operands as registers: lane (g, c) gets operand column c and the constants
+// of head c % GQ.
+template <int BITS, int D, int GQ>
+__device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
+                                    HistQueryLds<D, GQ>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
+                                    float& ul, float& esc) {
+  const int lane = threadIdx.x % kWave, g = lane / 16, c = lane % 16;
+  query_operands<BITS, D, GQ>(rr, qw, L, scale_log2e);
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const u32x4_t z = {0, 0, 0, 0};
@@ -221,6 +234,36 @@ __device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[
   uh = L.hsc[c % GQ][0];
   ul = L.hsc[c % GQ][1];
   esc = L.hsc[c % GQ][2];
+}
+
+// Query prologue kernel, used when a decode has many history workgroups (each would otherwise
+// repeat the rotation and the R_K reads): one workgroup per (request, kv-head, code width) writes
+// the operands of query_operands to the workspace, in the LDS layout, for the history workgroups to
+// load.
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) HistQueryLds<D, GQ> L;
+  const Dims& dm = a.dm;
+  const int bk = blockIdx.x, kv = bk % dm.hkv, b = bk / dm.hkv, wsel = blockIdx.y;
+  const int tid = threadIdx.x;
+  QRotRows<D> rr;
+  rr.load(a.rot_k + (size_t)kv * D * D, tid);
+  uint32_t qw[kQueryWords<D, GQ>];
+  const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * dm.hq + (size_t)kv * GQ) * D);
+#pragma unroll
+  for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
+    const int e = tid + 256 * i;
+    qw[i] = e < GQ * D / 2 ? qsrc[e] : 0u;
+  }
+  if (wsel == 0)
+    query_operands<2, D, GQ>(rr, qw, L, a.scale_log2e);
+  else
+    query_operands<4, D, GQ>(rr, qw, L, a.scale_log2e);
+  const size_t unit = (size_t)wsel * dm.batch * dm.hkv + bk;
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.ws.qop + unit * 2 * GQ * D);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&L.op[0][0][0]);
+  for (int i = tid; i < 2 * GQ * D / 8; i += 256) dst[i] = src[i];
+  if (tid < 4 * GQ) a.ws.qhs[unit * 4 * GQ + tid] = (&L.hsc[0][0])[tid];
 }
 
 // ------------------------------------------------------------------ per-wave softmax state
@@ -873,10 +916,23 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const int pidx = wp0 + lane;
   const int32_t raw_page = pt[min(pidx, dm.pt_stride - 1)];
   const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
+  // query operands: precomputed by the prologue kernel (then loaded here), or formed below
+  const bool qpre = a.ws.qpre != 0;
   QRotRows<D> rr;
-  rr.load(a.rot_k + (size_t)kv * D * D, tid);
   uint32_t qw[kQueryWords<D, GQ>];
-  {
+  u32x4_t qv[D / 32];
+  float4 qk = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (qpre) {
+    const size_t unit = (size_t)(BITS == 4) * dm.batch * dm.hkv + bk;
+    const uint16_t* qop = a.ws.qop + (unit * 2 + (c < GQ ? 0 : 1)) * GQ * D + (size_t)(c % GQ) * D + 8 * (lane / 16);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const u32x4_t z = {0, 0, 0, 0};
+      qv[kk] = c < 2 * GQ ? *reinterpret_cast<const u32x4_t*>(qop + 32 * kk) : z;
+    }
+    qk = *reinterpret_cast<const float4*>(a.ws.qhs + (unit * GQ + c % GQ) * 4);
+  } else {
+    rr.load(a.rot_k + (size_t)kv * D * D, tid);
     const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + qbase * D);
 #pragma unroll
     for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
@@ -923,7 +979,15 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
     half8_t bq[D / 32];
     float uh, ul, esc;
-    hist_query_operands<BITS, D, GQ>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
+    if (qpre) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) bq[kk] = __builtin_bit_cast(half8_t, qv[kk]);
+      uh = qk.x;
+      ul = qk.y;
+      esc = qk.z;
+    } else {
+      hist_query_operands<BITS, D, GQ>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
+    }
     float4_t acc = qk_page<BITS, D, GQ>(buf[0], bq);
     for (int pg = wp0; pg < wp1; pg += NB) {
       progress_priority(pg - wp0, wp1 - wp0);
@@ -1292,12 +1356,15 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
     if (a.events) (void)hipEventRecord(a.events[i], stream);
   };
   mark(0);
+  if (a.ws.qpre)
+    hipLaunchKernelGGL((q_prologue_kernel<D, GQ>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0, stream, a);
+  mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
 #ifndef OSCAR_SPLIT_LDS_PAD
 #define OSCAR_SPLIT_LDS_PAD 0
 #endif
   hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream, a, cw);
-  mark(1);
+  mark(2);
   const int groups = dm.batch * dm.hkv;
   if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {
     hipLaunchKernelGGL((merge_kernel<D, GQ, 1>), dim3(groups * GQ), dim3(kMergeThreads), 0, stream, a, cw);
@@ -1306,7 +1373,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
   } else {
     hipLaunchKernelGGL((merge_kernel<D, GQ, GQ>), dim3(groups), dim3(kMergeThreads), 0, stream, a, cw);
   }
-  mark(2);
+  mark(3);
   return hipGetLastError();
 }
 

@@ -20,6 +20,11 @@ struct Dims {
 // Workspace carve-up of a decode call (all device pointers).
 struct DecodeWs {
   uint32_t* flags;         // [64]; word 0 bit 0: skipped page id
+  // query operands, when precomputed (qpre): [width 2, 4][B * Hkv][high, low][gq][d] fp16 and
+  // [width][B * Hkv][gq][4] fp32 {sum of high parts, sum of low parts, 2^E, 0}
+  uint16_t* qop;
+  float* qhs;
+  int qpre;
   float* part_o;           // [B][Hkv][NS][gq][d]
   float* part_lse;         // [B][Hkv][NS][gq]  (log2 units)
   // Slots per (b, kv), in order: nwin window slots (one per window workgroup; in a fused step the
@@ -50,7 +55,8 @@ struct DecodeArgs {
   float* out;                // [B][Hq][d] fp32
   DecodeWs ws;
   int step;                  // fused decode step: demote + append ride along (CacheWriteArgs)
-  hipEvent_t* events;        // host: optional, 3 events recorded around the two kernels
+  hipEvent_t* events;        // host: optional, 4 events: before the query prologue (if any),
+                             // before the split, after it, after the merge
 };
 
 struct CacheWriteArgs {

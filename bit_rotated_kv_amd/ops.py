@@ -139,8 +139,9 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
                 max_seq_len: int, out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
                 page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                 events: Optional[list] = None) -> torch.Tensor:
-    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (3 torch.cuda.Event), calls the
-    timing variant, which records them around the two kernels of the call (split, merge)."""
+    """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (4 torch.cuda.Event), calls the
+    timing variant, which records them around the kernels of the call (query prologue when
+    launched, split, merge)."""
     _need(q, torch.bfloat16, "q")
     _need(seq_len, torch.int32, "seq_len")
     _need(window, torch.uint8, "window")
@@ -178,8 +179,9 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
                 n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
                 page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                 events: Optional[list] = None) -> torch.Tensor:
-    """kv_demote's cache update and decode_attn over the updated cache, in one call (two kernels:
-    split, merge). With ``events`` (3 torch.cuda.Event), calls the timing variant."""
+    """kv_demote's cache update and decode_attn over the updated cache, in one call (split and
+    merge, after the query prologue for large batches). With ``events`` (4 torch.cuda.Event), calls
+    the timing variant."""
     _need(seq_len, torch.int32, "seq_len")
     _need(new_k, torch.bfloat16, "new_k")
     _need(new_v, torch.bfloat16, "new_v")

@@ -199,10 +199,12 @@ oscar_status_t oscar_decode_attn(const oscar_layout_t* layout, int32_t batch, in
                                  hipStream_t stream);
 
 /*
- * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..2]
- * (n_events >= 3, all created by the caller) before the split kernel (BF16 window, INT2 and INT4
- * history pages in one launch; each history workgroup also rotates its queries), after it, and
- * after the merge. Intervals between consecutive events time each kernel of the call.
+ * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..3]
+ * (n_events >= 4, all created by the caller): before the query prologue kernel, before the split
+ * kernel (BF16 window, INT2 and INT4 history pages in one launch), after it, and after the merge.
+ * The prologue kernel runs only for decodes with many history workgroups (otherwise each history
+ * workgroup rotates its own queries and events[0..1] bracket nothing). Intervals between
+ * consecutive events time each kernel of the call.
  */
 oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                           const void* q, const int32_t* seq_len, const int32_t* n_int4,
@@ -215,7 +217,8 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t 
 /*
  * One whole decode step (OSCAR overview page, method paragraph; study note, SGLang case): the
  * cache update of oscar_kv_demote (new_k/new_v appended, the oldest recent token demoted) and the
- * attention of oscar_decode_attn over the updated cache, in two kernels (split, merge). The cache
+ * attention of oscar_decode_attn over the updated cache, in the same kernels (split and merge,
+ * after the query prologue kernel when there are many history workgroups). The cache
  * after the call -- pool, window, seq_len_out, n_int4_out (both outputs required here, not
  * aliasing the inputs) -- is bit for bit what the two calls in sequence leave. The attention is
  * the same function of the updated cache; it reads the cache as it stands before the step and
@@ -233,8 +236,8 @@ oscar_status_t oscar_decode_step(const oscar_layout_t* layout, int32_t batch, in
                                  hipStream_t stream);
 
 /*
- * oscar_decode_step with timing: identical work, plus hipEventRecord on `stream` of events[0..2]
- * (n_events >= 3, created by the caller) before the split kernel, after it and after the merge.
+ * oscar_decode_step with timing: identical work, plus hipEventRecord on `stream` of events[0..3]
+ * (n_events >= 4, created by the caller), placed as in oscar_decode_attn_profiled.
  */
 oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                           const int32_t* seq_len, const int32_t* n_int4, const void* new_k,

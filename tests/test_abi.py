@@ -137,13 +137,13 @@ def test_step_argument_checks(lib):
 
 
 def test_profiled_argument_checks(lib):
-    """The timing variants need 3 caller-created events; nothing is enqueued otherwise."""
+    """The timing variants need 4 caller-created events; nothing is enqueued otherwise."""
     L = ctypes.byref(layout())
     p = 1
-    ev2 = (ctypes.c_void_p * 2)(1, 1)
-    ev3null = (ctypes.c_void_p * 3)(1, None, 1)
+    ev3 = (ctypes.c_void_p * 3)(1, 1, 1)
+    ev4null = (ctypes.c_void_p * 4)(1, 1, None, 1)
     da = lib.oscar_decode_attn_profiled
-    for evs, n in ((None, 3), (ctypes.cast(ev2, ctypes.c_void_p), 2), (ctypes.cast(ev3null, ctypes.c_void_p), 3)):
+    for evs, n in ((None, 4), (ctypes.cast(ev3, ctypes.c_void_p), 3), (ctypes.cast(ev4null, ctypes.c_void_p), 4)):
         assert da(L, 1, 1000, p, p, None, p, p, p, None, 100, p, p, 0.0, p, 1 << 30, p, evs, n, None) == -1
         assert lib.oscar_decode_step_profiled(L, 1, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, 2, None,
                                               0.0, p, 1 << 30, p, evs, n, None) == -1
