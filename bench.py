@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurement")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
     return ap.parse_args()
@@ -213,6 +214,53 @@ def time_int2(setup, steps, warmup, eager):
     torch.cuda.synchronize()
     k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
     return ms, k.mean(axis=0), mode
+
+
+# ---------------------------------------------------------------- prefill (rotate + quantise on MFMA)
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def time_prefill(w, batch, context, reps=5):
+    """One prefill of a `context`-token prefix per request into a fresh INT2 cache: window copy
+    plus the history rotation (bf16 matrix cores, three exact parts of R), clip, quantise and pack.
+    Timed with events around the library call, inputs resident in HBM."""
+    import torch
+    import bit_rotated_kv_amd as brk
+    import synth
+    K, V, _ = workload_inputs(w, batch, context, seed_offset=11, fast=True)
+    rk, rv = rotations(w)
+    hist_pages = (context - 320 + PAGE - 1) // PAGE
+    order = synth.page_permutation(w.seed, batch * hist_pages)
+    cb = brk.allocate_cache(w.num_q_heads, w.num_kv_heads, w.head_dim, batch, context,
+                            pages2_per_request=hist_pages, page_order2=order)
+    cb.seq_len.fill_(context)
+
+    def run():
+        brk.kv_prefill(cb.layout, cb.seq_len, K, V, rk, rv, cb.pool, cb.page_table, cb.window)
+
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    d, hkv = w.head_dim, w.num_kv_heads
+    hist = context - 320
+    nbytes = batch * hkv * (context * 2 * d * 2 + 320 * 2 * d * 2 + hist * (2 * (d * 2 // 8) + 8))
+    rot_flops = 2.0 * batch * hkv * 2 * hist * d * d          # x . R for every history key and value
+    issued = 3.0 * 2.0 * batch * hkv * 2 * (-(-hist // 64) * 64) * d * d   # three bf16 parts, 64-row tiles
+    del K, V, cb
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill of {batch} x {context} tokens (history {hist}), {hkv} kv-heads, d {d}",
+            "ms": round(ms, 4), "tokens_per_s": round(batch * context / (ms * 1e-3), 1),
+            "hbm_GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_tflops_issued": round(issued / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(issued / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "rotation_tflops": round(rot_flops / (ms * 1e-3) / 1e12, 1), "bytes": nbytes}
 
 
 # ---------------------------------------------------------------- BF16 baseline
@@ -380,6 +428,9 @@ def main():
     torch.cuda.empty_cache()
     log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (prologue, split, merge) us: "
         f"{', '.join(f'{x * 1e3:.2f}' for x in kern)}")
+    if not args.no_prefill:
+        log("timing the prefill (matrix-core rotation + quantise)")
+        result["prefill"] = time_prefill(w, batch, context)
     if not args.no_bf16:
         log("timing the BF16 baseline")
         bms, bbytes = time_bf16(w, batch, context, args.steps, args.warmup, True)
@@ -404,6 +455,8 @@ def main():
                           "kernel_ms": [round(float(x), 5) for x in k32]}
         del s32
         torch.cuda.empty_cache()
+        if not args.no_prefill:
+            result["bs32"]["prefill"] = time_prefill(w32, 32, c32)
         if not args.no_bf16:
             bms32, bb32 = time_bf16(w32, 32, c32, args.steps, args.warmup, True)
             result["bs32"]["bf16_baseline_ms"] = round(bms32, 5)

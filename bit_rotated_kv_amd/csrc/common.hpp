@@ -126,6 +126,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // s = bf16(fp32(hi - lo)/L), z = bf16(lo), code = clamp(rint_even(fp32(clamp(x,lo,hi) - z)/s), 0, L).
 struct QuantGrid {
   float lo, hi, s, z;
+  float rs;                 // hardware reciprocal of s (estimate for quant_code)
   uint32_t s_bits, z_bits;
 };
 
@@ -139,17 +140,39 @@ __device__ __forceinline__ QuantGrid make_grid(float mn, float mx, float clip, i
   g.z_bits = f32_to_bf16_bits(g.lo);
   g.s = bf16_bits_to_f32(g.s_bits);
   g.z = bf16_bits_to_f32(g.z_bits);
+  g.rs = __builtin_amdgcn_rcpf(g.s);
   return g;
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, const QuantGrid& g, int levels) {
+// The quotient t = fl(d / s) only feeds rint, so it is first estimated as d * rcp(s): the hardware
+// reciprocal is within 1 ulp, the estimate within 2^-17 of d / s for |t| < 32, and the correctly
+// rounded quotient within 2^-19. Unless the estimate lies within 2^-14 of a rounding midpoint
+// k + 1/2 (or is not below 32 in magnitude, or not a number), both round to the same integer.
+// quant_code_fast returns the code of the estimate and sets `redo` in those cases, where
+// quant_code_exact (the correctly rounded division) decides; quant_code chains the two. Every
+// variant returns the code of the exact rule.
+// (branch-free: the clamps are median-of-three, the tests combine with bitwise operators)
+__device__ __forceinline__ uint32_t quant_code_fast(float x, const QuantGrid& g, int levels, bool& redo) {
+#pragma clang fp contract(off)
+  const float xc = __builtin_amdgcn_fmed3f(x, g.lo, g.hi);
+  const float t = (xc - g.z) * g.rs;
+  redo = (g.s != 0.0f) & (!(fabsf(t) < 32.0f) | (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) <= 0x1p-14f));
+  const float r = __builtin_amdgcn_fmed3f(rintf(t), 0.0f, (float)levels);
+  return g.s == 0.0f ? 0u : (uint32_t)r;
+}
+
+__device__ __forceinline__ uint32_t quant_code_exact(float x, const QuantGrid& g, int levels) {
 #pragma clang fp contract(off)
   if (g.s == 0.0f) return 0u;
   const float xc = fminf(fmaxf(x, g.lo), g.hi);
   const float t = __fdiv_rn(xc - g.z, g.s);
-  float r = rintf(t);
-  r = fminf(fmaxf(r, 0.0f), (float)levels);
-  return (uint32_t)r;
+  return (uint32_t)fminf(fmaxf(rintf(t), 0.0f), (float)levels);
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, const QuantGrid& g, int levels) {
+  bool redo;
+  const uint32_t c = quant_code_fast(x, g, levels, redo);
+  return redo ? quant_code_exact(x, g, levels) : c;
 }
 
 // ------------------------------------------------------------------ history code placement

@@ -444,12 +444,12 @@ __device__ __forceinline__ void load_bf16_query(u32x4_t* bq, const uint16_t* q, 
 // ------------------------------------------------------------------ step role (fused decode step)
 template <int D, int GQ>
 struct StepLds {
-  float xs[2 + GQ][D];                    // demoted key, demoted value, queries (fp32)
-  float parts[RotCol<D>::NP][1 + GQ][D];  // rotation part sums
-  float xr[2][D];                         // rotated demoted key, value
-  float vq[GQ][D];                        // rotated, log2-scaled queries
-  uint8_t cs[2][D];                       // codes of the demoted key, value
-  uint32_t szs[2];                        // their bf16 (scale, zero)
+  uint16_t xs[1 + GQ][D];   // demoted key (row 0) and the queries (rows 1..GQ), bf16
+  uint16_t xv[D];           // demoted value, bf16
+  float xr[2][D];           // rotated demoted key, value
+  float vq[GQ][D];          // rotated, log2-scaled queries
+  uint8_t cs[2][D];         // codes of the demoted key, value
+  uint32_t szs[2];          // their bf16 (scale, zero)
 };
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -468,13 +468,10 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // token's window copy is written by the merge, after every window read.
 template <int D, int GQ>
 __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk, int wslot, StepLds<D, GQ>& L) {
-  constexpr int NP = RotCol<D>::NP;
+  constexpr int SL = D / 32;   // 32-column slices of the rotation
   const Dims& dm = a.dm;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int j = tid % D, part = tid / D;
-  RotCol<D> rc;
-  rc.load(a.rot_k + (size_t)kv * D * D, j, part);
   // cache-side lengths exactly as the demote kernel reads them
   const int T = a.seq_len[b] < 0 ? 0 : a.seq_len[b];
   const int n4 = (dm.mixed && a.n_int4) ? a.n_int4[b] : 0;
@@ -489,32 +486,30 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   const uint16_t* og = reinterpret_cast<const uint16_t*>(a.window + ((size_t)bk * dm.wpages + opg) * pb);
   for (int idx = tid; idx < (2 + GQ) * D; idx += kSplitWaves * kWave) {
     const int r = idx / D, ch = idx % D;
-    float x = 0.0f;
-    if (r >= 2)
-      x = bf16_bits_to_f32(a.q[(qrow + r - 2) * D + ch]);
-    else if (demote)
-      x = bf16_bits_to_f32(og[r ? bf16_value_index(D, ot, ch) : bf16_key_index(D, ot, ch)]);
-    L.xs[r][ch] = x;
+    if (r == 0)
+      L.xs[0][ch] = demote ? og[bf16_key_index(D, ot, ch)] : (uint16_t)0;
+    else if (r == 1)
+      L.xv[ch] = demote ? og[bf16_value_index(D, ot, ch)] : (uint16_t)0;
+    else
+      L.xs[r - 1][ch] = a.q[(qrow + r - 2) * D + ch];
   }
   __syncthreads();
-  // the key (row 0) and the queries (rows 1..GQ) share the R_K column held in registers
-  L.parts[part][0][j] = rc.part_sum(L.xs[0], part);
+  // one matrix-core pass rotates the key (row 0, the demote's own arithmetic) and the queries
+  // (rows 1..GQ) with R_K; a second rotates the value with R_V
+  if (wave < SL) {
+    const float16v_t acc = rotate_rows_streamed<D>(a.rot_k + (size_t)kv * D * D, wave, &L.xs[0][0], D, 1 + GQ, lane);
+    const int n = 32 * wave + lane % 32;
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) L.parts[part][1 + h][j] = rc.part_sum(L.xs[2 + h], part);
-  __syncthreads();
-  rc.load(a.rot_v + (size_t)kv * D * D, j, part);
-  if (tid < D) {
-    L.xr[0][tid] = RotCol<D>::combine(&L.parts[0][0][tid], (1 + GQ) * D);
-    for (int h = 0; h < GQ; ++h) {
-      float sacc = 0.0f;
-      for (int p = 0; p < NP; ++p) sacc += L.parts[p][1 + h][tid];
-      L.vq[h][tid] = sacc * a.scale_log2e;
+    for (int j = 0; j < 16; ++j) {
+      const int m = 8 * (j / 4) + 4 * (lane / 32) + j % 4;
+      if (m == 0)
+        L.xr[0][n] = acc[j];
+      else if (m <= GQ)
+        L.vq[m - 1][n] = acc[j] * a.scale_log2e;
     }
+    const float16v_t accv = rotate_rows_streamed<D>(a.rot_v + (size_t)kv * D * D, wave, L.xv, D, 1, lane);
+    if (lane < 32) L.xr[1][n] = accv[0];
   }
-  __syncthreads();
-  L.parts[part][0][j] = rc.part_sum(L.xs[1], part);
-  __syncthreads();
-  if (tid < D) L.xr[1][tid] = RotCol<D>::combine(&L.parts[0][0][tid], (1 + GQ) * D);
   __syncthreads();
   if (demote && wave < 2) {
     const float clip = bw == 4 ? (wave ? cw.clip_v4 : cw.clip_k4) : (wave ? cw.clip_v : cw.clip_k);
@@ -538,7 +533,7 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
     double ld = 0.0, ln = 0.0;
     for (int ch = lane; ch < D; ch += kWave) {
       if (demote) ld += (double)L.vq[h][ch] * (sk * (double)L.cs[0][ch] + zk);
-      ln += (double)L.xs[2 + h][ch] * (double)bf16_bits_to_f32(nk[ch]);
+      ln += (double)bf16_bits_to_f32(L.xs[1 + h][ch]) * (double)bf16_bits_to_f32(nk[ch]);
     }
     ld = wave_sum_f64(ld);
     ln = wave_sum_f64(ln);

@@ -1,6 +1,6 @@
 // Device code shared by the cache writers and the fused decode step: history page-head
-// addressing, packed code stores, the fp32 rotation in a fixed summation order, and the per-step
-// demote of the oldest recent token.
+// addressing, packed code stores, the rotation on the matrix cores (one arithmetic for every
+// writer), and the per-step demote of the oldest recent token.
 #pragma once
 #include "common.hpp"
 #include "launch.hpp"
@@ -72,41 +72,106 @@ __device__ inline void store_value_codes(uint8_t* ph, int d, int bits, int t, co
   }
 }
 
-// ------------------------------------------------------------------ rotation order
-// x_rot[j] = sum_i x[i] R[i][j] in fp32, always in the same order so that the prefill and the
-// demote write identical codes for a token: the input channels are split into four quarters, each
-// quarter is a fused-multiply-add chain in ascending order, and the quarter sums are added as
-// (q0 + q1) + (q2 + q3). A workgroup of 256 threads holds column j of R split in 256/D parts
-// (thread (j, part)) in registers.
-template <int D>
-struct RotCol {
-  static constexpr int NP = 256 / D;  // parts per column
-  static constexpr int RP = D / NP;   // rows per part
-  float r[RP];
-  __device__ void load(const float* rot, int j, int part) {
+// ------------------------------------------------------------------ rotation on the matrix cores
+// x_rot = x . R for bf16 rows x and the fp32 rotation R of a kv-head, with
+// v_mfma_f32_32x32x16_bf16. R is split exactly into three bf16 parts, R = R_hi + R_mid + R_lo (each
+// the round-to-nearest-even bf16 of what the previous parts leave; 8 + 8 + 8 significant bits
+// cover fp32's 24), so every product x_k * R_part[k][n] is exact and only the fp32 accumulation
+// rounds. The accumulation order is fixed -- 16-channel k-steps in ascending order, and within a
+// k-step the parts lo, mid, hi -- and a row's result depends on that row alone, so the prefill,
+// the demote and the fused decode step give a token the same x_rot and the same codes. The
+// prefill holds its wavefront's slice of R in registers across tiles (RotSlice, rotate_tile);
+// the single-row writers stream it one k-step at a time (rotate_rows_streamed) in the same order.
+//
+// Operand layout of the 32x32x16 product (lane l, row/column m = n = l % 32): A holds row m,
+// channels 16*kk + 8*(l/32) .. +7; B holds those channels of output column n; the 16 accumulators
+// of lane l are rows 8*(j/4) + 4*(l/32) + j%4 of column n.
+typedef float float16v_t __attribute__((ext_vector_type(16)));
+
+// The three bf16 parts of the rotation entries r[0..7] (exact: r = hi + mid + lo).
+__device__ __forceinline__ void split_rotation(const float (&r)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
 #pragma unroll
-    for (int i = 0; i < RP; ++i) r[i] = rot[(part * RP + i) * D + j];
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = f32_to_bf16_bits(r[i]);
+    const float r1 = r[i] - bf16_bits_to_f32(h);   // exact
+    const uint32_t m = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(m);     // exact, at most 8 significant bits
+    const uint32_t l = f32_to_bf16_bits(r2);       // exact
+    hi[i] = __builtin_bit_cast(__bf16, (uint16_t)h);
+    mid[i] = __builtin_bit_cast(__bf16, (uint16_t)m);
+    lo[i] = __builtin_bit_cast(__bf16, (uint16_t)l);
   }
-  // partial sum of this part over the input row x (LDS, broadcast reads)
-  __device__ float part_sum(const float* x, int part) const {
-    constexpr int Q = D / 4;
-    float qa = 0.0f, qb = 0.0f;
+}
+
+// The rotation entries of lane `lane` for k-step kk of the slice of wavefront w (column 32w + l%32).
+template <int D>
+__device__ __forceinline__ void rotation_entries(const float* rot, int w, int kk, int lane, float (&r)[8]) {
+  const int n = 32 * w + lane % 32;
 #pragma unroll
-    for (int i = 0; i < Q; ++i) qa = fmaf(x[part * RP + i], r[i], qa);
-    if constexpr (RP == 2 * Q) {
+  for (int i = 0; i < 8; ++i) r[i] = rot[(size_t)(16 * kk + 8 * (lane / 32) + i) * D + n];
+}
+
+// A operand of lane `lane` for k-step kk: row lane % 32 of x (zero for rows >= nrows).
+template <typename XPtr>
+__device__ __forceinline__ bf16x8_t rotation_a(XPtr x, int stride, int nrows, int kk, int lane) {
+  const int m = lane % 32;
+  u32x4_t w = {0, 0, 0, 0};
+  if (m < nrows) w = *reinterpret_cast<const u32x4_t*>(x + (size_t)m * stride + 16 * kk + 8 * (lane / 32));
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+__device__ __forceinline__ float16v_t rotation_step(const bf16x8_t& a, const bf16x8_t& hi, const bf16x8_t& mid,
+                                                    const bf16x8_t& lo, float16v_t acc) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, mid, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, acc, 0, 0, 0);
+}
+
+template <int D>
+struct RotSlice {
+  static constexpr int KS = D / 16;       // k-steps
+  static constexpr int SLICES = D / 32;   // 32-column slices (wavefronts 0..SLICES-1 hold one)
+  bf16x8_t hi[KS], mid[KS], lo[KS];
+  // wavefront w < SLICES: columns 32w .. 32w+31 of rot ([D][D] fp32, row-major)
+  __device__ void load(const float* rot, int w, int lane) {
 #pragma unroll
-      for (int i = 0; i < Q; ++i) qb = fmaf(x[part * RP + Q + i], r[Q + i], qb);
-      return qa + qb;
-    } else {
-      return qa;
+    for (int kk = 0; kk < KS; ++kk) {
+      float r[8];
+      rotation_entries<D>(rot, w, kk, lane, r);
+      split_rotation(r, hi[kk], mid[kk], lo[kk]);
     }
   }
-  // combines the NP part sums (stride apart) into the final value
-  __device__ static float combine(const float* p, int stride) {
-    if constexpr (NP == 2) return p[0] + p[stride];
-    else return (p[0] + p[stride]) + (p[2 * stride] + p[3 * stride]);
-  }
 };
+
+// Rows 0..31 of x (bf16 bits; row m at x + m * stride, rows m >= nrows read as zero) times the
+// wavefront's slice of R held in registers. Returns the accumulators of lane `lane`.
+template <int D, typename XPtr>
+__device__ __forceinline__ float16v_t rotate_tile(const RotSlice<D>& rs, XPtr x, int stride, int nrows, int lane) {
+  bf16x8_t a[RotSlice<D>::KS];
+#pragma unroll
+  for (int kk = 0; kk < RotSlice<D>::KS; ++kk) a[kk] = rotation_a(x, stride, nrows, kk, lane);
+  float16v_t acc = {};
+#pragma unroll
+  for (int kk = 0; kk < RotSlice<D>::KS; ++kk) acc = rotation_step(a[kk], rs.hi[kk], rs.mid[kk], rs.lo[kk], acc);
+  return acc;
+}
+
+// rotate_tile with the slice of wavefront w read from rot one k-step at a time (few registers; the
+// same products in the same order).
+template <int D, typename XPtr>
+__device__ __forceinline__ float16v_t rotate_rows_streamed(const float* rot, int w, XPtr x, int stride, int nrows,
+                                                           int lane) {
+  float16v_t acc = {};
+#pragma unroll 2
+  for (int kk = 0; kk < D / 16; ++kk) {
+    float r[8];
+    rotation_entries<D>(rot, w, kk, lane, r);
+    bf16x8_t hi, mid, lo;
+    split_rotation(r, hi, mid, lo);
+    acc = rotation_step(rotation_a(x, stride, nrows, kk, lane), hi, mid, lo, acc);
+  }
+  return acc;
+}
 
 // ------------------------------------------------------------------ demote
 // Page id of history slot `slot` of width bw for request b; -1 when the slot lies past the page
@@ -167,18 +232,14 @@ __device__ inline void store_token(const CacheWriteArgs& a, int64_t page, int kv
 // request's page id are fetched before anything waits on them.
 template <int D>
 __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, int b) {
-  constexpr int NP = RotCol<D>::NP;
-  __shared__ float xs[D];
-  __shared__ float parts[NP][D];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[D];
   __shared__ float xr[D];
   __shared__ uint8_t cs[D];
   __shared__ uint32_t szs;
   const Dims& dm = a.dm;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int j = tid % D, part = tid / D;
-  RotCol<D> rc;
-  rc.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, j, part);
+  const float* rot = (sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D;
   const int T = a.seq_len[b] < 0 ? 0 : a.seq_len[b];
   const int64_t pb = bf16_page_head_bytes(D);
   uint8_t* wb = a.window + (size_t)(b * dm.hkv + kv) * dm.wpages * pb;
@@ -193,11 +254,12 @@ __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, in
     int pgw, t;
     window_slot(T - dm.recent, dm, pgw, t);
     const uint16_t* pg = reinterpret_cast<const uint16_t*>(wb + pgw * pb);
-    if (tid < D) xs[tid] = bf16_bits_to_f32(pg[sel ? bf16_value_index(D, t, tid) : bf16_key_index(D, t, tid)]);
+    if (tid < D) xs[tid] = pg[sel ? bf16_value_index(D, t, tid) : bf16_key_index(D, t, tid)];
     __syncthreads();
-    parts[part][j] = rc.part_sum(xs, part);
-    __syncthreads();
-    if (tid < D) xr[tid] = RotCol<D>::combine(&parts[0][tid], D);
+    if (wave < D / 32) {
+      const float16v_t acc = rotate_rows_streamed<D>(rot, wave, xs, D, 1, lane);
+      if (lane < 32) xr[32 * wave + lane] = acc[0];   // row 0
+    }
     __syncthreads();
     if (wave == 0) {
       const float clip = bw == 4 ? (sel ? a.clip_v4 : a.clip_k4) : (sel ? a.clip_v : a.clip_k);

@@ -24,25 +24,24 @@ __device__ inline int window_position(int j, int t, int T, int sink, int recent)
 }
 
 // ------------------------------------------------------------------ prefill: window + counts
+// One workgroup per (window page, kv-head, request); the first page's workgroup of kv-head 0 also
+// counts the request's INT4 history tokens.
 __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
   const Dims& dm = a.dm;
-  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = dm.d;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
   const int64_t pb = bf16_page_head_bytes(d);
-  uint8_t* wb = a.window + (size_t)(b * dm.hkv + kv) * dm.wpages * pb;
+  uint16_t* pg = reinterpret_cast<uint16_t*>(a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + j) * pb);
   const size_t src = ((size_t)b * dm.hkv + kv) * dm.max_seq_len;
-  for (int idx = tid; idx < dm.wpages * kPage * d; idx += 256) {
-    const int slot = idx / d, ch = idx % d, j = slot / kPage, t = slot % kPage;
+  for (int idx = tid; idx < kPage * d; idx += 256) {
+    const int t = idx / d, ch = idx % d;
     const int p = window_position(j, t, T, dm.sink, dm.recent);
-    const uint16_t kb = p >= 0 ? a.k[(src + p) * d + ch] : (uint16_t)0;
-    const uint16_t vb = p >= 0 ? a.v[(src + p) * d + ch] : (uint16_t)0;
-    uint16_t* pg = reinterpret_cast<uint16_t*>(wb + j * pb);
-    pg[bf16_key_index(d, t, ch)] = kb;
-    pg[bf16_value_index(d, t, ch)] = vb;
+    pg[bf16_key_index(d, t, ch)] = p >= 0 ? a.k[(src + p) * d + ch] : (uint16_t)0;
+    pg[bf16_value_index(d, t, ch)] = p >= 0 ? a.v[(src + p) * d + ch] : (uint16_t)0;
   }
-  if (kv == 0 && a.n_int4_out) {
+  if (j == 0 && kv == 0 && a.n_int4_out) {
     __shared__ int red[256];
     int cnt = 0;
     const int h1 = T - dm.recent;
@@ -59,99 +58,207 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
 }
 
 // ------------------------------------------------------------------ prefill: history pages
-// One workgroup per (32-position chunk of the history, kv-head, request).
+// One workgroup per (run of kPrefillChunks 64-position chunks of the history, kv-head, request x
+// {K, V}). Wavefront w holds the 32-column slice w of R (three bf16 parts) in registers for the
+// whole run. Per chunk: the rows are rotated on the matrix cores (rotate_tile, two 32-row tiles),
+// each row is clipped, quantised and packed with the demote's grid and code functions (so every
+// token gets the codes the demote would give it), and the next chunk's rows are already loading.
+// In an INT2-only cache a chunk starts on a page boundary and owns whole pages: its key and value
+// words are assembled whole and stored plainly. In a mixed cache INT2 and INT4 tokens take
+// consecutive slots of their own tables, so a chunk shares its edge pages with its neighbours and
+// value bits are merged per slot.
+constexpr int kPrefillChunk = 64;
+constexpr int kPrefillChunks = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_hist_kernel(CacheWriteArgs a) {
-  constexpr int CH = 32;                    // positions per workgroup
-  constexpr int NP = RotCol<D>::NP;
-  __shared__ float xs[CH * D];              // inputs, then rotated rows
-  __shared__ float parts[NP][CH * D];
-  __shared__ uint8_t cs[CH * D];
+  constexpr int CH = kPrefillChunk;
+  constexpr int XS = D + 8;     // bf16 row pitch (16-byte pad)
+  constexpr int RS = D + 8;     // fp32 row pitch: the two lane halves of an accumulator store
+                                // (rows 4 apart) fall on disjoint banks
+  constexpr int CSP = D + 4;    // code row pitch: rows two apart no longer share banks
+  constexpr int SL = RotSlice<D>::SLICES;
+  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[CH][XS];
+  __shared__ float xr[CH][RS];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[CH][CSP];
   __shared__ uint32_t szs[CH];
   __shared__ int slot_s[CH];
   __shared__ int bits_s[CH];
   __shared__ int red[256];
   const Dims& dm = a.dm;
-  const int chunk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int kv = blockIdx.y, b = blockIdx.z / 2, sel = blockIdx.z % 2;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
   const int hist = T - dm.sink - dm.recent;
-  if (CH * chunk >= hist) return;
-  const int n = min(CH, hist - CH * chunk);
-  const int p0 = dm.sink + CH * chunk;
+  const int chunk0 = kPrefillChunks * blockIdx.x;
+  if (CH * chunk0 >= hist) return;
+  const int nchunks = min(kPrefillChunks, (hist - CH * chunk0 + CH - 1) / CH);
   const uint8_t* bitsrow = (a.bits && dm.mixed) ? a.bits + (size_t)b * dm.max_seq_len : nullptr;
-
-  // slot of each token: its rank among history tokens of the same width
-  int before4 = 0;
+  const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
+  RotSlice<D> rs;
+  if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
+  // rows of a chunk: thread pieces tid + 256 e (row = piece / (D/8), 8 channels each)
+  auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
+    const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
+#pragma unroll
+    for (int e = 0; e < XW; ++e) {
+      const int idx = tid + 256 * e, row = idx / (D / 8), c8 = idx % (D / 8);
+      w[e] = u32x4_t{0, 0, 0, 0};
+      if (row < n) w[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(p0 + row) * D + 8 * c8);
+    }
+  };
+  u32x4_t xw[XW];
+  load_rows(chunk0, xw);
+  // INT4 tokens before the run (mixed caches): slots are ranks among tokens of the same width
+  int c4 = 0;
   if (bitsrow) {
     int cnt = 0;
-    for (int p = dm.sink + tid; p < p0; p += 256) cnt += bitsrow[p] == 4;
+    for (int p = dm.sink + tid; p < dm.sink + CH * chunk0; p += 256) cnt += bitsrow[p] == 4;
     red[tid] = cnt;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (tid < o) red[tid] += red[tid + o];
       __syncthreads();
     }
-    before4 = red[0];
+    c4 = red[0];
+    __syncthreads();
   }
-  if (tid == 0) {
-    int c4 = before4;
-    for (int i = 0; i < n; ++i) {
-      const int p = p0 + i;
-      const int bw = (bitsrow && bitsrow[p] == 4) ? 4 : 2;
-      bits_s[i] = bw;
-      slot_s[i] = bw == 4 ? c4 : (p - dm.sink) - c4;
-      c4 += bw == 4;
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int chunk = chunk0 + ci;
+    const int n = min(CH, hist - CH * chunk);
+    const int p0 = dm.sink + CH * chunk;
+#pragma unroll
+    for (int e = 0; e < XW; ++e) {
+      const int idx = tid + 256 * e;
+      *reinterpret_cast<u32x4_t*>(&xs[idx / (D / 8)][8 * (idx % (D / 8))]) = xw[e];
     }
-  }
-  const size_t src = ((size_t)b * dm.hkv + kv) * dm.max_seq_len;
-  const int j = tid % D, part = tid / D;
-  for (int sel = 0; sel < 2; ++sel) {
-    const uint16_t* xsrc = sel ? a.v : a.k;
-    RotCol<D> rc;
-    rc.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, j, part);
-    __syncthreads();
-    for (int idx = tid; idx < CH * D; idx += 256) {
-      const int i = idx / D, c = idx % D;
-      xs[idx] = i < n ? bf16_bits_to_f32(xsrc[(src + p0 + i) * D + c]) : 0.0f;
-    }
-    __syncthreads();
-    for (int t = 0; t < n; ++t) parts[part][t * D + j] = rc.part_sum(xs + t * D, part);
-    __syncthreads();
-    for (int idx = tid; idx < n * D; idx += 256) xs[idx] = RotCol<D>::combine(&parts[0][idx], CH * D);
-    __syncthreads();
-    for (int i = wave; i < n; i += 4) {
-      const int bw = bits_s[i];
-      const float clip = bw == 4 ? (sel ? a.clip_v4 : a.clip_k4) : (sel ? a.clip_v : a.clip_k);
-      float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-      for (int c = lane; c < D; c += kWave) {
-        mn = fminf(mn, xs[i * D + c]);
-        mx = fmaxf(mx, xs[i * D + c]);
+    if (tid == 0) {
+      for (int i = 0; i < n; ++i) {
+        const int p = p0 + i;
+        const int bw = (bitsrow && bitsrow[p] == 4) ? 4 : 2;
+        bits_s[i] = bw;
+        slot_s[i] = bw == 4 ? c4 : (p - dm.sink) - c4;
+        c4 += bw == 4;
       }
-      mn = wave_min(mn);
-      mx = wave_max(mx);
-      const int levels = (1 << bw) - 1;
-      const QuantGrid g = make_grid(mn, mx, clip, levels);
-      for (int c = lane; c < D; c += kWave) cs[i * D + c] = (uint8_t)quant_code(xs[i * D + c], g, levels);
-      if (lane == 0) szs[i] = g.s_bits | (g.z_bits << 16);
     }
     __syncthreads();
-    // each wave writes the tokens it quantised
-    for (int i = wave; i < n; i += 4) {
-      const int bw = bits_s[i], slot = slot_s[i];
-      const int32_t* pt = (bw == 4 ? a.pt4 : a.pt2) + (size_t)b * dm.pt_stride;
-      if (slot / kPage >= dm.pt_stride) continue;
-      const int64_t page = pt[slot / kPage];
-      if (!page_ok(page, bw, dm)) continue;
-      uint8_t* ph = page_head_mut(a.pool, page, kv, dm);
-      const int t = slot % kPage;
-      if (sel == 0)
-        store_key_codes(ph, D, bw, t, cs + i * D, lane, kWave);
-      else
-        store_value_codes(ph, D, bw, t, cs + i * D, lane, kWave);
-      if (lane == 0) reinterpret_cast<uint32_t*>(ph + 4 * D * bw)[2 * t + sel] = szs[i];
+    if (ci + 1 < nchunks) load_rows(chunk + 1, xw);   // in flight during this chunk
+    if (wave < SL) {
+#pragma unroll
+      for (int tile = 0; tile < CH / 32; ++tile) {
+        const float16v_t acc = rotate_tile<D>(rs, &xs[32 * tile][0], XS, n - 32 * tile, lane);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          xr[32 * tile + 8 * (j / 4) + 4 * (lane / 32) + j % 4][32 * wave + lane % 32] = acc[j];
+      }
     }
+    __syncthreads();
+    // row i = tid / 4: four threads, D/4 channels each (every lane takes part in the reductions)
+    {
+      constexpr int QC = D / 4;
+      const int i = tid / 4, q = tid % 4;
+      const bool live = i < n;
+      const int bw = live ? bits_s[i] : 2;
+      float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+      if (live)
+        for (int c = 0; c < QC; ++c) {
+          mn = fminf(mn, xr[i][q * QC + c]);
+          mx = fmaxf(mx, xr[i][q * QC + c]);
+        }
+#pragma unroll
+      for (int o = 1; o < 4; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+      }
+      if (live) {
+        const float clip = bw == 4 ? (sel ? a.clip_v4 : a.clip_k4) : (sel ? a.clip_v : a.clip_k);
+        const int levels = (1 << bw) - 1;
+        const QuantGrid g = make_grid(mn, mx, clip, levels);
+        uint32_t redo = 0;   // channels whose code the exact division decides (rare)
+#pragma unroll
+        for (int c4 = 0; c4 < QC / 4; ++c4) {
+          const float4 x4 = *reinterpret_cast<const float4*>(&xr[i][q * QC + 4 * c4]);
+          const float xe[4] = {x4.x, x4.y, x4.z, x4.w};
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool r;
+            packed |= quant_code_fast(xe[e], g, levels, r) << (8 * e);
+            redo |= (uint32_t)r << (4 * c4 + e);
+          }
+          *reinterpret_cast<uint32_t*>(&cs[i][q * QC + 4 * c4]) = packed;
+        }
+        while (redo) {
+          const int c = __builtin_ctz(redo);
+          redo &= redo - 1;
+          cs[i][q * QC + c] = (uint8_t)quant_code_exact(xr[i][q * QC + c], g, levels);
+        }
+        if (q == 0) szs[i] = g.s_bits | (g.z_bits << 16);
+      }
+    }
+    __syncthreads();
+    if (!dm.mixed) {
+      // INT2, whole pages: slot = position - sink, so token i sits in page (CH*chunk + i)/16, slot i%16
+      constexpr int CB = D * 2 / 32;   // bytes of one lane-chunk part (key or value)
+      constexpr int NWL = CB / 4;      // words of it
+      const int32_t* pt = a.pt2 + (size_t)b * dm.pt_stride;
+      const int pg0 = CH * chunk / kPage;
+      // (scale, zero) of each token
+      for (int i = tid; i < n; i += 256) {
+        const int pi = pg0 + i / kPage;
+        if (pi >= dm.pt_stride) continue;
+        const int64_t page = pt[pi];
+        if (page_ok(page, 2, dm))
+          reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + 4 * D * 2)[2 * (i % kPage) + sel] = szs[i];
+      }
+      if (sel == 0) {
+        // key words: (token, g, a), each owned by one slot
+        for (int idx = tid; idx < n * 4 * NWL; idx += 256) {
+          const int i = idx / (4 * NWL), g = (idx / NWL) % 4, aw = idx % NWL;
+          const int pi = pg0 + i / kPage, t = i % kPage;
+          if (pi >= dm.pt_stride) continue;
+          const int64_t page = pt[pi];
+          if (!page_ok(page, 2, dm)) continue;
+          uint32_t w = 0;
+          for (int k2 = 0; k2 < 2; ++k2)
+            for (int m = 0; m < 4; ++m)
+              for (int hf = 0; hf < 2; ++hf)
+                w |= (uint32_t)cs[i][32 * (2 * aw + k2) + 8 * g + 2 * m + hf] << (8 * k2 + 2 * m + 16 * hf);
+          reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + (size_t)(16 * g + t) * 2 * CB)[aw] = w;
+        }
+      } else {
+        // value words: (page, token group g', channel c, a), all four slots of a group at once
+        const int npg = (n + kPage - 1) / kPage;
+        for (int idx = tid; idx < npg * 64 * NWL; idx += 256) {
+          const int j = idx / (64 * NWL), r = idx % (64 * NWL);
+          const int gg = r / (16 * NWL), c = (r / NWL) % 16, aw = r % NWL;
+          const int pi = pg0 + j;
+          if (pi >= dm.pt_stride) continue;
+          const int64_t page = pt[pi];
+          if (!page_ok(page, 2, dm)) continue;
+          uint32_t w = 0;
+          for (int m = 0; m < 2; ++m)
+            for (int hf = 0; hf < 2; ++hf) {
+              const int i = kPage * j + 4 * gg + 2 * m + hf;
+              if (i >= n) continue;
+              for (int n4 = 0; n4 < 4; ++n4)
+                w |= (uint32_t)cs[i][16 * (4 * aw + n4) + c] << (2 * n4 + 8 * m + 16 * hf);
+            }
+          reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + (size_t)(16 * gg + c) * 2 * CB + CB)[aw] = w;
+        }
+      }
+    } else {
+      // mixed widths: each wavefront stores the tokens it owns, merging value bits per slot
+      for (int i = wave; i < n; i += 4) {
+        const int bw = bits_s[i], slot = slot_s[i];
+        const int32_t* pt = (bw == 4 ? a.pt4 : a.pt2) + (size_t)b * dm.pt_stride;
+        if (slot / kPage >= dm.pt_stride) continue;
+        store_token<D>(a, pt[slot / kPage], kv, bw, slot % kPage, sel, cs[i], szs[i], lane, kWave);
+      }
+    }
+    __syncthreads();   // xs, xr, cs and the slot tables are rewritten by the next chunk
   }
 }
 
@@ -186,12 +293,13 @@ __global__ __launch_bounds__(256) void bf16_fill_kernel(Bf16Args a) {
 hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream) {
   const Dims& dm = a.dm;
   if (dm.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_window_kernel, dim3(dm.hkv, dm.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prefill_window_kernel, dim3(dm.wpages, dm.hkv, dm.batch), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int hmax = dm.max_seq_len - dm.sink - dm.recent;
   if (hmax <= 0) return hipSuccess;
-  const dim3 grid((hmax + 31) / 32, dm.hkv, dm.batch);
+  const int runs = (hmax + kPrefillChunk * kPrefillChunks - 1) / (kPrefillChunk * kPrefillChunks);
+  const dim3 grid(runs, dm.hkv, 2 * dm.batch);   // z: request x {K, V}
   if (dm.d == 128)
     hipLaunchKernelGGL(prefill_hist_kernel<128>, grid, dim3(256), 0, stream, a);
   else

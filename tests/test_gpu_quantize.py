@@ -59,6 +59,46 @@ def test_quantize_pack_edge_groups():
         assert np.array_equal(gc, oc), (bits, clip)
 
 
+def _bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("bits,clip", [(2, 0.96), (2, 0.92), (4, 1.0), (2, 1.0)])
+def test_quantize_pack_near_rounding_midpoints(bits, clip):
+    """Values a few ulps either side of every code midpoint z + (k + 1/2) s of their group, where the
+    kernel's reciprocal estimate hands the decision to the exact division (and exact midpoints,
+    which round to even): codes equal the oracle's. Sentinels at channels 0 and 1 fix each group's
+    range, so the grid is known before the row is filled."""
+    rng = np.random.default_rng(17 + bits)
+    n, dim = 96, 128
+    base = np.zeros((n, dim), np.float32)
+    base[:, 0] = -rng.uniform(0.05, 40.0, n).astype(np.float32)
+    base[:, 1] = rng.uniform(0.05, 40.0, n).astype(np.float32)
+    _, sz = oracle.quantize_rows(base, dim, bits, clip)
+    sz = np.asarray(sz).reshape(n, 2)
+    s, z = _bf16_to_f32(sz[:, 0]), _bf16_to_f32(sz[:, 1])
+    levels = (1 << bits) - 1
+    x = base.copy()
+    for r in range(n):
+        vals = []
+        for k in range(levels):
+            m = np.float32(z[r] + np.float32(np.float32(k + 0.5) * s[r]))
+            v = m
+            for _ in range(3):
+                v = np.nextafter(v, np.float32(-np.inf))
+            for _ in range(7):
+                vals.append(v)
+                v = np.nextafter(v, np.float32(np.inf))
+        vals = np.array(vals, np.float32)[: dim - 2]
+        x[r, 2:2 + len(vals)] = vals
+    _, sz2 = oracle.quantize_rows(x, dim, bits, clip)
+    assert np.array_equal(np.asarray(sz2).reshape(n, 2), sz)      # the sentinels still set the grid
+    gc, gs = gpu_qp(x, dim, bits, clip)
+    oc, os_ = oracle_qp(x, dim, bits, clip)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
+
+
 def test_quantize_pack_many_rows_ragged_tail():
     x = rows_with_outliers(5, 100_003, 128, 1.0)
     gc, gs = gpu_qp(x, 128, 2, 0.96)
