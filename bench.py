@@ -263,6 +263,44 @@ def time_prefill(w, batch, context, reps=5):
             "rotation_tflops": round(rot_flops / (ms * 1e-3) / 1e12, 1), "bytes": nbytes}
 
 
+# ---------------------------------------------------------------- TriAxialKV allocation + routing
+def time_allocation(reps=20):
+    """The mixed workload's class allocation (host: greedy and exhaustive over its 22 tag classes)
+    and the routing of its 16 x 65,536 token tags to widths on the GPU."""
+    import torch
+    import bit_rotated_kv_amd as brk
+    import synth
+    w = synth.workload(5)
+    d2, d4 = synth.tag_sensitivity(w)
+    n = synth.tag_nominal_counts(w)
+    res = {"classes": int(w.n_tag_classes), "budget_bits": w.bit_budget}
+    for method in ("greedy", "exhaustive"):
+        brk.allocate_bits(d2, d4, n, w.bit_budget, method)
+        t = time.perf_counter()
+        k = reps if method == "greedy" else 3
+        for _ in range(k):
+            bits, cost = brk.allocate_bits(d2, d4, n, w.bit_budget, method)
+        res[f"{method}_ms"] = round((time.perf_counter() - t) / k * 1e3, 4)
+        res[f"{method}_int4_share"] = round(float((n * (bits == 4)).sum() / n.sum()), 4)
+        res[f"{method}_distortion"] = cost
+    B, T = w.batch, w.seq_lens[0]
+    tags = torch.randint(0, w.n_tag_classes, (B, T), dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T), dtype=torch.uint8, device="cuda")
+    brk.route_tokens(lens, tags, bits, out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        brk.route_tokens(lens, tags, bits, out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    res["route"] = {"tokens": B * T, "ms": round(ms, 5), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                    "GB_per_s": round(B * T * 5 / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
 # ---------------------------------------------------------------- BF16 baseline
 def time_bf16(w, batch, context, steps, warmup, fast_inputs):
     import torch
@@ -431,6 +469,8 @@ def main():
     if not args.no_prefill:
         log("timing the prefill (matrix-core rotation + quantise)")
         result["prefill"] = time_prefill(w, batch, context)
+        log("timing the TriAxialKV allocation and routing")
+        result["allocation"] = time_allocation()
     if not args.no_bf16:
         log("timing the BF16 baseline")
         bms, bbytes = time_bf16(w, batch, context, args.steps, args.warmup, True)

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboscar.so")
@@ -46,6 +46,8 @@ _SIGS = {
                                     _P, _P, c_float, _P, c_size_t, _P, _P]),
     "oscar_decode_step_profiled": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              c_int32, _P, _P, _P, c_float, _P, c_size_t, _P, _P, c_int32, _P]),
+    "oscar_allocate_bits": (c_int32, [c_int32, _P, _P, _P, c_double, c_int32, _P, _P]),
+    "oscar_route_tokens": (c_int32, [c_int32, c_int32, _P, _P, c_int32, _P, _P, _P]),
     "oscar_bf16_fill": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, c_int64, _P, c_int32, _P]),
     "oscar_bf16_decode_workspace_bytes": (c_size_t, [_P, c_int32, c_int32]),
     "oscar_bf16_decode_attn": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, c_int64, _P, c_int32, c_float, _P,

@@ -239,3 +239,46 @@ def bf16_decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, pag
                                        num_pages, _p(page_table), page_table.shape[1], softmax_scale, _p(workspace),
                                        workspace.numel(), _p(out), _stream()), "oscar_bf16_decode_attn")
     return out
+
+
+ALLOC_METHODS = {"greedy": 0, "exhaustive": 1}
+
+
+def allocate_bits(d2, d4, counts, budget_bits: float, method: str = "greedy"):
+    """INT2/INT4 width per tag class (host call): returns (bits uint8 [n], total distortion)."""
+    import ctypes
+
+    import numpy as np
+    d2 = np.ascontiguousarray(d2, np.float64)
+    d4 = np.ascontiguousarray(d4, np.float64)
+    counts = np.ascontiguousarray(counts, np.int64)
+    n = len(d2)
+    if len(d4) != n or len(counts) != n:
+        raise ValueError("d2, d4 and counts must have one entry per class")
+    if method not in ALLOC_METHODS:
+        raise ValueError(f"method must be one of {sorted(ALLOC_METHODS)}")
+    bits = np.zeros(n, np.uint8)
+    cost = ctypes.c_double(0.0)
+    check(lib().oscar_allocate_bits(n, d2.ctypes.data, d4.ctypes.data, counts.ctypes.data, float(budget_bits),
+                                    ALLOC_METHODS[method], bits.ctypes.data, ctypes.byref(cost)),
+          "oscar_allocate_bits")
+    return bits, cost.value
+
+
+def route_tokens(seq_len: torch.Tensor, tags: torch.Tensor, class_bits, token_bits: Optional[torch.Tensor] = None
+                 ) -> torch.Tensor:
+    """tags [B, max_seq_len] int32 (device) -> token widths [B, max_seq_len] uint8 (positions below
+    seq_len[b] written; a fresh output starts at 2 bits)."""
+    import numpy as np
+    _need(seq_len, torch.int32, "seq_len")
+    _need(tags, torch.int32, "tags")
+    cb = np.ascontiguousarray(class_bits, np.uint8)
+    if token_bits is None:
+        token_bits = torch.full(tags.shape, 2, dtype=torch.uint8, device=tags.device)
+    _need(token_bits, torch.uint8, "token_bits")
+    if token_bits.shape != tags.shape or tags.dim() != 2 or seq_len.shape[0] != tags.shape[0]:
+        raise ValueError("tags and token_bits must be [B, max_seq_len] with B = len(seq_len)")
+    check(lib().oscar_route_tokens(tags.shape[0], tags.shape[1], _p(seq_len), _p(tags), len(cb),
+                                   c_void_p(cb.ctypes.data) if len(cb) else None, _p(token_bits), _stream()),
+          "oscar_route_tokens")
+    return token_bits

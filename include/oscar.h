@@ -275,6 +275,45 @@ oscar_status_t oscar_bf16_decode_attn(const oscar_layout_t* layout, int32_t batc
                                       float softmax_scale, void* workspace, size_t workspace_bytes,
                                       float* out, hipStream_t stream);
 
+/* ------------------------------------------------------------------ TriAxialKV bit allocation */
+
+/* Allocation methods of oscar_allocate_bits. */
+enum { OSCAR_ALLOC_GREEDY = 0, OSCAR_ALLOC_EXHAUSTIVE = 1 };
+
+/*
+ * INT2/INT4 width per tag class (TriAxialKV reading note, section 3): minimise
+ * sum_k D_k(b_k) subject to sum_k N_k b_k <= budget_bits * sum_k N_k, b_k in {2, 4}. Host
+ * function: every pointer is host memory and nothing is enqueued on a device.
+ *   d2, d4       [n_classes] distortion of class k at 2 and at 4 bits (finite)
+ *   counts       [n_classes] tokens of class k (0 .. 2^50)
+ *   budget_bits  average bits per element the allocation may spend (>= 2)
+ *   method       OSCAR_ALLOC_GREEDY: raise classes from 2 to 4 bits in descending order of the
+ *                gain per extra bit rho_k = (D_k(2) - D_k(4)) / (2 N_k) (ties: lower class index
+ *                first); classes without a positive gain or without tokens stay at 2; the first
+ *                class whose raise would exceed the budget ends it.
+ *                OSCAR_ALLOC_EXHAUSTIVE: the least total distortion over all 2^n_classes choices
+ *                that meet the budget (n_classes <= 24, else OSCAR_ERR_UNSUPPORTED); among equal
+ *                costs any one is returned.
+ *   bits_out     [n_classes] written with 2 or 4
+ *   cost_out     optional: sum_k D_k(bits_out[k])
+ * The budget test allows 1e-9 bits of slack for the rounding of budget_bits * sum N_k.
+ */
+oscar_status_t oscar_allocate_bits(int32_t n_classes, const double* d2, const double* d4,
+                                   const int64_t* counts, double budget_bits, int32_t method,
+                                   uint8_t* bits_out, double* cost_out);
+
+/*
+ * Token widths from tag classes (TriAxialKV reading note, sections 3-4: the class allocation
+ * routes every token to the INT2 or the INT4 pool): token_bits[b][t] = class_bits[tags[b][t]]
+ * for t < seq_len[b] (device arrays [batch][max_seq_len]; positions at or past seq_len[b] are
+ * not written). A tag outside [0, n_classes) routes to 2 bits. class_bits is a host array of
+ * n_classes <= 64 entries, each 2 or 4, copied into the launch. The result feeds the
+ * token_bits argument of oscar_kv_prefill.
+ */
+oscar_status_t oscar_route_tokens(int32_t batch, int32_t max_seq_len, const int32_t* seq_len,
+                                  const int32_t* tags, int32_t n_classes, const uint8_t* class_bits,
+                                  uint8_t* token_bits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

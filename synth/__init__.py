@@ -22,7 +22,7 @@ import numpy as np
 _ROLE = {
     "chan_k": 1, "chan_v": 2, "chan_q": 3, "mix_q": 4, "kv": 5, "q": 6,
     "u": 7, "cal_q": 8, "cal_ctx": 9, "pages": 10, "lens": 11, "tags": 12,
-    "tagprob": 13, "int4cls": 14, "rows": 15,
+    "tagprob": 13, "int4cls": 14, "rows": 15, "tagsens": 16,
 }
 
 
@@ -49,7 +49,7 @@ class Workload:
     paged_shuffle: bool        # page table = seeded permutation of a shared pool
     mixed: bool = False        # INT2/INT4 history (tag classes)
     n_tag_classes: int = 0
-    int4_token_frac: float = 0.0
+    bit_budget: float = 0.0    # average bits per history element the allocation may spend
     fp32_inputs: bool = False  # tiny reference config draws fp32 activations
     cal_tokens: int = 8878     # calibration query count for C_Q
     cal_ctx: int = 4096        # calibration context for C_S
@@ -80,7 +80,7 @@ def workload(n: int, **over) -> Workload:
                      (10.0, 30.0), True, "eig", True)
     elif n == 5:
         w = Workload("mixed-int2-int4-bs16-64k", 4, 16, 32, 8, 128, 128, (65_536,) * 16, 8, (10.0, 30.0), True,
-                     "eig", True, mixed=True, n_tag_classes=22, int4_token_frac=0.30)
+                     "eig", True, mixed=True, n_tag_classes=22, bit_budget=2.6)
     else:
         raise ValueError(f"no workload {n}")
     return dataclasses.replace(w, **over) if over else w
@@ -201,18 +201,19 @@ def tag_class_probs(w: Workload) -> np.ndarray:
     return rng_for(w.seed, "tagprob").dirichlet(np.ones(w.n_tag_classes))
 
 
-def int4_classes(w: Workload) -> np.ndarray:
-    """A seeded set of tag classes stored at 4 bits, drawn so that their total token
-    share is close to ``int4_token_frac``: classes are visited in a seeded order and
-    added while the share stays at or below the target."""
-    probs = tag_class_probs(w)
-    order = rng_for(w.seed, "int4cls").permutation(w.n_tag_classes)
-    chosen, share = [], 0.0
-    for c in order:
-        if share + probs[c] <= w.int4_token_frac + 1e-12:
-            chosen.append(int(c))
-            share += probs[c]
-    return np.array(sorted(chosen), np.int32)
+def tag_sensitivity(w: Workload) -> tuple:
+    """A seeded synthetic sensitivity table (d2, d4) [n_tag_classes]: the attention-output
+    distortion of each tag class stored at 2 and at 4 bits (d2 > d4 > 0, spread over decades,
+    standing in for a calibration measurement)."""
+    r = rng_for(w.seed, "tagsens")
+    d4 = 10.0 ** r.uniform(-4.0, -2.0, w.n_tag_classes)
+    d2 = d4 + 10.0 ** r.uniform(-3.0, -0.5, w.n_tag_classes)
+    return d2, d4
+
+
+def tag_nominal_counts(w: Workload, tokens: int = 1_000_000) -> np.ndarray:
+    """Expected tokens per tag class in a cache of ``tokens`` tokens (int64)."""
+    return np.rint(tag_class_probs(w) * tokens).astype(np.int64)
 
 
 def standard_rows(seed: int, n: int, d: int, scale: float = 1.0) -> np.ndarray:

@@ -49,12 +49,17 @@ def rotations(w: synth.Workload):
     return np.stack(rk), np.stack(rv)
 
 
+def class_bits(w: synth.Workload) -> np.ndarray:
+    """Bits of each tag class: the oracle's TriAxialKV greedy over the workload's sensitivity table,
+    nominal class counts and bit budget."""
+    d2, d4 = synth.tag_sensitivity(w)
+    return oracle.greedy_bit_allocation(d2, d4, synth.tag_nominal_counts(w), w.bit_budget)
+
+
 def token_bits(w: synth.Workload, b: int, T: int) -> np.ndarray:
     if not w.mixed:
         return np.full(T, 2, np.int64)
-    cls = synth.tag_classes(w, b, T)
-    four = np.isin(cls, synth.int4_classes(w))
-    return np.where(four, 4, 2).astype(np.int64)
+    return class_bits(w)[synth.tag_classes(w, b, T)].astype(np.int64)
 
 
 def make_problem(w: synth.Workload, shuffle: bool = True, with_oracle: bool = True) -> Problem:
