@@ -85,19 +85,53 @@ def workload_inputs(w, batch, context, seed_offset=0, fast=False):
     return K, V, torch.from_numpy(q).cuda().bfloat16()
 
 
-def rotations(w):
-    """R_K, R_V [Hkv, d, d] fp32 from the product calibration (offline step)."""
+def calibration_inputs(w):
+    """The workload's calibration activations as bf16 device tensors: queries [Hkv, g, N, d] and a
+    calibration context K, V [Hkv, n, d]."""
     import torch
     import synth
+    q = np.stack([synth.calibration_queries(w, kv) for kv in range(w.num_kv_heads)])
+    ctx = [synth.calibration_context(w, kv) for kv in range(w.num_kv_heads)]
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    return bf(q), bf(np.stack([c[0] for c in ctx])), bf(np.stack([c[1] for c in ctx]))
+
+
+def rotations(w):
+    """R_K, R_V [Hkv, d, d] fp32 from the library's calibration (covariances on the GPU matrix
+    cores, eigendecomposition on the host): the offline step that ships the rotations."""
     from bit_rotated_kv_amd import calib
-    rk, rv = [], []
-    for kv in range(w.num_kv_heads):
-        qc = torch.from_numpy(synth.calibration_queries(w, kv))
-        kc, vc = synth.calibration_context(w, kv)
-        rk.append(calib.rotation(calib.eigvecs_descending(calib.query_covariance(qc))))
-        cs = calib.value_covariance(qc[:, :1024], torch.from_numpy(kc), torch.from_numpy(vc), 1.0 / math.sqrt(w.head_dim))
-        rv.append(calib.rotation(calib.eigvecs_descending(cs)))
-    return torch.stack(rk).cuda(), torch.stack(rv).cuda()
+    q, k, v = calibration_inputs(w)
+    return calib.rotations_on_gpu(q, k, v, 1024, 1.0 / math.sqrt(w.head_dim))
+
+
+def time_calibration(w, reps=5):
+    """GPU covariances of the workload's calibration set: C_Q over every calibration query of the
+    query heads of each kv-head, C_S over the first 1,024 of them and the calibration context."""
+    import torch
+    import bit_rotated_kv_amd as brk
+    q, k, v = calibration_inputs(w)
+    qv = q[:, :, :1024].contiguous()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    hkv, g, n, d = q.shape
+    res = {"workload": f"{hkv} kv-heads x {g} query heads, {n} calibration queries (C_Q), 1024 queries over "
+                       f"{k.shape[1]} context tokens (C_S), d {d}"}
+    for name, fn, flops in (
+            ("query_cov", lambda: brk.calib_query_cov(q), 2.0 * hkv * g * n * d * d),
+            ("value_cov", lambda: brk.calib_value_cov(qv, k, v, scale),
+             hkv * g * 1024 * k.shape[1] * d * 2.0 * 3 + 3 * 2.0 * hkv * g * 1024 * d * d)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"{name}_ms"] = round(ms, 4)
+        res[f"{name}_mfma_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        res[f"{name}_mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    return res
 
 
 # ---------------------------------------------------------------- INT2 path
@@ -471,6 +505,8 @@ def main():
         result["prefill"] = time_prefill(w, batch, context)
         log("timing the TriAxialKV allocation and routing")
         result["allocation"] = time_allocation()
+        log("timing the calibration covariances")
+        result["calibration"] = time_calibration(w)
     if not args.no_bf16:
         log("timing the BF16 baseline")
         bms, bbytes = time_bf16(w, batch, context, args.steps, args.warmup, True)

@@ -66,3 +66,17 @@ def value_covariance(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: f
     s = torch.softmax(scale * q @ k.to(torch.float64).T, dim=-1)
     sv = s @ v.to(torch.float64)
     return torch.einsum("hni,hnj->ij", sv, sv) / q.shape[1]
+
+
+def rotations_on_gpu(q_cal: torch.Tensor, k_ctx: torch.Tensor, v_ctx: torch.Tensor, n_value_queries: int,
+                     scale: float) -> tuple:
+    """R_K, R_V [Hkv, d, d] fp32 (device) from calibration activations on the GPU: q_cal
+    [Hkv, gq, N, d] bf16 queries, k_ctx, v_ctx [Hkv, n, d] bf16 context. The covariances are
+    accumulated on the matrix cores (C_Q over all N queries, C_S over the first n_value_queries);
+    their eigenvectors and R = U . H . P_br are formed on the host in float64."""
+    from .ops import calib_query_cov, calib_value_cov
+    cq = calib_query_cov(q_cal).double().cpu()
+    cs = calib_value_cov(q_cal[:, :, :n_value_queries].contiguous(), k_ctx, v_ctx, scale).double().cpu()
+    rk = torch.stack([rotation(eigvecs_descending(c)) for c in cq])
+    rv = torch.stack([rotation(eigvecs_descending(c)) for c in cs])
+    return rk.to(q_cal.device), rv.to(q_cal.device)

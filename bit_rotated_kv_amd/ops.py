@@ -282,3 +282,30 @@ def route_tokens(seq_len: torch.Tensor, tags: torch.Tensor, class_bits, token_bi
                                    c_void_p(cb.ctypes.data) if len(cb) else None, _p(token_bits), _stream()),
           "oscar_route_tokens")
     return token_bits
+
+
+def calib_query_cov(q: torch.Tensor) -> torch.Tensor:
+    """q [Hkv, gq, N, d] bf16 (calibration queries) -> C_Q [Hkv, d, d] fp32 on the GPU."""
+    _need(q, torch.bfloat16, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [Hkv, gq, N, d]")
+    hkv, gq, n, d = q.shape
+    ws = torch.empty(lib().oscar_calib_workspace_bytes(hkv, gq, n, d), dtype=torch.uint8, device=q.device)
+    cov = torch.empty((hkv, d, d), dtype=torch.float32, device=q.device)
+    check(lib().oscar_calib_query_cov(hkv, gq, n, d, _p(q), _p(ws), ws.numel(), _p(cov), _stream()),
+          "oscar_calib_query_cov")
+    return cov
+
+
+def calib_value_cov(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float = 0.0) -> torch.Tensor:
+    """q [Hkv, gq, N, d], k, v [Hkv, n, d] bf16 -> C_S [Hkv, d, d] fp32 on the GPU."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, name)
+    if q.dim() != 4 or k.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[3]:
+        raise ValueError("q must be [Hkv, gq, N, d] and k, v [Hkv, n, d]")
+    hkv, gq, n, d = q.shape
+    ws = torch.empty(lib().oscar_calib_workspace_bytes(hkv, gq, n, d), dtype=torch.uint8, device=q.device)
+    cov = torch.empty((hkv, d, d), dtype=torch.float32, device=q.device)
+    check(lib().oscar_calib_value_cov(hkv, gq, n, k.shape[1], d, _p(q), _p(k), _p(v), softmax_scale, _p(ws),
+                                      ws.numel(), _p(cov), _stream()), "oscar_calib_value_cov")
+    return cov

@@ -314,6 +314,43 @@ oscar_status_t oscar_route_tokens(int32_t batch, int32_t max_seq_len, const int3
                                   const int32_t* tags, int32_t n_classes, const uint8_t* class_bits,
                                   uint8_t* token_bits, hipStream_t stream);
 
+/* ------------------------------------------------------------------ calibration statistics */
+
+/*
+ * Workspace bytes of the calibration calls for n_rows calibration queries per query head
+ * (n_tokens of oscar_calib_query_cov, n_queries of oscar_calib_value_cov).
+ */
+size_t oscar_calib_workspace_bytes(int32_t num_kv_heads, int32_t gq, int32_t n_rows, int32_t head_dim);
+
+/*
+ * Query covariance of every kv-head ("Together AI open-sources OSCAR", section on what makes OSCAR
+ * different): cov[kv] = (1/N) sum_h sum_n q^T q over the gq query heads of the kv-head and the
+ * N = n_tokens calibration queries of each. Its eigenvectors (descending eigenvalues) are U_Q of
+ * R_K = U_Q . H . P_br (the eigendecomposition is a host step).
+ *   q     [num_kv_heads][gq][n_tokens][head_dim] bf16 (device)
+ *   cov   [num_kv_heads][head_dim][head_dim] fp32 (device)
+ * bf16 products are exact on the matrix cores; sums are fp32, in a fixed order (deterministic).
+ * head_dim 64 or 128.
+ */
+oscar_status_t oscar_calib_query_cov(int32_t num_kv_heads, int32_t gq, int32_t n_tokens, int32_t head_dim,
+                                     const void* q, void* workspace, size_t workspace_bytes, float* cov,
+                                     hipStream_t stream);
+
+/*
+ * Score-weighted value covariance (same section): cov[kv] = (1/N) sum_h (S_h V)^T (S_h V) with
+ * S_h = softmax(scale q_h K^T) over a calibration context (rows over its n_ctx keys), for the
+ * N = n_queries calibration queries of each of the gq heads. Eigenvectors give U_S of R_V.
+ *   q     [num_kv_heads][gq][n_queries][head_dim] bf16; k, v [num_kv_heads][n_ctx][head_dim] bf16
+ *   softmax_scale 0 -> 1/sqrt(head_dim)
+ *   cov   [num_kv_heads][head_dim][head_dim] fp32
+ * S V is formed in fp32 (probabilities enter the product as bf16 high + low parts) and its Gram
+ * matrix from bf16 high + low parts of each element (about 16 significant bits).
+ */
+oscar_status_t oscar_calib_value_cov(int32_t num_kv_heads, int32_t gq, int32_t n_queries, int32_t n_ctx,
+                                     int32_t head_dim, const void* q, const void* k, const void* v,
+                                     float softmax_scale, void* workspace, size_t workspace_bytes, float* cov,
+                                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
