@@ -382,18 +382,19 @@ def time_bf16(w, batch, context, steps, warmup, fast_inputs):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_traffic.txt")
 
 
+SPLIT_SOURCES = ("api.hip", "common.hpp", "decode.hip", "demote.hpp", "launch.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources that define the decode kernels and their launch plan (file
-    names and contents, sorted): everything in csrc/ except the prefill writers and the
-    stand-alone quantiser, which the decode step never launches."""
+    """sha256 over the HIP sources that define the decode split kernel and its launch plan (file
+    names and contents, in this order)."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "bit_rotated_kv_amd", "csrc")
-    for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".hpp")) and name not in ("kvwrite.hip", "quantize.hip"):
-            h.update(name.encode())
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(f.read())
+    for name in SPLIT_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
