@@ -1,6 +1,7 @@
 // C ABI of the OSCAR gfx950 library (declared and documented in include/oscar.h): host-side
 // validation, workspace planning and kernel launches. Nothing here touches device memory.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "common.hpp"
@@ -85,7 +86,14 @@ DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len, int 
   if (hist < 0) hist = 0;
   const int hp = (hist + kPage - 1) / kPage;
   constexpr int W = kSplitWaves;
-  p.nwin = ((L->sink_len + L->recent_len) / kPage + W - 1) / W;
+#ifndef OSCAR_WINDOW_WORKGROUPS
+#define OSCAR_WINDOW_WORKGROUPS 1
+#endif
+  // window workgroups per (b, kv): each wavefront walks window pages with a stride (at most one
+  // page per wavefront is useful)
+  const int wpg = (L->sink_len + L->recent_len) / kPage;
+  p.nwin = std::min(OSCAR_WINDOW_WORKGROUPS, (wpg + W - 1) / W);
+  if (p.nwin < 1) p.nwin = 1;
   // history workgroups aim at what the window (and step) workgroups leave of the target
   const int64_t nwin_all = (int64_t)batch * L->num_kv_heads * (p.nwin + step);
   const int64_t hist_target = nwin_all < kTargetWorkgroups / 2 ? kTargetWorkgroups - nwin_all : kTargetWorkgroups / 2;

@@ -553,9 +553,10 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   }
 }
 
-// Window role: workgroup wi of (b, kv) covers window pages 4*wi .. 4*wi+3, one per wavefront; in a
-// fused step the last window workgroup of (b, kv) is the step workgroup, and the ring slot of the
-// demoted token (position T - recent) is left to it.
+// Window role: the nw window workgroups of (b, kv) (in a fused step the last one is the step
+// workgroup) share the window pages; wavefront w of workgroup wi takes pages 4 wi + w, stepping by
+// 4 (nw - step), with the next page loading while one is processed. In a fused step the ring slot of
+// the demoted token (position T - recent) is left to the step workgroup.
 template <int D, int GQ>
 __device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int idx, float (*o_lds)[2 * GQ][D],
                             float (*st_lds)[3][8], StepLds<D, GQ>& slds) {
@@ -573,11 +574,14 @@ __device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int i
   load_bf16_query<D, GQ>(bq, a.q, (size_t)b * dm.hq + (size_t)kv * GQ, lane);
   WaveState<D, GQ> st;
   st.init();
-  const int pg = kSplitWaves * wi + wave;
-  if (pg < dm.wpages) {
-    const uint8_t* ph = a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + pg) * bf16_page_head_bytes(D);
-    Bf16Page<D> pr;
-    load_bf16_page<D>(pr, ph, lane);
+  const int64_t pb = bf16_page_head_bytes(D);
+  const uint8_t* wbase = a.window + (size_t)bk * dm.wpages * pb;
+  const int stride = kSplitWaves * (nw - a.step);
+  int pg = kSplitWaves * wi + wave;
+  Bf16Page<D> cur, nxt;
+  if (pg < dm.wpages) load_bf16_page<D>(cur, wbase + pg * pb, lane);
+  for (; pg < dm.wpages; pg += stride) {
+    if (pg + stride < dm.wpages) load_bf16_page<D>(nxt, wbase + (pg + stride) * pb, lane);
     bool valid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -593,7 +597,8 @@ __device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int i
         valid[r] = T - 1 - back >= dm.sink && !(a.step && back == dm.recent - 1);
       }
     }
-    process_bf16_page<D, GQ>(st, pr, bq, valid, a.scale_log2e, lane);
+    process_bf16_page<D, GQ>(st, cur, bq, valid, a.scale_log2e, lane);
+    cur = nxt;
   }
   const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + wi;
   workgroup_merge<D, GQ, 16, false, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
