@@ -15,6 +15,9 @@ computes, written from the OSCAR pages:
   recent 256 (core point 3).
 * The TriAxialKV reading note (miraclefarms.github.io): INT2/INT4 dual pool split at an
   address offset (section 4) and bitwidth-homogeneous decode splits.
+* The OSCAR overview page, the paragraph that sets OSCAR beside TurboQuant: a Lloyd-Max
+  codebook with the attention-aware rotation (``codebook.py``, pinned against textbook
+  Lloyd-Max values, brute force and the uniform codec).
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
 of ``bench.py``. The product package never imports, links or runs anything here, and this
@@ -34,5 +37,8 @@ from .cache import (SINK, RECENT, segments, effective_bits, OracleCache)
 from .attention import (softmax_attention, lse_merge, decode_attention, plain_decode_attention,
                         partial_attention)
 from .allocate import greedy_bit_allocation, exhaustive_bit_allocation
+from .codebook import (UNIFORM_LEVELS, fp16_levels, fp16_patterns, thresholds_fp32, code_of_coordinate,
+                       group_coordinates, quantize_rows_codebook, dequantize_rows_codebook, lloyd_max,
+                       fit_codebook)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

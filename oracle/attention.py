@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quant import bf16_round, dequantize_rows
+from .quant import bf16_round
 
 
 def softmax_attention(logits, values):
@@ -55,7 +55,8 @@ def decode_attention(cache, q, scale=None):
     """Attention output of decode queries q [Hq, d] over an ``OracleCache``; fp64 [Hq, d].
 
     Sink/recent logits: scale * q . k in the original basis. History logits:
-    scale * (q . R_K) . x_hat_K with x_hat = s * code + z in the rotated basis. One softmax
+    scale * (q . R_K) . x_hat_K with x_hat = s * code + z in the rotated basis (s * l[code] + z
+    under a codebook). One softmax
     over all logits; o = sum_BF16 p v + (sum_hist p x_hat_V) . R_V^T."""
     q = bf16_round(np.asarray(q, np.float32)).astype(np.float64)
     hq, d = q.shape
@@ -65,8 +66,7 @@ def decode_attention(cache, q, scale=None):
     for h in range(hq):
         kv = h // g
         kb, vb, _ = cache.bf16_rows(kv)
-        xk = dequantize_rows(cache.k_codes[kv], cache.k_sz[kv], cache.group)
-        xv = dequantize_rows(cache.v_codes[kv], cache.v_sz[kv], cache.group)
+        xk, xv = cache.history_rows(kv)
         q_rot = q[h] @ cache.rot_k[kv].astype(np.float64)
         logits = np.concatenate([scale * (kb @ q[h]), scale * (xk @ q_rot)])
         if logits.size == 0:

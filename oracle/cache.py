@@ -17,12 +17,15 @@ Readings where the pages are silent:
 * Mixed INT2/INT4 history (TriAxialKV reading note, section 4): each token carries a bit
   width chosen when it is created; it is quantised at that width when demoted, with the
   INT4 clip ratio (1.0 unless given, since TriAxialKV names no clipping).
+* Optional Lloyd-Max codebooks (``codebook.py``): per kv-head four fp16 levels for K and for
+  V replace the uniform INT2 levels; INT4 tokens keep the uniform levels.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .quant import bf16_round, rotate_rows_fp32, quantize_rows
+from .quant import bf16_round, rotate_rows_fp32, quantize_rows, dequantize_rows
+from .codebook import quantize_rows_codebook, dequantize_rows_codebook
 
 SINK = 64
 RECENT = 256
@@ -55,13 +58,17 @@ class OracleCache:
     (rotated space) for history positions, for every kv-head."""
 
     def __init__(self, rot_k32, rot_v32, group: int, clip_k: float = 0.96, clip_v: float = 0.92,
-                 clip_k4: float = 1.0, clip_v4: float = 1.0, sink: int = SINK, recent: int = RECENT):
+                 clip_k4: float = 1.0, clip_v4: float = 1.0, sink: int = SINK, recent: int = RECENT,
+                 codebook_k=None, codebook_v=None):
         self.rot_k = np.asarray(rot_k32, dtype=np.float32)   # [Hkv, d, d]
         self.rot_v = np.asarray(rot_v32, dtype=np.float32)
         self.hkv, self.d = self.rot_k.shape[0], self.rot_k.shape[1]
         self.group = group
         self.clip = {2: (clip_k, clip_v), 4: (clip_k4, clip_v4)}
         self.sink, self.recent = sink, recent
+        # INT2 codebooks [Hkv, 4] (fp16-valued levels), or None for the uniform levels
+        self.codebook = {"k": None if codebook_k is None else np.asarray(codebook_k, np.float32),
+                         "v": None if codebook_v is None else np.asarray(codebook_v, np.float32)}
         self.T = 0
         self.bf16_k = {}    # pos -> [Hkv, d] float32 (bf16 values)
         self.bf16_v = {}
@@ -80,11 +87,29 @@ class OracleCache:
         ck, cv = self.clip.get(bits, (1.0, 1.0))
         kc, ks, vc, vs = [], [], [], []
         for h in range(self.hkv):
-            c, s = quantize_rows(rotate_rows_fp32(k_rows[h], self.rot_k[h]), self.group, bits, ck)
+            c, s = self._quantize(rotate_rows_fp32(k_rows[h], self.rot_k[h]), bits, ck, "k", h)
             kc.append(c); ks.append(s)
-            c, s = quantize_rows(rotate_rows_fp32(v_rows[h], self.rot_v[h]), self.group, bits, cv)
+            c, s = self._quantize(rotate_rows_fp32(v_rows[h], self.rot_v[h]), bits, cv, "v", h)
             vc.append(c); vs.append(s)
         return np.stack(kc), np.stack(ks), np.stack(vc), np.stack(vs)
+
+    def _quantize(self, x, bits, clip, which, h):
+        cb = self.codebook[which]
+        if bits == 2 and cb is not None:
+            return quantize_rows_codebook(x, self.group, clip, cb[h])
+        return quantize_rows(x, self.group, bits, clip)
+
+    def history_rows(self, kv: int):
+        """Dequantised history rows (rotated basis) of a kv-head: (K_hat, V_hat) fp64 [n, d]."""
+        out = []
+        for which, codes, sz in (("k", self.k_codes, self.k_sz), ("v", self.v_codes, self.v_sz)):
+            x = dequantize_rows(codes[kv], sz[kv], self.group)
+            cb = self.codebook[which]
+            sel = self.hist_bits == 2
+            if cb is not None and sel.any():
+                x[sel] = dequantize_rows_codebook(codes[kv][sel], sz[kv][sel], self.group, cb[kv])
+            out.append(x)
+        return out[0], out[1]
 
     def _push_history(self, pos, bits, kc, ks, vc, vs):
         self.hist_pos = np.concatenate([self.hist_pos, np.asarray(pos, np.int64)])
