@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurement")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-codebook", action="store_true", help="skip the Lloyd-Max codebook variant")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
     return ap.parse_args()
@@ -136,7 +137,7 @@ def time_calibration(w, reps=5):
 
 # ---------------------------------------------------------------- INT2 path
 class Int2Setup:
-    def __init__(self, w, batch, context, copies, steps_total, fast_inputs):
+    def __init__(self, w, batch, context, copies, steps_total, fast_inputs, codebook=None):
         import torch
         import bit_rotated_kv_amd as brk
         import synth
@@ -150,7 +151,7 @@ class Int2Setup:
         self.q = q
         self.rk, self.rv = rotations(w)
         base = brk.allocate_cache(w.num_q_heads, w.num_kv_heads, w.head_dim, batch, self.max_seq,
-                                  pages2_per_request=hist_pages, page_order2=order)
+                                  pages2_per_request=hist_pages, page_order2=order, codebook=codebook)
         self.layout = base.layout
         base.seq_len.fill_(t0)
         Kp = torch.zeros((batch, w.num_kv_heads, self.max_seq, w.head_dim), dtype=torch.bfloat16, device="cuda")
@@ -248,6 +249,40 @@ def time_int2(setup, steps, warmup, eager):
     torch.cuda.synchronize()
     k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
     return ms, k.mean(axis=0), mode
+
+
+# ---------------------------------------------------------------- Lloyd-Max codebook variant
+def time_codebook(w, batch, context, steps, warmup, eager, fast_inputs, reps=3):
+    """The INT2 history with Lloyd-Max codebooks: the fit on the GPU (calibration context rotated by
+    the workload's rotations; K and V of every kv-head), then the same decode step as the uniform
+    codec with the codebook cache (codes enter both products as their levels)."""
+    import torch
+    from bit_rotated_kv_amd import calib
+    _, kc, vc = calibration_inputs(w)
+    rk, rv = rotations(w)
+    calib.codebooks_on_gpu(kc, vc, rk, rv)                  # warm-up
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        table, levels, iters = calib.codebooks_on_gpu(kc, vc, rk, rv)
+    fit_ms = (time.perf_counter() - t) / reps * 1e3
+    est = batch * w.num_kv_heads * (context - 320) * 72
+    copies = max(2, math.ceil(1.0e9 / est))
+    setup = Int2Setup(w, batch, context, copies, steps + warmup, fast_inputs, codebook=table)
+    ms, kern, mode = time_int2(setup, steps, warmup, eager)
+    int2, bf16, demote = setup.bytes_per_step()
+    split_gbs = (int2 + bf16) / (float(kern[1]) * 1e-3) / 1e9
+    del setup
+    torch.cuda.empty_cache()
+    return {"workload": f"batch {batch}, context {context}, Lloyd-Max INT2 codebooks per kv-head (K and V)",
+            "fit_ms": round(fit_ms, 3), "fit_iterations": iters.tolist(),
+            "fit_calibration_rows": int(kc.shape[1]),
+            "levels_kv0": [[round(float(x), 4) for x in levels[0, j]] for j in range(2)],
+            "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+            "GB_per_s": round((int2 + bf16 + demote) / (ms * 1e-3) / 1e9, 1),
+            "kernel_ms": [round(float(x), 5) for x in kern],
+            "split_GB_per_s": round(split_gbs, 1), "split_frac": round(split_gbs / HBM_PEAK_GBS, 4),
+            "launch": mode}
 
 
 # ---------------------------------------------------------------- prefill (rotate + quantise on MFMA)
@@ -508,6 +543,9 @@ def main():
         result["allocation"] = time_allocation()
         log("timing the calibration covariances")
         result["calibration"] = time_calibration(w)
+    if not args.no_codebook:
+        log("timing the Lloyd-Max codebook variant (fit + decode step)")
+        result["codebook"] = time_codebook(w, batch, context, args.steps, args.warmup, args.eager, False)
     if not args.no_bf16:
         log("timing the BF16 baseline")
         bms, bbytes = time_bf16(w, batch, context, args.steps, args.warmup, True)
@@ -534,6 +572,8 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_prefill:
             result["bs32"]["prefill"] = time_prefill(w32, 32, c32)
+        if not args.no_codebook:
+            result["bs32"]["codebook"] = time_codebook(w32, 32, c32, args.steps, args.warmup, args.eager, True)
         if not args.no_bf16:
             bms32, bb32 = time_bf16(w32, 32, c32, args.steps, args.warmup, True)
             result["bs32"]["bf16_baseline_ms"] = round(bms32, 5)

@@ -24,7 +24,7 @@ class Layout(ctypes.Structure):
                 ("group_size", c_int32), ("sink_len", c_int32), ("recent_len", c_int32),
                 ("page_size", c_int32), ("mixed", c_int32), ("int4_page_offset", c_int64),
                 ("pool_pages", c_int64), ("clip_k", c_float), ("clip_v", c_float),
-                ("clip_k4", c_float), ("clip_v4", c_float)]
+                ("clip_k4", c_float), ("clip_v4", c_float), ("codebook", c_void_p)]
 
 
 _P = c_void_p
@@ -35,6 +35,10 @@ _SIGS = {
     "oscar_window_bytes": (c_size_t, [_P, c_int32]),
     "oscar_pool_bytes": (c_size_t, [_P]),
     "oscar_quantize_pack": (c_int32, [c_int64, c_int32, c_int32, c_int32, c_float, _P, _P, _P, _P]),
+    "oscar_quantize_pack_codebook": (c_int32, [c_int64, c_int32, c_int32, c_float, _P, _P, _P, _P, _P]),
+    "oscar_codebook_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "oscar_codebook_fit": (c_int32, [c_int32, c_int32, c_int32, _P, _P, c_float, c_int32, c_double, _P, c_size_t,
+                                     _P, _P, _P, _P]),
     "oscar_kv_prefill": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_int32, _P, _P, _P]),
     "oscar_kv_demote": (c_int32, [_P, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_int32, _P, _P, _P, _P]),
     "oscar_decode_workspace_bytes": (c_size_t, [_P, c_int32, c_int32]),

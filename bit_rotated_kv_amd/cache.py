@@ -37,12 +37,13 @@ def allocate_cache(num_q_heads: int, num_kv_heads: int, head_dim: int, batch: in
                    pages4_per_request: int = 0, pages2_per_request: Optional[int] = None,
                    page_order2: Optional[np.ndarray] = None, page_order4: Optional[np.ndarray] = None,
                    clip_k: float = 0.96, clip_v: float = 0.92, clip_k4: float = 1.0, clip_v4: float = 1.0,
-                   device: str = "cuda") -> CacheBuffers:
+                   codebook: Optional[torch.Tensor] = None, device: str = "cuda") -> CacheBuffers:
     """Allocate buffers for ``batch`` requests of up to ``max_seq_len`` tokens.
 
     INT2 page ids are [0, P2) and INT4 page ids [P2, P2 + P4) (the INT4 region starts at the
     pool offset). ``page_order2``/``page_order4`` are permutations giving which pool page each
-    table entry points at (a shuffled shared pool); identity when omitted."""
+    table entry points at (a shuffled shared pool); identity when omitted. ``codebook``: optional
+    INT2 codebook table [Hkv, 2, 4] int16 (device) that the layout points at."""
     hist = max(0, max_seq_len - sink_len - recent_len)
     hp = (hist + 15) // 16
     pp2 = hp if pages2_per_request is None else pages2_per_request
@@ -50,7 +51,7 @@ def allocate_cache(num_q_heads: int, num_kv_heads: int, head_dim: int, batch: in
     p2, p4 = batch * pp2, batch * pp4
     layout = ops.make_layout(num_q_heads, num_kv_heads, head_dim, sink_len=sink_len, recent_len=recent_len,
                              mixed=mixed, int4_page_offset=p2 if mixed else 0, pool_pages=p2 + p4, clip_k=clip_k,
-                             clip_v=clip_v, clip_k4=clip_k4, clip_v4=clip_v4)
+                             clip_v=clip_v, clip_k4=clip_k4, clip_v4=clip_v4, codebook=codebook)
     stride = max(pp2, pp4, 1)
     o2 = np.arange(p2, dtype=np.int64) if page_order2 is None else np.asarray(page_order2, np.int64)
     pt2 = np.zeros((batch, stride), np.int32)

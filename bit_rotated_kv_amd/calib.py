@@ -80,3 +80,16 @@ def rotations_on_gpu(q_cal: torch.Tensor, k_ctx: torch.Tensor, v_ctx: torch.Tens
     rk = torch.stack([rotation(eigvecs_descending(c)) for c in cq])
     rv = torch.stack([rotation(eigvecs_descending(c)) for c in cs])
     return rk.to(q_cal.device), rv.to(q_cal.device)
+
+
+def codebooks_on_gpu(k_ctx: torch.Tensor, v_ctx: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor,
+                     clip_k: float = 0.96, clip_v: float = 0.92, max_iter: int = 100, tol: float = 1e-7):
+    """INT2 codebook table [Hkv, 2, 4] int16 (device; fp16 level patterns, K then V) from the
+    library's Lloyd-Max fit over a calibration context k_ctx, v_ctx [Hkv, n, d] bf16 rotated by
+    R_K, R_V. Also returns the fitted levels [Hkv, 2, 4] float64 and iterations [Hkv, 2]."""
+    import numpy as np
+    from .ops import codebook_fit
+    lk, pk, ik = codebook_fit(k_ctx, rot_k, clip_k, max_iter, tol)
+    lv, pv, iv = codebook_fit(v_ctx, rot_v, clip_v, max_iter, tol)
+    table = torch.from_numpy(np.ascontiguousarray(np.stack([pk, pv], axis=1))).to(k_ctx.device)
+    return table, np.stack([lk, lv], axis=1), np.stack([ik, iv], axis=1)

@@ -45,7 +45,20 @@ oscar_status_t check_layout(const oscar_layout_t* L) {
   if (L->page_size != kPage) return OSCAR_ERR_UNSUPPORTED;
   if (L->sink_len % kPage || L->recent_len % kPage || L->sink_len > 256 || L->recent_len > 1024)
     return OSCAR_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(L->codebook) % 4) return OSCAR_ERR_INVALID_ARG;
   return OSCAR_OK;
+}
+
+// Four finite, strictly increasing fp16 levels.
+bool levels_ok(const uint16_t* levels) {
+  if (!levels) return false;
+  float prev = -__builtin_huge_valf();
+  for (int j = 0; j < 4; ++j) {
+    const float l = host_f16_to_f32(levels[j]);
+    if (!(l > prev) || l == __builtin_huge_valf()) return false;
+    prev = l;
+  }
+  return true;
 }
 
 Dims make_dims(const oscar_layout_t* L, int batch, int max_seq_len, int pt_stride) {
@@ -190,7 +203,20 @@ oscar_status_t oscar_quantize_pack(int64_t rows, int32_t dim, int32_t group, int
   if (dim > 1024) return OSCAR_ERR_UNSUPPORTED;
   if (rows == 0) return OSCAR_OK;
   if (!x || !codes || !scale_zero) return OSCAR_ERR_INVALID_ARG;
-  return launch_quantize_pack(rows, dim, group, bits, clip, x, codes, scale_zero, stream) == hipSuccess
+  return launch_quantize_pack(rows, dim, group, bits, clip, x, codes, scale_zero, nullptr, stream) == hipSuccess
+             ? OSCAR_OK
+             : OSCAR_ERR_LAUNCH;
+}
+
+oscar_status_t oscar_quantize_pack_codebook(int64_t rows, int32_t dim, int32_t group, float clip, const float* x,
+                                            const uint16_t* levels, uint8_t* codes, uint16_t* scale_zero,
+                                            hipStream_t stream) {
+  if (rows < 0 || dim <= 0 || group <= 0 || dim % group || group % 4) return OSCAR_ERR_INVALID_ARG;
+  if (!(clip > 0.0f && clip <= 1.0f) || !levels_ok(levels)) return OSCAR_ERR_INVALID_ARG;
+  if (dim > 1024) return OSCAR_ERR_UNSUPPORTED;
+  if (rows == 0) return OSCAR_OK;
+  if (!x || !codes || !scale_zero) return OSCAR_ERR_INVALID_ARG;
+  return launch_quantize_pack(rows, dim, group, 2, clip, x, codes, scale_zero, levels, stream) == hipSuccess
              ? OSCAR_OK
              : OSCAR_ERR_LAUNCH;
 }
@@ -221,6 +247,7 @@ oscar_status_t oscar_kv_prefill(const oscar_layout_t* L, int32_t batch, int32_t 
   a.clip_v = L->clip_v;
   a.clip_k4 = L->clip_k4;
   a.clip_v4 = L->clip_v4;
+  a.codebook = L->codebook;
   a.pool = static_cast<uint8_t*>(pool);
   a.pt2 = page_table;
   a.pt4 = page_table4;
@@ -256,6 +283,7 @@ static oscar_status_t build_demote(const oscar_layout_t* L, int32_t batch, const
   a.clip_v = L->clip_v;
   a.clip_k4 = L->clip_k4;
   a.clip_v4 = L->clip_v4;
+  a.codebook = L->codebook;
   a.pool = static_cast<uint8_t*>(pool);
   a.pt2 = page_table;
   a.pt4 = page_table4;
@@ -314,6 +342,7 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.pt4 = page_table4;
   a.rot_k = rot_k;
   a.rot_v = rot_v;
+  a.codebook = L->codebook;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)L->head_dim);
   a.scale_log2e = scale * 1.4426950408889634f;
   a.out = out;

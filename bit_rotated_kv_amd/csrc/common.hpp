@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <string.h>
 #include <stdint.h>
 
 #include "oscar.h"
@@ -57,6 +58,23 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// fp16 pattern -> fp32 on the host (exact for every pattern; NaN patterns map to NaN).
+inline float host_f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31, e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  uint32_t u;
+  if (e == 0x1Fu) {
+    u = sign | 0x7F800000u | (m << 13);
+  } else if (e != 0) {
+    u = sign | ((e + 112u) << 23) | (m << 13);
+  } else {
+    float f = (float)m * 0x1p-24f;   // subnormal: m * 2^-24, exact
+    return sign ? -f : f;
+  }
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
 }
 
 // ------------------------------------------------------------------ wavefront reductions
@@ -173,6 +191,90 @@ __device__ __forceinline__ uint32_t quant_code(float x, const QuantGrid& g, int 
   bool redo;
   const uint32_t c = quant_code_fast(x, g, levels, redo);
   return redo ? quant_code_exact(x, g, levels) : c;
+}
+
+// ------------------------------------------------------------------ INT2 codebook
+// Lloyd-Max codebook of the INT2 history (OSCAR overview page, the paragraph that sets OSCAR beside
+// TurboQuant): four increasing fp16 levels l_0..l_3 replace the uniform levels 0..3 of the group
+// coordinate u = (clip(x) - z) / s, so a code restores as z + s * l[code]. A code is the nearest
+// level: [u > t_0] + [u >= t_1] + [u > t_2] with the midpoints t_j = (l_j + l_{j+1}) / 2 (exact in
+// fp32), which sends a u on a threshold to the even code -- the levels 0, 1, 2, 3 give back the
+// uniform round-half-to-even code. The table holds [kv-head][K, V][4] fp16 patterns.
+struct Codebook {
+  uint32_t lut_lo, lut_hi;      // fp16 patterns l_0 | l_1 << 16 and l_2 | l_3 << 16
+  uint32_t plane_lo, plane_hi;  // byte planes: low bytes of l_0..l_3, high bytes of l_0..l_3
+  float t0, t1, t2;             // decision thresholds
+  bool on;                      // false: the uniform levels (this struct is then unused)
+};
+
+__device__ __forceinline__ Codebook load_codebook(const uint16_t* table, int kv, int sel) {
+  Codebook c;
+  c.on = table != nullptr;
+  c.lut_lo = 0x3C000000u;   // uniform levels 0, 1, 2, 3
+  c.lut_hi = 0x42004000u;
+  if (c.on) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(table + ((size_t)kv * 2 + sel) * 4);
+    c.lut_lo = p[0];
+    c.lut_hi = p[1];
+  }
+  c.plane_lo = __builtin_amdgcn_perm(c.lut_hi, c.lut_lo, 0x06040200u);
+  c.plane_hi = __builtin_amdgcn_perm(c.lut_hi, c.lut_lo, 0x07050301u);
+  const float l0 = f16_bits_to_f32(c.lut_lo & 0xFFFFu), l1 = f16_bits_to_f32(c.lut_lo >> 16);
+  const float l2 = f16_bits_to_f32(c.lut_hi & 0xFFFFu), l3 = f16_bits_to_f32(c.lut_hi >> 16);
+  // uniform values: kept in scalar registers
+  c.t0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (l0 + l1) * 0.5f)));
+  c.t1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (l1 + l2) * 0.5f)));
+  c.t2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (l2 + l3) * 0.5f)));
+  return c;
+}
+
+// Level of a code (fp32 value of its fp16 pattern).
+__device__ __forceinline__ float codebook_level(const Codebook& c, uint32_t code) {
+  const uint32_t w = code < 2 ? c.lut_lo : c.lut_hi;
+  return f16_bits_to_f32((code & 1u) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// Levels of packed codes in two byte permutes. codebook_spread copies byte 0 of each half-word of
+// w (bytes 1 and 3 when odd) into both bytes of that half-word; codebook_levels2 then takes the
+// codes at bits 2m..2m+1 of those bytes and returns their fp16 levels, the low half-word's code
+// in the low half: the selector bytes are (c, 4 + c) per half-word, which pick the low and high
+// byte of l[c] from the two byte planes.
+__device__ __forceinline__ uint32_t codebook_spread(uint32_t w, bool odd) {
+  return __builtin_amdgcn_perm(w, w, odd ? 0x03030101u : 0x02020000u);
+}
+__device__ __forceinline__ uint32_t codebook_levels2(const Codebook& c, uint32_t z, int m) {
+  // the selector as one v_and_or_b32 (the compiler would spend an AND and an OR with literals)
+  uint32_t sel;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(sel) : "v"(z >> (2 * m)), "s"(0x03030303u), "v"(0x04000400u));
+  return __builtin_amdgcn_perm(c.plane_hi, c.plane_lo, sel);
+}
+
+// Codebook decisions with the estimate / exact split of quant_code: the estimate decides unless it
+// lies within 2^-14 of a threshold (or is not below 32 in magnitude, or not a number).
+__device__ __forceinline__ uint32_t cb_code_of(float t, const Codebook& c) {
+  return (uint32_t)(t > c.t0) + (uint32_t)(t >= c.t1) + (uint32_t)(t > c.t2);
+}
+
+__device__ __forceinline__ uint32_t cb_code_fast(float x, const QuantGrid& g, const Codebook& c, bool& redo) {
+#pragma clang fp contract(off)
+  const float xc = __builtin_amdgcn_fmed3f(x, g.lo, g.hi);
+  const float t = (xc - g.z) * g.rs;
+  const float near = fminf(fminf(fabsf(t - c.t0), fabsf(t - c.t1)), fabsf(t - c.t2));
+  redo = (g.s != 0.0f) & (!(fabsf(t) < 32.0f) | !(near > 0x1p-14f));
+  return g.s == 0.0f ? 0u : cb_code_of(t, c);
+}
+
+__device__ __forceinline__ uint32_t cb_code_exact(float x, const QuantGrid& g, const Codebook& c) {
+#pragma clang fp contract(off)
+  if (g.s == 0.0f) return 0u;
+  const float xc = fminf(fmaxf(x, g.lo), g.hi);
+  return cb_code_of(__fdiv_rn(xc - g.z, g.s), c);
+}
+
+__device__ __forceinline__ uint32_t cb_code(float x, const QuantGrid& g, const Codebook& c) {
+  bool redo;
+  const uint32_t k = cb_code_fast(x, g, c, redo);
+  return redo ? cb_code_exact(x, g, c) : k;
 }
 
 // ------------------------------------------------------------------ history code placement

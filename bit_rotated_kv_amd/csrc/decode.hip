@@ -132,7 +132,9 @@ constexpr int kQueryWords = (GQ * D / 2 + 255) / 256;
 // scaled per code bit position p (a code c at bit p of its fp16 slot has the value c*2^(p-24)):
 // operand = v*2^(24-p-E), one exponent E per head. Operand column c of the products holds the
 // high parts of head c for c < GQ and the low parts of head c-GQ for GQ <= c < 2GQ.
-template <int BITS, int D, int GQ>
+// LUT: the key operand holds codebook levels (normal fp16 values, no bit-position factor), so
+// every channel takes p = 0 and the products carry 2^(24-E) instead of 2^-E.
+template <int BITS, int D, int GQ, bool LUT = false>
 __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
                                HistQueryLds<D, GQ>& L, float scale_log2e) {
   constexpr int CG = QRotRows<D>::CG, QR = QRotRows<D>::QR;
@@ -180,7 +182,7 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
       const int j = lane + kWave * k;
       v[k] = ((L.ps[0][h][j] + L.ps[1][h][j]) + (L.ps[2][h][j] + L.ps[3][h][j])) * scale_log2e;
       const int m = (j % 8) / 2;
-      const int p = BITS == 2 ? 2 * m : 4 * (m % 2);
+      const int p = LUT ? 0 : (BITS == 2 ? 2 * m : 4 * (m % 2));
       vmax = fmaxf(vmax, fabsf(v[k]));
       me = fmaxf(me, ldexpf(fabsf(v[k]), 24 - p));
     }
@@ -197,7 +199,7 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
     for (int k = 0; k < NC; ++k) {
       const int j = lane + kWave * k;
       const int m = (j % 8) / 2;
-      const int p = BITS == 2 ? 2 * m : 4 * (m % 2);
+      const int p = LUT ? 0 : (BITS == 2 ? 2 * m : 4 * (m % 2));
       const float v_hi = ldexpf(rintf(ldexpf(v[k], 11 - ev)), ev - 11);
       const float v_lo = v[k] - v_hi;
       sh += v_hi;
@@ -210,7 +212,7 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
     if (lane == 0) {
       L.hsc[h][0] = sh;
       L.hsc[h][1] = sl;
-      L.hsc[h][2] = ldexpf(1.0f, e);
+      L.hsc[h][2] = ldexpf(1.0f, LUT ? e - 24 : e);
       L.hsc[h][3] = 0.0f;
     }
   }
@@ -219,12 +221,12 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
 
 // The operands of query_operands as registers: lane (g, c) gets operand column c and the constants
 // of head c % GQ.
-template <int BITS, int D, int GQ>
+template <int BITS, int D, int GQ, bool LUT = false>
 __device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
                                     HistQueryLds<D, GQ>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
                                     float& ul, float& esc) {
   const int lane = threadIdx.x % kWave, g = lane / 16, c = lane % 16;
-  query_operands<BITS, D, GQ>(rr, qw, L, scale_log2e);
+  query_operands<BITS, D, GQ, LUT>(rr, qw, L, scale_log2e);
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const u32x4_t z = {0, 0, 0, 0};
@@ -240,7 +242,7 @@ __device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[
 // repeat the rotation and the R_K reads): one workgroup per (request, kv-head, code width) writes
 // the operands of query_operands to the workspace, in the LDS layout, for the history workgroups to
 // load.
-template <int D, int GQ>
+template <int D, int GQ, bool LUT>
 __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) HistQueryLds<D, GQ> L;
   const Dims& dm = a.dm;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
     qw[i] = e < GQ * D / 2 ? qsrc[e] : 0u;
   }
   if (wsel == 0)
-    query_operands<2, D, GQ>(rr, qw, L, a.scale_log2e);
+    query_operands<2, D, GQ, LUT>(rr, qw, L, a.scale_log2e);
   else
     query_operands<4, D, GQ>(rr, qw, L, a.scale_log2e);
   const size_t unit = (size_t)wsel * dm.batch * dm.hkv + bk;
@@ -513,7 +515,7 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   __syncthreads();
   if (demote && wave < 2) {
     const float clip = bw == 4 ? (wave ? cw.clip_v4 : cw.clip_k4) : (wave ? cw.clip_v : cw.clip_k);
-    quantize_token<D>(L.xr[wave], clip, bw, L.cs[wave], &L.szs[wave], lane);
+    quantize_token<D>(L.xr[wave], clip, bw, L.cs[wave], &L.szs[wave], lane, load_codebook(cw.codebook, kv, wave));
   }
   __syncthreads();
   if (demote) {
@@ -529,10 +531,15 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   const uint16_t* nv = cw.v + (size_t)bk * D;
   const double sk = __uint_as_float(L.szs[0] << 16), zk = __uint_as_float(L.szs[0] & 0xFFFF0000u);
   const float sv = __uint_as_float(L.szs[1] << 16), zv = __uint_as_float(L.szs[1] & 0xFFFF0000u);
+  // restored values: z + s * level (the code itself, or the codebook's level of an INT2 code)
+  const bool lvk = bw == 2 && cw.codebook != nullptr;
+  const Codebook cbk = load_codebook(lvk ? cw.codebook : nullptr, kv, 0);
+  const Codebook cbv = load_codebook(lvk ? cw.codebook : nullptr, kv, 1);
+  auto level = [&](const Codebook& cb, uint32_t code) { return lvk ? codebook_level(cb, code) : (float)code; };
   for (int h = wave; h < GQ; h += kSplitWaves) {
     double ld = 0.0, ln = 0.0;
     for (int ch = lane; ch < D; ch += kWave) {
-      if (demote) ld += (double)L.vq[h][ch] * (sk * (double)L.cs[0][ch] + zk);
+      if (demote) ld += (double)L.vq[h][ch] * (sk * (double)level(cbk, L.cs[0][ch]) + zk);
       ln += (double)bf16_bits_to_f32(L.xs[1 + h][ch]) * (double)bf16_bits_to_f32(nk[ch]);
     }
     ld = wave_sum_f64(ld);
@@ -544,7 +551,7 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   }
   for (int idx = tid; idx < GQ * D; idx += kSplitWaves * kWave) {
     const int ch = idx % D;
-    if (demote) po_d[idx] = fmaf(sv, (float)L.cs[1][ch], zv);
+    if (demote) po_d[idx] = fmaf(sv, level(cbv, L.cs[1][ch]), zv);
     po_n[idx] = bf16_bits_to_f32(nv[ch]);
   }
   if (kv == 0 && tid == 0) {
@@ -678,14 +685,19 @@ __device__ __forceinline__ uint32_t split_f16(float w) {
 
 // QK^T of one page: rows = the 16 token slots, columns = query operand columns (high parts of
 // the GQ heads in columns 0..GQ-1, low parts in GQ..2GQ-1, so one product covers both parts).
-template <int BITS, int D, int GQ>
-__device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const half8_t* bq) {
+// LUT: the codes become their codebook levels (two per byte permute) instead of subnormal slots.
+template <int BITS, int D, int GQ, bool LUT = false>
+__device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const half8_t* bq, const Codebook& cbk) {
   constexpr int NKK = D / 32;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     u32x4_t av;
-    if constexpr (BITS == 2) {
+    if constexpr (LUT) {
+      const uint32_t z = codebook_spread(pr.kw[kk / 2], kk & 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[m] = codebook_levels2(cbk, z, m);
+    } else if constexpr (BITS == 2) {
       const uint32_t w = (kk & 1) ? (pr.kw[kk / 2] >> 8) : pr.kw[kk / 2];
       av[0] = w & 0x00030003u;
       av[1] = w & 0x000C000Cu;
@@ -715,13 +727,16 @@ __device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl
   return (p1 + p2) + ((r1 + r2) + fmaf(s, xl, z * ul));
 }
 
-template <int BITS, int D, int GQ>
+template <int BITS, int D, int GQ, bool LUT = false>
 __device__ __forceinline__ void pv_page(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, uint32_t a01,
-                                        uint32_t a23) {
+                                        uint32_t a23, const Codebook& cbv) {
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
     uint32_t b0, b1;
-    if constexpr (BITS == 2) {
+    if constexpr (LUT) {
+      b0 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], false), nb % 4);
+      b1 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], true), nb % 4);
+    } else if constexpr (BITS == 2) {
       const uint32_t w = pr.vw[nb / 4];
       const uint32_t mask = 0x00030003u << (2 * (nb % 4));
       b0 = w & mask;
@@ -788,10 +803,10 @@ __device__ __forceinline__ void redist_softmax(WaveState<D, GQ>& st, const float
 
 // Softmax and PV product of one page, given its QK^T result `acc`: column c < GQ holds the
 // high-part product of head c, column GQ + c the low-part product.
-template <int BITS, int D, int GQ>
+template <int BITS, int D, int GQ, bool LUT = false>
 __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, float4_t acc,
                                               float uh, float ul, float esc, uint32_t psel, int slot0, int ntok,
-                                              int lane) {
+                                              int lane, const Codebook& cbv) {
   const int g = lane / 16, c = lane % 16;
   if constexpr (GQ == 4) {
     // lane (g, c) takes token 4g + c/4 of head c%4: high part from column c%4, low part from
@@ -820,7 +835,7 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const uint32_t v8 = dpp_row_shl_into<8, 0x3>(P, P);
     const uint32_t a01 = __builtin_amdgcn_perm(y, P, psel);
     const uint32_t a23 = __builtin_amdgcn_perm(u, v8, psel);
-    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
   } else if constexpr (GQ == 8) {
     // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8; high parts from columns 0..7,
     // low parts from columns 8..15
@@ -845,7 +860,7 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     // row c >= 8: low parts of head c-8, tokens 4g, 4g+1 (lane c-8) and 4g+2, 4g+3 (own)
     const uint32_t a01 = dpp_row_shr_into<8, 0xC>(P0, L0);
     const uint32_t a23 = dpp_row_shl_into<8, 0x3>(L0, P0);
-    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
   } else {
     float lg[4];
 #pragma unroll
@@ -871,7 +886,7 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const uint32_t s01 = row_shr_or_zero<GQ>(pack_hi16(q0, q1)), s23 = row_shr_or_zero<GQ>(pack_hi16(q2, q3));
     const uint32_t a01 = c < GQ ? pack_lo16(q0, q1) : (c < 2 * GQ ? s01 : 0u);
     const uint32_t a23 = c < GQ ? pack_lo16(q2, q3) : (c < 2 * GQ ? s23 : 0u);
-    pv_page<BITS, D, GQ>(st, pr, a01, a23);
+    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
   }
 }
 
@@ -892,7 +907,8 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   }
 }
 
-template <int BITS, int D, int GQ>
+// LUT (INT2 with a codebook): codes enter both products as their codebook levels.
+template <int BITS, int D, int GQ, bool LUT = false>
 __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
                           HistQueryLds<D, GQ>& qlds) {
   const Dims& dm = a.dm;
@@ -986,18 +1002,20 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
       ul = qk.y;
       esc = qk.z;
     } else {
-      hist_query_operands<BITS, D, GQ>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
+      hist_query_operands<BITS, D, GQ, LUT>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
     }
-    float4_t acc = qk_page<BITS, D, GQ>(buf[0], bq);
+    const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
+    const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
+    float4_t acc = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
     for (int pg = wp0; pg < wp1; pg += NB) {
       progress_priority(pg - wp0, wp1 - wp0);
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
         if (pg + k < wp1) {
-          const float4_t acc_next = qk_page<BITS, D, GQ>(buf[(k + 1) % NB], bq);
+          const float4_t acc_next = qk_page<BITS, D, GQ, LUT>(buf[(k + 1) % NB], bq, cbk);
           if (ok[k]) {
-            process_qpage<BITS, D, GQ>(st, buf[k], acc, uh, ul, esc, psel, (pg + k) * kPage, ntok, lane);
+            process_qpage<BITS, D, GQ, LUT>(st, buf[k], acc, uh, ul, esc, psel, (pg + k) * kPage, ntok, lane, cbv);
           } else if (lane == 0) {
             atomicOr(a.ws.flags, 1u);
           }
@@ -1008,7 +1026,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
-  workgroup_merge<D, GQ, BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
+  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
                                                              a.ws.part_lse + pbase * GQ);
 }
 
@@ -1020,7 +1038,8 @@ union alignas(16) SplitScratch {
   StepLds<D, GQ> step;
 };
 
-template <int D, int GQ>
+// CB: the INT2 history uses the codebook table of the decode arguments.
+template <int D, int GQ, bool CB>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a, CacheWriteArgs cw) {
   __shared__ float o_lds[kSplitWaves][2 * GQ][D];
   __shared__ float st_lds[kSplitWaves][3][8];
@@ -1032,7 +1051,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a
   if (bid < n_win) {
     window_role<D, GQ>(a, cw, bid, o_lds, st_lds, scr.step);
   } else if (bid < n_win + n_int2) {
-    hist_role<2, D, GQ>(a, bid - n_win, o_lds, st_lds, scr.hist);
+    hist_role<2, D, GQ, CB>(a, bid - n_win, o_lds, st_lds, scr.hist);
   } else {
     hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds, scr.hist);
   }
@@ -1357,13 +1376,23 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
   };
   mark(0);
   if (a.ws.qpre)
-    hipLaunchKernelGGL((q_prologue_kernel<D, GQ>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0, stream, a);
+    if (a.codebook)
+      hipLaunchKernelGGL((q_prologue_kernel<D, GQ, true>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((q_prologue_kernel<D, GQ, false>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
+                         stream, a);
   mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
 #ifndef OSCAR_SPLIT_LDS_PAD
 #define OSCAR_SPLIT_LDS_PAD 0
 #endif
-  hipLaunchKernelGGL((split_kernel<D, GQ>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream, a, cw);
+  if (a.codebook)
+    hipLaunchKernelGGL((split_kernel<D, GQ, true>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream,
+                       a, cw);
+  else
+    hipLaunchKernelGGL((split_kernel<D, GQ, false>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream,
+                       a, cw);
   mark(2);
   const int groups = dm.batch * dm.hkv;
   if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {

@@ -195,9 +195,11 @@ __device__ inline void window_slot(int p, const Dims& dm, int& pgw, int& t) {
 }
 
 // One wavefront: range of the rotated token xr[0..D), clipped grid of width bw, and its codes
-// (cs) and packed bf16 (scale, zero) (szs, scale in the low half).
+// (cs) and packed bf16 (scale, zero) (szs, scale in the low half); INT2 codes follow the codebook
+// when one is given.
 template <int D>
-__device__ inline void quantize_token(const float* xr, float clip, int bw, uint8_t* cs, uint32_t* szs, int lane) {
+__device__ inline void quantize_token(const float* xr, float clip, int bw, uint8_t* cs, uint32_t* szs, int lane,
+                                      const Codebook& cb) {
   float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
   for (int c = lane; c < D; c += kWave) {
     mn = fminf(mn, xr[c]);
@@ -207,7 +209,10 @@ __device__ inline void quantize_token(const float* xr, float clip, int bw, uint8
   mx = wave_max(mx);
   const int levels = (1 << bw) - 1;
   const QuantGrid g = make_grid(mn, mx, clip, levels);
-  for (int c = lane; c < D; c += kWave) cs[c] = (uint8_t)quant_code(xr[c], g, levels);
+  if (bw == 2 && cb.on)
+    for (int c = lane; c < D; c += kWave) cs[c] = (uint8_t)cb_code(xr[c], g, cb);
+  else
+    for (int c = lane; c < D; c += kWave) cs[c] = (uint8_t)quant_code(xr[c], g, levels);
   if (lane == 0) *szs = g.s_bits | (g.z_bits << 16);
 }
 
@@ -263,7 +268,7 @@ __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, in
     __syncthreads();
     if (wave == 0) {
       const float clip = bw == 4 ? (sel ? a.clip_v4 : a.clip_k4) : (sel ? a.clip_v : a.clip_k);
-      quantize_token<D>(xr, clip, bw, cs, &szs, lane);
+      quantize_token<D>(xr, clip, bw, cs, &szs, lane, load_codebook(a.codebook, kv, sel));
     }
     __syncthreads();
     store_token<D>(a, page, kv, bw, slot % kPage, sel, cs, szs, tid, 256);

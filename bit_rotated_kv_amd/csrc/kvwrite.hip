@@ -70,8 +70,10 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
 constexpr int kPrefillChunk = 64;
 constexpr int kPrefillChunks = 8;
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_hist_kernel(CacheWriteArgs a) {
+// CBK: INT2 codes follow the codebook table of the arguments (a separate instantiation keeps the
+// uniform quantiser's code unchanged).
+template <int D, bool CBK>
+__global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) {
   constexpr int CH = kPrefillChunk;
   constexpr int XS = D + 8;     // bf16 row pitch (16-byte pad)
   constexpr int RS = D + 8;     // fp32 row pitch: the two lane halves of an accumulator store
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(256) void prefill_hist_kernel(CacheWriteArgs a) {
   const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
   RotSlice<D> rs;
   if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
+  const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
   // rows of a chunk: thread pieces tid + 256 e (row = piece / (D/8), 8 channels each)
   auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
     const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
@@ -177,23 +180,44 @@ __global__ __launch_bounds__(256) void prefill_hist_kernel(CacheWriteArgs a) {
         const int levels = (1 << bw) - 1;
         const QuantGrid g = make_grid(mn, mx, clip, levels);
         uint32_t redo = 0;   // channels whose code the exact division decides (rare)
+        if (CBK && bw == 2) {
 #pragma unroll
-        for (int c4 = 0; c4 < QC / 4; ++c4) {
-          const float4 x4 = *reinterpret_cast<const float4*>(&xr[i][q * QC + 4 * c4]);
-          const float xe[4] = {x4.x, x4.y, x4.z, x4.w};
-          uint32_t packed = 0;
+          for (int c4 = 0; c4 < QC / 4; ++c4) {
+            const float4 x4 = *reinterpret_cast<const float4*>(&xr[i][q * QC + 4 * c4]);
+            const float xe[4] = {x4.x, x4.y, x4.z, x4.w};
+            uint32_t packed = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bool r;
-            packed |= quant_code_fast(xe[e], g, levels, r) << (8 * e);
-            redo |= (uint32_t)r << (4 * c4 + e);
+            for (int e = 0; e < 4; ++e) {
+              bool r;
+              packed |= cb_code_fast(xe[e], g, cb, r) << (8 * e);
+              redo |= (uint32_t)r << (4 * c4 + e);
+            }
+            *reinterpret_cast<uint32_t*>(&cs[i][q * QC + 4 * c4]) = packed;
           }
-          *reinterpret_cast<uint32_t*>(&cs[i][q * QC + 4 * c4]) = packed;
-        }
-        while (redo) {
-          const int c = __builtin_ctz(redo);
-          redo &= redo - 1;
-          cs[i][q * QC + c] = (uint8_t)quant_code_exact(xr[i][q * QC + c], g, levels);
+          while (redo) {
+            const int c = __builtin_ctz(redo);
+            redo &= redo - 1;
+            cs[i][q * QC + c] = (uint8_t)cb_code_exact(xr[i][q * QC + c], g, cb);
+          }
+        } else {
+#pragma unroll
+          for (int c4 = 0; c4 < QC / 4; ++c4) {
+            const float4 x4 = *reinterpret_cast<const float4*>(&xr[i][q * QC + 4 * c4]);
+            const float xe[4] = {x4.x, x4.y, x4.z, x4.w};
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bool r;
+              packed |= quant_code_fast(xe[e], g, levels, r) << (8 * e);
+              redo |= (uint32_t)r << (4 * c4 + e);
+            }
+            *reinterpret_cast<uint32_t*>(&cs[i][q * QC + 4 * c4]) = packed;
+          }
+          while (redo) {
+            const int c = __builtin_ctz(redo);
+            redo &= redo - 1;
+            cs[i][q * QC + c] = (uint8_t)quant_code_exact(xr[i][q * QC + c], g, levels);
+          }
         }
         if (q == 0) szs[i] = g.s_bits | (g.z_bits << 16);
       }
@@ -300,10 +324,17 @@ hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream) {
   if (hmax <= 0) return hipSuccess;
   const int runs = (hmax + kPrefillChunk * kPrefillChunks - 1) / (kPrefillChunk * kPrefillChunks);
   const dim3 grid(runs, dm.hkv, 2 * dm.batch);   // z: request x {K, V}
-  if (dm.d == 128)
-    hipLaunchKernelGGL(prefill_hist_kernel<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_hist_kernel<64>, grid, dim3(256), 0, stream, a);
+  if (a.codebook) {
+    if (dm.d == 128)
+      hipLaunchKernelGGL((prefill_hist_kernel<128, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_hist_kernel<64, true>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (dm.d == 128)
+      hipLaunchKernelGGL((prefill_hist_kernel<128, false>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_hist_kernel<64, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

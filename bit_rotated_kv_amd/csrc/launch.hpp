@@ -51,6 +51,7 @@ struct DecodeArgs {
   const int32_t* pt4;
   const float* rot_k;
   const float* rot_v;
+  const uint16_t* codebook;  // INT2 codebook table [Hkv][K, V][4] fp16, or null (uniform levels)
   float scale_log2e;         // softmax scale * log2(e)
   float* out;                // [B][Hq][d] fp32
   DecodeWs ws;
@@ -69,6 +70,7 @@ struct CacheWriteArgs {
   const float* rot_k;
   const float* rot_v;
   float clip_k, clip_v, clip_k4, clip_v4;
+  const uint16_t* codebook;  // INT2 codebook table [Hkv][K, V][4] fp16, or null (uniform levels)
   uint8_t* pool;
   const int32_t* pt2;
   const int32_t* pt4;
@@ -94,7 +96,7 @@ struct Bf16Args {
 };
 
 hipError_t launch_quantize_pack(int64_t rows, int dim, int group, int bits, float clip, const float* x,
-                                uint8_t* codes, uint16_t* sz, hipStream_t stream);
+                                uint8_t* codes, uint16_t* sz, const uint16_t* levels, hipStream_t stream);
 hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_demote(const CacheWriteArgs& a, hipStream_t stream);
 // Decode attention; with a.step, also the demote + append of `cw` (a fused decode step).

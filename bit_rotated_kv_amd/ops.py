@@ -18,10 +18,24 @@ PAGE = 16
 def make_layout(num_q_heads: int, num_kv_heads: int, head_dim: int, group_size: Optional[int] = None,
                 sink_len: int = 64, recent_len: int = 256, mixed: bool = False, int4_page_offset: int = 0,
                 pool_pages: int = 0, clip_k: float = 0.96, clip_v: float = 0.92, clip_k4: float = 1.0,
-                clip_v4: float = 1.0) -> Layout:
-    return Layout(num_q_heads, num_kv_heads, head_dim, head_dim if group_size is None else group_size, sink_len,
-                  recent_len, PAGE, 1 if mixed else 0, int4_page_offset, pool_pages, clip_k, clip_v, clip_k4,
-                  clip_v4)
+                clip_v4: float = 1.0, codebook: Optional[torch.Tensor] = None) -> Layout:
+    """``codebook``: optional INT2 codebook table, a device int16 tensor [Hkv, 2, 4] of fp16 level
+    patterns (K, then V); the layout keeps a reference to it."""
+    lay = Layout(num_q_heads, num_kv_heads, head_dim, head_dim if group_size is None else group_size, sink_len,
+                 recent_len, PAGE, 1 if mixed else 0, int4_page_offset, pool_pages, clip_k, clip_v, clip_k4,
+                 clip_v4, None)
+    set_codebook(lay, codebook)
+    return lay
+
+
+def set_codebook(layout: Layout, codebook: Optional[torch.Tensor]) -> None:
+    """Point the layout at an INT2 codebook table [Hkv, 2, 4] int16 (fp16 patterns), or at none."""
+    if codebook is not None:
+        _need(codebook, torch.int16, "codebook")
+        if tuple(codebook.shape) != (layout.num_kv_heads, 2, 4):
+            raise ValueError(f"codebook must be [{layout.num_kv_heads}, 2, 4], got {tuple(codebook.shape)}")
+    layout.codebook = None if codebook is None else codebook.data_ptr()
+    layout._codebook_ref = codebook
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -86,6 +100,49 @@ def quantize_pack(x: torch.Tensor, group: int, bits: int, clip: float, codes: Op
     check(lib().oscar_quantize_pack(rows, dim, group, bits, clip, _p(x), _p(codes), _p(scale_zero), _stream()),
           "oscar_quantize_pack")
     return codes, scale_zero
+
+
+def quantize_pack_codebook(x: torch.Tensor, group: int, clip: float, levels, codes: Optional[torch.Tensor] = None,
+                           scale_zero: Optional[torch.Tensor] = None):
+    """INT2 codes under a codebook: x [rows, dim] fp32, levels four fp16 patterns (host ints)."""
+    import ctypes
+    _need(x, torch.float32, "x")
+    rows, dim = x.shape
+    lv = (ctypes.c_uint16 * 4)(*[int(v) & 0xFFFF for v in levels])
+    if codes is None:
+        codes = torch.empty((rows, dim // 4), dtype=torch.uint8, device=x.device)
+    if scale_zero is None:
+        scale_zero = torch.empty((rows, dim // group, 2), dtype=torch.int16, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scale_zero, torch.int16, "scale_zero")
+    check(lib().oscar_quantize_pack_codebook(rows, dim, group, clip, _p(x), ctypes.cast(lv, c_void_p), _p(codes),
+                                             _p(scale_zero), _stream()), "oscar_quantize_pack_codebook")
+    return codes, scale_zero
+
+
+def codebook_workspace_bytes(num_kv_heads: int, n_rows: int, head_dim: int) -> int:
+    return int(lib().oscar_codebook_workspace_bytes(num_kv_heads, n_rows, head_dim))
+
+
+def codebook_fit(x: torch.Tensor, rot: torch.Tensor, clip: float, max_iter: int = 100, tol: float = 1e-7,
+                 workspace: Optional[torch.Tensor] = None):
+    """Lloyd-Max INT2 codebooks of calibration rows x [Hkv, n, d] bf16 under rotations rot [Hkv, d, d]
+    fp32. Returns (levels float64 [Hkv, 4], fp16 patterns int16 [Hkv, 4], iterations int32 [Hkv])."""
+    import ctypes
+    import numpy as np
+    _need(x, torch.bfloat16, "x")
+    _need(rot, torch.float32, "rot")
+    hkv, n, d = x.shape
+    if workspace is None:
+        workspace = torch.empty(max(codebook_workspace_bytes(hkv, n, d), 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace")
+    levels = np.zeros((hkv, 4), np.float64)
+    pats = np.zeros((hkv, 4), np.uint16)
+    iters = np.zeros(hkv, np.int32)
+    check(lib().oscar_codebook_fit(hkv, n, d, _p(x), _p(rot), clip, max_iter, tol, _p(workspace),
+                                   workspace.numel(), levels.ctypes.data_as(c_void_p), pats.ctypes.data_as(c_void_p),
+                                   iters.ctypes.data_as(c_void_p), _stream()), "oscar_codebook_fit")
+    return levels, pats.view(np.int16), iters
 
 
 def kv_prefill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rot_k: torch.Tensor,

@@ -106,6 +106,15 @@ typedef struct oscar_layout {
   int64_t pool_pages;       /* number of valid page ids in the pool arena                    */
   float clip_k, clip_v;     /* INT2 clip ratios c_K, c_V (study note, case 2: 0.96, 0.92)    */
   float clip_k4, clip_v4;   /* INT4 clip ratios (1.0: no clipping)                           */
+  /* INT2 Lloyd-Max codebooks (OSCAR overview page, the paragraph that sets OSCAR beside
+   * TurboQuant): NULL for the uniform levels 0..3, else a device table [Hkv][2][4] of fp16
+   * patterns (K levels, then V levels, per kv-head), 4-byte aligned, each row four finite,
+   * strictly increasing levels l_0 < l_1 < l_2 < l_3 (the library reads it on the device and
+   * cannot check that; other contents give meaningless codes, never a fault). A group
+   * coordinate u = (clip(x) - z)/s gets code [u > t_0] + [u >= t_1] + [u > t_2] with
+   * t_j = (l_j + l_{j+1})/2 (fp32), and restores as z + s*l[code]. INT4 tokens keep the
+   * uniform levels. Owned by the caller; read by prefill, demote, decode and step. */
+  const uint16_t* codebook;
 } oscar_layout_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -133,6 +142,44 @@ size_t oscar_pool_bytes(const oscar_layout_t* layout);                  /* whole
 oscar_status_t oscar_quantize_pack(int64_t rows, int32_t dim, int32_t group, int32_t bits,
                                    float clip, const float* x, uint8_t* codes,
                                    uint16_t* scale_zero, hipStream_t stream);
+
+/*
+ * INT2 group quantise + pack of already-rotated fp32 rows with a Lloyd-Max codebook (OSCAR
+ * overview page, the paragraph that sets OSCAR beside TurboQuant): the grid (s, z) and the
+ * packing of oscar_quantize_pack with bits = 2; the code of a coordinate
+ * u = fp32(fp32(clamp(x,lo,hi) - z)/s) is [u > t_0] + [u >= t_1] + [u > t_2] with
+ * t_j = (l_j + l_{j+1})/2 in fp32 (the nearest level, ties to the even code); all codes 0 when
+ * s == 0. levels: host array of four fp16 patterns, finite and strictly increasing (else
+ * OSCAR_ERR_INVALID_ARG). The levels 0, 1, 2, 3 give exactly oscar_quantize_pack's codes.
+ */
+oscar_status_t oscar_quantize_pack_codebook(int64_t rows, int32_t dim, int32_t group, float clip,
+                                            const float* x, const uint16_t* levels, uint8_t* codes,
+                                            uint16_t* scale_zero, hipStream_t stream);
+
+/*
+ * Lloyd-Max fit of INT2 codebooks on the GPU (OSCAR overview page, the paragraph that sets OSCAR
+ * beside TurboQuant; Lloyd-Max after Max, 1960). For each kv-head h the calibration rows
+ * x[h] ([n_rows][head_dim] bf16, device) are rotated by rot[h] ([head_dim][head_dim] fp32,
+ * device) exactly as the cache writers rotate a token, each row gets the INT2 grid with `clip`
+ * (group = head_dim), and the coordinates u = fp32(fp32(clamp(x,lo,hi) - z)/s) of every channel
+ * (rows with s == 0 are left out) are the samples. Starting from the levels 0, 1, 2, 3, each
+ * iteration puts thresholds at the midpoints of the levels (fp64), assigns every sample to the
+ * nearest level (on a threshold: the even level) and moves each level to its cell mean (fp64; an
+ * empty cell keeps its level); a kv-head stops after the first iteration in which no level moved
+ * by more than `tol`, or after max_iter iterations.
+ *   levels_out    host [Hkv][4] fp64 fitted levels
+ *   patterns_out  host [Hkv][4] their fp16 patterns (round to nearest even): one half of a codebook
+ *                 table row (fit K with rot_k, clip_k and V with rot_v, clip_v)
+ *   iters_out     host [Hkv] iterations run (may be NULL)
+ * Synchronous: returns after `stream` has drained (each iteration copies its partial sums back).
+ * Workspace: oscar_codebook_workspace_bytes(num_kv_heads, n_rows, head_dim) bytes of device memory.
+ * head_dim in {64, 128}; n_rows >= 0 (0: the uniform levels come back); max_iter >= 1; tol >= 0.
+ */
+size_t oscar_codebook_workspace_bytes(int32_t num_kv_heads, int32_t n_rows, int32_t head_dim);
+oscar_status_t oscar_codebook_fit(int32_t num_kv_heads, int32_t n_rows, int32_t head_dim, const void* x,
+                                  const float* rot, float clip, int32_t max_iter, double tol,
+                                  void* workspace, size_t workspace_bytes, double* levels_out,
+                                  uint16_t* patterns_out, int32_t* iters_out, hipStream_t stream);
 
 /*
  * Build the cache of a batch from full prefixes (prefill): writes the sink and recent windows

@@ -17,13 +17,25 @@ def n_int4_counts(p: P.Problem):
     return [int((p.bits[b][64:max(64, T - 256)] == 4).sum()) for b, T in enumerate(p.w.seq_lens)]
 
 
+def codebook_tensor(p: P.Problem):
+    """The problem's INT2 codebook table on the device (None for the uniform levels)."""
+    if p.codebook is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(P.codebook_patterns(p.codebook))).cuda()
+
+
+def allocate(p: P.Problem, tmax: int):
+    w = p.w
+    return brk.allocate_cache(w.num_q_heads, w.num_kv_heads, w.head_dim, w.batch, tmax, mixed=p.mixed,
+                              pages2_per_request=p.pages2, pages4_per_request=p.pages4, page_order2=p.order2,
+                              page_order4=p.order4, codebook=codebook_tensor(p))
+
+
 def build_cache(p: P.Problem, oracle_written: bool, max_seq_len: int = None):
     """Allocate buffers for p and fill them (GPU prefill, or the oracle's codes via layout_ref)."""
     w = p.w
     tmax = max(P.max_len(p), 1) if max_seq_len is None else max_seq_len
-    cb = brk.allocate_cache(w.num_q_heads, w.num_kv_heads, w.head_dim, w.batch, tmax, mixed=p.mixed,
-                            pages2_per_request=p.pages2, pages4_per_request=p.pages4, page_order2=p.order2,
-                            page_order4=p.order4)
+    cb = allocate(p, tmax)
     cb.seq_len.copy_(torch.tensor(list(w.seq_lens), dtype=torch.int32))
     rk = torch.from_numpy(p.rot_k).cuda()
     rv = torch.from_numpy(p.rot_v).cuda()

@@ -31,6 +31,7 @@ class Problem:
     pages4: int
     order2: np.ndarray
     order4: np.ndarray
+    codebook: np.ndarray = None   # [Hkv, 2, 4] fp16-valued INT2 levels (K, V), or None (uniform)
 
 
 def rotations(w: synth.Workload):
@@ -49,6 +50,23 @@ def rotations(w: synth.Workload):
     return np.stack(rk), np.stack(rv)
 
 
+def fit_codebooks(w: synth.Workload, rk: np.ndarray, rv: np.ndarray) -> np.ndarray:
+    """INT2 codebooks [Hkv, 2, 4] (fp16 values): the oracle's Lloyd-Max fit on the workload's
+    calibration context, rotated per kv-head, with the INT2 clip ratios."""
+    out = np.zeros((w.num_kv_heads, 2, 4), np.float32)
+    for kv in range(w.num_kv_heads):
+        kc, vc = synth.calibration_context(w, kv)
+        for j, (x, r, clip) in enumerate(((kc, rk[kv], 0.96), (vc, rv[kv], 0.92))):
+            xr = oracle.rotate_rows_fp32(oracle.bf16_round(x.astype(np.float32)), r)
+            out[kv, j] = oracle.fit_codebook(xr, w.group_size, clip)[1]
+    return out
+
+
+def codebook_patterns(cb: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns [Hkv, 2, 4] as int16 (the library's codebook table)."""
+    return oracle.fp16_patterns(cb).view(np.int16)
+
+
 def class_bits(w: synth.Workload) -> np.ndarray:
     """Bits of each tag class: the oracle's TriAxialKV greedy over the workload's sensitivity table,
     nominal class counts and bit budget."""
@@ -62,7 +80,8 @@ def token_bits(w: synth.Workload, b: int, T: int) -> np.ndarray:
     return class_bits(w)[synth.tag_classes(w, b, T)].astype(np.int64)
 
 
-def make_problem(w: synth.Workload, shuffle: bool = True, with_oracle: bool = True) -> Problem:
+def make_problem(w: synth.Workload, shuffle: bool = True, with_oracle: bool = True, codebook=None) -> Problem:
+    """``codebook``: None (uniform INT2 levels), "fit" (``fit_codebooks``) or a [Hkv, 2, 4] array."""
     B = w.batch
     K, V, bits = [], [], []
     for b in range(B):
@@ -76,10 +95,15 @@ def make_problem(w: synth.Workload, shuffle: bool = True, with_oracle: bool = Tr
         bits.append(token_bits(w, b, T))
     q = np.stack([synth.decode_query(w, b) for b in range(B)])
     rk, rv = rotations(w)
+    if isinstance(codebook, str):
+        codebook = fit_codebooks(w, rk, rv)
+    cbk = None if codebook is None else codebook[:, 0]
+    cbv = None if codebook is None else codebook[:, 1]
     caches = []
     if with_oracle:
         for b in range(B):
-            caches.append(oracle.OracleCache.from_prefix(K[b], V[b], rk, rv, w.group_size, bits=bits[b]))
+            caches.append(oracle.OracleCache.from_prefix(K[b], V[b], rk, rv, w.group_size, bits=bits[b],
+                                                         codebook_k=cbk, codebook_v=cbv))
     n2 = [max(0, T - 320) - int((bits[b][64:max(64, T - 256)] == 4).sum()) for b, T in enumerate(w.seq_lens)]
     n4 = [int((bits[b][64:max(64, T - 256)] == 4).sum()) for b, T in enumerate(w.seq_lens)]
     pages2 = max([(n + 15) // 16 for n in n2] + [1])
@@ -87,7 +111,7 @@ def make_problem(w: synth.Workload, shuffle: bool = True, with_oracle: bool = Tr
     r = np.random.default_rng(w.seed + 1000)
     order2 = r.permutation(B * pages2) if shuffle else np.arange(B * pages2)
     order4 = r.permutation(max(B * pages4, 0)) if shuffle else np.arange(B * pages4)
-    return Problem(w, K, V, q, rk, rv, bits, caches, w.mixed, pages2, pages4, order2, order4)
+    return Problem(w, K, V, q, rk, rv, bits, caches, w.mixed, pages2, pages4, order2, order4, codebook)
 
 
 def max_len(p: Problem) -> int:

@@ -49,7 +49,8 @@ def test_status_strings(lib):
 
 
 def test_layout_struct_size():
-    assert ctypes.sizeof(_lib.Layout) == 64
+    assert ctypes.sizeof(_lib.Layout) == 72
+    assert _lib.Layout.codebook.offset == 64
 
 
 def layout(**kw):
@@ -166,6 +167,61 @@ def test_quantize_pack_argument_checks(lib):
     assert q(4, 2048, 128, 2, 0.96, 1, 1, 1, None) == -2    # dim beyond this build
     assert q(4, 128, 128, 2, 0.96, None, 1, 1, None) == -1  # null x
     assert q(0, 128, 128, 2, 0.96, None, None, None, None) == 0
+
+
+def test_quantize_pack_codebook_argument_checks(lib):
+    q = lib.oscar_quantize_pack_codebook
+
+    def lv(*v):
+        return ctypes.cast((ctypes.c_uint16 * 4)(*v), ctypes.c_void_p)
+
+    good = lv(0x0000, 0x3C00, 0x4000, 0x4200)     # 0, 1, 2, 3
+    assert q(0, 128, 128, 0.96, None, good, None, None, None) == 0
+    assert q(4, 128, 128, 0.96, 1, None, 1, 1, None) == -1                        # no levels
+    assert q(4, 128, 128, 0.96, 1, lv(0x0000, 0x4000, 0x3C00, 0x4200), 1, 1, None) == -1   # not increasing
+    assert q(4, 128, 128, 0.96, 1, lv(0x0000, 0x3C00, 0x3C00, 0x4200), 1, 1, None) == -1   # repeated level
+    assert q(4, 128, 128, 0.96, 1, lv(0x0000, 0x3C00, 0x4000, 0x7E00), 1, 1, None) == -1   # NaN
+    assert q(4, 128, 128, 0.96, 1, lv(0x0000, 0x3C00, 0x4000, 0x7C00), 1, 1, None) == -1   # infinity
+    assert q(4, 128, 48, 0.96, 1, good, 1, 1, None) == -1
+    assert q(4, 6, 6, 0.96, 1, good, 1, 1, None) == -1
+    assert q(4, 128, 128, 1.5, 1, good, 1, 1, None) == -1
+    assert q(4, 2048, 128, 0.96, 1, good, 1, 1, None) == -2
+    assert q(4, 128, 128, 0.96, None, good, 1, 1, None) == -1
+
+
+def test_codebook_fit_argument_checks(lib):
+    """Invalid arguments are rejected before any device work; with no rows the uniform levels come
+    back after one iteration (no device call is made)."""
+    f = lib.oscar_codebook_fit
+    lv = (ctypes.c_double * 8)()
+    pats = (ctypes.c_uint16 * 8)()
+    its = (ctypes.c_int32 * 2)()
+    P_ = ctypes.c_void_p
+    out = (ctypes.cast(lv, P_), ctypes.cast(pats, P_), ctypes.cast(its, P_))
+    assert f(2, 0, 128, None, None, 0.96, 100, 1e-7, None, 0, *out, None) == 0
+    assert list(lv) == [0.0, 1.0, 2.0, 3.0] * 2 and list(pats) == [0x0000, 0x3C00, 0x4000, 0x4200] * 2
+    assert list(its) == [1, 1]
+    assert f(0, 10, 128, 1, 1, 0.96, 100, 1e-7, 1, 1 << 30, *out, None) == -1      # no heads
+    assert f(2, 10, 96, 1, 1, 0.96, 100, 1e-7, 1, 1 << 30, *out, None) == -2       # head_dim
+    assert f(2, 10, 128, 1, 1, 0.0, 100, 1e-7, 1, 1 << 30, *out, None) == -1       # clip
+    assert f(2, 10, 128, 1, 1, 0.96, 0, 1e-7, 1, 1 << 30, *out, None) == -1        # max_iter
+    assert f(2, 10, 128, 1, 1, 0.96, 100, -1.0, 1, 1 << 30, *out, None) == -1      # tol
+    assert f(2, 10, 128, None, 1, 0.96, 100, 1e-7, 1, 1 << 30, *out, None) == -1   # null rows
+    assert f(2, 10, 128, 1, 1, 0.96, 100, 1e-7, 1, 1 << 30, None, out[1], None, None) == -1
+    assert f(2, 10, 128, 1, 1, 0.96, 100, 1e-7, 1, 16, *out, None) == -3           # workspace
+    assert brk.codebook_workspace_bytes(2, 10, 128) >= 2 * 10 * 128 * 4
+    assert brk.codebook_workspace_bytes(2, 10, 96) == 0
+
+
+def test_misaligned_codebook_rejected(lib):
+    L = layout()
+    L.codebook = 0x1002
+    assert brk.page_bytes(L, 2) == 0 and brk.decode_workspace_bytes(L, 1, 1000) == 0
+    r = lib.oscar_decode_attn(ctypes.byref(L), 1, 1000, 1, 1, None, 1, 1, 1, None, 100, 1, 1, 0.0, 1, 1 << 30, 1,
+                              None)
+    assert r == -1
+    L.codebook = 0x1000
+    assert brk.page_bytes(L, 2) == 8 * 1152
 
 
 def test_bf16_argument_checks(lib):
