@@ -44,11 +44,13 @@ def _kv_device(w, T_max, sampled):
     return K, V
 
 
-def _run(w, sampled):
+def _run(w, sampled, codebook=False):
     B, hq, hkv, d, g = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.gqa
     lens = list(w.seq_lens)
     tmax = max(lens) + EXTRA
     rk, rv = P.rotations(w)
+    cbk = P.fit_codebooks(w, rk, rv) if codebook else None
+    table = torch.from_numpy(np.ascontiguousarray(P.codebook_patterns(cbk))).cuda() if codebook else None
     bits = [P.token_bits(w, b, lens[b]) for b in range(B)]
     hist = [max(0, T - 320) for T in lens]
     n4 = [int((bits[b][64:64 + hist[b]] == 4).sum()) for b in range(B)]
@@ -59,7 +61,7 @@ def _run(w, sampled):
     order2 = synth.page_permutation(w.seed, B * pages2)
     order4 = synth.page_permutation(w.seed + 1, B * pages4) if w.mixed else None
     cb = brk.allocate_cache(hq, hkv, d, B, tmax, mixed=w.mixed, pages2_per_request=pages2,
-                            pages4_per_request=pages4, page_order2=order2, page_order4=order4)
+                            pages4_per_request=pages4, page_order2=order2, page_order4=order4, codebook=table)
     K, V = _kv_device(w, tmax, sampled)
     rkt, rvt = torch.from_numpy(rk).cuda(), torch.from_numpy(rv).cuda()
     tb = None
@@ -95,8 +97,9 @@ def _run(w, sampled):
     results = []
     for b, kv in sampled:
         ks, vs = synth.kv_slice(w, b, kv, lens[b])
+        kw = {} if cbk is None else dict(codebook_k=cbk[kv:kv + 1, 0], codebook_v=cbk[kv:kv + 1, 1])
         cache = oracle.OracleCache.from_prefix(ks[None], vs[None], rk[kv:kv + 1], rv[kv:kv + 1], w.group_size,
-                                               bits=bits[b])
+                                               bits=bits[b], **kw)
         ref = oracle.decode_attention(cache, q[b, kv * g:(kv + 1) * g])
         worst, mab = G.check_close(got[b:b + 1, kv * g:(kv + 1) * g], ref[None], tag=f"{w.name} b{b} kv{kv}")
         results.append((b, kv, worst, mab))
@@ -127,3 +130,14 @@ def test_fullsize_ragged_bs8_gqa8():
 def test_fullsize_mixed_int2_int4_bs16_64k():
     print("case mixed INT2/INT4 bs16 64k", flush=True)
     _run(synth.workload(5), sampled=[(0, 1), (9, 4)])
+
+
+def test_fullsize_codebook_qwen3_8b_bs1_100k():
+    """The bench workload with Lloyd-Max INT2 codebooks (fitted on the calibration context)."""
+    print("case codebook qwen3-8b bs1 100k", flush=True)
+    _run(synth.workload(2), sampled=[(0, 3), (0, 6)], codebook=True)
+
+
+def test_fullsize_codebook_paged_bs32_32k():
+    print("case codebook paged bs32 32k", flush=True)
+    _run(synth.workload(3), sampled=[(5, 1), (30, 4)], codebook=True)
