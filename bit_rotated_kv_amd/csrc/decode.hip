@@ -1375,13 +1375,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
     if (a.events) (void)hipEventRecord(a.events[i], stream);
   };
   mark(0);
-  if (a.ws.qpre)
+  if (a.ws.qpre) {
     if (a.codebook)
       hipLaunchKernelGGL((q_prologue_kernel<D, GQ, true>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
                          stream, a);
     else
       hipLaunchKernelGGL((q_prologue_kernel<D, GQ, false>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
                          stream, a);
+  }
   mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
 #ifndef OSCAR_SPLIT_LDS_PAD
