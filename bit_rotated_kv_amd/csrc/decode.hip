@@ -632,18 +632,28 @@ struct QPage {
   uint32_t mt[Redist<GQ>::meta_words];
 };
 
-template <int BITS, int D, int GQ, typename Ptr>
-__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, Ptr ph, int lane) {
+// Raw buffer descriptor of one page-head (gfx9 family: base, stride 0, size in bytes, word 3
+// 0x00020000): the page's loads then take the same per-lane byte offsets on every page, and a
+// byte past the page-head would read as zero instead of touching the next one.
+template <int BITS, int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0, 4 * D * BITS + kMetaBytes,
+                                           0x00020000);
+}
+
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head, int lane) {
   constexpr int CW = QPage<BITS, D, GQ>::CW;
   const int g = lane / 16, c = lane % 16;
+  const __amdgpu_buffer_rsrc_t r = qpage_rsrc<BITS, D>(head);
   if constexpr (CW == 1) {
-    const u32x2_t v = *reinterpret_cast<GPtr<u32x2_t>>(ph + lane * 8);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0);
     pr.kw[0] = v[0];
     pr.vw[0] = v[1];
   } else {
 #pragma unroll
     for (int j = 0; j < 2 * CW / 4; ++j) {
-      const u32x4_t v = *reinterpret_cast<GPtr<u32x4_t>>(ph + lane * 8 * CW + 16 * j);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 8 * CW + 16 * j, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * j + e;
@@ -652,18 +662,18 @@ __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, Ptr ph, int l
       }
     }
   }
-  const auto meta = ph + 4 * D * BITS;
+  constexpr int meta = 4 * D * BITS;
   if constexpr (GQ == 4) {
-    const u32x2_t m = *reinterpret_cast<GPtr<u32x2_t>>(meta + 8 * (4 * g + c / 4));
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(r, meta + 8 * (4 * g + c / 4), 0, 0);
     pr.mt[0] = m[0];
     pr.mt[1] = m[1];
   } else if constexpr (GQ == 8) {
-    const u32x4_t m = *reinterpret_cast<GPtr<u32x4_t>>(meta + 8 * (4 * g + 2 * (c / 8)));
+    const u32x4_t m = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 8 * (4 * g + 2 * (c / 8)), 0, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr.mt[e] = m[e];
   } else {
-    const u32x4_t a = *reinterpret_cast<GPtr<u32x4_t>>(meta + 32 * g);
-    const u32x4_t b = *reinterpret_cast<GPtr<u32x4_t>>(meta + 32 * g + 16);
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g, 0, 0);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g + 16, 0, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pr.mt[e] = a[e];
@@ -715,16 +725,12 @@ __device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const 
   return acc;
 }
 
-// History logit s*X + z*U + (s*X_lo + z*U_lo) of one token and head, where X = sum c*v_hi and
-// U = sum v_hi are exact fp32 multiples of the query grid: the two large products are formed
-// without rounding error (fma residuals), so cancellation between them costs no precision.
-__device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl, float uh, float ul) {
-#pragma clang fp contract(off)
-  const float p1 = s * xh;
-  const float r1 = fmaf(s, xh, -p1);
-  const float p2 = z * uh;
-  const float r2 = fmaf(z, uh, -p2);
-  return (p1 + p2) + ((r1 + r2) + fmaf(s, xl, z * ul));
+// History logit s*X + z*U of one token and head: X = (X_hi + X_lo) * 2^E from the high-part
+// product (an exact multiple of the query grid) and the low-part product, U = sum of the query
+// operand (per head). Formed in fp32 (a few roundings of the larger of s*X and z*U; the two
+// nearly cancel only as far as the group's zero point exceeds the spread of its values).
+__device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl, float esc, float u) {
+  return fmaf(s, (xh + xl) * esc, z * u);
 }
 
 template <int BITS, int D, int GQ, bool LUT = false>
@@ -802,11 +808,12 @@ __device__ __forceinline__ void redist_softmax(WaveState<D, GQ>& st, const float
 }
 
 // Softmax and PV product of one page, given its QK^T result `acc`: column c < GQ holds the
-// high-part product of head c, column GQ + c the low-part product.
+// high-part product of head c, column GQ + c the low-part product. `lim` = tokens of the history
+// from the page's first slot on: slots at or past it are masked.
 template <int BITS, int D, int GQ, bool LUT = false>
 __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, float4_t acc,
-                                              float uh, float ul, float esc, uint32_t psel, int slot0, int ntok,
-                                              int lane, const Codebook& cbv) {
+                                              float uq, float esc, uint32_t psel, int lim, int lane,
+                                              const Codebook& cbv) {
   const int g = lane / 16, c = lane % 16;
   if constexpr (GQ == 4) {
     // lane (g, c) takes token 4g + c/4 of head c%4: high part from column c%4, low part from
@@ -819,8 +826,8 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     xl = __uint_as_float(dpp_row_shl_into<4, 0x1>(__float_as_uint(xl), __float_as_uint(acc[0])));
     xl = dpp_row_shr_into<4, 0x4>(xl, acc[2]);
     xl = dpp_row_shr_into<8, 0x8>(xl, acc[3]);
-    float lg[1] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh * esc, xl * esc, uh, ul)};
-    lg[0] = slot0 + 4 * g + c / 4 < ntok ? lg[0] : kNegInf;
+    float lg[1] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh, xl, esc, uq)};
+    lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;
     float p[1];
     redist_softmax<D, GQ, 1>(st, lg, p, lane);
     st.l_part += p[0];
@@ -843,11 +850,11 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const float h1 = dpp_row_shr_into<8, 0xC>(acc[1], acc[3]);
     const float l0 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[2]), __float_as_uint(acc[0])));
     const float l1 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[3]), __float_as_uint(acc[1])));
-    const int t0 = slot0 + 4 * g + 2 * (c / 8);
-    float lg[2] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0 * esc, l0 * esc, uh, ul),
-                   hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1 * esc, l1 * esc, uh, ul)};
-    lg[0] = t0 < ntok ? lg[0] : kNegInf;
-    lg[1] = t0 + 1 < ntok ? lg[1] : kNegInf;
+    float lg[2] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0, l0, esc, uq),
+                   hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1, l1, esc, uq)};
+    const int t0 = 4 * g + 2 * (c / 8);
+    lg[0] = t0 < lim ? lg[0] : kNegInf;
+    lg[1] = t0 + 1 < lim ? lg[1] : kNegInf;
     float p[2];
     redist_softmax<D, GQ, 2>(st, lg, p, lane);
     st.l_part += p[0] + p[1];
@@ -866,9 +873,8 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float xl = __uint_as_float(dpp_row_shl<GQ>(__float_as_uint(acc[r])));
-      lg[r] = slot0 + 4 * g + r < ntok
-                  ? hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r] * esc, xl * esc, uh, ul)
-                  : kNegInf;
+      lg[r] = hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r], xl, esc, uq);
+      lg[r] = 4 * g + r < lim ? lg[r] : kNegInf;
     }
     float p[4];
     softmax_page<D, GQ>(st, lg, p, lane);
@@ -985,7 +991,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
       const int li = min(pg - wp0, kWave - 1);
       const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, li) << 32);
-      load_qpage<BITS, D, GQ>(pr, reinterpret_cast<GPtr<uint8_t>>(ad), lane);
+      load_qpage<BITS, D, GQ>(pr, ad, lane);
       return pg < wp1 && ((valid_mask >> li) & 1u);
     };
     QPage<BITS, D, GQ> buf[NB];
@@ -1004,6 +1010,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     } else {
       hist_query_operands<BITS, D, GQ, LUT>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
     }
+    const float uq = uh + ul;   // sum of the query operand of this lane's head
     const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
     const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
     float4_t acc = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
@@ -1015,7 +1022,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
         if (pg + k < wp1) {
           const float4_t acc_next = qk_page<BITS, D, GQ, LUT>(buf[(k + 1) % NB], bq, cbk);
           if (ok[k]) {
-            process_qpage<BITS, D, GQ, LUT>(st, buf[k], acc, uh, ul, esc, psel, (pg + k) * kPage, ntok, lane, cbv);
+            process_qpage<BITS, D, GQ, LUT>(st, buf[k], acc, uq, esc, psel, ntok - (pg + k) * kPage, lane, cbv);
           } else if (lane == 0) {
             atomicOr(a.ws.flags, 1u);
           }
