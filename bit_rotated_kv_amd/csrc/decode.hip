@@ -46,11 +46,14 @@ namespace oscar {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 #ifndef OSCAR_HIST_PIPE2
-#define OSCAR_HIST_PIPE2 4
+#define OSCAR_HIST_PIPE2 6
+#endif
+#ifndef OSCAR_HIST_PIPE4
+#define OSCAR_HIST_PIPE4 6
 #endif
 // history pages in the per-wave load ring (INT2 page-heads are 1152 B, INT4 2176 B at d = 128)
 constexpr int kHistPipe2 = OSCAR_HIST_PIPE2;
-constexpr int kHistPipe4 = 4;
+constexpr int kHistPipe4 = OSCAR_HIST_PIPE4;
 constexpr int kBf16Pipe = 2;   // BF16 pages in the per-wave load ring (8 KB each)
 
 __device__ __forceinline__ float4_t mfma32_f16(const u32x4_t& a, const half8_t& b, float4_t c) {
@@ -283,13 +286,15 @@ struct WaveState {
   }
 };
 
-// Online-softmax update for one page given the 4 logits of this lane (tokens 4g+r of head
-// h = lane%16); returns the 4 probabilities. Rescales only when the page max exceeds the running
-// max by more than 8 (log2 units), so probabilities stay below 2^8.
-template <int D, int GQ>
-__device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float lg[4], float p[4], int lane) {
+// Online-softmax update given NL logits of this lane (4 per page: tokens 4g+r of head h =
+// lane%16); returns the probabilities. Rescales only when the maximum exceeds the running max by
+// more than 8 (log2 units), so probabilities stay below 2^8.
+template <int D, int GQ, int NL>
+__device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float (&lg)[NL], float (&p)[NL], int lane) {
   const int h = lane % 16, g = lane / 16;
-  float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+  float mx = lg[0];
+#pragma unroll
+  for (int i = 1; i < NL; ++i) mx = fmaxf(mx, lg[i]);
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
   const bool need = (h < GQ) && (mx > st.m_run + 8.0f);
@@ -307,7 +312,7 @@ __device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float l
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = (h < GQ && lg[r] != kNegInf) ? __builtin_amdgcn_exp2f(lg[r] - st.m_run) : 0.0f;
+  for (int i = 0; i < NL; ++i) p[i] = (h < GQ && lg[i] != kNegInf) ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
 }
 
 // Writes the wave's state to LDS and merges the 4 waves of the workgroup into one partial
@@ -412,7 +417,7 @@ __device__ __forceinline__ void process_bf16_page(WaveState<D, GQ>& st, const Bf
 #pragma unroll
   for (int r = 0; r < 4; ++r) lg[r] = valid[r] ? acc[r] * sl2e : kNegInf;
   float p[4];
-  softmax_page<D, GQ>(st, lg, p, lane);
+  softmax_page<D, GQ, 4>(st, lg, p, lane);
   st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
   uint32_t hb[4], lb[4];
 #pragma unroll
@@ -733,27 +738,44 @@ __device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl
   return fmaf(s, (xh + xl) * esc, z * u);
 }
 
-template <int BITS, int D, int GQ, bool LUT = false>
-__device__ __forceinline__ void pv_page(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, uint32_t a01,
-                                        uint32_t a23, const Codebook& cbv) {
+// B operand words of the PV product for value columns 16nb..16nb+15 of one page: the codes of the
+// lane's 4 token slots as fp16 subnormal slots (or, with LUT, as their codebook levels).
+template <int BITS, int D, int GQ, bool LUT>
+__device__ __forceinline__ void value_words(const QPage<BITS, D, GQ>& pr, int nb, const Codebook& cbv, uint32_t& b0,
+                                            uint32_t& b1) {
+  if constexpr (LUT) {
+    b0 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], false), nb % 4);
+    b1 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], true), nb % 4);
+  } else if constexpr (BITS == 2) {
+    const uint32_t w = pr.vw[nb / 4];
+    const uint32_t mask = 0x00030003u << (2 * (nb % 4));
+    b0 = w & mask;
+    b1 = (w >> 8) & mask;
+  } else {
+    const uint32_t w = pr.vw[nb / 2];
+    const uint32_t mask = 0x000F000Fu << (4 * (nb % 2));
+    b0 = w & mask;
+    b1 = (w >> 8) & mask;
+  }
+}
+
+// PV product of a page pair, one 16x16x32 product per 16 value columns: the reduction runs over
+// the lane group's 4 token slots of the first page, then the same 4 slots of the second, in A
+// (probabilities) and B (codes) alike. `a` = {first page's A words, second page's A words}.
+template <int BITS, int D, int GQ, bool LUT>
+__device__ __forceinline__ void pv_pair(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& p0,
+                                        const QPage<BITS, D, GQ>& p1, const u32x4_t& a, const Codebook& cbv) {
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
-    uint32_t b0, b1;
-    if constexpr (LUT) {
-      b0 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], false), nb % 4);
-      b1 = codebook_levels2(cbv, codebook_spread(pr.vw[nb / 4], true), nb % 4);
-    } else if constexpr (BITS == 2) {
-      const uint32_t w = pr.vw[nb / 4];
-      const uint32_t mask = 0x00030003u << (2 * (nb % 4));
-      b0 = w & mask;
-      b1 = (w >> 8) & mask;
-    } else {
-      const uint32_t w = pr.vw[nb / 2];
-      const uint32_t mask = 0x000F000Fu << (4 * (nb % 2));
-      b0 = w & mask;
-      b1 = (w >> 8) & mask;
-    }
-    st.o[nb] = mfma16_f16(a01, a23, b0, b1, st.o[nb]);
+    u32x4_t b;
+    uint32_t w0, w1, w2, w3;
+    value_words<BITS, D, GQ, LUT>(p0, nb, cbv, w0, w1);
+    value_words<BITS, D, GQ, LUT>(p1, nb, cbv, w2, w3);
+    b[0] = w0;
+    b[1] = w1;
+    b[2] = w2;
+    b[3] = w3;
+    st.o[nb] = mfma32_f16(a, __builtin_bit_cast(half8_t, b), st.o[nb]);
   }
 }
 
@@ -807,13 +829,17 @@ __device__ __forceinline__ void redist_softmax(WaveState<D, GQ>& st, const float
   for (int i = 0; i < NL; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);  // 0 for -inf logits
 }
 
-// Softmax and PV product of one page, given its QK^T result `acc`: column c < GQ holds the
-// high-part product of head c, column GQ + c the low-part product. `lim` = tokens of the history
-// from the page's first slot on: slots at or past it are masked.
-template <int BITS, int D, int GQ, bool LUT = false>
-__device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr, float4_t acc,
-                                              float uq, float esc, uint32_t psel, int lim, int lane,
-                                              const Codebook& cbv) {
+// Logits per lane and history page: GQA 4 and 8 spread the 16 x GQ logits of a page over the
+// wavefront; other widths keep the 4 token slots of the lane's row.
+template <int GQ>
+constexpr int kPageLogits = GQ == 4 ? 1 : (GQ == 8 ? 2 : 4);
+
+// Logits of one page from its QK^T result `acc` (column c < GQ: high-part product of head c,
+// column GQ + c: low-part product). `lim` = tokens of the history from the page's first slot on:
+// slots at or past it get -inf.
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void page_logits(const QPage<BITS, D, GQ>& pr, float4_t acc, float uq, float esc, int lim,
+                                            int lane, float (&lg)[kPageLogits<GQ>]) {
   const int g = lane / 16, c = lane % 16;
   if constexpr (GQ == 4) {
     // lane (g, c) takes token 4g + c/4 of head c%4: high part from column c%4, low part from
@@ -826,23 +852,8 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     xl = __uint_as_float(dpp_row_shl_into<4, 0x1>(__float_as_uint(xl), __float_as_uint(acc[0])));
     xl = dpp_row_shr_into<4, 0x4>(xl, acc[2]);
     xl = dpp_row_shr_into<8, 0x8>(xl, acc[3]);
-    float lg[1] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh, xl, esc, uq)};
+    lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh, xl, esc, uq);
     lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;
-    float p[1];
-    redist_softmax<D, GQ, 1>(st, lg, p, lane);
-    st.l_part += p[0];
-    st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), st.z_part);
-    // A operand of the PV product: row c < 4 holds the fp16 high parts of head c for tokens
-    // 4g..4g+3 (lanes c, c+4, c+8, c+12), row 4 + c the low parts (lanes c, c+4, c+8, c+12 seen
-    // from row 4 + c: offsets -4, 0, +4, +8); rows 8..15 are zero (selector bytes 0x0C).
-    // (lanes 8..15 of y, u, v8 keep whatever they hold: the selector zeroes those rows)
-    const uint32_t P = split_f16(p[0] * lo_bf16(pr.mt[1]));
-    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(P, P), P);
-    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(P, P), P);
-    const uint32_t v8 = dpp_row_shl_into<8, 0x3>(P, P);
-    const uint32_t a01 = __builtin_amdgcn_perm(y, P, psel);
-    const uint32_t a23 = __builtin_amdgcn_perm(u, v8, psel);
-    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
   } else if constexpr (GQ == 8) {
     // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8; high parts from columns 0..7,
     // low parts from columns 8..15
@@ -850,13 +861,43 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const float h1 = dpp_row_shr_into<8, 0xC>(acc[1], acc[3]);
     const float l0 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[2]), __float_as_uint(acc[0])));
     const float l1 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[3]), __float_as_uint(acc[1])));
-    float lg[2] = {hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0, l0, esc, uq),
-                   hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1, l1, esc, uq)};
+    lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0, l0, esc, uq);
+    lg[1] = hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1, l1, esc, uq);
     const int t0 = 4 * g + 2 * (c / 8);
     lg[0] = t0 < lim ? lg[0] : kNegInf;
     lg[1] = t0 + 1 < lim ? lg[1] : kNegInf;
-    float p[2];
-    redist_softmax<D, GQ, 2>(st, lg, p, lane);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float xl = __uint_as_float(dpp_row_shl<GQ>(__float_as_uint(acc[r])));
+      lg[r] = hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r], xl, esc, uq);
+      lg[r] = 4 * g + r < lim ? lg[r] : kNegInf;
+    }
+  }
+}
+
+// Probability and zero-point sums of one page, and its A words of the PV product: row c of the
+// lane group holds fp16 parts of p * s_V for the group's 4 token slots (high parts of head c in
+// rows c < GQ, low parts in rows GQ + c).
+template <int BITS, int D, int GQ>
+__device__ __forceinline__ void page_operand(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr,
+                                             const float (&p)[kPageLogits<GQ>], uint32_t psel, int lane,
+                                             uint32_t& a01, uint32_t& a23) {
+  const int c = lane % 16;
+  if constexpr (GQ == 4) {
+    st.l_part += p[0];
+    st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), st.z_part);
+    // row c < 4 holds the fp16 high parts of head c for tokens 4g..4g+3 (lanes c, c+4, c+8,
+    // c+12), row 4 + c the low parts (lanes c, c+4, c+8, c+12 seen from row 4 + c: offsets -4, 0,
+    // +4, +8); rows 8..15 are zero (selector bytes 0x0C). Lanes 8..15 of y, u, v8 keep whatever
+    // they hold: the selector zeroes those rows.
+    const uint32_t P = split_f16(p[0] * lo_bf16(pr.mt[1]));
+    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(P, P), P);
+    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(P, P), P);
+    const uint32_t v8 = dpp_row_shl_into<8, 0x3>(P, P);
+    a01 = __builtin_amdgcn_perm(y, P, psel);
+    a23 = __builtin_amdgcn_perm(u, v8, psel);
+  } else if constexpr (GQ == 8) {
     st.l_part += p[0] + p[1];
     st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), fmaf(p[1], hi_bf16(pr.mt[3]), st.z_part));
     const uint32_t q0 = split_f16(p[0] * lo_bf16(pr.mt[1]));
@@ -865,19 +906,9 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     const uint32_t L0 = pack_hi16(q0, q1);   // low parts of both tokens
     // row c < 8: high parts of head c, tokens 4g, 4g+1 (own) and 4g+2, 4g+3 (lane c+8);
     // row c >= 8: low parts of head c-8, tokens 4g, 4g+1 (lane c-8) and 4g+2, 4g+3 (own)
-    const uint32_t a01 = dpp_row_shr_into<8, 0xC>(P0, L0);
-    const uint32_t a23 = dpp_row_shl_into<8, 0x3>(L0, P0);
-    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
+    a01 = dpp_row_shr_into<8, 0xC>(P0, L0);
+    a23 = dpp_row_shl_into<8, 0x3>(L0, P0);
   } else {
-    float lg[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float xl = __uint_as_float(dpp_row_shl<GQ>(__float_as_uint(acc[r])));
-      lg[r] = hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r], xl, esc, uq);
-      lg[r] = 4 * g + r < lim ? lg[r] : kNegInf;
-    }
-    float p[4];
-    softmax_page<D, GQ>(st, lg, p, lane);
     float W[4];
     float lsum = 0.0f, zsum = 0.0f;
 #pragma unroll
@@ -890,10 +921,45 @@ __device__ __forceinline__ void process_qpage(WaveState<D, GQ>& st, const QPage<
     st.z_part += zsum;
     const uint32_t q0 = split_f16(W[0]), q1 = split_f16(W[1]), q2 = split_f16(W[2]), q3 = split_f16(W[3]);
     const uint32_t s01 = row_shr_or_zero<GQ>(pack_hi16(q0, q1)), s23 = row_shr_or_zero<GQ>(pack_hi16(q2, q3));
-    const uint32_t a01 = c < GQ ? pack_lo16(q0, q1) : (c < 2 * GQ ? s01 : 0u);
-    const uint32_t a23 = c < GQ ? pack_lo16(q2, q3) : (c < 2 * GQ ? s23 : 0u);
-    pv_page<BITS, D, GQ, LUT>(st, pr, a01, a23, cbv);
+    a01 = c < GQ ? pack_lo16(q0, q1) : (c < 2 * GQ ? s01 : 0u);
+    a23 = c < GQ ? pack_lo16(q2, q3) : (c < 2 * GQ ? s23 : 0u);
   }
+}
+
+// Softmax and PV product of a page pair given the QK^T results of both pages; `lim0`, `lim1` as
+// in page_logits (0 masks a whole page). The online-softmax update covers both pages at once.
+template <int BITS, int D, int GQ, bool LUT>
+__device__ __forceinline__ void process_qpair(WaveState<D, GQ>& st, const QPage<BITS, D, GQ>& pr0,
+                                              const QPage<BITS, D, GQ>& pr1, float4_t acc0, float4_t acc1,
+                                              float uq, float esc, uint32_t psel, int lim0, int lim1, int lane,
+                                              const Codebook& cbv) {
+  constexpr int NL = kPageLogits<GQ>;
+  float l0[NL], l1[NL];
+  page_logits<BITS, D, GQ>(pr0, acc0, uq, esc, lim0, lane, l0);
+  page_logits<BITS, D, GQ>(pr1, acc1, uq, esc, lim1, lane, l1);
+  float lg[2 * NL], p[2 * NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    lg[i] = l0[i];
+    lg[NL + i] = l1[i];
+  }
+  if constexpr (Redist<GQ>::on) redist_softmax<D, GQ, 2 * NL>(st, lg, p, lane);
+  else softmax_page<D, GQ, 2 * NL>(st, lg, p, lane);
+  float p0[NL], p1[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    p0[i] = p[i];
+    p1[i] = p[NL + i];
+  }
+  uint32_t w0, w1, w2, w3;
+  page_operand<BITS, D, GQ>(st, pr0, p0, psel, lane, w0, w1);
+  page_operand<BITS, D, GQ>(st, pr1, p1, psel, lane, w2, w3);
+  u32x4_t a;
+  a[0] = w0;
+  a[1] = w1;
+  a[2] = w2;
+  a[3] = w3;
+  pv_pair<BITS, D, GQ, LUT>(st, pr0, pr1, a, cbv);
 }
 
 #ifndef OSCAR_PROGRESS_PRIORITY
@@ -983,10 +1049,12 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   const uint64_t valid_mask = __ballot(page_ok);
   const uint32_t addr_lo = (uint32_t)my_addr, addr_hi = (uint32_t)(my_addr >> 32);
   if (dm.pool_pages > 0) {
-    // Load ring of NB page buffers (compile-time indices; prefetches past the range read the
-    // dummy page-head) with the QK^T product one page ahead: the matrix cores work on page k+1
-    // while the vector units run the softmax of page k.
+    // Load ring of NB page buffers, taken as NB/2 page pairs (compile-time indices; prefetches
+    // past the range read the dummy page-head). The QK^T products run one pair ahead: the matrix
+    // cores work on pair k+1 while the vector units run the softmax of pair k, and the loads of
+    // pair k+2 are in flight.
     constexpr int NB = BITS == 2 ? kHistPipe2 : kHistPipe4;
+    static_assert(NB % 2 == 0 && NB >= 6, "the history ring holds three or more page pairs");
     auto load = [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
       const int li = min(pg - wp0, kWave - 1);
       const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
@@ -997,7 +1065,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     QPage<BITS, D, GQ> buf[NB];
     bool ok[NB];
 #pragma unroll
-    for (int k = 0; k < NB - 1; ++k) ok[k] = load(buf[k], wp0 + k);
+    for (int k = 0; k < NB - 2; ++k) ok[k] = load(buf[k], wp0 + k);
     __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
     half8_t bq[D / 32];
     float uh, ul, esc;
@@ -1013,20 +1081,27 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     const float uq = uh + ul;   // sum of the query operand of this lane's head
     const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
     const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
-    float4_t acc = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
+    float4_t acc0 = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
+    float4_t acc1 = qk_page<BITS, D, GQ, LUT>(buf[1], bq, cbk);
     for (int pg = wp0; pg < wp1; pg += NB) {
       progress_priority(pg - wp0, wp1 - wp0);
 #pragma unroll
-      for (int k = 0; k < NB; ++k) {
+      for (int k = 0; k < NB; k += 2) {
+        ok[(k + NB - 2) % NB] = load(buf[(k + NB - 2) % NB], pg + k + NB - 2);
         ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
         if (pg + k < wp1) {
-          const float4_t acc_next = qk_page<BITS, D, GQ, LUT>(buf[(k + 1) % NB], bq, cbk);
-          if (ok[k]) {
-            process_qpage<BITS, D, GQ, LUT>(st, buf[k], acc, uq, esc, psel, ntok - (pg + k) * kPage, lane, cbv);
-          } else if (lane == 0) {
-            atomicOr(a.ws.flags, 1u);
+          const float4_t n0 = qk_page<BITS, D, GQ, LUT>(buf[(k + 2) % NB], bq, cbk);
+          const float4_t n1 = qk_page<BITS, D, GQ, LUT>(buf[(k + 3) % NB], bq, cbk);
+          // a page past the range is masked; a page id outside the pool or of the other width is
+          // masked and flagged (every page of the range carries at least one token)
+          if (ok[k] || ok[k + 1]) {
+            process_qpair<BITS, D, GQ, LUT>(st, buf[k], buf[k + 1], acc0, acc1, uq, esc, psel,
+                                            ok[k] ? ntok - (pg + k) * kPage : 0,
+                                            ok[k + 1] ? ntok - (pg + k + 1) * kPage : 0, lane, cbv);
           }
-          acc = acc_next;
+          if ((!ok[k] || (!ok[k + 1] && pg + k + 1 < wp1)) && lane == 0) atomicOr(a.ws.flags, 1u);
+          acc0 = n0;
+          acc1 = n1;
         }
       }
     }
