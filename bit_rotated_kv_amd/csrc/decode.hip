@@ -1126,16 +1126,18 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a
   __shared__ float o_lds[kSplitWaves][2 * GQ][D];
   __shared__ float st_lds[kSplitWaves][3][8];
   __shared__ SplitScratch<D, GQ> scr;
-  const int nwin = a.ws.nwin, s2 = a.ws.s2;
-  const int n_win = a.dm.batch * a.dm.hkv * nwin;
-  const int n_int2 = a.dm.batch * a.dm.hkv * s2;
+  // Long roles first: the history workgroups take the low indices, so the dispatcher starts them
+  // first, and the shorter window and step workgroups fill the compute units that free up while
+  // the last history workgroups run.
+  const int n_int2 = a.dm.batch * a.dm.hkv * a.ws.s2;
+  const int n_hist = n_int2 + a.dm.batch * a.dm.hkv * a.ws.s4;
   const int bid = blockIdx.x;
-  if (bid < n_win) {
-    window_role<D, GQ>(a, cw, bid, o_lds, st_lds, scr.step);
-  } else if (bid < n_win + n_int2) {
-    hist_role<2, D, GQ, CB>(a, bid - n_win, o_lds, st_lds, scr.hist);
+  if (bid < n_int2) {
+    hist_role<2, D, GQ, CB>(a, bid, o_lds, st_lds, scr.hist);
+  } else if (bid < n_hist) {
+    hist_role<4, D, GQ>(a, bid - n_int2, o_lds, st_lds, scr.hist);
   } else {
-    hist_role<4, D, GQ>(a, bid - n_win - n_int2, o_lds, st_lds, scr.hist);
+    window_role<D, GQ>(a, cw, bid - n_hist, o_lds, st_lds, scr.step);
   }
 }
 
