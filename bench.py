@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
-    ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurement")
+    ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurements")
+    ap.add_argument("--no-bs32-100k", action="store_true", help="skip the batch-32 x 100K-context measurement")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-codebook", action="store_true", help="skip the Lloyd-Max codebook variant")
@@ -248,6 +249,9 @@ def time_int2(setup, steps, warmup, eager):
         setup.step(base + i, events=evs[i])
     torch.cuda.synchronize()
     k = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
+    span = np.array([evs[i][0].elapsed_time(evs[i][3]) for i in range(steps)])
+    # spread of the eagerly launched steps (first to last event of a step), microseconds
+    setup.step_spread_us = [round(float(x) * 1e3, 2) for x in np.percentile(span, [10, 50, 90])]
     return ms, k.mean(axis=0), mode
 
 
@@ -413,6 +417,34 @@ def time_bf16(w, batch, context, steps, warmup, fast_inputs):
     return ms, nbytes
 
 
+def time_bs32_100k(args):
+    """The metric's literal batch-32 point: workload 3's paged batch (shared pool, seeded page
+    permutation, demote in step) at a 100,000-token context per request, with the BF16 baseline
+    over the same context."""
+    import torch
+    import synth
+    w = synth.workload(3)
+    batch, context = 32, 100_000
+    est = batch * w.num_kv_heads * (context - 320) * 72
+    s = Int2Setup(w, batch, context, max(2, math.ceil(1.0e9 / est)), args.steps + args.warmup, fast_inputs=True)
+    ms, k, mode = time_int2(s, args.steps, args.warmup, args.eager)
+    i2, b2, d2 = s.bytes_per_step()
+    split = (i2 + b2) / (float(k[1]) * 1e-3) / 1e9
+    r = {"workload": "paged batch 32 x 100,000 tokens, demote in step", "ms_per_step": round(ms, 5),
+         "us_per_step": round(ms * 1e3, 2), "GB_per_s": round((i2 + b2 + d2) / (ms * 1e-3) / 1e9, 1),
+         "tokens_per_s": round(batch / (ms * 1e-3), 1), "split_GB_per_s": round(split, 1),
+         "split_frac": round(split / HBM_PEAK_GBS, 4), "kernel_ms": [round(float(x), 5) for x in k],
+         "eager_step_us_p10_p50_p90": s.step_spread_us, "cache_copies": s.copies, "launch": mode}
+    del s
+    torch.cuda.empty_cache()
+    if not args.no_bf16:
+        bms, _ = time_bf16(w, batch, context, args.steps, args.warmup, True)
+        r["bf16_baseline_ms"] = round(bms, 5)
+        r["speedup_step"] = round(bms / ms, 3)
+        torch.cuda.empty_cache()
+    return r
+
+
 # ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_traffic.txt")
 
@@ -525,6 +557,7 @@ def main():
         "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
         "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
                       "merge": round(float(kern[2]), 5)},
+        "eager_step_us_p10_p50_p90": setup.step_spread_us,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                      "kernel": "split_kernel<128,4,false> (BF16 window + INT2 history split-K + step workgroups, "
@@ -567,7 +600,8 @@ def main():
                           "tokens_per_s": round(32 / (ms32 * 1e-3), 1),
                           "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
                           "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "kernel_ms": [round(float(x), 5) for x in k32]}
+                          "kernel_ms": [round(float(x), 5) for x in k32],
+                          "eager_step_us_p10_p50_p90": s32.step_spread_us}
         del s32
         torch.cuda.empty_cache()
         if not args.no_prefill:
@@ -579,6 +613,9 @@ def main():
             result["bs32"]["bf16_baseline_ms"] = round(bms32, 5)
             result["bs32"]["speedup_step"] = round(bms32 / ms32, 3)
             torch.cuda.empty_cache()
+        if not args.no_bs32_100k:
+            log("batch-32 x 100K-context measurement")
+            result["bs32_100k"] = time_bs32_100k(args)
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -119,6 +119,13 @@ def test_fullsize_paged_bs32_32k():
     _run(synth.workload(3), sampled=[(0, 2), (17, 7), (31, 0)])
 
 
+def test_fullsize_paged_bs32_100k():
+    """The metric's literal batch-32 point: workload 3's paged batch at 100,000 tokens per request."""
+    print("case paged bs32 100k", flush=True)
+    w = synth.workload(3, seq_lens=(100_000,) * 32)
+    _run(w, sampled=[(0, 3), (31, 6)])
+
+
 def test_fullsize_ragged_bs8_gqa8():
     print("case ragged bs8 up to 131k, GQA 8", flush=True)
     w = synth.workload(4)
