@@ -1214,20 +1214,46 @@ __device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, in
   }
 }
 
+// Sum / maximum over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or 16), every lane of
+// the group receiving it: quad swaps, then the half-row and row mirrors (DPP, no LDS traffic).
+// Every lane of the wavefront must be active.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
+  if constexpr (N >= 2) v += dpp_f<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_f<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_f<0x141>(v);
+  if constexpr (N >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 template <int D, int GQ, int HW>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, CacheWriteArgs cw) {
   constexpr int NT = kMergeThreads;
   constexpr int C4 = D / 4;           // float4 columns of a partial
   constexpr int TPH = NT / HW;        // threads per head
   constexpr int NG = TPH / C4;        // slot groups per head
-  constexpr int NP = NT / D;          // parts of an R_V row
+  constexpr int SUB = NT / (HW * D);  // combine: threads per output column (adjacent lanes)
+  constexpr int GPS = NG / SUB;       // slot groups per combine thread (4)
+  constexpr int NP = NT / D;          // un-rotation: threads per R_V row (adjacent lanes)
   constexpr int RP = D / NP;
-  constexpr int RS = D + 1;           // padded LDS row of R_V (conflict-free column walks)
+  constexpr int RS = D + NP;          // padded LDS row of R_V: the NP parts of a row walk distinct banks
+  constexpr int AS = D + 4;           // padded LDS row of a group's sums
+  static_assert(GPS * SUB == NG && NP * RP == D && SUB <= 16 && NP <= 16, "merge thread layout");
   __shared__ float rv_s[D * RS];
-  __shared__ float4 acc_h[NG][HW][C4], acc_w[NG][HW][C4];
+  __shared__ __attribute__((aligned(16))) float acc_h[NG][HW][AS];
+  __shared__ __attribute__((aligned(16))) float acc_w[NG][HW][AS];
   __shared__ float m_s[NG][HW], w_s[NG][HW];
-  __shared__ float hsum[HW][D];
-  __shared__ float part_s[NP][HW][D];
+  __shared__ float hsum[HW][D], wsum_s[HW][D], wtot_s[HW];
   const Dims& dm = a.dm;
   const int bk = blockIdx.x / (GQ / HW), h0 = HW * (blockIdx.x % (GQ / HW));
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
@@ -1255,61 +1281,69 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
     merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, 0, true);
     for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, base, false);
   }
-  const float m = ms_st.m, wsum = ms_st.wsum;
-  const float4 ah = ms_st.ah, aw = ms_st.aw;
-  acc_h[grp][hl][c4] = ah;
-  acc_w[grp][hl][c4] = aw;
+  *reinterpret_cast<float4*>(&acc_h[grp][hl][4 * c4]) = ms_st.ah;
+  *reinterpret_cast<float4*>(&acc_w[grp][hl][4 * c4]) = ms_st.aw;
   if (c4 == 0) {
-    m_s[grp][hl] = m;
-    w_s[grp][hl] = wsum;
+    m_s[grp][hl] = ms_st.m;
+    w_s[grp][hl] = ms_st.wsum;
   }
   __syncthreads();
-  for (int t = tid; t < HW * D; t += NT) {
-    const int h2 = t / D, ch = t % D;
+  // Combine the groups of each output column: lane group of SUB threads per column, thread `sub`
+  // taking groups sub, sub + SUB, ... (so the lanes of a half-wavefront read distinct banks); the
+  // maximum and the sums are folded across the SUB lanes.
+  {
+    const int col = tid / SUB, sub = tid % SUB;
+    const int h2 = col / D, ch = col % D;
+    float mg[GPS];
     float M = kNegInf;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg][h2]);
-    float hs = 0.0f;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const float e = m_s[gg][h2] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_s[gg][h2] - M);
-      hs = fmaf(e, reinterpret_cast<const float*>(&acc_h[gg][h2][0])[ch], hs);
+    for (int q = 0; q < GPS; ++q) {
+      mg[q] = m_s[sub + SUB * q][h2];
+      M = fmaxf(M, mg[q]);
     }
-    hsum[h2][ch] = hs;
+    M = lanes_max<SUB>(M);
+    float hs = 0.0f, ws = 0.0f, W = 0.0f;
+#pragma unroll
+    for (int q = 0; q < GPS; ++q) {
+      const int gg = sub + SUB * q;
+      const float e = mg[q] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mg[q] - M);
+      hs = fmaf(e, acc_h[gg][h2][ch], hs);
+      ws = fmaf(e, acc_w[gg][h2][ch], ws);
+      W = fmaf(e, w_s[gg][h2], W);
+    }
+    hs = lanes_sum<SUB>(hs);
+    ws = lanes_sum<SUB>(ws);
+    W = lanes_sum<SUB>(W);
+    if (sub == 0) {
+      hsum[h2][ch] = hs;
+      wsum_s[h2][ch] = ws;
+      if (ch == 0) wtot_s[h2] = W;
+    }
   }
   __syncthreads();
-  // un-rotation: thread (j, part) forms its part of out[h][j] = sum_i hsum[h][i] R_V[j][i]
+  // un-rotation: thread (j, part) forms part of out[h][j] = sum_i hsum[h][i] R_V[j][i] over
+  // i = part, part + NP, ...; the parts are folded across the NP lanes of row j
   {
-    const int j = tid % D, part = tid / D;
-    const float* rrow = rv_s + j * RS + part * RP;
+    const int j = tid / NP, part = tid % NP;
+    const float* rrow = rv_s + j * RS + part;
     float acc[HW];
 #pragma unroll
     for (int h2 = 0; h2 < HW; ++h2) acc[h2] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
-      const float rji = rrow[i];
+    for (int k = 0; k < RP; ++k) {
+      const float rji = rrow[NP * k];
 #pragma unroll
-      for (int h2 = 0; h2 < HW; ++h2) acc[h2] = fmaf(hsum[h2][part * RP + i], rji, acc[h2]);
+      for (int h2 = 0; h2 < HW; ++h2) acc[h2] = fmaf(hsum[h2][part + NP * k], rji, acc[h2]);
     }
 #pragma unroll
-    for (int h2 = 0; h2 < HW; ++h2) part_s[part][h2][j] = acc[h2];
-  }
-  __syncthreads();
-  for (int t = tid; t < HW * D; t += NT) {
-    const int h2 = t / D, ch = t % D;
-    float M = kNegInf;
+    for (int h2 = 0; h2 < HW; ++h2) acc[h2] = lanes_sum<NP>(acc[h2]);
+    if (part == 0) {
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg][h2]);
-    float oh = 0.0f, ow = 0.0f, W = 0.0f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) oh += part_s[p][h2][ch];
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const float e = m_s[gg][h2] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_s[gg][h2] - M);
-      ow = fmaf(e, reinterpret_cast<const float*>(&acc_w[gg][h2][0])[ch], ow);
-      W = fmaf(e, w_s[gg][h2], W);
+      for (int h2 = 0; h2 < HW; ++h2) {
+        const float W = wtot_s[h2];
+        a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h0 + h2) * D + j] = W > 0.0f ? (acc[h2] + wsum_s[h2][j]) / W : 0.0f;
+      }
     }
-    a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h0 + h2) * D + ch] = W > 0.0f ? (oh + ow) / W : 0.0f;
   }
   if (ring) {
     // the new token takes its window slot (the demoted token's ring slot, or position T), as the
