@@ -14,6 +14,7 @@ constexpr int kPage = 16;       // tokens per page
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kMetaBytes = 128; // 16 token slots x {sK, zK, sV, zV} bf16
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));

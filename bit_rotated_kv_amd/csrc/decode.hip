@@ -692,10 +692,13 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
-// fp16 high part in the low half, fp16 low part (W - high) in the high half
+// fp16 high part in the low half, fp16 low part (W - high) in the high half (built as a half pair,
+// so the two conversions write the two halves in place)
 __device__ __forceinline__ uint32_t split_f16(float w) {
-  const uint32_t h = f32_to_f16_bits(w);
-  return h | (f32_to_f16_bits(w - f16_bits_to_f32(h)) << 16);
+  half2_t v;
+  v.x = (_Float16)w;
+  v.y = (_Float16)(w - (float)v.x);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // QK^T of one page: rows = the 16 token slots, columns = query operand columns (high parts of
