@@ -92,26 +92,38 @@ def test_decode_reuses_a_dirty_workspace():
     assert int(ws[:4].view(torch.int32).item()) == 0
 
 
-def test_decode_skips_out_of_range_page_ids():
-    p = P.make_problem(small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)))
+@pytest.mark.parametrize("name,make,bad", [
+    # the history is processed in page pairs: a bad id as the second page of a pair, the first
+    # page, a whole pair, and a run across pairs; GQA 4, 8 and 2 (d = 64) take different paths
+    ("gq4-second", lambda: small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)), (3,)),
+    ("gq4-first", lambda: small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)), (2,)),
+    ("gq4-pair", lambda: small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)), (2, 3)),
+    ("gq4-run", lambda: small(2, batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=(900,)), (0, 1, 2, 5)),
+    ("gq8-first", lambda: small(4, batch=1, num_q_heads=16, num_kv_heads=2, seq_lens=(1000,)), (4,)),
+    ("d64-gq2", lambda: synth.workload(1, batch=1, num_q_heads=4, num_kv_heads=2, seq_lens=(1100,)), (1, 2)),
+])
+def test_decode_skips_out_of_range_page_ids(name, make, bad):
+    p = P.make_problem(make())
     cb, rk, rv = G.build_cache(p, oracle_written=True)
     pt = cb.page_table.clone()
-    cb.page_table[0, 3] = cb.layout.pool_pages          # one page id beyond the pool
+    for i in bad:
+        cb.page_table[0, i] = cb.layout.pool_pages + i     # page ids beyond the pool
     got, ws = G.decode(p, cb, rk, rv)
+    cb.page_table.copy_(pt)
     assert int(ws[:4].view(torch.int32).item()) & 1
     assert np.all(np.isfinite(got))
-    # the result equals attention without that page's 16 tokens
+    # the result equals attention without those pages' 16 tokens each
     c = p.caches[0]
     keep = np.ones(len(c.hist_pos), bool)
     order = np.argsort(c.hist_pos)
-    keep[order[48:64]] = False
-    for name in ("hist_pos", "hist_bits"):
-        setattr(c, name, getattr(c, name)[keep])
-    for name in ("k_codes", "v_codes", "k_sz", "v_sz"):
-        setattr(c, name, getattr(c, name)[:, keep])
+    for i in bad:
+        keep[order[16 * i:16 * (i + 1)]] = False
+    for attr in ("hist_pos", "hist_bits"):
+        setattr(c, attr, getattr(c, attr)[keep])
+    for attr in ("k_codes", "v_codes", "k_sz", "v_sz"):
+        setattr(c, attr, getattr(c, attr)[:, keep])
     ref = oracle.decode_attention(c, p.q[0])[None]
-    G.check_close(got, ref, tag="skip")
-    cb.page_table.copy_(pt)
+    G.check_close(got, ref, tag=f"skip {name}")
 
 
 @pytest.mark.parametrize("name,kw", [
