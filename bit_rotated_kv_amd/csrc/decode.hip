@@ -640,6 +640,14 @@ struct QPage {
 // Raw buffer descriptor of one page-head (gfx9 family: base, stride 0, size in bytes, word 3
 // 0x00020000): the page's loads then take the same per-lane byte offsets on every page, and a
 // byte past the page-head would read as zero instead of touching the next one.
+// Cache policy of the history page loads: nt (streaming) where every load instruction of a wavefront
+// covers whole 128-byte lines (INT2 codes at one 16-byte or 8-byte word per lane, and the metadata at
+// GQA 4 and 8). A page-head is read once per step, so it should not displace what the step re-reads
+// from the L2 (R_K, page tables, query operands). Where two instructions share lines (INT4 codes, the
+// metadata at other widths) a non-allocating load would fetch the line twice: default policy there.
+template <int BITS, int D, int GQ>
+constexpr int kPageLoadPolicy = (D * BITS / 128 <= 2 && (GQ == 4 || GQ == 8)) ? 2 : 0;
+
 template <int BITS, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head) {
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0, 4 * D * BITS + kMetaBytes,
@@ -649,16 +657,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head) {
 template <int BITS, int D, int GQ>
 __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head, int lane) {
   constexpr int CW = QPage<BITS, D, GQ>::CW;
+  constexpr int POL = kPageLoadPolicy<BITS, D, GQ>;
   const int g = lane / 16, c = lane % 16;
   const __amdgpu_buffer_rsrc_t r = qpage_rsrc<BITS, D>(head);
   if constexpr (CW == 1) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, POL);
     pr.kw[0] = v[0];
     pr.vw[0] = v[1];
   } else {
 #pragma unroll
     for (int j = 0; j < 2 * CW / 4; ++j) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 8 * CW + 16 * j, 0, 0);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 8 * CW + 16 * j, 0, POL);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * j + e;
@@ -669,16 +678,16 @@ __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head
   }
   constexpr int meta = 4 * D * BITS;
   if constexpr (GQ == 4) {
-    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(r, meta + 8 * (4 * g + c / 4), 0, 0);
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(r, meta + 8 * (4 * g + c / 4), 0, POL);
     pr.mt[0] = m[0];
     pr.mt[1] = m[1];
   } else if constexpr (GQ == 8) {
-    const u32x4_t m = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 8 * (4 * g + 2 * (c / 8)), 0, 0);
+    const u32x4_t m = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 8 * (4 * g + 2 * (c / 8)), 0, POL);
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr.mt[e] = m[e];
   } else {
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g, 0, 0);
-    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g + 16, 0, 0);
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g, 0, POL);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, meta + 32 * g + 16, 0, POL);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pr.mt[e] = a[e];
@@ -1344,7 +1353,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
 #pragma unroll
       for (int h2 = 0; h2 < HW; ++h2) {
         const float W = wtot_s[h2];
-        a.out[((size_t)b * dm.hq + (size_t)kv * GQ + h0 + h2) * D + j] = W > 0.0f ? (acc[h2] + wsum_s[h2][j]) / W : 0.0f;
+        const size_t o = ((size_t)b * dm.hq + (size_t)kv * GQ + h0 + h2) * D + j;
+        a.out[o] = W > 0.0f ? (acc[h2] + wsum_s[h2][j]) / W : 0.0f;
       }
     }
   }
