@@ -88,6 +88,10 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) 
   __shared__ int slot_s[CH];
   __shared__ int bits_s[CH];
   __shared__ int red[256];
+  // INT2-only caches: page ids of the run's pages, resolved once (-1: outside the table or not a
+  // valid INT2 page), so the stores of a chunk wait on no table load
+  constexpr int RUN_PAGES = kPrefillChunks * CH / kPage;
+  __shared__ int64_t page_s[RUN_PAGES];
   const Dims& dm = a.dm;
   const int kv = blockIdx.y, b = blockIdx.z / 2, sel = blockIdx.z % 2;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -114,6 +118,11 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) 
   };
   u32x4_t xw[XW];
   load_rows(chunk0, xw);
+  if (!dm.mixed && tid < RUN_PAGES) {
+    const int pi = CH * chunk0 / kPage + tid;
+    const int64_t page = pi < dm.pt_stride ? (int64_t)a.pt2[(size_t)b * dm.pt_stride + pi] : -1;
+    page_s[tid] = page_ok(page, 2, dm) ? page : -1;
+  }
   // INT4 tokens before the run (mixed caches): slots are ranks among tokens of the same width
   int c4 = 0;
   if (bitsrow) {
@@ -137,14 +146,20 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) 
       const int idx = tid + 256 * e;
       *reinterpret_cast<u32x4_t*>(&xs[idx / (D / 8)][8 * (idx % (D / 8))]) = xw[e];
     }
-    if (tid == 0) {
-      for (int i = 0; i < n; ++i) {
-        const int p = p0 + i;
-        const int bw = (bitsrow && bitsrow[p] == 4) ? 4 : 2;
-        bits_s[i] = bw;
-        slot_s[i] = bw == 4 ? c4 : (p - dm.sink) - c4;
-        c4 += bw == 4;
+    if (bitsrow) {
+      // mixed widths: slots are ranks among the tokens of the same width (one thread, in order)
+      if (tid == 0) {
+        for (int i = 0; i < n; ++i) {
+          const int p = p0 + i;
+          const int bw = bitsrow[p] == 4 ? 4 : 2;
+          bits_s[i] = bw;
+          slot_s[i] = bw == 4 ? c4 : (p - dm.sink) - c4;
+          c4 += bw == 4;
+        }
       }
+    } else if (tid < n) {
+      bits_s[tid] = 2;
+      slot_s[tid] = p0 + tid - dm.sink;
     }
     __syncthreads();
     if (ci + 1 < nchunks) load_rows(chunk + 1, xw);   // in flight during this chunk
@@ -227,24 +242,20 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) 
       // INT2, whole pages: slot = position - sink, so token i sits in page (CH*chunk + i)/16, slot i%16
       constexpr int CB = D * 2 / 32;   // bytes of one lane-chunk part (key or value)
       constexpr int NWL = CB / 4;      // words of it
-      const int32_t* pt = a.pt2 + (size_t)b * dm.pt_stride;
-      const int pg0 = CH * chunk / kPage;
+      const int64_t* pgs = page_s + CH * ci / kPage;   // the chunk's pages
       // (scale, zero) of each token
       for (int i = tid; i < n; i += 256) {
-        const int pi = pg0 + i / kPage;
-        if (pi >= dm.pt_stride) continue;
-        const int64_t page = pt[pi];
-        if (page_ok(page, 2, dm))
+        const int64_t page = pgs[i / kPage];
+        if (page >= 0)
           reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + 4 * D * 2)[2 * (i % kPage) + sel] = szs[i];
       }
       if (sel == 0) {
         // key words: (token, g, a), each owned by one slot
         for (int idx = tid; idx < n * 4 * NWL; idx += 256) {
           const int i = idx / (4 * NWL), g = (idx / NWL) % 4, aw = idx % NWL;
-          const int pi = pg0 + i / kPage, t = i % kPage;
-          if (pi >= dm.pt_stride) continue;
-          const int64_t page = pt[pi];
-          if (!page_ok(page, 2, dm)) continue;
+          const int t = i % kPage;
+          const int64_t page = pgs[i / kPage];
+          if (page < 0) continue;
           uint32_t w = 0;
           for (int k2 = 0; k2 < 2; ++k2)
             for (int m = 0; m < 4; ++m)
@@ -258,10 +269,8 @@ __global__ __launch_bounds__(256, 2) void prefill_hist_kernel(CacheWriteArgs a) 
         for (int idx = tid; idx < npg * 64 * NWL; idx += 256) {
           const int j = idx / (64 * NWL), r = idx % (64 * NWL);
           const int gg = r / (16 * NWL), c = (r / NWL) % 16, aw = r % NWL;
-          const int pi = pg0 + j;
-          if (pi >= dm.pt_stride) continue;
-          const int64_t page = pt[pi];
-          if (!page_ok(page, 2, dm)) continue;
+          const int64_t page = pgs[j];
+          if (page < 0) continue;
           uint32_t w = 0;
           for (int m = 0; m < 2; ++m)
             for (int hf = 0; hf < 2; ++hf) {
