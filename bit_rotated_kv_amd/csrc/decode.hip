@@ -26,16 +26,17 @@
 // token (rotated basis, history side) and the new token (window side). The window role skips the
 // ring slot of the demoted token, whose BF16 copy the merge then overwrites with the new token.
 //
-// Matrix-core mapping (v_mfma_f32_16x16x32_f16 for QK^T, v_mfma_f32_16x16x16_f16 for PV; BF16
+// Matrix-core mapping (v_mfma_f32_16x16x32_f16 for QK^T and, over a pair of pages, for PV; BF16
 // variants for the window): the 16 tokens of a page on the M rows of QK^T, the query heads of the
 // GQA group on the N columns. The QK^T result layout (lane l holds tokens 4*(l/16)+r of head
-// l%16) is exactly the A-operand layout of PV (rows = heads, k = tokens), so the softmax weights
-// never leave their lanes. Codes reach the matrix cores as fp16 subnormals: masking a code c at
-// bit p of a half-word gives the fp16 value c * 2^(p-24); the 2^(24-p) factor is folded into the
-// query operand (keys) or applied once to the accumulator (values). Query and softmax weights are
-// split into high + low fp16 parts (~22 significant bits); the pair sits in spare rows (PV) or in
-// a second MFMA (QK^T). Each wavefront keeps the next page's loads in flight while it computes
-// the current one, with all its page ids fetched by one vector load up front.
+// l%16) is the A-operand layout of PV (rows = heads, k = tokens); at GQA 4 and 8 the logits are
+// spread over the wavefront for the softmax and gathered back with DPP moves. Codes reach the
+// matrix cores as fp16 subnormals: masking a code c at bit p of a half-word gives the fp16 value
+// c * 2^(p-24); the 2^(24-p) factor is folded into the query operand (keys) or applied once to the
+// accumulator (values). Query and softmax weights are split into high + low fp16 parts (~22
+// significant bits); the two parts sit in spare columns (QK^T) and spare rows (PV). Each
+// wavefront keeps a six-page load ring (three page pairs), with all its page ids fetched by one
+// vector load up front.
 #include <type_traits>
 
 #include "common.hpp"
@@ -58,11 +59,6 @@ constexpr int kBf16Pipe = 2;   // BF16 pages in the per-wave load ring (8 KB eac
 
 __device__ __forceinline__ float4_t mfma32_f16(const u32x4_t& a, const half8_t& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4_t mfma16_f16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
-  const u32x2_t av = {a0, a1}, bv = {b0, b1};
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), __builtin_bit_cast(half4_t, bv), c,
-                                               0, 0, 0);
 }
 __device__ __forceinline__ float4_t mfma32_bf16(const u32x4_t& a, const u32x4_t& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
