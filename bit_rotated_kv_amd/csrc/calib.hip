@@ -5,7 +5,8 @@
 // R = U . H . P_br.
 //
 // Both are Gram matrices of rows (queries; rows of S V), formed on the matrix cores
-// (v_mfma_f32_32x32x16_bf16) in chunks of 256 rows whose partial sums are added in chunk order.
+// (v_mfma_f32_32x32x16_bf16) in chunks of whole 256-row sub-chunks whose partial sums are added in
+// chunk order.
 // bf16 rows are exact operands; fp32 rows (S V) are split into bf16 high and low parts and the
 // three leading products (hi.hi, hi.lo, lo.hi) are accumulated, for about 16 significant bits per
 // element. S V comes from a flash-attention pass: for a tile of 32 context keys, S^T = K Q^T on the
@@ -29,80 +30,136 @@ __device__ __forceinline__ float16v_t mfma32(const bf16x8_t& a, const bf16x8_t& 
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) { return (uint16_t)f32_to_bf16_bits(x); }
 
-constexpr int kGramRows = 256;   // rows per Gram workgroup
+constexpr int kGramRows = 256;   // rows per staged sub-chunk of a Gram workgroup
+constexpr int kGramTargetWorkgroups = 512;   // about two workgroups per compute unit
+
+// Sub-chunks of 256 rows per Gram workgroup: as few as keep the launch near two workgroups per CU
+// (fewer partial Gram matrices to write and add).
+inline int gram_subchunks(int hkv, int64_t rows) {
+  const int64_t subs = ((int64_t)hkv * ((rows + kGramRows - 1) / kGramRows) + kGramTargetWorkgroups - 1) /
+                       kGramTargetWorkgroups;
+  return (int)(subs < 1 ? 1 : (subs > 64 ? 64 : subs));
+}
+inline int64_t gram_chunks(int hkv, int64_t rows) {
+  const int64_t per = (int64_t)kGramRows * gram_subchunks(hkv, rows);
+  return (rows + per - 1) / per;
+}
 
 // ------------------------------------------------------------------ Gram of rows
-// Workgroup (chunk, kv): rows [256 chunk, 256 chunk + 256) of the kv-head's rows x[kv] ([R][D],
-// bf16 or fp32), transposed into LDS (channel-major), times themselves. Wavefront w < D/32 owns the
+// Workgroup (chunk, kv): rows [chunk * subs * 256, ...) of the kv-head's rows x[kv] ([R][D], bf16
+// or fp32), in sub-chunks of 256 rows: each is transposed into LDS (channel-major) and multiplied
+// by itself, the products accumulating in registers in row order. Wavefront w < D/32 owns the
 // output rows 32w .. 32w+31 (all D/32 column tiles). Writes the chunk's partial Gram (fp32 [D][D]).
 template <int D, bool F32>
-__global__ __launch_bounds__(256) void gram_kernel(const void* x, int64_t rows, float* partial) {
+__global__ __launch_bounds__(256) void gram_kernel(const void* x, int64_t rows, int subs, float* partial) {
   constexpr int NP = F32 ? 2 : 1;       // bf16 parts per element
   constexpr int RP = kGramRows + 8;     // padded row pitch of the transposed tile (bf16)
   constexpr int CT = D / 32;            // 32-wide tiles per dimension
+  constexpr int TPC = 256 / D;          // staging threads per channel
+  constexpr int NGI = kGramRows / 8 / TPC;   // 8-row groups per staging thread
+  constexpr int GB = NGI < 4 ? NGI : 4;      // groups whose loads are issued together
   __shared__ __attribute__((aligned(16))) uint16_t xt[NP][D][RP];
   const int chunk = blockIdx.x, kv = blockIdx.y;
   const int nchunks = gridDim.x;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int64_t r0 = (int64_t)chunk * kGramRows;
-  const int n = (int)min<int64_t>(kGramRows, rows - r0);
-  // transposed staging: thread (channel c, row-group phase) gathers 8 consecutive rows of its
-  // channel (each load instruction reads consecutive channels of one row) and stores them as one
-  // 16-byte piece of the channel-major tile
-  {
-    constexpr int TPC = 256 / D;          // threads per channel
-    const int c = tid % D, ph = tid / D;
-    for (int g = ph; g < kGramRows / 8; g += TPC) {
-      float v[8];
+  const int c = tid % D, ph = tid / D;
+  float16v_t acc[CT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * g + e;
-        float x32 = 0.0f;
-        if (r < n) {
-          const size_t at = ((size_t)kv * rows + r0 + r) * D + c;
-          if constexpr (F32)
-            x32 = static_cast<const float*>(x)[at];
-          else
-            x32 = bf16_bits_to_f32(static_cast<const uint16_t*>(x)[at]);
+  for (int t = 0; t < CT; ++t) acc[t] = float16v_t{};
+  for (int sc = 0; sc < subs; ++sc) {
+    const int64_t r0 = ((int64_t)chunk * subs + sc) * kGramRows;
+    if (r0 >= rows) break;
+    const int n = (int)min<int64_t>(kGramRows, rows - r0);
+    const size_t base = ((size_t)kv * rows + r0) * D + c;   // element index of (row r0, channel c)
+    if (sc > 0) __syncthreads();   // the previous sub-chunk's products have read the tile
+    if constexpr (!F32) {
+      // bf16 rows: thread (channel quad cq, phase ph) loads 8 bytes (4 channels) of each row of its
+      // 8-row groups, all loads in flight at once (a wavefront instruction reads whole row
+      // segments), then byte-permutes them into one 16-byte channel-major piece per channel
+      constexpr int NQ = D / 4, PH = 256 / NQ, GPT = kGramRows / 8 / PH;
+      const int cq = tid % NQ, rph = tid / NQ;
+      const uint16_t* xb = static_cast<const uint16_t*>(x) + ((size_t)kv * rows + r0) * D + 4 * cq;
+      u32x2_t w[GPT][8];
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * (rph + PH * gi) + e;
+          w[gi][e] = r < n ? *reinterpret_cast<const u32x2_t*>(xb + (uint32_t)(r * D)) : u32x2_t{0u, 0u};
         }
-        v[e] = x32;
-      }
-      u32x4_t hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t h0 = bf16_rne(v[2 * e]), h1 = bf16_rne(v[2 * e + 1]);
-        hi[e] = h0 | (h1 << 16);
-        if constexpr (F32)
-          lo[e] = (uint32_t)bf16_rne(v[2 * e] - bf16_bits_to_f32(h0)) |
-                  ((uint32_t)bf16_rne(v[2 * e + 1] - bf16_bits_to_f32(h1)) << 16);
+      for (int gi = 0; gi < GPT; ++gi) {
+        const int g = rph + PH * gi;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const uint32_t sel = (ch & 1) ? 0x07060302u : 0x05040100u;   // high or low half-words
+          u32x4_t piece;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            piece[k] = __builtin_amdgcn_perm(w[gi][2 * k + 1][ch / 2], w[gi][2 * k][ch / 2], sel);
+          *reinterpret_cast<u32x4_t*>(&xt[0][4 * cq + ch][8 * g]) = piece;
+        }
       }
-      *reinterpret_cast<u32x4_t*>(&xt[0][c][8 * g]) = hi;
-      if constexpr (F32) *reinterpret_cast<u32x4_t*>(&xt[NP - 1][c][8 * g]) = lo;
+    } else
+    // fp32 rows: thread (channel c, phase ph) gathers 8 consecutive rows of its channel per group
+    // (each load instruction reads consecutive channels of one row) and stores the bf16 high and low
+    // parts as 16-byte pieces of the channel-major tiles; the loads of GB groups go out before any
+    // is used
+    for (int gb = 0; gb < NGI; gb += GB) {
+      float v[GB][8];
+#pragma unroll
+      for (int gi = 0; gi < GB; ++gi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * (ph + TPC * (gb + gi)) + e;
+          float x32 = 0.0f;
+          if (r < n) {
+            if constexpr (F32)
+              x32 = static_cast<const float*>(x)[base + (uint32_t)(r * D)];
+            else
+              x32 = bf16_bits_to_f32(static_cast<const uint16_t*>(x)[base + (uint32_t)(r * D)]);
+          }
+          v[gi][e] = x32;
+        }
+#pragma unroll
+      for (int gi = 0; gi < GB; ++gi) {
+        const int g = ph + TPC * (gb + gi);
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t h0 = bf16_rne(v[gi][2 * e]), h1 = bf16_rne(v[gi][2 * e + 1]);
+          hi[e] = h0 | (h1 << 16);
+          if constexpr (F32)
+            lo[e] = (uint32_t)bf16_rne(v[gi][2 * e] - bf16_bits_to_f32(h0)) |
+                    ((uint32_t)bf16_rne(v[gi][2 * e + 1] - bf16_bits_to_f32(h1)) << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(&xt[0][c][8 * g]) = hi;
+        if constexpr (F32) *reinterpret_cast<u32x4_t*>(&xt[NP - 1][c][8 * g]) = lo;
+      }
+    }
+    __syncthreads();
+    if (wave < CT) {
+      const int m = 32 * wave + lane % 32;
+      for (int kk = 0; kk < kGramRows / 16; ++kk) {
+        const int k0 = 16 * kk + 8 * (lane / 32);
+        bf16x8_t a[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) a[p] = *reinterpret_cast<const bf16x8_t*>(&xt[p][m][k0]);
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          const int nn = 32 * t + lane % 32;
+          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&xt[0][nn][k0]);
+          if constexpr (F32) {
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&xt[1][nn][k0]);
+            acc[t] = mfma32(a[1], bh, acc[t]);   // lo . hi
+            acc[t] = mfma32(a[0], bl, acc[t]);   // hi . lo
+          }
+          acc[t] = mfma32(a[0], bh, acc[t]);     // hi . hi
+        }
+      }
     }
   }
-  __syncthreads();
   if (wave < CT) {
-    float16v_t acc[CT];
-#pragma unroll
-    for (int t = 0; t < CT; ++t) acc[t] = float16v_t{};
-    const int m = 32 * wave + lane % 32;
-    for (int kk = 0; kk < kGramRows / 16; ++kk) {
-      const int k0 = 16 * kk + 8 * (lane / 32);
-      bf16x8_t a[NP];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) a[p] = *reinterpret_cast<const bf16x8_t*>(&xt[p][m][k0]);
-#pragma unroll
-      for (int t = 0; t < CT; ++t) {
-        const int nn = 32 * t + lane % 32;
-        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&xt[0][nn][k0]);
-        if constexpr (F32) {
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&xt[1][nn][k0]);
-          acc[t] = mfma32(a[1], bh, acc[t]);   // lo . hi
-          acc[t] = mfma32(a[0], bl, acc[t]);   // hi . lo
-        }
-        acc[t] = mfma32(a[0], bh, acc[t]);     // hi . hi
-      }
-    }
     float* out = partial + ((size_t)kv * nchunks + chunk) * D * D;
 #pragma unroll
     for (int t = 0; t < CT; ++t)
@@ -120,6 +177,7 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* partial, 
   if (e >= D * D) return;
   const float* p = partial + (size_t)kv * nchunks * D * D + e;
   float s = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) s += p[(size_t)c * D * D];
   cov[(size_t)kv * D * D + e] = s * inv_n;
 }
@@ -127,8 +185,9 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* partial, 
 template <int D, bool F32>
 hipError_t launch_gram(const void* x, int hkv, int64_t rows, float inv_n, float* partial, float* cov,
                        hipStream_t stream) {
-  const int nchunks = (int)((rows + kGramRows - 1) / kGramRows);
-  hipLaunchKernelGGL((gram_kernel<D, F32>), dim3(nchunks, hkv), dim3(256), 0, stream, x, rows, partial);
+  const int subs = gram_subchunks(hkv, rows);
+  const int nchunks = (int)gram_chunks(hkv, rows);
+  hipLaunchKernelGGL((gram_kernel<D, F32>), dim3(nchunks, hkv), dim3(256), 0, stream, x, rows, subs, partial);
   hipLaunchKernelGGL((gram_reduce_kernel<D>), dim3((D * D + 255) / 256, hkv), dim3(256), 0, stream, partial, nchunks,
                      inv_n, cov);
   return hipGetLastError();
@@ -254,8 +313,7 @@ __global__ __launch_bounds__(256) void calib_sv_kernel(const uint16_t* q, const 
 }
 
 size_t gram_partial_bytes(int hkv, int64_t rows, int d) {
-  const int64_t nchunks = (rows + kGramRows - 1) / kGramRows;
-  return (size_t)hkv * nchunks * d * d * 4;
+  return (size_t)hkv * gram_chunks(hkv, rows) * d * d * 4;
 }
 
 bool supported(int d) { return d == 64 || d == 128; }
