@@ -228,25 +228,57 @@ __global__ __launch_bounds__(256) void calib_sv_kernel(const uint16_t* q, const 
 #pragma unroll
   for (int t = 0; t < CT; ++t) o[t] = float16v_t{};
   float m_run = -__builtin_huge_valf(), l_run = 0.0f;
-  for (int k0 = 0; k0 < nctx; k0 += 32) {
-    // K tile: 16-byte pieces; V tile channel-major: thread (channel, key group) gathers 8 keys
-    for (int idx = tid; idx < 32 * D / 8; idx += 256) {
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      u32x4_t w = {0, 0, 0, 0};
-      if (k0 + r < nctx) w = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + r) * D + 8 * c8);
-      *reinterpret_cast<u32x4_t*>(&ks[r][8 * c8]) = w;
+  // A tile's loads go out two tiles ahead into registers (K: 16-byte pieces; V: thread (channel, key
+  // group) gathers 8 keys of one channel), and are written to LDS when the tile's turn comes.
+  constexpr int KPT = 32 * D / 8 / 256, VIT = 4 * D / 256;
+  struct TileRegs {
+    u32x4_t kw[KPT];
+    u32x4_t vw[VIT];
+  };
+  auto fetch = [&](int k0, TileRegs& R) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = tid + 256 * i, r = idx / (D / 8), c8 = idx % (D / 8);
+      R.kw[i] = u32x4_t{0, 0, 0, 0};
+      if (k0 + r < nctx) R.kw[i] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + r) * D + 8 * c8);
     }
-    for (int idx = tid; idx < 4 * D; idx += 256) {
-      const int c = idx % D, g = idx / D;
-      u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+      const int idx = tid + 256 * i, c = idx % D, g = idx / D;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r0 = k0 + 8 * g + 2 * e;
         const uint32_t lo = r0 < nctx ? vb[(size_t)r0 * D + c] : 0u;
         const uint32_t hi = r0 + 1 < nctx ? vb[(size_t)(r0 + 1) * D + c] : 0u;
-        w[e] = lo | (hi << 16);
+        R.vw[i][e] = lo | (hi << 16);
       }
-      *reinterpret_cast<u32x4_t*>(&vt[c][8 * g]) = w;
+    }
+  };
+  auto stage = [&](const TileRegs& R) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = tid + 256 * i, r = idx / (D / 8), c8 = idx % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&ks[r][8 * c8]) = R.kw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+      const int idx = tid + 256 * i, c = idx % D, g = idx / D;
+      *reinterpret_cast<u32x4_t*>(&vt[c][8 * g]) = R.vw[i];
+    }
+  };
+  TileRegs ra, rb;
+  fetch(0, ra);
+  fetch(32, rb);
+  for (int k0 = 0; k0 < nctx; k0 += 32) {
+    // tiles alternate between the two register sets (k0 / 32 even: ra); the set just written to
+    // LDS takes the loads of the tile two ahead
+    const bool even = ((k0 / 32) & 1) == 0;
+    if (even) {
+      stage(ra);
+      fetch(k0 + 64, ra);
+    } else {
+      stage(rb);
+      fetch(k0 + 64, rb);
     }
     __syncthreads();
     float16v_t s = {};
