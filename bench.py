@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-bs32", action="store_true", help="skip the batch-32 companion measurements")
     ap.add_argument("--no-bs32-100k", action="store_true", help="skip the batch-32 x 100K-context measurement")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the decode-only GQA-8 ragged and mixed INT2/INT4 measurements")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-codebook", action="store_true", help="skip the Lloyd-Max codebook variant")
@@ -445,6 +447,91 @@ def time_bs32_100k(args):
     return r
 
 
+def time_decode_workload(w, steps, warmup):
+    """Decode attention alone (no demote) over a whole workload batch at its own lengths: the
+    ragged GQA-8 batch (workload 4) or the mixed INT2/INT4 batch (workload 5), whose token widths
+    come from the library's class allocation and tag routing. K/V are GPU draws of the workload's
+    channel law; cache copies rotate so the Infinity Cache cannot serve repeats."""
+    import torch
+    import bit_rotated_kv_amd as brk
+    import synth
+    B, hq, hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens = [int(T) for T in w.seq_lens]
+    tmax = max(lens)
+    rk, rv = rotations(w)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    hist = [max(0, T - 320) for T in lens]
+    tb, n4 = None, [0] * B
+    if w.mixed:
+        d2, d4 = synth.tag_sensitivity(w)
+        class_bits, _ = brk.allocate_bits(d2, d4, synth.tag_nominal_counts(w), w.bit_budget, "greedy")
+        tags = np.zeros((B, tmax), np.int32)
+        for b_ in range(B):
+            tags[b_, :lens[b_]] = synth.tag_classes(w, b_, lens[b_])
+        tb = brk.route_tokens(seq, torch.from_numpy(tags).cuda(), class_bits)
+        tbn = tb.cpu().numpy()
+        n4 = [int((tbn[b_, 64:64 + hist[b_]] == 4).sum()) for b_ in range(B)]
+    n2 = [hist[b_] - n4[b_] for b_ in range(B)]
+    pages2 = max((n + PAGE - 1) // PAGE for n in n2) + 1
+    pages4 = max((n + PAGE - 1) // PAGE for n in n4) + 1 if w.mixed else 0
+    order2 = synth.page_permutation(w.seed, B * pages2)
+    order4 = synth.page_permutation(w.seed + 1, B * pages4) if w.mixed else None
+    cb = brk.allocate_cache(hq, hkv, d, B, tmax, mixed=w.mixed, pages2_per_request=pages2,
+                            pages4_per_request=pages4, page_order2=order2, page_order4=order4)
+    K, V, q = workload_inputs(w, B, tmax, fast=True)
+    cb.seq_len.copy_(seq)
+    brk.kv_prefill(cb.layout, cb.seq_len, K, V, rk, rv, cb.pool, cb.page_table, cb.window, token_bits=tb,
+                   page_table4=cb.page_table4, n_int4_out=cb.n_int4)
+    del K, V
+    torch.cuda.synchronize()
+    int2 = hkv * sum(n2) * 72
+    int4 = hkv * sum(n4) * 136
+    bf16 = hkv * sum(min(T, 320) for T in lens) * 2 * d * 2
+    nbytes = int2 + int4 + bf16
+    copies = max(2, math.ceil(1.0e9 / nbytes))
+    pools = [cb.pool] + [cb.pool.clone() for _ in range(copies - 1)]
+    windows = [cb.window] + [cb.window.clone() for _ in range(copies - 1)]
+    ws = torch.zeros(brk.decode_workspace_bytes(cb.layout, B, tmax), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+
+    def call(i, events=None):
+        brk.decode_attn(cb.layout, q, cb.seq_len, windows[i % copies], pools[i % copies], cb.page_table, rk, rv, ws,
+                        tmax, out=out, n_int4=cb.n_int4, page_table4=cb.page_table4, events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            call(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        for x in e:
+            x.record()        # creates the event
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(1e8))
+    for i in range(steps):
+        call(i, evs[i])
+    torch.cuda.synchronize()
+    split = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in range(steps)]))
+    r = {"workload": f"{w.name}: batch {B}, lengths {min(lens)}..{tmax}, {hq}q/{hkv}kv heads, d {d}, decode only",
+         "us_per_call": round(ms * 1e3, 2), "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+         "split_us": round(split * 1e3, 2), "split_frac": round(nbytes / (split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "bytes": {"int2_history": int2, "int4_history": int4, "bf16_window": bf16, "total": nbytes},
+         "cache_copies": copies, "launch": "graph"}
+    del pools, windows, cb
+    torch.cuda.empty_cache()
+    return r
+
+
 # ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_traffic.txt")
 
@@ -616,6 +703,10 @@ def main():
         if not args.no_bs32_100k:
             log("batch-32 x 100K-context measurement")
             result["bs32_100k"] = time_bs32_100k(args)
+    if not args.no_other_workloads:
+        log("decode-only measurements: ragged GQA-8 batch, mixed INT2/INT4 batch")
+        result["gqa8_ragged"] = time_decode_workload(synth.workload(4), args.steps, args.warmup)
+        result["mixed_int2_int4"] = time_decode_workload(synth.workload(5), args.steps, args.warmup)
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
