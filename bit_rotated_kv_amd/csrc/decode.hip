@@ -37,6 +37,8 @@
 // significant bits); the two parts sit in spare columns (QK^T) and spare rows (PV). Each
 // wavefront keeps a six-page load ring (three page pairs), with all its page ids fetched by one
 // vector load up front.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -1510,18 +1512,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
       hipLaunchKernelGGL((q_prologue_kernel<D, GQ, false>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
                          stream, a);
   }
-  mark(1);
   const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-#ifndef OSCAR_SPLIT_LDS_PAD
-#define OSCAR_SPLIT_LDS_PAD 0
-#endif
-  if (a.codebook)
-    hipLaunchKernelGGL((split_kernel<D, GQ, true>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream,
-                       a, cw);
-  else
-    hipLaunchKernelGGL((split_kernel<D, GQ, false>), dim3(nblk), dim3(kSplitWaves * kWave), OSCAR_SPLIT_LDS_PAD, stream,
-                       a, cw);
-  mark(2);
+  // the timing variant brackets the split kernel with the dispatch's own start and stop stamps
+  // (events 1 and 2), so its interval is the kernel's execution time
+  const dim3 grid(nblk), block(kSplitWaves * kWave);
+  if (a.events) {
+    if (a.codebook)
+      hipExtLaunchKernelGGL((split_kernel<D, GQ, true>), grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
+    else
+      hipExtLaunchKernelGGL((split_kernel<D, GQ, false>), grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
+  } else if (a.codebook) {
+    hipLaunchKernelGGL((split_kernel<D, GQ, true>), grid, block, 0, stream, a, cw);
+  } else {
+    hipLaunchKernelGGL((split_kernel<D, GQ, false>), grid, block, 0, stream, a, cw);
+  }
   const int groups = dm.batch * dm.hkv;
   if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {
     hipLaunchKernelGGL((merge_kernel<D, GQ, 1>), dim3(groups * GQ), dim3(kMergeThreads), 0, stream, a, cw);
