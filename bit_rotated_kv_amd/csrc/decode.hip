@@ -1118,6 +1118,8 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
+  // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
+  __syncthreads();
   workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
                                                              a.ws.part_lse + pbase * GQ);
 }
@@ -1128,14 +1130,22 @@ template <int D, int GQ>
 union alignas(16) SplitScratch {
   HistQueryLds<D, GQ> hist;
   StepLds<D, GQ> step;
+  float o[kSplitWaves][2 * GQ][D];   // workgroup merge of the history and window roles
 };
 
-// CB: the INT2 history uses the codebook table of the decode arguments.
-template <int D, int GQ, bool CB>
-__global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a, CacheWriteArgs cw) {
-  __shared__ float o_lds[kSplitWaves][2 * GQ][D];
+// Workgroups of a split launch that a compute unit should hold: three at GQA 8 in an INT2-only
+// cache (the register count is then bounded to fit), else what the resources give.
+template <int GQ, bool MIXED>
+constexpr int kSplitMinBlocks = (GQ == 8 && !MIXED) ? 3 : 1;
+
+// CB: the INT2 history uses the codebook table of the decode arguments. MIXED: the cache has INT4
+// pages (an INT2-only launch carries no INT4 role, which keeps its register count down).
+template <int D, int GQ, bool CB, bool MIXED>
+__global__ __launch_bounds__(kSplitWaves * kWave, (kSplitMinBlocks<GQ, MIXED>)) void split_kernel(DecodeArgs a,
+                                                                                               CacheWriteArgs cw) {
   __shared__ float st_lds[kSplitWaves][3][8];
   __shared__ SplitScratch<D, GQ> scr;
+  float (*o_lds)[2 * GQ][D] = scr.o;
   // Long roles first: the history workgroups take the low indices, so the dispatcher starts them
   // first, and the shorter window and step workgroups fill the compute units that free up while
   // the last history workgroups run.
@@ -1144,7 +1154,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(DecodeArgs a
   const int bid = blockIdx.x;
   if (bid < n_int2) {
     hist_role<2, D, GQ, CB>(a, bid, o_lds, st_lds, scr.hist);
-  } else if (bid < n_hist) {
+  } else if (MIXED && bid < n_hist) {
     hist_role<4, D, GQ>(a, bid - n_int2, o_lds, st_lds, scr.hist);
   } else {
     window_role<D, GQ>(a, cw, bid - n_hist, o_lds, st_lds, scr.step);
@@ -1516,15 +1526,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
   // the timing variant brackets the split kernel with the dispatch's own start and stop stamps
   // (events 1 and 2), so its interval is the kernel's execution time
   const dim3 grid(nblk), block(kSplitWaves * kWave);
-  if (a.events) {
-    if (a.codebook)
-      hipExtLaunchKernelGGL((split_kernel<D, GQ, true>), grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
-    else
-      hipExtLaunchKernelGGL((split_kernel<D, GQ, false>), grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
-  } else if (a.codebook) {
-    hipLaunchKernelGGL((split_kernel<D, GQ, true>), grid, block, 0, stream, a, cw);
+  auto go = [&](auto kernel) {
+    if (a.events) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
+    else hipLaunchKernelGGL(kernel, grid, block, 0, stream, a, cw);
+  };
+  if (dm.mixed) {
+    if (a.codebook) go(split_kernel<D, GQ, true, true>);
+    else go(split_kernel<D, GQ, false, true>);
   } else {
-    hipLaunchKernelGGL((split_kernel<D, GQ, false>), grid, block, 0, stream, a, cw);
+    if (a.codebook) go(split_kernel<D, GQ, true, false>);
+    else go(split_kernel<D, GQ, false, false>);
   }
   const int groups = dm.batch * dm.hkv;
   if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {
