@@ -647,7 +647,7 @@ def main():
         "eager_step_us_p10_p50_p90": setup.step_spread_us,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "split_kernel<128,4,false> (BF16 window + INT2 history split-K + step workgroups, "
+                     "kernel": "split_kernel<128,4,false,false> (BF16 window + INT2 history split-K + step workgroups, "
                                "one launch)",
                      "bytes_per_launch": int2 + bf16},
         "setup_s": round(setup_s, 1),
