@@ -296,8 +296,19 @@ __device__ __forceinline__ uint32_t cb_code(float x, const QuantGrid& g, const C
 }
 
 // ------------------------------------------------------------------ history code placement
-// Word index (within the lane chunk) and bit position of a key / value code, for page slot t and
-// channel ch (the layouts documented in oscar.h).
+// Byte offset of lane l's key / value part in a history page-head (cb = bytes of one part,
+// d * bits / 32). INT2: a lane's two parts sit together (a 2*cb-byte lane chunk). INT4: the 64 key
+// parts, then the 64 value parts, so that at d <= 128 one load instruction of a wavefront reads
+// consecutive whole 128-byte lines of either part.
+__host__ __device__ inline size_t key_part_offset(int bits, int cb, int lane) {
+  return bits == 2 ? (size_t)lane * 2 * cb : (size_t)lane * cb;
+}
+__host__ __device__ inline size_t value_part_offset(int bits, int cb, int lane) {
+  return bits == 2 ? (size_t)lane * 2 * cb + cb : (size_t)(64 + lane) * cb;
+}
+
+// Word index (within the lane's key or value part) and bit position of a key / value code, for page
+// slot t and channel ch (the layouts documented in oscar.h).
 struct CodePos {
   int lane, word, bit;
 };

@@ -630,7 +630,7 @@ struct Redist {
 
 template <int BITS, int D, int GQ>
 struct QPage {
-  static constexpr int CW = D * BITS / 128;  // 32-bit words of one lane-chunk part
+  static constexpr int CW = D * BITS / 128;  // 32-bit words of one lane's key or value part
   uint32_t kw[CW], vw[CW];
   uint32_t mt[Redist<GQ>::meta_words];
 };
@@ -639,12 +639,13 @@ struct QPage {
 // 0x00020000): the page's loads then take the same per-lane byte offsets on every page, and a
 // byte past the page-head would read as zero instead of touching the next one.
 // Cache policy of the history page loads: nt (streaming) where every load instruction of a wavefront
-// covers whole 128-byte lines (INT2 codes at one 16-byte or 8-byte word per lane, and the metadata at
-// GQA 4 and 8). A page-head is read once per step, so it should not displace what the step re-reads
-// from the L2 (R_K, page tables, query operands). Where two instructions share lines (INT4 codes, the
+// covers whole 128-byte lines: the codes at d <= 128 (an INT2 lane chunk of 8 or 16 bytes; an INT4
+// key or value part of 8 or 16 bytes, the parts of all lanes consecutive) and the metadata at GQA 4
+// and 8. A page-head is read once per step, so it should not displace what the step re-reads from
+// the L2 (R_K, page tables, query operands). Where two instructions share lines (d = 256, the
 // metadata at other widths) a non-allocating load would fetch the line twice: default policy there.
 template <int BITS, int D, int GQ>
-constexpr int kPageLoadPolicy = (D * BITS / 128 <= 2 && (GQ == 4 || GQ == 8)) ? 2 : 0;
+constexpr int kPageLoadPolicy = (D <= 128 && (GQ == 4 || GQ == 8)) ? 2 : 0;
 
 template <int BITS, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head) {
@@ -658,11 +659,11 @@ __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head
   constexpr int POL = kPageLoadPolicy<BITS, D, GQ>;
   const int g = lane / 16, c = lane % 16;
   const __amdgpu_buffer_rsrc_t r = qpage_rsrc<BITS, D>(head);
-  if constexpr (CW == 1) {
+  if constexpr (BITS == 2 && CW == 1) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, POL);
     pr.kw[0] = v[0];
     pr.vw[0] = v[1];
-  } else {
+  } else if constexpr (BITS == 2) {
 #pragma unroll
     for (int j = 0; j < 2 * CW / 4; ++j) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 8 * CW + 16 * j, 0, POL);
@@ -671,6 +672,24 @@ __device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head
         const int w = 4 * j + e;
         if (w < CW) pr.kw[w] = v[e];
         else pr.vw[w - CW] = v[e];
+      }
+    }
+  } else if constexpr (CW == 2) {  // INT4: key parts of all lanes, then value parts
+    const u32x2_t k = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, POL);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, 64 * 8 + lane * 8, 0, POL);
+    pr.kw[0] = k[0];
+    pr.kw[1] = k[1];
+    pr.vw[0] = v[0];
+    pr.vw[1] = v[1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      const u32x4_t k = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 4 * CW + 16 * j, 0, POL);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, 64 * 4 * CW + lane * 4 * CW + 16 * j, 0, POL);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr.kw[4 * j + e] = k[e];
+        pr.vw[4 * j + e] = v[e];
       }
     }
   }
@@ -1538,13 +1557,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
     else go(split_kernel<D, GQ, false, false>);
   }
   const int groups = dm.batch * dm.hkv;
-  if (GQ >= 2 && groups * GQ <= kMergeWorkgroupsPerRound) {
-    hipLaunchKernelGGL((merge_kernel<D, GQ, 1>), dim3(groups * GQ), dim3(kMergeThreads), 0, stream, a, cw);
-  } else if (GQ >= 4 && groups * GQ / 2 <= kMergeWorkgroupsPerRound) {
-    hipLaunchKernelGGL((merge_kernel<D, GQ, 2>), dim3(groups * GQ / 2), dim3(kMergeThreads), 0, stream, a, cw);
-  } else {
-    hipLaunchKernelGGL((merge_kernel<D, GQ, GQ>), dim3(groups), dim3(kMergeThreads), 0, stream, a, cw);
+  bool merged = false;
+  if constexpr (GQ >= 2) {
+    if (groups * GQ <= kMergeWorkgroupsPerRound) {
+      hipLaunchKernelGGL((merge_kernel<D, GQ, 1>), dim3(groups * GQ), dim3(kMergeThreads), 0, stream, a, cw);
+      merged = true;
+    }
   }
+  if constexpr (GQ >= 4) {
+    if (!merged && groups * GQ / 2 <= kMergeWorkgroupsPerRound) {
+      hipLaunchKernelGGL((merge_kernel<D, GQ, 2>), dim3(groups * GQ / 2), dim3(kMergeThreads), 0, stream, a, cw);
+      merged = true;
+    }
+  }
+  if (!merged) hipLaunchKernelGGL((merge_kernel<D, GQ, GQ>), dim3(groups), dim3(kMergeThreads), 0, stream, a, cw);
   mark(3);
   return hipGetLastError();
 }

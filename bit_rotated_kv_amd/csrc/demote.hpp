@@ -19,7 +19,7 @@ __device__ inline uint8_t* page_head_mut(uint8_t* pool, int64_t page, int kv, co
 
 // Key codes of slot t: whole 32-bit words owned by the slot (plain stores).
 __device__ inline void store_key_codes(uint8_t* ph, int d, int bits, int t, const uint8_t* cs, int tid, int nthr) {
-  const int cb = d * bits / 32;  // bytes of the key part of a lane chunk
+  const int cb = d * bits / 32;  // bytes of one lane's key part
   const int nwl = cb / 4;
   for (int idx = tid; idx < 4 * nwl; idx += nthr) {
     const int g = idx / nwl, a = idx % nwl;
@@ -38,7 +38,7 @@ __device__ inline void store_key_codes(uint8_t* ph, int d, int bits, int t, cons
           w |= (uint32_t)cs[ch] << (4 * m + 16 * hf);
         }
     }
-    reinterpret_cast<uint32_t*>(ph + (size_t)(16 * g + t) * 2 * cb)[a] = w;
+    reinterpret_cast<uint32_t*>(ph + key_part_offset(bits, cb, 16 * g + t))[a] = w;
   }
 }
 
@@ -66,7 +66,7 @@ __device__ inline void store_value_codes(uint8_t* ph, int d, int bits, int t, co
         val |= (uint32_t)cs[ch] << bit;
       }
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(ph + (size_t)(16 * g + c) * 2 * cb + cb) + a;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(ph + value_part_offset(bits, cb, 16 * g + c)) + a;
     atomicAnd(dst, ~mask);
     atomicOr(dst, val);
   }

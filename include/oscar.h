@@ -35,15 +35,18 @@
  * History page ("page-head" = one page of one kv-head; a page holds 16 token slots).
  *   INT2 page-head, d = head_dim: 64 lane chunks of (K: d/16 bytes, then V: d/16 bytes), then
  *   16 x 8 bytes of metadata. Total 4*d*2 + 128 bytes (1152 at d = 128, 640 at d = 64).
- *   INT4 page-head: 64 lane chunks of (K: d/8 bytes, V: d/8 bytes), then 128 bytes of
- *   metadata. Total 4*d*4 + 128 bytes (2176 at d = 128).
+ *   INT4 page-head: 64 key parts of d/8 bytes (lane order), then 64 value parts of d/8 bytes,
+ *   then 128 bytes of metadata: lane L's key part at byte L*d/8, its value part at (64 + L)*d/8
+ *   (so a 16-byte load per lane of either part reads 1 KB of whole lines at d = 128).
+ *   Total 4*d*4 + 128 bytes (2176 at d = 128).
  *   A page = num_kv_heads consecutive page-heads. Page id p < int4_page_offset is an INT2 page
  *   at pool + p*P2; page id p >= int4_page_offset is an INT4 page at
  *   pool + int4_page_offset*P2 + (p - int4_page_offset)*P4 (P2, P4 = page bytes). A single
  *   compare of the id decides the width, as in the TriAxialKV dual pool.
  *   Metadata of token slot t (0..15): bf16 {sK, zK, sV, zV} at byte 8*t of the metadata block,
  *   where (s, z) are the group's scale and zero: x_hat = s*code + z (rotated basis).
- *   Codes are 32-bit little-endian words inside each lane chunk (word a = bytes 4a..4a+3):
+ *   Codes are 32-bit little-endian words inside each lane's key or value part (word a = bytes
+ *   4a..4a+3 of the part):
  *   INT2 key of slot t, channel ch:  kk = ch/32, g = (ch%32)/8, m = (ch%8)/2, hf = ch%2;
  *       lane L = 16*g + t, word a = kk/2, bit 8*(kk%2) + 2*m + 16*hf.
  *   INT2 value of slot t, channel ch: nb = ch/16, c = ch%16, g = t/4, m = (t%4)/2, hf = t%2;

@@ -30,7 +30,8 @@ def key_offsets(d: int, bits: int):
         word, bit = kk // 2, 8 * (kk % 2) + 2 * m + 16 * hf
     else:
         word, bit = kk, 4 * m + 16 * hf
-    byte = lane * 2 * cb + 4 * word + bit // 8
+    part = lane * 2 * cb if bits == 2 else lane * cb     # INT4: all key parts come first
+    byte = part + 4 * word + bit // 8
     return np.broadcast_to(byte, (PAGE, d)), np.broadcast_to(bit % 8, (PAGE, d))
 
 
@@ -44,7 +45,8 @@ def value_offsets(d: int, bits: int):
         word, bit = nb // 4, 2 * (nb % 4) + 8 * m + 16 * hf
     else:
         word, bit = nb // 2, 4 * (nb % 2) + 8 * m + 16 * hf
-    byte = lane * 2 * cb + cb + 4 * word + bit // 8
+    part = lane * 2 * cb + cb if bits == 2 else (64 + lane) * cb
+    byte = part + 4 * word + bit // 8
     return np.broadcast_to(byte, (PAGE, d)), np.broadcast_to(bit % 8, (PAGE, d))
 
 

@@ -15,17 +15,32 @@ def test_code_positions_are_a_bijection(d, bits):
     assert used.min() == 1 and used.max() == 1        # every code bit exactly once, codes region full
 
 
-@pytest.mark.parametrize("d,bits", [(64, 2), (128, 2), (128, 4)])
-def test_key_lane_chunk_belongs_to_one_slot(d, bits):
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 2), (64, 4), (128, 4)])
+def test_key_lane_part_belongs_to_one_slot(d, bits):
     byte, _ = layout_ref.key_offsets(d, bits)
     cb = d * bits // 32
-    lane = byte // (2 * cb)
-    assert np.all((byte % (2 * cb)) < cb)             # key part of the chunk
+    if bits == 2:                                     # lane chunks: key part, then value part
+        lane = byte // (2 * cb)
+        assert np.all((byte % (2 * cb)) < cb)
+    else:                                             # INT4: the 64 key parts, then the 64 value parts
+        lane = byte // cb
+        assert np.all(byte < 64 * cb)
     for t in range(16):
         assert set(np.unique(lane[t] % 16)) == {t}    # lane 16g+t holds slot t only
 
 
-@pytest.mark.parametrize("d,bits", [(64, 2), (128, 2), (128, 4)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int4_value_parts_follow_the_key_parts(d):
+    byte, _ = layout_ref.value_offsets(d, 4)
+    cb = d * 4 // 32
+    assert np.all(byte >= 64 * cb) and np.all(byte < 128 * cb)
+    lane = byte // cb - 64
+    nb_c = np.arange(d) % 16                          # value lane 16*(t/4) + ch%16
+    for t in range(16):
+        assert np.array_equal(lane[t], 16 * (t // 4) + nb_c)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 2), (64, 4), (128, 4)])
 def test_pack_round_trip(d, bits):
     r = np.random.default_rng(3)
     ck = r.integers(0, 1 << bits, (16, d)).astype(np.uint8)
