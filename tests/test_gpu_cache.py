@@ -20,6 +20,8 @@ CASES = {
                                                cal_tokens=1500, cal_ctx=512),
     "d128-mixed": lambda: synth.workload(5, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(1500, 900),
                                          cal_tokens=1500, cal_ctx=512),
+    "d64-mixed": lambda: synth.workload(5, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, group_size=64,
+                                        seq_lens=(1300, 800), cal_tokens=1500, cal_ctx=512),
 }
 
 

@@ -31,6 +31,9 @@ DECODE = {
     "edge-lengths": lambda: small(2, batch=16, num_q_heads=4, num_kv_heads=1,
                                   seq_lens=(0, 1, 15, 16, 63, 64, 65, 200, 319, 320, 321, 336, 337, 352, 353, 700)),
     "mixed": lambda: small(5, batch=3, num_q_heads=8, num_kv_heads=2, seq_lens=(1500, 700, 2300)),
+    # d = 64: INT4 parts of 8 bytes (two 8-byte loads per lane)
+    "mixed-d64": lambda: small(5, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, group_size=64,
+                               seq_lens=(1300, 2100)),
 }
 
 

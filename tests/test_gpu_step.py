@@ -25,6 +25,8 @@ CASES = {
     "int2-d128-gq4": dict(base=2, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(1000, 400)),
     "int2-d64-gq8": dict(base=1, batch=2, num_q_heads=16, num_kv_heads=2, seq_lens=(330, 900)),
     "mixed-d128-gq4": dict(base=5, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(1200, 700)),
+    "mixed-d64-gq8": dict(base=5, batch=2, num_q_heads=16, num_kv_heads=2, head_dim=64, group_size=64,
+                          seq_lens=(900, 500)),
     # the first demote (T = 320) and the sink boundary (T = 64) inside the stepped range
     "int2-d128-gq4-boundaries": dict(base=2, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(317, 61)),
     "int2-d128-gq1": dict(base=2, batch=1, num_q_heads=2, num_kv_heads=2, seq_lens=(500,)),
