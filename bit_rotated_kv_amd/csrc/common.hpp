@@ -307,40 +307,6 @@ __host__ __device__ inline size_t value_part_offset(int bits, int cb, int lane) 
   return bits == 2 ? (size_t)lane * 2 * cb + cb : (size_t)(64 + lane) * cb;
 }
 
-// Word index (within the lane's key or value part) and bit position of a key / value code, for page
-// slot t and channel ch (the layouts documented in oscar.h).
-struct CodePos {
-  int lane, word, bit;
-};
-
-__host__ __device__ inline CodePos key_pos(int bits, int t, int ch) {
-  const int kk = ch / 32, g = (ch % 32) / 8, m = (ch % 8) / 2, hf = ch % 2;
-  CodePos p;
-  p.lane = 16 * g + t;
-  if (bits == 2) {
-    p.word = kk / 2;
-    p.bit = 8 * (kk % 2) + 2 * m + 16 * hf;
-  } else {
-    p.word = kk;
-    p.bit = 4 * m + 16 * hf;
-  }
-  return p;
-}
-
-__host__ __device__ inline CodePos value_pos(int bits, int t, int ch) {
-  const int nb = ch / 16, c = ch % 16, g = t / 4, m = (t % 4) / 2, hf = t % 2;
-  CodePos p;
-  p.lane = 16 * g + c;
-  if (bits == 2) {
-    p.word = nb / 4;
-    p.bit = 2 * (nb % 4) + 8 * m + 16 * hf;
-  } else {
-    p.word = nb / 2;
-    p.bit = 4 * (nb % 2) + 8 * m + 16 * hf;
-  }
-  return p;
-}
-
 // BF16 page-head element offsets (in bf16 units).
 __host__ __device__ inline int bf16_key_index(int d, int t, int ch) {
   const int kk = ch / 32, g = (ch % 32) / 8, i = ch % 8;
