@@ -1013,9 +1013,14 @@ template <int BITS, int D, int GQ, bool LUT = false>
 __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
                           HistQueryLds<D, GQ>& qlds) {
   const Dims& dm = a.dm;
-  const int S = BITS == 2 ? a.ws.s2 : a.ws.s4;
-  const int s = idx % S;
-  const int bk = idx / S;
+  // Split-major order: consecutive workgroups take split s of consecutive (request, kv-head)
+  // groups. The dispatcher deals workgroups to the 8 XCDs in turn, so with the (request, kv-head)
+  // index fastest every XCD gets the same share of each split; with the split index fastest (and 8
+  // dividing the split count) split s would always land on the same XCD, and where only the low
+  // splits hold pages (ragged lengths, a mixed cache's two widths) a few XCDs would do the work.
+  const int nbk = dm.batch * dm.hkv;
+  const int s = idx / nbk;
+  const int bk = idx % nbk;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int ppw = a.ws.ppw;
   const int pg_begin = s * kSplitWaves * ppw;
