@@ -56,6 +56,7 @@ _SIGS = {
     "oscar_calib_query_cov": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, c_size_t, _P, _P]),
     "oscar_calib_value_cov": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, _P, _P, _P, c_float, _P,
                                         c_size_t, _P, _P]),
+    "oscar_rotation_from_covariance": (c_int32, [c_int32, c_int32, _P, _P, _P, _P]),
     "oscar_bf16_fill": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, c_int64, _P, c_int32, _P]),
     "oscar_bf16_decode_workspace_bytes": (c_size_t, [_P, c_int32, c_int32]),
     "oscar_bf16_decode_attn": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, c_int64, _P, c_int32, c_float, _P,

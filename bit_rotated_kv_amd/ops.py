@@ -366,3 +366,25 @@ def calib_value_cov(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_s
     check(lib().oscar_calib_value_cov(hkv, gq, n, k.shape[1], d, _p(q), _p(k), _p(v), softmax_scale, _p(ws),
                                       ws.numel(), _p(cov), _stream()), "oscar_calib_value_cov")
     return cov
+
+
+def rotation_from_covariance(cov, return_eig: bool = False):
+    """R = U . H . P_br (fp32 numpy [n, d, d]) from symmetric covariances ``cov`` [n, d, d] or
+    [d, d] (any array-like; passed to the host call as fp64). With ``return_eig`` also returns the
+    descending eigenvalues [n, d] and eigenvectors U [n, d, d] (columns) the call formed."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(cov, dtype=np.float64))
+    single = c.ndim == 2
+    if single:
+        c = c[None]
+    if c.ndim != 3 or c.shape[1] != c.shape[2]:
+        raise ValueError("cov must be [n, d, d] or [d, d]")
+    n, d, _ = c.shape
+    rot = np.zeros((n, d, d), np.float32)
+    w = np.zeros((n, d), np.float64)
+    u = np.zeros((n, d, d), np.float64)
+    check(lib().oscar_rotation_from_covariance(n, d, c.ctypes.data, rot.ctypes.data, w.ctypes.data, u.ctypes.data),
+          "oscar_rotation_from_covariance")
+    if single:
+        rot, w, u = rot[0], w[0], u[0]
+    return (rot, w, u) if return_eig else rot

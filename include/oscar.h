@@ -401,6 +401,26 @@ oscar_status_t oscar_calib_value_cov(int32_t num_kv_heads, int32_t gq, int32_t n
                                      float softmax_scale, void* workspace, size_t workspace_bytes, float* cov,
                                      hipStream_t stream);
 
+/*
+ * Rotations from covariances ("Together AI open-sources OSCAR", section on what makes OSCAR
+ * different): for each of n_mats symmetric matrices C (C_Q for R_K, C_S for R_V) forms
+ * R = U . H . P_br, where U holds the eigenvectors of C as columns in descending eigenvalue
+ * order, each column's largest-magnitude entry (the first, on ties) made positive; H is the
+ * orthonormal Sylvester Hadamard matrix (H_1 = [1], H_2n = [[H, H], [H, -H]], scaled by
+ * 1/sqrt(d)) and P_br the bit-reversal permutation with P[i, rev(i)] = 1, so that
+ * R[i][j] = sum_k U[i][k] H[k][rev(j)]. Host function: every pointer is host memory, nothing is
+ * enqueued on a device. The eigenvectors come from the cyclic Jacobi method in fp64 on the
+ * symmetric part (C + C^T)/2 of each input; R is formed in fp64 and rounded once to fp32.
+ *   cov_host      [n_mats][d][d] fp64, finite (else OSCAR_ERR_INVALID_ARG)
+ *   rot_host      [n_mats][d][d] fp32 out, row-major (a row x is rotated as x . R)
+ *   eigvals_host  [n_mats][d] fp64 out, descending (may be NULL)
+ *   eigvecs_host  [n_mats][d][d] fp64 out, U row-major (eigenvector j in column j; may be NULL)
+ * head_dim: a power of two, at most 256 (larger: OSCAR_ERR_UNSUPPORTED). Synchronous, about
+ * 0.1 s per matrix at d = 128.
+ */
+oscar_status_t oscar_rotation_from_covariance(int32_t n_mats, int32_t head_dim, const double* cov_host,
+                                              float* rot_host, double* eigvals_host, double* eigvecs_host);
+
 #ifdef __cplusplus
 }
 #endif

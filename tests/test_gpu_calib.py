@@ -75,7 +75,7 @@ def test_gpu_eigenbases_fit_the_oracle_covariances():
     for i in range(len(kvs)):
         for gpu_c, ref_c in ((cq[i], oracle.query_covariance(qv[i])),
                              (cs[i], oracle.score_weighted_value_covariance(qv[i, :, :1024], kvv[i], vv[i], scale))):
-            u = calib.eigvecs_descending(gpu_c).numpy()
+            _, _, u = brk.rotation_from_covariance(gpu_c.numpy(), return_eig=True)
             lam = np.einsum("ij,ik,kj->j", u, ref_c, u)
             resid = np.linalg.norm(ref_c @ u - u * lam[None, :], axis=0).max()
             gap = np.linalg.norm(gpu_c.numpy() - ref_c, 2)
