@@ -59,6 +59,37 @@ def _need(t: Optional[torch.Tensor], dtype, name: str, optional: bool = False):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t: Optional[torch.Tensor], shape: tuple, name: str):
+    """Exact shape check (the library cannot see buffer sizes: an undersized tensor would be an
+    out-of-bounds device access)."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _bytes_at_least(t: Optional[torch.Tensor], n: int, name: str):
+    if t is not None and t.numel() * t.element_size() < n:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the layout needs {n}")
+
+
+def _tables(batch: int, page_table: torch.Tensor, page_table4: Optional[torch.Tensor]) -> int:
+    """[B, stride] page tables (INT2 and, for mixed caches, INT4 with the same stride)."""
+    if page_table.dim() != 2 or page_table.shape[0] != batch:
+        raise ValueError(f"page_table must be [{batch}, stride], got {tuple(page_table.shape)}")
+    _shape(page_table4, tuple(page_table.shape), "page_table4")
+    return page_table.shape[1]
+
+
+def _rotations(layout: Layout, rot_k: torch.Tensor, rot_v: torch.Tensor):
+    d = layout.head_dim
+    _shape(rot_k, (layout.num_kv_heads, d, d), "rot_k")
+    _shape(rot_v, (layout.num_kv_heads, d, d), "rot_v")
+
+
+def _cache(layout: Layout, batch: int, pool: torch.Tensor, window: torch.Tensor):
+    _bytes_at_least(pool, pool_bytes(layout), "pool")
+    _bytes_at_least(window, window_bytes(layout, batch), "window")
+
+
 def _ref(layout: Layout):
     import ctypes
     return ctypes.byref(layout)
@@ -97,6 +128,10 @@ def quantize_pack(x: torch.Tensor, group: int, bits: int, clip: float, codes: Op
         scale_zero = torch.empty((rows, dim // group, 2), dtype=torch.int16, device=x.device)
     _need(codes, torch.uint8, "codes")
     _need(scale_zero, torch.int16, "scale_zero")
+    if group <= 0 or dim % group or bits not in (2, 4):
+        raise ValueError("group must divide dim and bits must be 2 or 4")
+    _shape(codes, (rows, dim * bits // 8), "codes")
+    _shape(scale_zero, (rows, dim // group, 2), "scale_zero")
     check(lib().oscar_quantize_pack(rows, dim, group, bits, clip, _p(x), _p(codes), _p(scale_zero), _stream()),
           "oscar_quantize_pack")
     return codes, scale_zero
@@ -115,6 +150,10 @@ def quantize_pack_codebook(x: torch.Tensor, group: int, clip: float, levels, cod
         scale_zero = torch.empty((rows, dim // group, 2), dtype=torch.int16, device=x.device)
     _need(codes, torch.uint8, "codes")
     _need(scale_zero, torch.int16, "scale_zero")
+    if group <= 0 or dim % group:
+        raise ValueError("group must divide dim")
+    _shape(codes, (rows, dim // 4), "codes")
+    _shape(scale_zero, (rows, dim // group, 2), "scale_zero")
     check(lib().oscar_quantize_pack_codebook(rows, dim, group, clip, _p(x), ctypes.cast(lv, c_void_p), _p(codes),
                                              _p(scale_zero), _stream()), "oscar_quantize_pack_codebook")
     return codes, scale_zero
@@ -133,6 +172,7 @@ def codebook_fit(x: torch.Tensor, rot: torch.Tensor, clip: float, max_iter: int 
     _need(x, torch.bfloat16, "x")
     _need(rot, torch.float32, "rot")
     hkv, n, d = x.shape
+    _shape(rot, (hkv, d, d), "rot")
     if workspace is None:
         workspace = torch.empty(max(codebook_workspace_bytes(hkv, n, d), 1), dtype=torch.uint8, device=x.device)
     _need(workspace, torch.uint8, "workspace")
@@ -161,9 +201,19 @@ def kv_prefill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.
     _need(token_bits, torch.uint8, "token_bits", optional=True)
     _need(page_table4, torch.int32, "page_table4", optional=True)
     _need(n_int4_out, torch.int32, "n_int4_out", optional=True)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, max_seq_len, d]")
     B, hkv, tmax, d = k.shape
+    _shape(k, (B, layout.num_kv_heads, tmax, layout.head_dim), "k")
+    _shape(v, tuple(k.shape), "v")
+    _shape(seq_len, (B,), "seq_len")
+    _shape(token_bits, (B, tmax), "token_bits")
+    _shape(n_int4_out, (B,), "n_int4_out")
+    _rotations(layout, rot_k, rot_v)
+    _cache(layout, B, pool, window)
+    stride = _tables(B, page_table, page_table4)
     check(lib().oscar_kv_prefill(_ref(layout), B, tmax, _p(seq_len), _p(k), _p(v), _p(token_bits), _p(rot_k),
-                                 _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                 _p(rot_v), _p(pool), _p(page_table), _p(page_table4), stride,
                                  _p(window), _p(n_int4_out), _stream()), "oscar_kv_prefill")
 
 
@@ -186,8 +236,16 @@ def kv_demote(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v:
         _need(t, torch.int32, n, optional=True)
     _need(demote_bits, torch.uint8, "demote_bits", optional=True)
     B = new_k.shape[0]
+    _shape(new_k, (B, layout.num_kv_heads, layout.head_dim), "new_k")
+    _shape(new_v, tuple(new_k.shape), "new_v")
+    for t, n in ((seq_len, "seq_len"), (n_int4, "n_int4"), (seq_len_out, "seq_len_out"), (n_int4_out, "n_int4_out"),
+                 (demote_bits, "demote_bits")):
+        _shape(t, (B,), n)
+    _rotations(layout, rot_k, rot_v)
+    _cache(layout, B, pool, window)
+    stride = _tables(B, page_table, page_table4)
     check(lib().oscar_kv_demote(_ref(layout), B, _p(seq_len), _p(n_int4), _p(new_k), _p(new_v), _p(demote_bits),
-                                _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), stride,
                                 _p(window), _p(seq_len_out), _p(n_int4_out), _stream()), "oscar_kv_demote")
 
 
@@ -213,16 +271,23 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
     B = q.shape[0]
+    _shape(q, (B, layout.num_q_heads, layout.head_dim), "q")
+    _shape(out, tuple(q.shape), "out")
+    _shape(seq_len, (B,), "seq_len")
+    _shape(n_int4, (B,), "n_int4")
+    _rotations(layout, rot_k, rot_v)
+    _cache(layout, B, pool, window)
+    stride = _tables(B, page_table, page_table4)
     if events is None:
         check(lib().oscar_decode_attn(_ref(layout), B, max_seq_len, _p(q), _p(seq_len), _p(n_int4), _p(window),
-                                      _p(pool), _p(page_table), _p(page_table4), page_table.shape[1], _p(rot_k),
+                                      _p(pool), _p(page_table), _p(page_table4), stride, _p(rot_k),
                                       _p(rot_v), softmax_scale, _p(workspace), workspace.numel(), _p(out), _stream()),
               "oscar_decode_attn")
         return out
     import ctypes
     arr = (c_void_p * len(events))(*[c_void_p(e.cuda_event) for e in events])
     check(lib().oscar_decode_attn_profiled(_ref(layout), B, max_seq_len, _p(q), _p(seq_len), _p(n_int4), _p(window),
-                                           _p(pool), _p(page_table), _p(page_table4), page_table.shape[1],
+                                           _p(pool), _p(page_table), _p(page_table4), stride,
                                            _p(rot_k), _p(rot_v), softmax_scale, _p(workspace), workspace.numel(),
                                            _p(out), ctypes.cast(arr, c_void_p), len(events), _stream()),
           "oscar_decode_attn_profiled")
@@ -256,6 +321,17 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
+    B = q.shape[0]
+    _shape(q, (B, layout.num_q_heads, layout.head_dim), "q")
+    _shape(out, tuple(q.shape), "out")
+    _shape(new_k, (B, layout.num_kv_heads, layout.head_dim), "new_k")
+    _shape(new_v, tuple(new_k.shape), "new_v")
+    for t, n in ((seq_len, "seq_len"), (n_int4, "n_int4"), (seq_len_out, "seq_len_out"), (n_int4_out, "n_int4_out"),
+                 (demote_bits, "demote_bits")):
+        _shape(t, (B,), n)
+    _rotations(layout, rot_k, rot_v)
+    _cache(layout, B, pool, window)
+    _tables(B, page_table, page_table4)
     args = (_ref(layout), q.shape[0], max_seq_len, _p(seq_len), _p(n_int4), _p(new_k), _p(new_v), _p(demote_bits),
             _p(q), _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1], _p(window),
             _p(seq_len_out), _p(n_int4_out), softmax_scale, _p(workspace), workspace.numel(), _p(out))
@@ -276,7 +352,14 @@ def bf16_fill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.T
     _need(v, torch.bfloat16, "v")
     _need(pages, torch.uint8, "pages")
     _need(page_table, torch.int32, "page_table")
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, max_seq_len, d]")
     B, hkv, tmax, d = k.shape
+    _shape(k, (B, layout.num_kv_heads, tmax, layout.head_dim), "k")
+    _shape(v, tuple(k.shape), "v")
+    _shape(seq_len, (B,), "seq_len")
+    _bytes_at_least(pages, num_pages * page_bytes(layout, 16), "pages")
+    _tables(B, page_table, None)
     check(lib().oscar_bf16_fill(_ref(layout), B, tmax, _p(seq_len), _p(k), _p(v), _p(pages), num_pages,
                                 _p(page_table), page_table.shape[1], _stream()), "oscar_bf16_fill")
 
@@ -292,6 +375,12 @@ def bf16_decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, pag
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
+    B = q.shape[0]
+    _shape(q, (B, layout.num_q_heads, layout.head_dim), "q")
+    _shape(out, tuple(q.shape), "out")
+    _shape(seq_len, (B,), "seq_len")
+    _bytes_at_least(pages, num_pages * page_bytes(layout, 16), "pages")
+    _tables(B, page_table, None)
     check(lib().oscar_bf16_decode_attn(_ref(layout), q.shape[0], max_seq_len, _p(q), _p(seq_len), _p(pages),
                                        num_pages, _p(page_table), page_table.shape[1], softmax_scale, _p(workspace),
                                        workspace.numel(), _p(out), _stream()), "oscar_bf16_decode_attn")
