@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a HIP graph")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-codebook", action="store_true", help="skip the Lloyd-Max codebook variant")
+    ap.add_argument("--timeline", type=int, default=0, metavar="N",
+                    help="diagnostic mode: run N eager steps of the workload with liboscar_timeline.so and print "
+                         "the per-workgroup phase percentiles instead of the benchmark line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
     return ap.parse_args()
@@ -605,11 +608,41 @@ def cpu_baseline(w, context, kv_heads=8):
             "seconds": round(sec, 3)}
 
 
+def timeline_main(args):
+    """Per-workgroup phases of the fused step (diagnostic library): entry, query operands ready, page
+    loop done and exit of every split workgroup, and the merge workgroups, over N eager steps."""
+    import torch
+    import synth
+    from bit_rotated_kv_amd import timeline
+    timeline.use_timeline_library()
+    w = synth.workload(2 if args.batch == 1 else 3)
+    batch, context = args.batch, args.context
+    est = batch * w.num_kv_heads * (context - 320) * 72
+    copies = args.copies or max(2, math.ceil(1.0e9 / est))
+    log(f"timeline: batch {batch}, context {context}, {copies} copies, {args.timeline} steps")
+    setup = Int2Setup(w, batch, context, copies, args.warmup + args.timeline, fast_inputs=batch > 1)
+    for i in range(args.warmup):
+        setup.step(i)
+    torch.cuda.synchronize()
+    tabs = []
+    for i in range(args.timeline):
+        timeline.clear()
+        setup.step(args.warmup + i)
+        torch.cuda.synchronize()
+        tabs.append(timeline.read())
+    res = timeline.summarize(tabs)
+    res["workload"] = f"{w.name}: batch {batch}, context {context}, fused decode step, eager launches"
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.timeline:
+        timeline_main(args)
+        return
     import torch
     import synth
     torch.manual_seed(0)

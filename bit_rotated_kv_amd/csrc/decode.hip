@@ -44,8 +44,13 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "demote.hpp"
+#include "timeline.hpp"
 
 namespace oscar {
+
+#ifdef OSCAR_TIMELINE
+__device__ uint64_t g_timeline[kTimelineSplitRows + kTimelineMergeRows][kTimelineCols];
+#endif
 
 constexpr float kNegInf = -__builtin_huge_valf();
 #ifndef OSCAR_HIST_PIPE2
@@ -574,9 +579,11 @@ __device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int i
   const int nw = a.ws.nwin;
   const int wi = idx % nw, bk = idx / nw, kv = bk % dm.hkv, b = bk / dm.hkv;
   if (a.step && wi == nw - 1) {
+    OSCAR_TL_SPLIT_VALUE(4, 3);
     step_role<D, GQ>(a, cw, bk, wi, slds);
     return;
   }
+  OSCAR_TL_SPLIT_VALUE(4, 2);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
@@ -1112,6 +1119,8 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     } else {
       hist_query_operands<BITS, D, GQ, LUT>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
     }
+    OSCAR_TL_SPLIT(1);
+    OSCAR_TL_SPLIT_VALUE(4, (BITS == 4 ? 1u : 0u) | ((uint32_t)(wp1 - wp0) << 8));
     const float uq = uh + ul;   // sum of the query operand of this lane's head
     const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
     const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
@@ -1142,6 +1151,7 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
   } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
+  OSCAR_TL_SPLIT(2);
   // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
   __syncthreads();
   workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
@@ -1176,6 +1186,10 @@ __global__ __launch_bounds__(kSplitWaves * kWave, (kSplitMinBlocks<GQ, MIXED>)) 
   const int n_int2 = a.dm.batch * a.dm.hkv * a.ws.s2;
   const int n_hist = n_int2 + a.dm.batch * a.dm.hkv * a.ws.s4;
   const int bid = blockIdx.x;
+  OSCAR_TL_SPLIT(0);
+#ifdef OSCAR_TIMELINE
+  OSCAR_TL_SPLIT_VALUE(5, timeline_placement());
+#endif
   if (bid < n_int2) {
     hist_role<2, D, GQ, CB>(a, bid, o_lds, st_lds, scr.hist);
   } else if (MIXED && bid < n_hist) {
@@ -1183,6 +1197,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave, (kSplitMinBlocks<GQ, MIXED>)) 
   } else {
     window_role<D, GQ>(a, cw, bid - n_hist, o_lds, st_lds, scr.step);
   }
+  OSCAR_TL_SPLIT(3);
 }
 
 // ------------------------------------------------------------------ merge
@@ -1298,6 +1313,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   __shared__ __attribute__((aligned(16))) float acc_w[NG][HW][AS];
   __shared__ float m_s[NG][HW], w_s[NG][HW];
   __shared__ float hsum[HW][D], wsum_s[HW][D], wtot_s[HW];
+  OSCAR_TL_MERGE(0);
   const Dims& dm = a.dm;
   const int bk = blockIdx.x / (GQ / HW), h0 = HW * (blockIdx.x % (GQ / HW));
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
@@ -1390,6 +1406,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
       }
     }
   }
+  OSCAR_TL_MERGE(3);
   if (ring) {
     // the new token takes its window slot (the demoted token's ring slot, or position T), as the
     // demote kernel writes it
@@ -1610,3 +1627,16 @@ hipError_t launch_bf16_decode(const Bf16Args& b, hipStream_t stream) {
 }
 
 }  // namespace oscar
+
+#ifdef OSCAR_TIMELINE
+// Diagnostic library only: copies the timeline table (rows of 8 uint64, split rows then merge rows)
+// to host memory, or clears it. Synchronous.
+extern "C" int oscar_timeline_read(void* host, size_t bytes) {
+  if (bytes > sizeof(oscar::g_timeline)) bytes = sizeof(oscar::g_timeline);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(oscar::g_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int oscar_timeline_clear(void) {
+  static uint64_t zero[oscar::kTimelineSplitRows + oscar::kTimelineMergeRows][oscar::kTimelineCols];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(oscar::g_timeline), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+}
+#endif
