@@ -61,6 +61,7 @@ def parse():
     ap.add_argument("--timeline", type=int, default=0, metavar="N",
                     help="diagnostic mode: run N eager steps of the workload with liboscar_timeline.so and print "
                          "the per-workgroup phase percentiles instead of the benchmark line")
+    ap.add_argument("--timeline-raw", default="", help="with --timeline: also save the raw tables (.npy)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
     return ap.parse_args()
@@ -203,7 +204,7 @@ class Int2Setup:
 
 
 def time_int2(setup, steps, warmup, eager):
-    """Returns (ms per step, mean kernel intervals [query prologue, split, merge] in ms, launch mode).
+    """Returns (ms per step, mean event intervals [launch gap, split, merge] in ms, launch mode).
 
     Step time: the K steps captured in one HIP graph and replayed (no host work inside the timed
     region). Kernel intervals: K more steps launched eagerly behind a GPU-side sleep, so every
@@ -289,7 +290,7 @@ def time_codebook(w, batch, context, steps, warmup, eager, fast_inputs, reps=3):
             "levels_kv0": [[round(float(x), 4) for x in levels[0, j]] for j in range(2)],
             "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
             "GB_per_s": round((int2 + bf16 + demote) / (ms * 1e-3) / 1e9, 1),
-            "kernel_ms": [round(float(x), 5) for x in kern],
+            "kernel_ms": {"split": round(float(kern[1]), 5), "merge": round(float(kern[2]), 5)},
             "split_GB_per_s": round(split_gbs, 1), "split_frac": round(split_gbs / HBM_PEAK_GBS, 4),
             "launch": mode}
 
@@ -438,7 +439,8 @@ def time_bs32_100k(args):
     r = {"workload": "paged batch 32 x 100,000 tokens, demote in step", "ms_per_step": round(ms, 5),
          "us_per_step": round(ms * 1e3, 2), "GB_per_s": round((i2 + b2 + d2) / (ms * 1e-3) / 1e9, 1),
          "tokens_per_s": round(batch / (ms * 1e-3), 1), "split_GB_per_s": round(split, 1),
-         "split_frac": round(split / HBM_PEAK_GBS, 4), "kernel_ms": [round(float(x), 5) for x in k],
+         "split_frac": round(split / HBM_PEAK_GBS, 4),
+         "kernel_ms": {"split": round(float(k[1]), 5), "merge": round(float(k[2]), 5)},
          "eager_step_us_p10_p50_p90": s.step_spread_us, "cache_copies": s.copies, "launch": mode}
     del s
     torch.cuda.empty_cache()
@@ -630,6 +632,8 @@ def timeline_main(args):
         setup.step(args.warmup + i)
         torch.cuda.synchronize()
         tabs.append(timeline.read())
+    if args.timeline_raw:
+        np.save(args.timeline_raw, np.stack(tabs))
     res = timeline.summarize(tabs)
     res["workload"] = f"{w.name}: batch {batch}, context {context}, fused decode step, eager launches"
     print(json.dumps(res), flush=True)
@@ -675,8 +679,7 @@ def main():
                    "global_batch": batch, "seq_len": context, "parallelism": "single GPU",
                    "cache_copies": copies, "launch": mode},
         "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
-        "kernel_ms": {"q_prologue": round(float(kern[0]), 5), "split": round(split_ms, 5),
-                      "merge": round(float(kern[2]), 5)},
+        "kernel_ms": {"split": round(split_ms, 5), "merge": round(float(kern[2]), 5)},
         "eager_step_us_p10_p50_p90": setup.step_spread_us,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
@@ -687,8 +690,7 @@ def main():
     }
     del setup
     torch.cuda.empty_cache()
-    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); kernels (prologue, split, merge) us: "
-        f"{', '.join(f'{x * 1e3:.2f}' for x in kern)}")
+    log(f"INT2 step {ms * 1e3:.2f} us ({mode}); split {kern[1] * 1e3:.2f} us, merge {kern[2] * 1e3:.2f} us")
     if not args.no_prefill:
         log("timing the prefill (matrix-core rotation + quantise)")
         result["prefill"] = time_prefill(w, batch, context)
@@ -720,7 +722,7 @@ def main():
                           "tokens_per_s": round(32 / (ms32 * 1e-3), 1),
                           "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
                           "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "kernel_ms": [round(float(x), 5) for x in k32],
+                          "kernel_ms": {"split": round(float(k32[1]), 5), "merge": round(float(k32[2]), 5)},
                           "eager_step_us_p10_p50_p90": s32.step_spread_us}
         del s32
         torch.cuda.empty_cache()

@@ -11,18 +11,22 @@ using namespace oscar;
 
 namespace {
 
-#ifndef OSCAR_TARGET_WORKGROUPS
-#define OSCAR_TARGET_WORKGROUPS 512
-#endif
-// history workgroups a decode aims for (pages per wavefront are sized from it, 1..64)
-constexpr int kTargetWorkgroups = OSCAR_TARGET_WORKGROUPS;
-#ifndef OSCAR_QPRE_MIN_WORKGROUPS
-#define OSCAR_QPRE_MIN_WORKGROUPS 1024
-#endif
-// Above this many history workgroups the query operands come from one prologue kernel; below it
-// every history workgroup forms its own (no extra launch, but each reads R_K and repeats the
-// rotation).
-constexpr int kQpreMinWorkgroups = OSCAR_QPRE_MIN_WORKGROUPS;
+// Upper bound of the decode split's workgroups per kv-head (besides one per request): the plan
+// shares this many out at most, so the workspace size does not depend on the device.
+constexpr int kMaxUnits = 2048;
+// Wide split workgroups (16 wavefronts) are used for GQA width 4 when this few (request, kv-head)
+// pairs would otherwise give each compute unit two or fewer 4-wavefront workgroups.
+constexpr int kWideMaxGroups = 16;
+// Plan costs: an INT2 history page costs 1, an INT4 page 2 (in the kernels); the step and the BF16
+// window are chains of latencies and cost about the pages their workgroup streams meanwhile
+// (per-workgroup timelines, one 100K-token request: the step's demote ~7 us, the window's 20 pages
+// ~5 us; a 16-wavefront workgroup streams ~17 pages per us, a 4-wavefront one ~6).
+int step_cost(int nw) { return nw >= kSplitWavesWide ? 160 : 64; }
+int window_cost(int nw) { return nw >= kSplitWavesWide ? 80 : 96; }
+
+// Smallest unit the plan aims for (cost of 16 INT2 pages): below it the per-workgroup overhead (query
+// prologue, workgroup merge, one more partial to merge) outweighs the spread.
+constexpr int kMinUnitCost = 16;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -79,7 +83,7 @@ Dims make_dims(const oscar_layout_t* L, int batch, int max_seq_len, int pt_strid
   return d;
 }
 
-int choose_ppw(int64_t total_pages, int waves, int64_t target = kTargetWorkgroups) {
+int choose_ppw(int64_t total_pages, int waves, int64_t target = 512) {
   int64_t p = (total_pages + (int64_t)waves * target - 1) / ((int64_t)waves * target);
   if (p < 1) p = 1;
   if (p > 64) p = 64;
@@ -87,48 +91,63 @@ int choose_ppw(int64_t total_pages, int waves, int64_t target = kTargetWorkgroup
 }
 
 struct DecodePlan {
-  int ppw, s2, s4, nwin, ns, qpre;
-  size_t off_qop, off_qhs, off_po, off_pl, total;
+  int nw, units_per_kv, step_cost, win_cost;
+  size_t off_po, off_pl, off_so, off_sl, off_ru, total;
 };
 
-// Split plan of a decode call; a fused step (step = 1) adds one window workgroup per (b, kv) and
-// one history slot.
-DecodePlan plan_decode(const oscar_layout_t* L, int batch, int max_seq_len, int step) {
-  DecodePlan p;
-  int hist = max_seq_len - L->sink_len - L->recent_len;
-  if (hist < 0) hist = 0;
-  const int hp = (hist + kPage - 1) / kPage;
-  constexpr int W = kSplitWaves;
-#ifndef OSCAR_WINDOW_WORKGROUPS
-#define OSCAR_WINDOW_WORKGROUPS 1
-#endif
-  // window workgroups per (b, kv): each wavefront walks window pages with a stride (at most one
-  // page per wavefront is useful)
-  const int wpg = (L->sink_len + L->recent_len) / kPage;
-  p.nwin = std::min(OSCAR_WINDOW_WORKGROUPS, (wpg + W - 1) / W);
-  if (p.nwin < 1) p.nwin = 1;
-  // history workgroups aim at what the window (and step) workgroups leave of the target
-  const int64_t nwin_all = (int64_t)batch * L->num_kv_heads * (p.nwin + step);
-  const int64_t hist_target = nwin_all < kTargetWorkgroups / 2 ? kTargetWorkgroups - nwin_all : kTargetWorkgroups / 2;
-  p.ppw = choose_ppw((int64_t)batch * L->num_kv_heads * hp, W, hist_target);
-  p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
-  p.s4 = L->mixed ? p.s2 : 0;
-  while (p.s2 + p.s4 > kMaxSlots && p.ppw < 64) {
-    p.ppw = p.ppw * 2 > 64 ? 64 : p.ppw * 2;
-    p.s2 = (hp + W * p.ppw - 1) / (W * p.ppw);
-    p.s4 = L->mixed ? p.s2 : 0;
-  }
-  p.nwin += step;
-  p.ns = p.nwin + p.s2 + p.s4 + step;
-  p.qpre = (int64_t)batch * L->num_kv_heads * (p.s2 + p.s4) > kQpreMinWorkgroups;
+
+int split_waves(const oscar_layout_t* L, int batch) {
   const int gq = L->num_q_heads / L->num_kv_heads;
-  const size_t bhq = (size_t)batch * L->num_q_heads;
-  p.off_qop = kAlign;
-  p.off_qhs = p.off_qop + align_up(2 * 2 * bhq * L->head_dim * 2);
-  p.off_po = p.off_qhs + align_up(2 * bhq * 16);
-  const size_t nsl = (size_t)batch * L->num_kv_heads * p.ns * gq;
-  p.off_pl = p.off_po + align_up(nsl * L->head_dim * 4);
-  p.total = p.off_pl + align_up(nsl * 4);
+  return (gq == 4 && (int64_t)batch * L->num_kv_heads <= kWideMaxGroups) ? kSplitWavesWide : kSplitWaves;
+}
+
+// Units per kv-head the split shares out: one round of workgroups on the device (every compute unit
+// holding as many as it can), at least one per request, no more than the cost bound of the batch at
+// max_seq_len allows with kMinUnitCost per unit, and at most the workspace bound.
+// `resident` < 0: the bound itself (workspace sizing).
+int units_per_kv(const oscar_layout_t* L, int batch, int max_seq_len, int step, int64_t resident) {
+  const int64_t bound = std::max<int64_t>(batch, kMaxUnits / L->num_kv_heads);
+  if (resident < 0) return (int)bound;
+  const int64_t hp = (std::max(0, max_seq_len - L->sink_len - L->recent_len) + kPage - 1) / kPage;
+  const int64_t cost = (step ? step_cost(split_waves(L, batch)) : 0) +
+                       window_cost(split_waves(L, batch)) + hp * (L->mixed ? 2 : 1);
+  const int64_t by_cost = (batch * cost + kMinUnitCost - 1) / kMinUnitCost;
+  const int64_t want = std::min(resident / L->num_kv_heads, by_cost);
+  return (int)std::min<int64_t>(bound, std::max<int64_t>(batch, want));
+}
+
+// Workgroups of the split kernel the current device holds at once (an estimate of 256 compute
+// units with two workgroups each when the device cannot be queried).
+int64_t resident_workgroups(const oscar_layout_t* L, int nw) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  int per_cu = split_workgroups_per_cu(L->head_dim, L->num_q_heads / L->num_kv_heads, L->codebook != nullptr,
+                                       L->mixed != 0, nw);
+  if (per_cu <= 0) per_cu = nw == kSplitWavesWide ? 1 : 2;
+  return (int64_t)cus * per_cu;
+}
+
+// Split plan of a decode call (units_per_kv from units_per_kv()); the workspace layout covers the
+// fused step's slots whether or not `step` is set, so one size serves both entry points.
+DecodePlan plan_decode(const oscar_layout_t* L, int batch, int step, int upk) {
+  DecodePlan p;
+  p.nw = split_waves(L, batch);
+  p.units_per_kv = upk;
+  p.step_cost = step ? step_cost(p.nw) : 0;
+  p.win_cost = window_cost(p.nw);
+  const int gq = L->num_q_heads / L->num_kv_heads;
+  const size_t units = (size_t)L->num_kv_heads * upk;
+  const size_t groups = (size_t)batch * L->num_kv_heads;
+  p.off_po = kAlign;
+  p.off_pl = p.off_po + align_up(units * 3 * gq * L->head_dim * 4);
+  p.off_so = p.off_pl + align_up(units * 3 * gq * 4);
+  p.off_sl = p.off_so + align_up(groups * 2 * gq * L->head_dim * 4);
+  p.off_ru = p.off_sl + align_up(groups * 2 * gq * 4);
+  p.total = p.off_ru + align_up((size_t)batch * 2 * 4);
   return p;
 }
 
@@ -308,7 +327,8 @@ oscar_status_t oscar_kv_demote(const oscar_layout_t* L, int32_t batch, const int
 
 size_t oscar_decode_workspace_bytes(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len) {
   if (check_layout(L) != OSCAR_OK || batch < 0 || max_seq_len < 0) return 0;
-  return plan_decode(L, batch, max_seq_len, 1).total;   // covers the fused step too
+  // the largest plan any device gets; the layout has the fused step's slots in both entry points
+  return plan_decode(L, batch, 1, units_per_kv(L, batch, max_seq_len, 1, -1)).total;
 }
 
 // Validates the decode arguments and fills `out`; batch == 0 is valid (nothing to do).
@@ -327,8 +347,9 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
     if (!pool || !page_table || pt_stride <= 0) return OSCAR_ERR_INVALID_ARG;
     if (L->mixed && !page_table4) return OSCAR_ERR_INVALID_ARG;
   }
-  const DecodePlan p = plan_decode(L, batch, max_seq_len, step);
-  if (p.s2 + p.s4 > kMaxSlots) return OSCAR_ERR_UNSUPPORTED;
+  const DecodePlan p =
+      plan_decode(L, batch, step,
+                  units_per_kv(L, batch, max_seq_len, step, resident_workgroups(L, split_waves(L, batch))));
   if (!workspace || workspace_bytes < p.total) return OSCAR_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   DecodeArgs a{};
@@ -347,16 +368,15 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.scale_log2e = scale * 1.4426950408889634f;
   a.out = out;
   a.ws.flags = reinterpret_cast<uint32_t*>(ws);
-  a.ws.qop = reinterpret_cast<uint16_t*>(ws + p.off_qop);
-  a.ws.qhs = reinterpret_cast<float*>(ws + p.off_qhs);
-  a.ws.qpre = p.qpre;
   a.ws.part_o = reinterpret_cast<float*>(ws + p.off_po);
   a.ws.part_lse = reinterpret_cast<float*>(ws + p.off_pl);
-  a.ws.ns = p.ns;
-  a.ws.nwin = p.nwin;
-  a.ws.s2 = p.s2;
-  a.ws.s4 = p.s4;
-  a.ws.ppw = p.ppw;
+  a.ws.step_o = reinterpret_cast<float*>(ws + p.off_so);
+  a.ws.step_lse = reinterpret_cast<float*>(ws + p.off_sl);
+  a.ws.req_units = reinterpret_cast<int32_t*>(ws + p.off_ru);
+  a.ws.units_per_kv = p.units_per_kv;
+  a.ws.nw = p.nw;
+  a.ws.step_cost = p.step_cost;
+  a.ws.win_cost = p.win_cost;
   a.step = step;
   *args = a;
   return OSCAR_OK;

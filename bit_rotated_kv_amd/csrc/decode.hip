@@ -62,6 +62,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // history pages in the per-wave load ring (INT2 page-heads are 1152 B, INT4 2176 B at d = 128)
 constexpr int kHistPipe2 = OSCAR_HIST_PIPE2;
 constexpr int kHistPipe4 = OSCAR_HIST_PIPE4;
+#ifndef OSCAR_WIDE_RING
+#define OSCAR_WIDE_RING 4
+#endif
 constexpr int kBf16Pipe = 2;   // BF16 pages in the per-wave load ring (8 KB each)
 
 __device__ __forceinline__ float4_t mfma32_f16(const u32x4_t& a, const half8_t& b, float4_t c) {
@@ -100,15 +103,151 @@ __device__ inline HistCounts hist_counts(const DecodeArgs& a, int b) {
   return c;
 }
 
-// ------------------------------------------------------------------ query prologue (per history workgroup)
-// Thread (column group cg, part) holds rows part*QR .. part*QR+QR-1 of columns 4cg .. 4cg+3 of
-// R_K (float4 loads issued with the workgroup's first loads).
-static_assert(kSplitWaves * kWave == 256, "split workgroups are 256 threads");
-template <int D>
+// ------------------------------------------------------------------ work plan (device side)
+// A request's n units cut its cost sequence [step | INT2 pages | INT4 pages | window] into n equal
+// cost ranges: an INT2 page costs 1, an INT4 page 2, the step step_cost and the BF16 window (sink
+// and recent pages, taken as one block by all wavefronts of its unit at once) win_cost; a page, the
+// step or the window belongs to the unit that holds its first cost position. The step and the
+// window are latency-bound, and their costs are the pages their unit would stream meanwhile; at
+// the two ends of the sequence they fall to different units. Requests get units in proportion to
+// their cost. Every wavefront that needs the plan computes it from the device lengths (the host
+// knows only max_seq_len), so the workgroups of a launch agree without communicating.
+constexpr int kInt4PageCost = 2;
+
+struct ReqCost {
+  int p2, p4;    // history pages of each width (cut at the page-table stride)
+  int cost;      // whole cost sequence
+};
+
+__device__ inline ReqCost request_cost(const DecodeArgs& a, int b) {
+  const HistCounts c = hist_counts(a, b);
+  ReqCost r;
+  r.p2 = min((c.n2 + kPage - 1) / kPage, a.dm.pt_stride);
+  r.p4 = min((c.n4 + kPage - 1) / kPage, a.dm.pt_stride);
+  r.cost = a.ws.step_cost + r.p2 + kInt4PageCost * r.p4 + a.ws.win_cost;
+  return r;
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the lanes of a wavefront.
+__device__ __forceinline__ int64_t wave_scan_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t y = __shfl_up(v, o, kWave);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Units of the requests before a request whose predecessors' costs add up to `cum`, minus the one
+// unit each of them holds at least: floor(extra * cum / C + 1/2) (cumulative rounding, so the
+// shares of all requests add up to `extra` exactly).
+__device__ __forceinline__ int64_t unit_share(int64_t extra, int64_t cum, int64_t total) {
+  return total > 0 ? (2 * extra * cum + total) / (2 * total) : 0;
+}
+
+struct RequestUnits {
+  int b;           // request (-1: none)
+  int first, n;    // units per kv-head before the request, and its own
+  ReqCost rc;
+};
+
+// The request that holds unit `key` of every kv-head, with its units. Wave-level: every lane
+// returns the same.
+__device__ RequestUnits request_units(const DecodeArgs& a, int key) {
+  const int B = a.dm.batch, lane = threadIdx.x % kWave;
+  if (B == 1) {   // one request holds every unit
+    RequestUnits r;
+    r.b = 0;
+    r.first = 0;
+    r.n = a.ws.units_per_kv;
+    r.rc = request_cost(a, 0);
+    return r;
+  }
+  const int64_t extra = max(0, a.ws.units_per_kv - B);
+  int64_t total = 0;
+  for (int b0 = 0; b0 < B; b0 += kWave) {
+    const int b = b0 + lane;
+    total += b < B ? request_cost(a, b).cost : 0;
+  }
+  total = wave_sum_i64(total);
+  RequestUnits r;
+  r.b = -1;
+  r.first = r.n = 0;
+  r.rc = ReqCost{0, 0, 0};
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < B; b0 += kWave) {
+    const int b = b0 + lane;
+    const ReqCost rc = b < B ? request_cost(a, b) : ReqCost{0, 0, 0};
+    const int64_t incl = wave_scan_i64(rc.cost, lane) + carry;
+    const int first = b + (int)unit_share(extra, incl - rc.cost, total);
+    const int next = b + 1 + (int)unit_share(extra, incl, total);
+    const bool hit = b < B && first <= key && key < next;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      r.b = __shfl(b, l, kWave);
+      r.first = __shfl(first, l, kWave);
+      r.n = __shfl(next - first, l, kWave);
+      r.rc.p2 = __shfl(rc.p2, l, kWave);
+      r.rc.p4 = __shfl(rc.p4, l, kWave);
+      r.rc.cost = __shfl(rc.cost, l, kWave);
+      return r;
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  return r;
+}
+
+// Segments of the unit with cost range [c0, c1) of a request's sequence.
+struct Segments {
+  bool step;
+  bool window;    // all window pages
+  int p20, p21;   // INT2 history pages
+  int p40, p41;   // INT4 history pages
+};
+
+__device__ __forceinline__ int ceil_pos(int x, int y) { return x <= 0 ? 0 : (x + y - 1) / y; }
+
+__device__ inline Segments unit_segments(const DecodeArgs& a, const ReqCost& rc, int c0, int c1) {
+  const int S = a.ws.step_cost;
+  const int base2 = S, base4 = base2 + rc.p2, basew = base4 + kInt4PageCost * rc.p4;
+  Segments sg;
+  sg.step = S > 0 && c0 == 0 && c1 > 0;
+  sg.window = c0 <= basew && basew < c1;
+  sg.p20 = min(max(c0 - base2, 0), rc.p2);
+  sg.p21 = min(max(c1 - base2, 0), rc.p2);
+  sg.p40 = min(ceil_pos(c0 - base4, kInt4PageCost), rc.p4);
+  sg.p41 = min(ceil_pos(c1 - base4, kInt4PageCost), rc.p4);
+  return sg;
+}
+
+// Cost range of unit j of a request with n units (32-bit division when the products fit).
+__device__ __forceinline__ void unit_range(const RequestUnits& r, int j, int& c0, int& c1) {
+  const uint64_t hi = (uint64_t)(j + 1) * (uint32_t)r.rc.cost;
+  if (hi <= 0xFFFFFFFFull) {
+    c0 = (int)((uint32_t)j * (uint32_t)r.rc.cost / (uint32_t)r.n);
+    c1 = (int)((uint32_t)hi / (uint32_t)r.n);
+  } else {
+    c0 = (int)((uint64_t)j * (uint32_t)r.rc.cost / (uint32_t)r.n);
+    c1 = (int)(hi / (uint32_t)r.n);
+  }
+}
+
+// ------------------------------------------------------------------ query prologue
+// Thread (column group cg, part) of an NT-thread workgroup holds rows part*QR .. part*QR+QR-1 of
+// columns 4cg .. 4cg+3 of R_K (float4 loads issued with the segment's first loads).
+template <int D, int NT>
 struct QRotRows {
   static constexpr int CG = D / 4;      // column groups of 4
-  static constexpr int NPQ = 256 / CG;  // parts of a column group
+  static constexpr int NPQ = NT / CG;   // parts of a column group
   static constexpr int QR = D / NPQ;    // rows per part
+  static_assert(NPQ * CG == NT && NPQ * QR == D, "the rotation rows split evenly over the threads");
   float4 r[QR];
   __device__ void load(const float* rot, int tid) {
     const int cg = tid % CG, part = tid / CG;
@@ -117,44 +256,86 @@ struct QRotRows {
   }
 };
 
-template <int D, int GQ>
+template <int D, int GQ, int NW>
 struct HistQueryLds {
   float qs[GQ][D];               // queries of the group (fp32)
-  float ps[kSplitWaves][GQ][D];  // per-wavefront partial products
+  float ps[NW][GQ][D];           // per-wavefront partial products
   uint16_t op[2][GQ][D];         // fp16 operands: high parts, low parts
   float hsc[GQ][4];              // per head: sum of high parts, sum of low parts, 2^E
 };
 
 // Words of the group's bf16 queries that each thread loads.
-template <int D, int GQ>
-constexpr int kQueryWords = (GQ * D / 2 + 255) / 256;
+template <int D, int GQ, int NT>
+constexpr int kQueryWords = (GQ * D / 2 + NT - 1) / NT;
 
-// Query operands of the GQ heads of a (request, kv-head) for code width BITS, into LDS (L.op,
-// L.hsc), by one 256-thread workgroup. v = q'_j (rotated,
-// log2-scaled) is split on a power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11): v_hi =
-// Delta*rint(v/Delta) has at most 11 significant bits, so its fp16 operand is exact and every
-// partial sum of c*v_hi over a head is an exact fp32 multiple of Delta (|sum| <= 15 * 128 *
-// 2^11 Delta < 2^24 Delta); v_lo = v - v_hi carries the rest. The products see v as fp16 operands
-// scaled per code bit position p (a code c at bit p of its fp16 slot has the value c*2^(p-24)):
-// operand = v*2^(24-p-E), one exponent E per head. Operand column c of the products holds the
-// high parts of head c for c < GQ and the low parts of head c-GQ for GQ <= c < 2GQ.
-// LUT: the key operand holds codebook levels (normal fp16 values, no bit-position factor), so
-// every channel takes p = 0 and the products carry 2^(24-E) instead of 2^-E.
-template <int BITS, int D, int GQ, bool LUT = false>
-__device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
-                               HistQueryLds<D, GQ>& L, float scale_log2e) {
-  constexpr int CG = QRotRows<D>::CG, QR = QRotRows<D>::QR;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+// The queries of a (request, kv-head) group that a thread of the prologue needs. Direct: the thread
+// loads the bf16 queries of its own rotation rows (GQ heads x QR rows, when that is a few words);
+// otherwise the group is staged through LDS, each thread loading kQueryWords words of it.
+template <int D, int GQ, int NT>
+struct QueryIn {
+  static constexpr int QR = QRotRows<D, NT>::QR;
+  static constexpr bool direct = QR % 2 == 0 && GQ * QR / 2 <= 8;
+  static constexpr int W = direct ? GQ * QR / 2 : kQueryWords<D, GQ, NT>;
+  uint32_t w[W];
+  // q: the group's queries [GQ][D] bf16
+  __device__ void load(const uint16_t* q, int tid) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q);
+    if constexpr (direct) {
+      const int part = tid / QRotRows<D, NT>::CG;
 #pragma unroll
-  for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
-    const int e = tid + 256 * i;
-    if (e < GQ * D / 2) {
-      float* qf = &L.qs[0][0];
-      qf[2 * e] = bf16_bits_to_f32(qw[i] & 0xFFFFu);
-      qf[2 * e + 1] = bf16_bits_to_f32(qw[i] >> 16);
+      for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int i = 0; i < QR / 2; ++i) w[h * (QR / 2) + i] = src[(h * D + part * QR) / 2 + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const int e = tid + NT * i;
+        w[i] = e < GQ * D / 2 ? src[e] : 0u;
+      }
     }
   }
-  __syncthreads();
+};
+
+// Sum of x[0..N) as a tree of adjacent pairs ((x0 + x1) + (x2 + x3)) + ...
+template <int N>
+__device__ __forceinline__ float sum_adjacent_tree(float (&x)[N]) {
+#pragma unroll
+  for (int w = N; w > 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) x[i] = x[2 * i] + x[2 * i + 1];
+  return x[0];
+}
+
+// Query operands of the GQ heads of a (request, kv-head) for code width BITS, into LDS (L.op,
+// L.hsc), by one workgroup of NW wavefronts. v = q'_j (rotated, log2-scaled) is split on a
+// power-of-two grid Delta = 2^(ceil(log2 max|v|) - 11): v_hi = Delta*rint(v/Delta) has at most 11
+// significant bits, so its fp16 operand is exact and every partial sum of c*v_hi over a head is an
+// exact fp32 multiple of Delta (|sum| <= 15 * 128 * 2^11 Delta < 2^24 Delta); v_lo = v - v_hi
+// carries the rest. The products see v as fp16 operands scaled per code bit position p (a code c at
+// bit p of its fp16 slot has the value c*2^(p-24)): operand = v*2^(24-p-E), one exponent E per
+// head. Operand column c of the products holds the high parts of head c for c < GQ and the low
+// parts of head c-GQ for GQ <= c < 2GQ.
+// LUT: the key operand holds codebook levels (normal fp16 values, no bit-position factor), so
+// every channel takes p = 0 and the products carry 2^(24-E) instead of 2^-E.
+template <int BITS, int D, int GQ, int NW, bool LUT = false>
+__device__ void query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<D, GQ, NW * kWave>& qin,
+                               HistQueryLds<D, GQ, NW>& L, float scale_log2e) {
+  constexpr int NT = NW * kWave;
+  constexpr int CG = QRotRows<D, NT>::CG, QR = QRotRows<D, NT>::QR;
+  using QI = QueryIn<D, GQ, NT>;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  if constexpr (!QI::direct) {
+#pragma unroll
+    for (int i = 0; i < QI::W; ++i) {
+      const int e = tid + NT * i;
+      if (e < GQ * D / 2) {
+        float* qf = &L.qs[0][0];
+        qf[2 * e] = bf16_bits_to_f32(qin.w[i] & 0xFFFFu);
+        qf[2 * e + 1] = bf16_bits_to_f32(qin.w[i] >> 16);
+      }
+    }
+    __syncthreads();
+  }
   {
     const int cg = tid % CG, part = tid / CG;
 #pragma unroll
@@ -162,7 +343,13 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
       float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < QR; ++i) {
-        const float x = L.qs[h][part * QR + i];
+        float x;
+        if constexpr (QI::direct) {
+          const uint32_t wd = qin.w[h * (QR / 2) + i / 2];
+          x = bf16_bits_to_f32((i & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+        } else {
+          x = L.qs[h][part * QR + i];
+        }
         acc.x = fmaf(x, rr.r[i].x, acc.x);
         acc.y = fmaf(x, rr.r[i].y, acc.y);
         acc.z = fmaf(x, rr.r[i].z, acc.z);
@@ -180,13 +367,16 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
   }
   __syncthreads();
   constexpr int NC = D / kWave;  // channels per lane in the head pass
-  for (int h = wave; h < GQ; h += kSplitWaves) {
+  for (int h = wave; h < GQ; h += NW) {
     float v[NC];
     float vmax = 0.0f, me = 0.0f;
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
       const int j = lane + kWave * k;
-      v[k] = ((L.ps[0][h][j] + L.ps[1][h][j]) + (L.ps[2][h][j] + L.ps[3][h][j])) * scale_log2e;
+      float parts[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) parts[w] = L.ps[w][h][j];
+      v[k] = sum_adjacent_tree<NW>(parts) * scale_log2e;
       const int m = (j % 8) / 2;
       const int p = LUT ? 0 : (BITS == 2 ? 2 * m : 4 * (m % 2));
       vmax = fmaxf(vmax, fabsf(v[k]));
@@ -227,12 +417,12 @@ __device__ void query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQuer
 
 // The operands of query_operands as registers: lane (g, c) gets operand column c and the constants
 // of head c % GQ.
-template <int BITS, int D, int GQ, bool LUT = false>
-__device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[kQueryWords<D, GQ>],
-                                    HistQueryLds<D, GQ>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
+template <int BITS, int D, int GQ, int NW, bool LUT = false>
+__device__ void hist_query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<D, GQ, NW * kWave>& qin,
+                                    HistQueryLds<D, GQ, NW>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
                                     float& ul, float& esc) {
   const int lane = threadIdx.x % kWave, g = lane / 16, c = lane % 16;
-  query_operands<BITS, D, GQ, LUT>(rr, qw, L, scale_log2e);
+  query_operands<BITS, D, GQ, NW, LUT>(rr, qin, L, scale_log2e);
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const u32x4_t z = {0, 0, 0, 0};
@@ -242,36 +432,6 @@ __device__ void hist_query_operands(const QRotRows<D>& rr, const uint32_t (&qw)[
   uh = L.hsc[c % GQ][0];
   ul = L.hsc[c % GQ][1];
   esc = L.hsc[c % GQ][2];
-}
-
-// Query prologue kernel, used when a decode has many history workgroups (each would otherwise
-// repeat the rotation and the R_K reads): one workgroup per (request, kv-head, code width) writes
-// the operands of query_operands to the workspace, in the LDS layout, for the history workgroups to
-// load.
-template <int D, int GQ, bool LUT>
-__global__ __launch_bounds__(256) void q_prologue_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) HistQueryLds<D, GQ> L;
-  const Dims& dm = a.dm;
-  const int bk = blockIdx.x, kv = bk % dm.hkv, b = bk / dm.hkv, wsel = blockIdx.y;
-  const int tid = threadIdx.x;
-  QRotRows<D> rr;
-  rr.load(a.rot_k + (size_t)kv * D * D, tid);
-  uint32_t qw[kQueryWords<D, GQ>];
-  const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * dm.hq + (size_t)kv * GQ) * D);
-#pragma unroll
-  for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
-    const int e = tid + 256 * i;
-    qw[i] = e < GQ * D / 2 ? qsrc[e] : 0u;
-  }
-  if (wsel == 0)
-    query_operands<2, D, GQ, LUT>(rr, qw, L, a.scale_log2e);
-  else
-    query_operands<4, D, GQ>(rr, qw, L, a.scale_log2e);
-  const size_t unit = (size_t)wsel * dm.batch * dm.hkv + bk;
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.ws.qop + unit * 2 * GQ * D);
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&L.op[0][0][0]);
-  for (int i = tid; i < 2 * GQ * D / 8; i += 256) dst[i] = src[i];
-  if (tid < 4 * GQ) a.ws.qhs[unit * 4 * GQ + tid] = (&L.hsc[0][0])[tid];
 }
 
 // ------------------------------------------------------------------ per-wave softmax state
@@ -320,9 +480,12 @@ __device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float (
 
 // Writes the wave's state to LDS and merges the 4 waves of the workgroup into one partial
 // (o normalised, lse in log2 units). VSH_BITS selects the value-code scale restore.
+// nws: the first nws wavefronts hold states to merge (the others hold none and only help with the
+// outputs). The loops over wavefronts are unrolled to NW with the weights predicated, so every LDS
+// read of an output is issued before the first is used.
 template <int D, int GQ, int VSH_BITS, bool REDIST = false, int NW = 4>
 __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
-                                float* part_o, float* part_lse) {
+                                float* part_o, float* part_lse, int nws = NW) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, h = lane % 16;
   float l_tot = st.l_part, z_tot = st.z_part;
   if constexpr (REDIST) {
@@ -337,33 +500,40 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
   l_tot += __shfl_xor(l_tot, 32, kWave);
   z_tot += __shfl_xor(z_tot, 16, kWave);
   z_tot += __shfl_xor(z_tot, 32, kWave);
-  if (g == 0 && h < GQ) {
+  if (g == 0 && h < GQ && wave < nws) {
     st_lds[wave][0][h] = st.m_run;
     st_lds[wave][1][h] = l_tot;
     st_lds[wave][2][h] = z_tot;
   }
+  if (wave < nws) {
 #pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb)
+    for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
+      }
+  }
   __syncthreads();
   for (int idx = tid; idx < GQ * D; idx += NW * kWave) {
     const int hh = idx / D, ch = idx % D, nb = ch / 16;
+    float mw[NW];
     float M = kNegInf;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, st_lds[w][0][hh]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = w < nws ? st_lds[w][0][hh] : kNegInf;
+      M = fmaxf(M, mw[w]);
+    }
     float L = 0.0f, Z = 0.0f, O = 0.0f;
-    if (M != kNegInf) {
-      for (int w = 0; w < NW; ++w) {
-        const float mw = st_lds[w][0][hh];
-        if (mw == kNegInf) continue;
-        const float aw = exp2f(mw - M);
-        L += aw * st_lds[w][1][hh];
-        Z += aw * st_lds[w][2][hh];
-        O += aw * (o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch]);
-      }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const bool live = mw[w] != kNegInf;
+      const float aw = live ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.0f;
+      const float lw = w < nws ? st_lds[w][1][hh] : 0.0f, zw = w < nws ? st_lds[w][2][hh] : 0.0f;
+      const float ow = w < nws ? o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch] : 0.0f;
+      L = fmaf(aw, lw, L);
+      Z = fmaf(aw, zw, Z);
+      O = fmaf(aw, ow, O);
     }
     float vscale = 1.0f;
     if (VSH_BITS == 2) vscale = ldexpf(1.0f, 24 - 2 * (nb % 4));
@@ -451,11 +621,12 @@ __device__ __forceinline__ void load_bf16_query(u32x4_t* bq, const uint16_t* q, 
   }
 }
 
-// ------------------------------------------------------------------ step role (fused decode step)
+// ------------------------------------------------------------------ step segment (fused decode step)
 template <int D, int GQ>
 struct StepLds {
   uint16_t xs[1 + GQ][D];   // demoted key (row 0) and the queries (rows 1..GQ), bf16
   uint16_t xv[D];           // demoted value, bf16
+  uint16_t nk[D], nv[D];    // the new token, bf16
   float xr[2][D];           // rotated demoted key, value
   float vq[GQ][D];          // rotated, log2-scaled queries
   uint8_t cs[2][D];         // codes of the demoted key, value
@@ -468,24 +639,76 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// One workgroup per (request, kv-head) of a fused step, with T = seq_len[b] tokens before the
-// step. Demote (T >= sink + recent): the token at T - recent is read from its ring slot, rotated
-// and quantised with the demote kernel's own arithmetic (same rotation order, same grid), and its
-// codes go into its history slot; its one-token partial -- lse = q' . k_hat, o = v_hat, rotated
-// basis -- fills the last slot (lse = -inf without a demote). The new token's one-token partial --
-// lse = scale * log2(e) * q . k_new, o = v_new -- fills window slot `wslot`. Both logits are
-// summed in fp64 from exact products. The lengths after the step are written here too; the new
-// token's window copy is written by the merge, after every window read.
-template <int D, int GQ>
-__device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk, int wslot, StepLds<D, GQ>& L) {
+// Whether request b's fused step runs: the cache must have room for the new token
+// (seq_len < max_seq_len). A request without room is left as it is -- no demote, no append, its
+// length unchanged, flag bit 1 -- and its attention covers the cache as it stands.
+__device__ __forceinline__ bool step_active(const DecodeArgs& a, int b) {
+  return a.step && a.seq_len[b] < a.dm.max_seq_len;
+}
+
+// The fp32 rotation entries of a wavefront's 32-column slice (rotation_entries per k-step), loaded
+// in H parts of D/16/H k-steps (the first part before anything waits; wide workgroups, bound to 128
+// registers, hold half a slice at a time).
+template <int D, int H>
+struct RotEntries {
+  static constexpr int KP = D / 16 / H;   // k-steps per part
+  float r[KP][8];
+  __device__ void load(const float* rot, int w, int part, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) rotation_entries<D>(rot, w, part * KP + kk, lane, r[kk]);
+  }
+};
+
+// rotate_rows_loaded on entries in registers, part by part: the same products in the same order.
+template <int D, int H, typename XPtr>
+__device__ __forceinline__ float16v_t rotate_rows_entries(RotEntries<D, H>& re, const float* rot, int w, XPtr x,
+                                                          int stride, int nrows, int lane) {
+  constexpr int KP = RotEntries<D, H>::KP;
+  float16v_t acc = {};
+#pragma unroll
+  for (int part = 0; part < H; ++part) {
+    if (part > 0) {
+      __builtin_amdgcn_sched_barrier(0);   // the next part's loads reuse this part's registers
+      re.load(rot, w, part, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) {
+      bf16x8_t hi, mid, lo;
+      split_rotation(re.r[kk], hi, mid, lo);
+      acc = rotation_step(rotation_a(x, stride, nrows, part * KP + kk, lane), hi, mid, lo, acc);
+    }
+  }
+  return acc;
+}
+
+// The step work of (request b, kv-head kv), with T = seq_len[b] tokens before the step. Demote
+// (T >= sink + recent): the token at T - recent is read from its ring slot, rotated and quantised
+// with the demote kernel's own arithmetic (same rotation order, same grid), and its codes go into
+// its history slot, which no history segment reads yet (it lies past their token count); its
+// one-token partial -- lse = q' . k_hat, o = v_hat, rotated basis -- fills step slot 0 (lse = -inf
+// without a demote). The new token's one-token partial -- lse = scale * log2(e) * q . k_new,
+// o = v_new -- fills step slot 1. Both logits are summed in fp64 from exact products. The lengths
+// after the step are written here too; the new token's window copy is written by the merge, after
+// every window read.
+// The segment is a chain of latencies, so every global load is issued before anything waits on
+// one: the lengths, then at once the demoted token, the queries, the new token, the page id of the
+// history slot, the codebooks and each wavefront's rotation slices.
+template <int D, int GQ, int NW>
+__device__ void step_seg(const DecodeArgs& a, const CacheWriteArgs& cw, int b, int kv, StepLds<D, GQ>& L) {
   constexpr int SL = D / 32;   // 32-column slices of the rotation
+  constexpr int NT = NW * kWave;
+  constexpr int ROWS = 4 + GQ; // demoted key, demoted value, new key, new value, queries
+  constexpr int PER = (ROWS * D + NT - 1) / NT;
+  // the value slices go to their own wavefronts when there are enough of them
+  constexpr bool VPAR = NW >= 2 * SL;
   const Dims& dm = a.dm;
-  const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int bk = b * dm.hkv + kv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   // cache-side lengths exactly as the demote kernel reads them
   const int T = a.seq_len[b] < 0 ? 0 : a.seq_len[b];
+  const bool active = step_active(a, b);
   const int n4 = (dm.mixed && a.n_int4) ? a.n_int4[b] : 0;
-  const bool demote = T >= dm.sink + dm.recent;
+  const bool demote = active && T >= dm.sink + dm.recent;
   const int bw = (demote && dm.mixed && cw.bits && cw.bits[b] == 4) ? 4 : 2;
   const int dslot = bw == 4 ? n4 : T - dm.sink - dm.recent - n4;
   const int64_t page = demote ? demote_page(cw, b, dslot, bw) : -1;
@@ -494,20 +717,51 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
   int opg = 0, ot = 0;
   if (demote) window_slot(T - dm.recent, dm, opg, ot);
   const uint16_t* og = reinterpret_cast<const uint16_t*>(a.window + ((size_t)bk * dm.wpages + opg) * pb);
-  for (int idx = tid; idx < (2 + GQ) * D; idx += kSplitWaves * kWave) {
+  uint16_t v[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + NT * e;
     const int r = idx / D, ch = idx % D;
-    if (r == 0)
-      L.xs[0][ch] = demote ? og[bf16_key_index(D, ot, ch)] : (uint16_t)0;
-    else if (r == 1)
-      L.xv[ch] = demote ? og[bf16_value_index(D, ot, ch)] : (uint16_t)0;
-    else
-      L.xs[r - 1][ch] = a.q[(qrow + r - 2) * D + ch];
+    uint16_t x = 0;
+    if (idx < ROWS * D) {
+      if (r == 0) x = demote ? og[bf16_key_index(D, ot, ch)] : (uint16_t)0;
+      else if (r == 1) x = demote ? og[bf16_value_index(D, ot, ch)] : (uint16_t)0;
+      else if (r == 2) x = cw.k[(size_t)bk * D + ch];
+      else if (r == 3) x = cw.v[(size_t)bk * D + ch];
+      else x = a.q[(qrow + r - 4) * D + ch];
+    }
+    v[e] = x;
+  }
+  const Codebook cbk = load_codebook(cw.codebook, kv, 0);
+  const Codebook cbv = load_codebook(cw.codebook, kv, 1);
+  // one slice per wavefront: K slices on wavefronts 0..SL-1, V slices on SL..2SL-1 (or, with fewer
+  // wavefronts, on 0..SL-1 again after their K products)
+  constexpr int H = NW >= 16 ? 2 : 1;
+  RotEntries<D, H> re;
+  const int vw = VPAR ? wave - SL : wave;
+  const bool vwave = VPAR ? (wave >= SL && wave < 2 * SL) : wave < SL;
+  const float* rk = a.rot_k + (size_t)kv * D * D;
+  const float* rvp = a.rot_v + (size_t)kv * D * D;
+  if (wave < SL) re.load(rk, wave, 0, lane);
+  else if (vwave) re.load(rvp, vw, 0, lane);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + NT * e;
+    const int r = idx / D, ch = idx % D;
+    if (idx < ROWS * D) {
+      if (r == 0) L.xs[0][ch] = v[e];
+      else if (r == 1) L.xv[ch] = v[e];
+      else if (r == 2) L.nk[ch] = v[e];
+      else if (r == 3) L.nv[ch] = v[e];
+      else L.xs[r - 3][ch] = v[e];
+    }
   }
   __syncthreads();
+  OSCAR_TL_SPLIT(9);
   // one matrix-core pass rotates the key (row 0, the demote's own arithmetic) and the queries
   // (rows 1..GQ) with R_K; a second rotates the value with R_V
   if (wave < SL) {
-    const float16v_t acc = rotate_rows_streamed<D>(a.rot_k + (size_t)kv * D * D, wave, &L.xs[0][0], D, 1 + GQ, lane);
+    const float16v_t acc = rotate_rows_entries<D, H>(re, rk, wave, &L.xs[0][0], D, 1 + GQ, lane);
     const int n = 32 * wave + lane % 32;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -517,88 +771,78 @@ __device__ void step_role(const DecodeArgs& a, const CacheWriteArgs& cw, int bk,
       else if (m <= GQ)
         L.vq[m - 1][n] = acc[j] * a.scale_log2e;
     }
-    const float16v_t accv = rotate_rows_streamed<D>(a.rot_v + (size_t)kv * D * D, wave, L.xv, D, 1, lane);
-    if (lane < 32) L.xr[1][n] = accv[0];
+  }
+  if (vwave) {
+    if (!VPAR) re.load(rvp, vw, 0, lane);
+    const float16v_t accv = rotate_rows_entries<D, H>(re, rvp, vw, L.xv, D, 1, lane);
+    if (lane < 32) L.xr[1][32 * vw + lane] = accv[0];
   }
   __syncthreads();
+  OSCAR_TL_SPLIT(10);
   if (demote && wave < 2) {
     const float clip = bw == 4 ? (wave ? cw.clip_v4 : cw.clip_k4) : (wave ? cw.clip_v : cw.clip_k);
-    quantize_token<D>(L.xr[wave], clip, bw, L.cs[wave], &L.szs[wave], lane, load_codebook(cw.codebook, kv, wave));
+    quantize_token<D>(L.xr[wave], clip, bw, L.cs[wave], &L.szs[wave], lane, wave ? cbv : cbk);
   }
   __syncthreads();
   if (demote) {
-    store_token<D>(cw, page, kv, bw, dslot % kPage, 0, L.cs[0], L.szs[0], tid, kSplitWaves * kWave);
-    store_token<D>(cw, page, kv, bw, dslot % kPage, 1, L.cs[1], L.szs[1], tid, kSplitWaves * kWave);
+    store_token<D>(cw, page, kv, bw, dslot % kPage, 0, L.cs[0], L.szs[0], tid, NT);
+    store_token<D>(cw, page, kv, bw, dslot % kPage, 1, L.cs[1], L.szs[1], tid, NT);
   }
-  const size_t sb = (size_t)bk * a.ws.ns;
-  float* po_d = a.ws.part_o + (sb + a.ws.ns - 1) * GQ * D;
-  float* pl_d = a.ws.part_lse + (sb + a.ws.ns - 1) * GQ;
-  float* po_n = a.ws.part_o + (sb + wslot) * GQ * D;
-  float* pl_n = a.ws.part_lse + (sb + wslot) * GQ;
-  const uint16_t* nk = cw.k + (size_t)bk * D;
-  const uint16_t* nv = cw.v + (size_t)bk * D;
+  OSCAR_TL_SPLIT(11);
+  float* po_d = a.ws.step_o + ((size_t)bk * 2) * GQ * D;
+  float* pl_d = a.ws.step_lse + ((size_t)bk * 2) * GQ;
+  float* po_n = po_d + GQ * D;
+  float* pl_n = pl_d + GQ;
   const double sk = __uint_as_float(L.szs[0] << 16), zk = __uint_as_float(L.szs[0] & 0xFFFF0000u);
   const float sv = __uint_as_float(L.szs[1] << 16), zv = __uint_as_float(L.szs[1] & 0xFFFF0000u);
   // restored values: z + s * level (the code itself, or the codebook's level of an INT2 code)
   const bool lvk = bw == 2 && cw.codebook != nullptr;
-  const Codebook cbk = load_codebook(lvk ? cw.codebook : nullptr, kv, 0);
-  const Codebook cbv = load_codebook(lvk ? cw.codebook : nullptr, kv, 1);
   auto level = [&](const Codebook& cb, uint32_t code) { return lvk ? codebook_level(cb, code) : (float)code; };
-  for (int h = wave; h < GQ; h += kSplitWaves) {
+  for (int h = wave; h < GQ; h += NW) {
     double ld = 0.0, ln = 0.0;
     for (int ch = lane; ch < D; ch += kWave) {
       if (demote) ld += (double)L.vq[h][ch] * (sk * (double)level(cbk, L.cs[0][ch]) + zk);
-      ln += (double)bf16_bits_to_f32(L.xs[1 + h][ch]) * (double)bf16_bits_to_f32(nk[ch]);
+      if (active) ln += (double)bf16_bits_to_f32(L.xs[1 + h][ch]) * (double)bf16_bits_to_f32(L.nk[ch]);
     }
     ld = wave_sum_f64(ld);
     ln = wave_sum_f64(ln);
     if (lane == 0) {
       pl_d[h] = demote ? (float)ld : kNegInf;
-      pl_n[h] = (float)(ln * (double)a.scale_log2e);
+      pl_n[h] = active ? (float)(ln * (double)a.scale_log2e) : kNegInf;
     }
   }
-  for (int idx = tid; idx < GQ * D; idx += kSplitWaves * kWave) {
+  for (int idx = tid; idx < GQ * D; idx += NT) {
     const int ch = idx % D;
-    if (demote) po_d[idx] = fmaf(sv, level(cbv, L.cs[1][ch]), zv);
-    po_n[idx] = bf16_bits_to_f32(nv[ch]);
+    po_d[idx] = demote ? fmaf(sv, level(cbv, L.cs[1][ch]), zv) : 0.0f;
+    po_n[idx] = active ? bf16_bits_to_f32(L.nv[ch]) : 0.0f;
   }
   if (kv == 0 && tid == 0) {
-    if (cw.seq_len_out) cw.seq_len_out[b] = T + 1;
+    if (cw.seq_len_out) cw.seq_len_out[b] = active ? T + 1 : a.seq_len[b];
     if (cw.n_int4_out) cw.n_int4_out[b] = n4 + ((demote && bw == 4) ? 1 : 0);
+    if (!active) atomicOr(a.ws.flags, 2u);
   }
 }
 
-// Window role: the nw window workgroups of (b, kv) (in a fused step the last one is the step
-// workgroup) share the window pages; wavefront w of workgroup wi takes pages 4 wi + w, stepping by
-// 4 (nw - step), with the next page loading while one is processed. In a fused step the ring slot of
-// the demoted token (position T - recent) is left to the step workgroup.
-template <int D, int GQ>
-__device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int idx, float (*o_lds)[2 * GQ][D],
-                            float (*st_lds)[3][8], StepLds<D, GQ>& slds) {
+// Window segment: the window pages w0, w0 + ws, w0 + 2 ws, ... of (b, kv) (sink pages, then the
+// recent ring); wavefront w takes the w-th, (w + NW)-th, ... of them, with the next page loading
+// while one is processed (single pages with many wavefronts: each has at most one or two). In a
+// fused step the ring slot of the demoted token (position T - recent) is left to the step segment.
+template <int D, int GQ, int NW>
+__device__ void window_seg(const DecodeArgs& a, int b, int kv, int w0, int ws, float* po, float* pl,
+                           float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8]) {
   const Dims& dm = a.dm;
-  const int nw = a.ws.nwin;
-  const int wi = idx % nw, bk = idx / nw, kv = bk % dm.hkv, b = bk / dm.hkv;
-  if (a.step && wi == nw - 1) {
-    OSCAR_TL_SPLIT_VALUE(4, 3);
-    step_role<D, GQ>(a, cw, bk, wi, slds);
-    return;
-  }
-  OSCAR_TL_SPLIT_VALUE(4, 2);
+  const int bk = b * dm.hkv + kv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
+  const bool skip_demoted = step_active(a, b);
   u32x4_t bq[D / 32];
   load_bf16_query<D, GQ>(bq, a.q, (size_t)b * dm.hq + (size_t)kv * GQ, lane);
   WaveState<D, GQ> st;
   st.init();
   const int64_t pb = bf16_page_head_bytes(D);
   const uint8_t* wbase = a.window + (size_t)bk * dm.wpages * pb;
-  const int stride = kSplitWaves * (nw - a.step);
-  int pg = kSplitWaves * wi + wave;
-  Bf16Page<D> cur, nxt;
-  if (pg < dm.wpages) load_bf16_page<D>(cur, wbase + pg * pb, lane);
-  for (; pg < dm.wpages; pg += stride) {
-    if (pg + stride < dm.wpages) load_bf16_page<D>(nxt, wbase + (pg + stride) * pb, lane);
+  auto process = [&](const Bf16Page<D>& cur, int pg) {
     bool valid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -611,15 +855,30 @@ __device__ void window_role(const DecodeArgs& a, const CacheWriteArgs& cw, int i
         const int sl = kPage * (pg - dm.sink / kPage) + t;
         int back = (T - 1 - sl) % dm.recent;
         if (back < 0) back += dm.recent;
-        valid[r] = T - 1 - back >= dm.sink && !(a.step && back == dm.recent - 1);
+        valid[r] = T - 1 - back >= dm.sink && !(skip_demoted && back == dm.recent - 1);
       }
     }
     process_bf16_page<D, GQ>(st, cur, bq, valid, a.scale_log2e, lane);
-    cur = nxt;
+  };
+  const int w1 = dm.wpages, stride = NW * ws;
+  int pg = w0 + wave * ws;
+  if constexpr (NW >= 8) {
+    for (; pg < w1; pg += stride) {
+      Bf16Page<D> cur;
+      load_bf16_page<D>(cur, wbase + pg * pb, lane);
+      process(cur, pg);
+    }
+  } else {
+    Bf16Page<D> cur, nxt;
+    if (pg < w1) load_bf16_page<D>(cur, wbase + pg * pb, lane);
+    for (; pg < w1; pg += stride) {
+      if (pg + stride < w1) load_bf16_page<D>(nxt, wbase + (pg + stride) * pb, lane);
+      process(cur, pg);
+      cur = nxt;
+    }
   }
-  const size_t pbase = ((size_t)b * dm.hkv + kv) * a.ws.ns + wi;
-  workgroup_merge<D, GQ, 16, false, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
-                                                 a.ws.part_lse + pbase * GQ);
+  // wavefronts past the unit's window pages hold no state
+  workgroup_merge<D, GQ, 16, false, NW>(st, o_lds, st_lds, po, pl, min(NW, (w1 - w0 + ws - 1) / ws));
 }
 
 // ------------------------------------------------------------------ INT2 / INT4 history pages
@@ -1015,93 +1274,74 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   }
 }
 
-// LUT (INT2 with a codebook): codes enter both products as their codebook levels.
-template <int BITS, int D, int GQ, bool LUT = false>
-__device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
-                          HistQueryLds<D, GQ>& qlds) {
+// Page ids of a chunk of a wavefront's pages: lane i holds the id of page cb + i (i < kIdChunk), or
+// -1 at or past wp1. A page's address is formed from its id on the scalar unit when it is loaded.
+constexpr int kIdChunk = 60;   // a multiple of both ring depths (4 and 6 pages)
+
+__device__ __forceinline__ int page_chunk(const int32_t* pt, int cb, int wp1, int lane) {
+  const int idx = cb + lane;
+  return (lane < kIdChunk && idx < wp1) ? pt[idx] : -1;
+}
+
+// History segment: pages [p0, p1) of width BITS of (b, kv), split into contiguous ranges of the NW
+// wavefronts; the workgroup's partial (rotated basis) goes to po / pl. LUT (INT2 with a codebook):
+// codes enter both products as their codebook levels.
+// PRE: the rotation rows (rr) are already loaded, and the queries (qin) too when q_ready.
+template <int BITS, int D, int GQ, int NW, bool LUT = false, bool PRE = false>
+__device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, float* po, float* pl,
+                         float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8], HistQueryLds<D, GQ, NW>& qlds,
+                         QRotRows<D, NW * kWave>& rr, QueryIn<D, GQ, NW * kWave>& qin, bool q_ready) {
+  constexpr int NT = NW * kWave;
+  // Load ring of NB page buffers, taken as NB/2 page pairs (compile-time indices). With six pages
+  // (below GQA 8) the QK^T products run one pair ahead: the matrix cores work on pair k+1 while the vector units
+  // run the softmax of pair k, and the loads of pair k+2 are in flight. Wide workgroups (four
+  // wavefronts per SIMD, 128 registers each) keep four pages: the loads of pair k+1 in flight while
+  // pair k is processed, and the other wavefronts of the SIMD fill the gaps.
+  constexpr int NB = NW >= 8 ? OSCAR_WIDE_RING : (BITS == 2 ? kHistPipe2 : kHistPipe4);
+  // at GQA 8 the products are formed right before their softmax: the two results held one pair
+  // ahead do not fit the register bound of three workgroups per compute unit
+  constexpr bool AHEAD = NB >= 6 && GQ < 8 && NW < 8;
+  static_assert(NB % 2 == 0 && NB >= 4 && kIdChunk % NB == 0, "the ring holds whole page pairs");
   const Dims& dm = a.dm;
-  // Split-major order: consecutive workgroups take split s of consecutive (request, kv-head)
-  // groups. The dispatcher deals workgroups to the 8 XCDs in turn, so with the (request, kv-head)
-  // index fastest every XCD gets the same share of each split; with the split index fastest (and 8
-  // dividing the split count) split s would always land on the same XCD, and where only the low
-  // splits hold pages (ragged lengths, a mixed cache's two widths) a few XCDs would do the work.
-  const int nbk = dm.batch * dm.hkv;
-  const int s = idx / nbk;
-  const int bk = idx % nbk;
-  const int kv = bk % dm.hkv, b = bk / dm.hkv;
-  const int ppw = a.ws.ppw;
-  const int pg_begin = s * kSplitWaves * ppw;
   const int tid = threadIdx.x, lane = tid % kWave, c = lane % 16;
   const int wave = uniform(tid / kWave);
-  const int wp0 = uniform(pg_begin + wave * ppw);
-  const int slot = a.ws.nwin + (BITS == 2 ? s : a.ws.s2 + s);
-  const size_t pbase = (size_t)bk * a.ws.ns + slot;
-
-  // Loads that do not depend on the request's length are issued first, branch-free and side by
-  // side with it: the page ids of this wavefront's range (lane i: page wp0+i; the index is clamped
-  // to the table stride, which is >= 1 whenever history splits exist), the rows of R_K and the
-  // queries of the group for the query prologue.
+  const int ppw = (p1 - p0 + NW - 1) / NW;
+  const int wp0 = uniform(min(p0 + wave * ppw, p1));
+  const int wp1 = uniform(min(wp0 + ppw, p1));
   const int32_t* pt = (BITS == 2 ? a.pt2 : a.pt4) + (size_t)b * dm.pt_stride;
-  const int pidx = wp0 + lane;
-  const int32_t raw_page = pt[min(pidx, dm.pt_stride - 1)];
   const size_t qbase = (size_t)b * dm.hq + (size_t)kv * GQ;
-  // query operands: precomputed by the prologue kernel (then loaded here), or formed below
-  const bool qpre = a.ws.qpre != 0;
-  QRotRows<D> rr;
-  uint32_t qw[kQueryWords<D, GQ>];
-  u32x4_t qv[D / 32];
-  float4 qk = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (qpre) {
-    const size_t unit = (size_t)(BITS == 4) * dm.batch * dm.hkv + bk;
-    const uint16_t* qop = a.ws.qop + (unit * 2 + (c < GQ ? 0 : 1)) * GQ * D + (size_t)(c % GQ) * D + 8 * (lane / 16);
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const u32x4_t z = {0, 0, 0, 0};
-      qv[kk] = c < 2 * GQ ? *reinterpret_cast<const u32x4_t*>(qop + 32 * kk) : z;
-    }
-    qk = *reinterpret_cast<const float4*>(a.ws.qhs + (unit * GQ + c % GQ) * 4);
-  } else {
-    rr.load(a.rot_k + (size_t)kv * D * D, tid);
-    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + qbase * D);
-#pragma unroll
-    for (int i = 0; i < kQueryWords<D, GQ>; ++i) {
-      const int e = tid + 256 * i;
-      qw[i] = e < GQ * D / 2 ? qsrc[e] : 0u;
-    }
-  }
+
+  // Loads first, side by side: the page ids of this wavefront's first two chunks, the rows of R_K and
+  // the queries of the group for the query prologue.
+  int cur = page_chunk(pt, wp0, wp1, lane);
+  int nxt = page_chunk(pt, wp0 + kIdChunk, wp1, lane);
+  if (!PRE) rr.load(a.rot_k + (size_t)kv * D * D, tid);
+  if (!PRE || !q_ready) qin.load(a.q + qbase * D, tid);
   const HistCounts hc = hist_counts(a, b);
   const int ntok = BITS == 2 ? hc.n2 : hc.n4;
-  const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
-  // a wavefront (or a whole workgroup) past the history processes no page and leaves an empty
-  // partial (lse = -inf)
-  const int wp1 = uniform(max(wp0, min(wp0 + ppw, npages)));
-  const int64_t page = (lane < ppw && pidx < dm.pt_stride) ? (int64_t)raw_page : -1;
 
   // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
   // hi/hi halves on lanes 4..7, zero elsewhere)
   const uint32_t psel = c < 4 ? 0x05040100u : (c < 8 ? 0x03020706u : 0x0C0C0C0Cu);
   WaveState<D, GQ> st;
   st.init();
-  const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
-  // Page-head addresses: ids outside the pool or of the other width are invalid and point at
-  // page-head 0 of the arena, which also serves the prefetches past the range.
-  const bool page_ok = page >= 0 && page < dm.pool_pages && (BITS == 2 ? page < off4 : page >= off4);
-  const uint64_t my_addr = (uint64_t)(page_ok ? page_head_addr(a.pool, page, kv, dm.hkv, D, off4) : a.pool);
-  const uint64_t valid_mask = __ballot(page_ok);
-  const uint32_t addr_lo = (uint32_t)my_addr, addr_hi = (uint32_t)(my_addr >> 32);
   if (dm.pool_pages > 0) {
-    // Load ring of NB page buffers, taken as NB/2 page pairs (compile-time indices; prefetches
-    // past the range read the dummy page-head). The QK^T products run one pair ahead: the matrix
-    // cores work on pair k+1 while the vector units run the softmax of pair k, and the loads of
-    // pair k+2 are in flight.
-    constexpr int NB = BITS == 2 ? kHistPipe2 : kHistPipe4;
-    static_assert(NB % 2 == 0 && NB >= 6, "the history ring holds three or more page pairs");
+    int cbase = wp0;
+    // Page-head address of a page (uniform): ids outside the pool or of the other width are invalid
+    // and read page-head 0 of the arena instead, as do the prefetches past the range.
+    const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
+    const int64_t head = qpage_head_bytes(D, BITS);
+    const uint64_t region = (uint64_t)a.pool + (BITS == 2 ? 0 : (uint64_t)(off4 * qpage_head_bytes(D, 2) * dm.hkv));
+    const int64_t first_id = BITS == 2 ? 0 : off4;
     auto load = [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
-      const int li = min(pg - wp0, kWave - 1);
-      const uint64_t ad = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_lo, li) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)addr_hi, li) << 32);
+      const int li = pg - cbase;
+      const int id_cur = __builtin_amdgcn_readlane(cur, min(li, kWave - 1));
+      const int id_nxt = __builtin_amdgcn_readlane(nxt, max(li - kIdChunk, 0));
+      const int64_t id = li < kIdChunk ? id_cur : id_nxt;
+      const bool valid = id >= first_id && id < (BITS == 2 ? off4 : dm.pool_pages);
+      const uint64_t ad = valid ? region + (uint64_t)(((id - first_id) * dm.hkv + kv) * head) : (uint64_t)a.pool;
       load_qpage<BITS, D, GQ>(pr, ad, lane);
-      return pg < wp1 && ((valid_mask >> li) & 1u);
+      return pg < wp1 && valid;
     };
     QPage<BITS, D, GQ> buf[NB];
     bool ok[NB];
@@ -1110,31 +1350,36 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
     __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
     half8_t bq[D / 32];
     float uh, ul, esc;
-    if (qpre) {
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) bq[kk] = __builtin_bit_cast(half8_t, qv[kk]);
-      uh = qk.x;
-      ul = qk.y;
-      esc = qk.z;
-    } else {
-      hist_query_operands<BITS, D, GQ, LUT>(rr, qw, qlds, a.scale_log2e, bq, uh, ul, esc);
-    }
-    OSCAR_TL_SPLIT(1);
-    OSCAR_TL_SPLIT_VALUE(4, (BITS == 4 ? 1u : 0u) | ((uint32_t)(wp1 - wp0) << 8));
+    hist_query_operands<BITS, D, GQ, NW, LUT>(rr, qin, qlds, a.scale_log2e, bq, uh, ul, esc);
+    OSCAR_TL_SPLIT(3);
     const float uq = uh + ul;   // sum of the query operand of this lane's head
     const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
     const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
-    float4_t acc0 = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
-    float4_t acc1 = qk_page<BITS, D, GQ, LUT>(buf[1], bq, cbk);
+    float4_t acc0, acc1;
+    if constexpr (AHEAD) {
+      acc0 = qk_page<BITS, D, GQ, LUT>(buf[0], bq, cbk);
+      acc1 = qk_page<BITS, D, GQ, LUT>(buf[1], bq, cbk);
+    }
     for (int pg = wp0; pg < wp1; pg += NB) {
       progress_priority(pg - wp0, wp1 - wp0);
+      if (pg - cbase >= kIdChunk) {   // the next chunk of page ids becomes the current one
+        cur = nxt;
+        cbase += kIdChunk;
+        nxt = page_chunk(pt, cbase + kIdChunk, wp1, lane);
+      }
 #pragma unroll
       for (int k = 0; k < NB; k += 2) {
         ok[(k + NB - 2) % NB] = load(buf[(k + NB - 2) % NB], pg + k + NB - 2);
         ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], pg + k + NB - 1);
         if (pg + k < wp1) {
-          const float4_t n0 = qk_page<BITS, D, GQ, LUT>(buf[(k + 2) % NB], bq, cbk);
-          const float4_t n1 = qk_page<BITS, D, GQ, LUT>(buf[(k + 3) % NB], bq, cbk);
+          float4_t n0, n1;
+          if constexpr (AHEAD) {
+            n0 = qk_page<BITS, D, GQ, LUT>(buf[(k + 2) % NB], bq, cbk);
+            n1 = qk_page<BITS, D, GQ, LUT>(buf[(k + 3) % NB], bq, cbk);
+          } else {
+            acc0 = qk_page<BITS, D, GQ, LUT>(buf[k], bq, cbk);
+            acc1 = qk_page<BITS, D, GQ, LUT>(buf[k + 1], bq, cbk);
+          }
           // a page past the range is masked; a page id outside the pool or of the other width is
           // masked and flagged (every page of the range carries at least one token)
           if (ok[k] || ok[k + 1]) {
@@ -1143,70 +1388,113 @@ __device__ void hist_role(const DecodeArgs& a, int idx, float (*o_lds)[2 * GQ][D
                                             ok[k + 1] ? ntok - (pg + k + 1) * kPage : 0, lane, cbv);
           }
           if ((!ok[k] || (!ok[k + 1] && pg + k + 1 < wp1)) && lane == 0) atomicOr(a.ws.flags, 1u);
-          acc0 = n0;
-          acc1 = n1;
+          if constexpr (AHEAD) {
+            acc0 = n0;
+            acc1 = n1;
+          }
         }
       }
     }
   } else if (lane == 0 && wp0 < wp1) {
     atomicOr(a.ws.flags, 1u);
   }
-  OSCAR_TL_SPLIT(2);
+  OSCAR_TL_SPLIT(4);
   // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
   __syncthreads();
-  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, kSplitWaves>(st, o_lds, st_lds, a.ws.part_o + pbase * GQ * D,
-                                                             a.ws.part_lse + pbase * GQ);
+  OSCAR_TL_SPLIT(8);
+  // wavefronts past the segment's pages hold no state
+  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl,
+                                                              ppw > 0 ? min(NW, (p1 - p0 + ppw - 1) / ppw) : 1);
 }
 
-// LDS of the roles that need more than the merge buffers (one role per workgroup); 16-byte aligned
-// for the vector reads of the query operands
-template <int D, int GQ>
+// LDS of the segments (one at a time per workgroup); 16-byte aligned for the vector reads of the
+// query operands
+template <int D, int GQ, int NW>
 union alignas(16) SplitScratch {
-  HistQueryLds<D, GQ> hist;
+  HistQueryLds<D, GQ, NW> hist;
   StepLds<D, GQ> step;
-  float o[kSplitWaves][2 * GQ][D];   // workgroup merge of the history and window roles
+  float o[NW][2 * GQ][D];   // workgroup merge of the history and window segments
 };
 
 // Workgroups of a split launch that a compute unit should hold: three at GQA 8 in an INT2-only
-// cache (the register count is then bounded to fit), else what the resources give.
-template <int GQ, bool MIXED>
-constexpr int kSplitMinBlocks = (GQ == 8 && !MIXED) ? 3 : 1;
+// cache (the register count is then bounded to fit), one of the wide workgroups, else what the
+// resources give.
+template <int GQ, bool MIXED, int NW>
+constexpr int kSplitMinBlocks = NW >= 16 ? 1 : (NW >= 8 ? 2 : ((GQ == 8 && !MIXED) ? 3 : 1));
 
+// One workgroup per unit of the work plan: workgroup g is unit (g / Hkv) of kv-head g % Hkv. It
+// runs the segments its cost range holds, in order: the step, window pages, INT2 pages, INT4 pages,
+// each writing its own partial (window: original basis; history: rotated basis); the partials of
+// kinds the unit does not hold get lse = -inf. The first unit of kv-head 0 of each request records
+// the request's units for the merge.
 // CB: the INT2 history uses the codebook table of the decode arguments. MIXED: the cache has INT4
-// pages (an INT2-only launch carries no INT4 role, which keeps its register count down).
-template <int D, int GQ, bool CB, bool MIXED>
-__global__ __launch_bounds__(kSplitWaves * kWave, (kSplitMinBlocks<GQ, MIXED>)) void split_kernel(DecodeArgs a,
-                                                                                               CacheWriteArgs cw) {
-  __shared__ float st_lds[kSplitWaves][3][8];
-  __shared__ SplitScratch<D, GQ> scr;
-  float (*o_lds)[2 * GQ][D] = scr.o;
-  // Long roles first: the history workgroups take the low indices, so the dispatcher starts them
-  // first, and the shorter window and step workgroups fill the compute units that free up while
-  // the last history workgroups run.
-  const int n_int2 = a.dm.batch * a.dm.hkv * a.ws.s2;
-  const int n_hist = n_int2 + a.dm.batch * a.dm.hkv * a.ws.s4;
-  const int bid = blockIdx.x;
+// pages (an INT2-only launch carries no INT4 segment, which keeps its register count down).
+// Wide workgroups (NW = 16, one per compute unit) load their rotation rows before the plan (the
+// kv-head does not depend on it).
+template <int D, int GQ, bool CB, bool MIXED, int NW>
+__global__ __launch_bounds__(NW * kWave, (kSplitMinBlocks<GQ, MIXED, NW>)) void split_kernel(DecodeArgs a,
+                                                                                         CacheWriteArgs cw) {
+  constexpr int NT = NW * kWave;
+  constexpr bool PRE = NW >= 16;
+  __shared__ float st_lds[NW][3][8];
+  __shared__ SplitScratch<D, GQ, NW> scr;
   OSCAR_TL_SPLIT(0);
 #ifdef OSCAR_TIMELINE
-  OSCAR_TL_SPLIT_VALUE(5, timeline_placement());
+  OSCAR_TL_SPLIT_VALUE(7, timeline_placement());
 #endif
-  if (bid < n_int2) {
-    hist_role<2, D, GQ, CB>(a, bid, o_lds, st_lds, scr.hist);
-  } else if (MIXED && bid < n_hist) {
-    hist_role<4, D, GQ>(a, bid - n_int2, o_lds, st_lds, scr.hist);
-  } else {
-    window_role<D, GQ>(a, cw, bid - n_hist, o_lds, st_lds, scr.step);
+  const int hkv = a.dm.hkv;
+  const int g = blockIdx.x, kv = g % hkv, tid = threadIdx.x;
+  QRotRows<D, NT> rr;
+  QueryIn<D, GQ, NT> qin;
+  if constexpr (PRE) rr.load(a.rot_k + (size_t)kv * D * D, tid);
+  const RequestUnits ru = request_units(a, g / hkv);   // the same in every wavefront
+  OSCAR_TL_SPLIT(1);
+  if (ru.b >= 0) {
+    const int j = g / hkv - ru.first;
+    int c0, c1;
+    unit_range(ru, j, c0, c1);
+    const Segments sg = unit_segments(a, ru.rc, c0, c1);
+    float* po = a.ws.part_o + (size_t)g * 3 * GQ * D;
+    float* pl = a.ws.part_lse + (size_t)g * 3 * GQ;
+    const bool has[3] = {sg.window, sg.p20 < sg.p21, MIXED && sg.p40 < sg.p41};
+    if (tid < 3 * GQ && !has[tid / GQ]) pl[tid] = kNegInf;
+    if (kv == 0 && j == 0 && tid == 0) {
+      a.ws.req_units[2 * ru.b] = ru.first;
+      a.ws.req_units[2 * ru.b + 1] = ru.n;
+    }
+    OSCAR_TL_SPLIT_VALUE(6, (sg.step ? 1u : 0u) | (has[0] ? 2u : 0u) | (has[1] ? 4u : 0u) | (has[2] ? 8u : 0u) |
+                                ((uint32_t)(has[1] ? sg.p21 - sg.p20 : sg.p41 - sg.p40) << 8));
+    if (sg.step) {
+      step_seg<D, GQ, NW>(a, cw, ru.b, kv, scr.step);
+      __syncthreads();
+    }
+    if (has[0]) {
+      window_seg<D, GQ, NW>(a, ru.b, kv, 0, 1, po, pl, scr.o, st_lds);
+      __syncthreads();
+    }
+    OSCAR_TL_SPLIT(2);
+    if (has[1]) {
+      hist_seg<2, D, GQ, NW, CB, PRE>(a, ru.b, kv, sg.p20, sg.p21, po + GQ * D, pl + GQ, scr.o, st_lds, scr.hist,
+                                       rr, qin, false);
+      __syncthreads();
+    }
+    if constexpr (MIXED) {
+      if (has[2])
+        hist_seg<4, D, GQ, NW>(a, ru.b, kv, sg.p40, sg.p41, po + 2 * GQ * D, pl + 2 * GQ, scr.o, st_lds, scr.hist,
+                               rr, qin, false);
+    }
   }
-  OSCAR_TL_SPLIT(3);
+  OSCAR_TL_SPLIT(5);
 }
 
 // ------------------------------------------------------------------ merge
 // One 1024-thread workgroup per (request, kv-head, group of HPW query heads) merges every partial
-// slot of the (request, kv-head) -- window slots, INT2 and INT4 history slots, the step's
-// one-token slots; slots of splits past the history hold lse = -inf -- for its heads, in one pass:
-// each thread folds its slots with a running maximum (lse in log2 units), the threads' states are
-// combined through LDS, the history sum (rotated basis of the values) is un-rotated with R_V^T
-// (each R_V row read once per workgroup) and added to the window sum.
+// of the (request, kv-head) for its heads, in one pass -- the window, INT2 and INT4 partials of each
+// of the request's units (found through the unit table the split writes; kinds a unit does not hold
+// carry lse = -inf) and the step's two one-token partials: each thread folds
+// its slots with a running maximum (lse in log2 units), the threads' states are combined through
+// LDS, the history sum (rotated basis of the values) is un-rotated with R_V^T (each R_V row read
+// once per workgroup) and added to the window sum.
 constexpr int kMergeThreads = 1024;
 // The merge is latency-bound: a launch gets the fewest query heads per workgroup (HW) that still
 // fits one workgroup per compute unit (a merge workgroup's LDS holds R_V, so a unit runs one).
@@ -1217,24 +1505,56 @@ struct MergeState {
   float4 ah, aw;   // weighted history / window sums of this thread's float4 column
 };
 struct MergeCtx {
-  const float* pl;     // lse of the group's slots [slot][GQ]
-  const float* po;     // o of the group's slots [slot][GQ][D]
-  const float* rv;     // R_V of the kv-head [D][D]
-  float* rv_s;         // LDS copy of R_V, padded rows
-  int n, nwin, grp, hh, c4, tid;   // hh: query head within the kv group
+  int first, units; // the request's units
+  int kv, bk;
+  int n;           // slots: 3 per unit (window, INT2, INT4), then 2 step slots in a fused step
+  const float* rv; // R_V of the kv-head [D][D]
+  float* rv_s;     // LDS copy of R_V, padded rows
+  int grp, hh, c4, tid;   // hh: query head within the kv group
 };
+
+// Partial slot i of a merge: its lse and o addresses (lse slot, o row of head hh) and whether it
+// is in the original basis (window) or the rotated one (history).
+template <int D, int GQ>
+__device__ __forceinline__ void merge_slot(const DecodeArgs& a, const MergeCtx& c, int i, size_t& lse_at,
+                                           size_t& o_at, bool& window, bool& step) {
+  const int nu = 3 * c.units;
+  step = i >= nu;
+  if (step) {
+    const size_t s = (size_t)c.bk * 2 + (i - nu);
+    lse_at = s * GQ + c.hh;
+    o_at = (s * GQ + c.hh) * D;
+    window = i - nu == 1;
+    return;
+  }
+  const int j = i / 3, kind = i - 3 * j;
+  window = kind == 0;
+  const size_t slot = ((size_t)a.dm.hkv * (c.first + j) + c.kv) * 3 + kind;
+  lse_at = slot * GQ + c.hh;
+  o_at = (slot * GQ + c.hh) * D;
+}
 
 // Folds slots base + grp + k*NG (k < MS) into the thread's state; with `stage`, also copies R_V
 // into LDS between issuing the slot loads and consuming them.
 template <int D, int GQ, int MS, int NG, int RS, int NT>
-__device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, int base, bool stage) {
+__device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, const MergeCtx& c, int base,
+                                           bool stage) {
   float lv[MS];
   float4 vv[MS];
+  bool use[MS], win[MS];
 #pragma unroll
   for (int k = 0; k < MS; ++k) {
-    const int i = min(base + c.grp + k * NG, c.n - 1);
-    lv[k] = c.pl[(size_t)i * GQ + c.hh];
-    vv[k] = *reinterpret_cast<const float4*>(c.po + ((size_t)i * GQ + c.hh) * D + 4 * c.c4);
+    const int i = base + c.grp + k * NG;
+    size_t la = 0, oa = 0;
+    bool window = false, step = false;
+    const bool live = i < c.n;
+    if (live) merge_slot<D, GQ>(a, c, i, la, oa, window, step);
+    use[k] = live;
+    win[k] = window;
+    const float* pl = step ? a.ws.step_lse : a.ws.part_lse;
+    const float* po = step ? a.ws.step_o : a.ws.part_o;
+    lv[k] = live ? pl[la] : kNegInf;
+    vv[k] = live ? *reinterpret_cast<const float4*>(po + oa + 4 * c.c4) : float4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   if (stage) {
     const float4* rv4 = reinterpret_cast<const float4*>(c.rv);
@@ -1251,9 +1571,8 @@ __device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, in
   }
 #pragma unroll
   for (int k = 0; k < MS; ++k) {
-    const int i = base + c.grp + k * NG;
-    // empty slots (lse = -inf, o not written) and clamped duplicates weigh 0
-    const float l = i < c.n ? lv[k] : kNegInf;
+    // slots past the last and empty partials (lse = -inf: no such segment, or no token) weigh 0
+    const float l = use[k] ? lv[k] : kNegInf;
     const bool live = l != kNegInf;
     const float m_new = fmaxf(st.m, l);
     const float sc = st.m == m_new ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);   // 0 when m is -inf
@@ -1261,7 +1580,7 @@ __device__ __forceinline__ void merge_fold(MergeState& st, const MergeCtx& c, in
     st.m = m_new;
     st.wsum = fmaf(st.wsum, sc, w);
     const float4 v = live ? vv[k] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-    const float wh = i < c.nwin ? 0.0f : w, ww = i < c.nwin ? w : 0.0f;
+    const float wh = win[k] ? 0.0f : w, ww = win[k] ? w : 0.0f;
     st.ah.x = fmaf(st.ah.x, sc, wh * v.x);
     st.ah.y = fmaf(st.ah.y, sc, wh * v.y);
     st.ah.z = fmaf(st.ah.z, sc, wh * v.z);
@@ -1318,28 +1637,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   const int bk = blockIdx.x / (GQ / HW), h0 = HW * (blockIdx.x % (GQ / HW));
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int tid = threadIdx.x;
-  const int nwin = a.ws.nwin, n = a.ws.ns;
-  const size_t sbase = (size_t)bk * n;
-  const float* pl = a.ws.part_lse + sbase * GQ;
-  const float* po = a.ws.part_o + sbase * GQ * D;
   const int hl = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
   // fused step: the new token's window slot is written at the end (every window read of the step
   // is done); its length is fetched now
-  const bool ring = a.step && h0 == 0 && tid < 2 * D;
+  const bool ring = step_active(a, b) && h0 == 0 && tid < 2 * D;
   const int t_len = ring ? a.seq_len[b] : 0;
-  // Slots are taken up to 12 at a time per thread: every load of a batch is issued (indices
-  // clamped to the last slot, so always in bounds) before any is consumed, and the first batch's
-  // loads share one round trip with the R_V staging.
+  const int first = a.ws.req_units[2 * b], units = a.ws.req_units[2 * b + 1];
+  const int n = 3 * units + (a.step ? 2 : 0);
+  // Slots are taken up to 12 at a time per thread: every load of a batch is issued (slots no segment
+  // wrote are not read) before any is consumed, and the first batch's loads share one round trip
+  // with the R_V staging.
   MergeState ms_st{kNegInf, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  const MergeCtx mc{pl, po, a.rot_v + (size_t)kv * D * D, rv_s, n, nwin, grp, h0 + hl, c4, tid};
+  const MergeCtx mc{first, units, kv, bk, n, a.rot_v + (size_t)kv * D * D, rv_s, grp, h0 + hl, c4, tid};
   const int per_thread = (n + NG - 1) / NG;   // uniform
   if (per_thread <= 4) {
-    merge_fold<D, GQ, 4, NG, RS, NT>(ms_st, mc, 0, true);
+    merge_fold<D, GQ, 4, NG, RS, NT>(a, ms_st, mc, 0, true);
   } else if (per_thread <= 12) {
-    merge_fold<D, GQ, 12, NG, RS, NT>(ms_st, mc, 0, true);
+    merge_fold<D, GQ, 12, NG, RS, NT>(a, ms_st, mc, 0, true);
   } else {
-    merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, 0, true);
-    for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(ms_st, mc, base, false);
+    merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, 0, true);
+    for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, base, false);
   }
   *reinterpret_cast<float4*>(&acc_h[grp][hl][4 * c4]) = ms_st.ah;
   *reinterpret_cast<float4*>(&acc_w[grp][hl][4 * c4]) = ms_st.aw;
@@ -1406,7 +1723,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
       }
     }
   }
-  OSCAR_TL_MERGE(3);
+  OSCAR_TL_MERGE(5);
   if (ring) {
     // the new token takes its window slot (the demoted token's ring slot, or position T), as the
     // demote kernel writes it
@@ -1548,36 +1865,59 @@ __global__ __launch_bounds__(256) void bf16_merge_kernel(Bf16Args a) {
 }
 
 // ------------------------------------------------------------------ launchers
+template <int D, int GQ, bool CB, bool MIXED, int NW>
+static const void* split_symbol() {
+  return reinterpret_cast<const void*>(&split_kernel<D, GQ, CB, MIXED, NW>);
+}
+
+// The split kernel instance of a launch (wide workgroups exist for GQA width 4 only).
+template <int D, int GQ>
+static const void* split_function(bool cb, bool mixed, int nw) {
+  if constexpr (GQ == 4) {
+    if (nw == kSplitWavesWide) {
+      if (mixed) return cb ? split_symbol<D, GQ, true, true, kSplitWavesWide>() : split_symbol<D, GQ, false, true, kSplitWavesWide>();
+      return cb ? split_symbol<D, GQ, true, false, kSplitWavesWide>() : split_symbol<D, GQ, false, false, kSplitWavesWide>();
+    }
+  }
+  if (nw != kSplitWaves) return nullptr;
+  if (mixed) return cb ? split_symbol<D, GQ, true, true, kSplitWaves>() : split_symbol<D, GQ, false, true, kSplitWaves>();
+  return cb ? split_symbol<D, GQ, true, false, kSplitWaves>() : split_symbol<D, GQ, false, false, kSplitWaves>();
+}
+
+static const void* split_function_of(int d, int gq, bool cb, bool mixed, int nw) {
+#define OSCAR_DISPATCH(DD, GG) \
+  if (d == DD && gq == GG) return split_function<DD, GG>(cb, mixed, nw);
+  OSCAR_DISPATCH(128, 1) OSCAR_DISPATCH(128, 2) OSCAR_DISPATCH(128, 4) OSCAR_DISPATCH(128, 8)
+  OSCAR_DISPATCH(64, 1) OSCAR_DISPATCH(64, 2) OSCAR_DISPATCH(64, 4) OSCAR_DISPATCH(64, 8)
+#undef OSCAR_DISPATCH
+  return nullptr;
+}
+
+int split_workgroups_per_cu(int d, int gq, bool cb, bool mixed, int nw) {
+  const void* f = split_function_of(d, gq, cb, mixed, nw);
+  int n = 0;
+  if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, nw * kWave, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
 template <int D, int GQ>
 static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream) {
   const Dims& dm = a.dm;
-  auto mark = [&](int i) {
-    if (a.events) (void)hipEventRecord(a.events[i], stream);
-  };
-  mark(0);
-  if (a.ws.qpre) {
-    if (a.codebook)
-      hipLaunchKernelGGL((q_prologue_kernel<D, GQ, true>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
-                         stream, a);
-    else
-      hipLaunchKernelGGL((q_prologue_kernel<D, GQ, false>), dim3(dm.batch * dm.hkv, dm.mixed ? 2 : 1), dim3(256), 0,
-                         stream, a);
-  }
-  const int nblk = dm.batch * dm.hkv * (a.ws.nwin + a.ws.s2 + (dm.mixed ? a.ws.s4 : 0));
-  // the timing variant brackets the split kernel with the dispatch's own start and stop stamps
-  // (events 1 and 2), so its interval is the kernel's execution time
-  const dim3 grid(nblk), block(kSplitWaves * kWave);
-  auto go = [&](auto kernel) {
-    if (a.events) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a.events[1], a.events[2], 0, a, cw);
-    else hipLaunchKernelGGL(kernel, grid, block, 0, stream, a, cw);
-  };
-  if (dm.mixed) {
-    if (a.codebook) go(split_kernel<D, GQ, true, true>);
-    else go(split_kernel<D, GQ, false, true>);
-  } else {
-    if (a.codebook) go(split_kernel<D, GQ, true, false>);
-    else go(split_kernel<D, GQ, false, false>);
-  }
+  const void* f = split_function<D, GQ>(a.codebook != nullptr, dm.mixed != 0, a.ws.nw);
+  if (!f) return hipErrorInvalidValue;
+  // the timing variant records event 0, then brackets the split kernel with the dispatch's own
+  // start and stop stamps (events 1 and 2), so its interval is the kernel's execution time
+  if (a.events) (void)hipEventRecord(a.events[0], stream);
+  const dim3 grid(dm.hkv * a.ws.units_per_kv), block(a.ws.nw * kWave);
+  DecodeArgs args = a;
+  CacheWriteArgs cwa = cw;
+  void* kargs[] = {&args, &cwa};
+  hipError_t e = a.events ? hipExtLaunchKernel(f, grid, block, kargs, 0, stream, a.events[1], a.events[2], 0)
+                          : hipLaunchKernel(f, grid, block, kargs, 0, stream);
+  if (e != hipSuccess) return e;
   const int groups = dm.batch * dm.hkv;
   bool merged = false;
   if constexpr (GQ >= 2) {
@@ -1593,7 +1933,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw,
     }
   }
   if (!merged) hipLaunchKernelGGL((merge_kernel<D, GQ, GQ>), dim3(groups), dim3(kMergeThreads), 0, stream, a, cw);
-  mark(3);
+  if (a.events) (void)hipEventRecord(a.events[3], stream);
   return hipGetLastError();
 }
 

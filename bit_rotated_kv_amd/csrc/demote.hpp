@@ -81,25 +81,27 @@ __device__ inline void store_value_codes(uint8_t* ph, int d, int bits, int t, co
 // k-step the parts lo, mid, hi -- and a row's result depends on that row alone, so the prefill,
 // the demote and the fused decode step give a token the same x_rot and the same codes. The
 // prefill holds its wavefront's slice of R in registers across tiles (RotSlice, rotate_tile);
-// the single-row writers stream it one k-step at a time (rotate_rows_streamed) in the same order.
+// the single-row writers read it as fp32 and split it one k-step at a time (rotate_rows_loaded) in the
+// same order.
 //
 // Operand layout of the 32x32x16 product (lane l, row/column m = n = l % 32): A holds row m,
 // channels 16*kk + 8*(l/32) .. +7; B holds those channels of output column n; the 16 accumulators
 // of lane l are rows 8*(j/4) + 4*(l/32) + j%4 of column n.
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 
-// The three bf16 parts of the rotation entries r[0..7] (exact: r = hi + mid + lo).
+// The three bf16 parts of the rotation entries r[0..7] (exact: r = hi + mid + lo). Each part is the
+// round-to-nearest-even bf16 of what the previous parts leave (the hardware conversion,
+// v_cvt_pk_bf16_f32, two entries per instruction); the residuals are exact fp32 differences.
 __device__ __forceinline__ void split_rotation(const float (&r)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t h = f32_to_bf16_bits(r[i]);
-    const float r1 = r[i] - bf16_bits_to_f32(h);   // exact
-    const uint32_t m = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(m);     // exact, at most 8 significant bits
-    const uint32_t l = f32_to_bf16_bits(r2);       // exact
-    hi[i] = __builtin_bit_cast(__bf16, (uint16_t)h);
-    mid[i] = __builtin_bit_cast(__bf16, (uint16_t)m);
-    lo[i] = __builtin_bit_cast(__bf16, (uint16_t)l);
+    const __bf16 h = (__bf16)r[i];
+    const float r1 = r[i] - (float)h;   // exact
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;     // exact, at most 8 significant bits
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = (__bf16)r2;                 // exact
   }
 }
 
@@ -156,18 +158,20 @@ __device__ __forceinline__ float16v_t rotate_tile(const RotSlice<D>& rs, XPtr x,
   return acc;
 }
 
-// rotate_tile with the slice of wavefront w read from rot one k-step at a time (few registers; the
-// same products in the same order).
+// rotate_tile for the single-row writers: the slice of wavefront w is read from rot as fp32 (every
+// entry loaded before the first product, one round trip to memory) and split as in RotSlice; the
+// same products in the same order.
 template <int D, typename XPtr>
-__device__ __forceinline__ float16v_t rotate_rows_streamed(const float* rot, int w, XPtr x, int stride, int nrows,
-                                                           int lane) {
+__device__ __forceinline__ float16v_t rotate_rows_loaded(const float* rot, int w, XPtr x, int stride, int nrows,
+                                                         int lane) {
+  float r[D / 16][8];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) rotation_entries<D>(rot, w, kk, lane, r[kk]);
   float16v_t acc = {};
-#pragma unroll 2
+#pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    float r[8];
-    rotation_entries<D>(rot, w, kk, lane, r);
     bf16x8_t hi, mid, lo;
-    split_rotation(r, hi, mid, lo);
+    split_rotation(r[kk], hi, mid, lo);
     acc = rotation_step(rotation_a(x, stride, nrows, kk, lane), hi, mid, lo, acc);
   }
   return acc;
@@ -262,7 +266,7 @@ __device__ inline void demote_block(const CacheWriteArgs& a, int sel, int kv, in
     if (tid < D) xs[tid] = pg[sel ? bf16_value_index(D, t, tid) : bf16_key_index(D, t, tid)];
     __syncthreads();
     if (wave < D / 32) {
-      const float16v_t acc = rotate_rows_streamed<D>(rot, wave, xs, D, 1, lane);
+      const float16v_t acc = rotate_rows_loaded<D>(rot, wave, xs, D, 1, lane);
       if (lane < 32) xr[32 * wave + lane] = acc[0];   // row 0
     }
     __syncthreads();

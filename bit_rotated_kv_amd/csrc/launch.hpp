@@ -17,28 +17,37 @@ struct Dims {
   int pt_stride;
 };
 
-// Workspace carve-up of a decode call (all device pointers).
+// Workspace carve-up of a decode call (all device pointers) and the plan scalars the split and
+// merge kernels share.
+//
+// Work plan: every (request, kv-head) has a cost sequence -- the step's demote and one-token
+// partials (cost step_cost, fused step only), the INT2 history pages (1 each), the INT4 history
+// pages (2 each: twice the bytes), the BF16 window as one block (win_cost) -- cut into n_b equal
+// cost ranges ("units"), one workgroup each. The kv-heads of a request share its unit count, and
+// the counts are apportioned to the requests by cost from the device lengths: n_b = 1 + a share
+// of units_per_kv - batch (cumulative rounding, so the shares add up exactly). Unit j of request b
+// and kv-head kv is workgroup hkv * (first_b + j) + kv.
 struct DecodeWs {
-  uint32_t* flags;         // [64]; word 0 bit 0: skipped page id
-  // query operands, when precomputed (qpre): [width 2, 4][B * Hkv][high, low][gq][d] fp16 and
-  // [width][B * Hkv][gq][4] fp32 {sum of high parts, sum of low parts, 2^E, 0}
-  uint16_t* qop;
-  float* qhs;
-  int qpre;
-  float* part_o;           // [B][Hkv][NS][gq][d]
-  float* part_lse;         // [B][Hkv][NS][gq]  (log2 units)
-  // Slots per (b, kv), in order: nwin window slots (one per window workgroup; in a fused step the
-  // last is the new token's), S2 INT2 history slots, S4 INT4 history slots, and in a fused step
-  // one more history slot for the demoted token. Slots below nwin are in the original basis.
-  int ns;
-  int nwin;                // window workgroups per (b, kv): ceil(window pages / 4) (+1 in a step)
-  int s2, s4;              // split slots per width
-  int ppw;                 // pages per wavefront in a history split (4 waves per split), <= 64
+  uint32_t* flags;         // [64]; word 0: bit 0 skipped page id, bit 1 step refused (no room)
+  float* part_o;           // [units][3][gq][d]: a unit's window, INT2 and INT4 partials
+  float* part_lse;         // [units][3][gq] (log2 units); -inf where the unit has no such segment
+  float* step_o;           // [B][Hkv][2][gq][d]: the demoted token (rotated basis), the new token
+  float* step_lse;         // [B][Hkv][2][gq]
+  int32_t* req_units;      // [B][2]: first unit and unit count of each request (written by the split)
+  int units_per_kv;        // workgroups per kv-head (>= batch); grid = hkv * units_per_kv
+  int nw;                  // wavefronts per split workgroup
+  int step_cost;           // cost of the step segment (0 outside a fused step)
+  int win_cost;            // cost of the BF16 window block
 };
 
-constexpr int kMaxSlots = 3200;  // history partial slots per (request, kv-head)
-// wavefronts of a decode split workgroup (6 was measured slower than 4 at both batch sizes)
+// wavefronts of a split workgroup at large batch, and when a few (request, kv-head) pairs must fill
+// the chip
+#ifndef OSCAR_WIDE_WAVES
+#define OSCAR_WIDE_WAVES 16
+#endif
 constexpr int kSplitWaves = 4;
+constexpr int kSplitWavesWide = OSCAR_WIDE_WAVES;
+constexpr int kMaxSlots = 3200;  // partial slots per (request, kv-head) of the BF16 baseline
 
 struct DecodeArgs {
   Dims dm;
@@ -56,8 +65,8 @@ struct DecodeArgs {
   float* out;                // [B][Hq][d] fp32
   DecodeWs ws;
   int step;                  // fused decode step: demote + append ride along (CacheWriteArgs)
-  hipEvent_t* events;        // host: optional, 4 events: before the query prologue (if any),
-                             // before the split, after it, after the merge
+  hipEvent_t* events;        // host: optional, 4 events: before the split, the split's start and
+                             // stop stamps, after the merge
 };
 
 struct CacheWriteArgs {
@@ -101,6 +110,8 @@ hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_demote(const CacheWriteArgs& a, hipStream_t stream);
 // Decode attention; with a.step, also the demote + append of `cw` (a fused decode step).
 hipError_t launch_decode(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream);
+// Split workgroups of `nw` wavefronts a compute unit of the current device holds (0 if unknown).
+int split_workgroups_per_cu(int d, int gq, bool cb, bool mixed, int nw);
 hipError_t launch_bf16_fill(const Bf16Args& a, hipStream_t stream);
 hipError_t launch_bf16_decode(const Bf16Args& a, hipStream_t stream);
 

@@ -3,10 +3,12 @@
 //
 // Thread 0 of a workgroup writes the constant-rate real-time counter (s_memrealtime, 100 MHz) at
 // fixed points of its run into a device table, one row per workgroup; the host copies the table
-// out with oscar_timeline_read. Split kernel columns: 0 entry, 1 query operands ready, 2 page
-// loop done, 3 exit, 4 role (0 INT2 history, 1 INT4 history, 2 window, 3 step) | pages of
-// wavefront 0 << 8, 5 XCC_ID << 32 | HW_ID. Merge kernel rows follow the split rows: 0 entry,
-// 3 exit.
+// out with oscar_timeline_read. Split kernel columns: 0 entry, 1 work plan known, 2 step and
+// window segments done, 3 query operands ready, 4 page loop done (wavefront 0), 5 exit,
+// 6 segments (bit 0 step, 1 window, 2 INT2, 3 INT4) | history pages of the unit << 8,
+// 7 XCC_ID << 32 | HW_ID, 8 every wavefront past its page loop (last history segment), 9 step
+// segment loads done, 10 step rotation done, 11 step codes stored. Merge
+// kernel rows follow the split rows: 0 entry, 5 exit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,7 +18,7 @@ namespace oscar {
 
 constexpr int kTimelineSplitRows = 16384;
 constexpr int kTimelineMergeRows = 2048;
-constexpr int kTimelineCols = 8;
+constexpr int kTimelineCols = 12;
 
 #ifdef OSCAR_TIMELINE
 extern __device__ uint64_t g_timeline[kTimelineSplitRows + kTimelineMergeRows][kTimelineCols];

@@ -11,9 +11,8 @@ import numpy as np
 from . import _lib
 
 TIMELINE_LIB = os.path.join(_lib.HERE, "liboscar_timeline.so")
-SPLIT_ROWS, MERGE_ROWS, COLS = 16384, 2048, 8
+SPLIT_ROWS, MERGE_ROWS, COLS = 16384, 2048, 12
 TICK_US = 0.01           # s_memrealtime counts at 100 MHz
-ROLES = {0: "int2_history", 1: "int4_history", 2: "window", 3: "step"}
 
 
 def use_timeline_library():
@@ -47,12 +46,14 @@ def _pct(x):
     x = np.asarray(x, np.float64)
     if x.size == 0:
         return None
-    return [round(float(v), 2) for v in np.percentile(x, [10, 50, 90])]
+    return [round(float(v), 2) for v in np.percentile(x, [10, 50, 90])] + [round(float(x.max()), 2)]
 
 
 def summarize(tabs) -> dict:
-    """p10/p50/p90 (microseconds) of each phase over the workgroups of several recorded launches;
-    times are relative to the first workgroup entry of the launch's split kernel."""
+    """p10/p50/p90 and the maximum (microseconds) of each phase over the workgroups of several recorded launches;
+    times are relative to the first workgroup entry of the launch's split kernel. Workgroups are
+    grouped by the segments they ran: "first_unit" (the step and/or window pages, then history) and
+    "history" (history pages only)."""
     acc = {}
     spans, merge_spans, ends = [], [], []
     n_split = n_merge = 0
@@ -62,46 +63,58 @@ def summarize(tabs) -> dict:
         if used.size == 0:
             continue
         n_split = max(n_split, int(used.max()) + 1)
-        t0 = sp[used, 0].min()
-        rel = lambda c: (sp[used, c].astype(np.int64) - np.int64(t0)) * TICK_US
-        entry, ready, loop, exit_ = rel(0), rel(1), rel(2), rel(3)
-        role = (sp[used, 4] & 0xFF).astype(int)
-        pages = (sp[used, 4] >> 8).astype(int)
-        xcc = (sp[used, 5] >> 32).astype(int) & 0xF
+        t0 = np.int64(sp[used, 0].min())
+        col = lambda c: sp[used, c].astype(np.int64)
+        rel = lambda c: (col(c) - t0) * TICK_US
+        dur = lambda c1, c0: (col(c1) - col(c0)) * TICK_US
+        segs = (col(6) & 0xFF).astype(int)
+        pages = (col(6) >> 8).astype(int)
+        xcc = (col(7) >> 32).astype(int) & 0xF
+        hist = (segs & 12) != 0
+        exit_ = rel(5)
         spans.append(float(exit_.max()))
-        for r, name in ROLES.items():
-            m = role == r
+        groups = {"first_unit": (segs & 3) != 0, "history": (segs & 3) == 0}
+        for name, m in groups.items():
             if not m.any():
                 continue
-            d = acc.setdefault(name, {"entry": [], "exit": [], "run": []})
-            d["entry"] += list(entry[m])
-            d["exit"] += list(exit_[m])
-            d["run"] += list(exit_[m] - entry[m])
-            if r in (0, 1):
-                d.setdefault("prologue", []).extend(list(ready[m] - entry[m]))
-                d.setdefault("page_loop", []).extend(list(loop[m] - ready[m]))
-                d.setdefault("wg_merge", []).extend(list(exit_[m] - loop[m]))
-                d.setdefault("pages_wave0", []).extend(list(pages[m]))
-        hist = role <= 1
-        if hist.any():
-            ends.append({int(x): round(float(exit_[hist & (xcc == x)].max()), 2) for x in np.unique(xcc[hist])})
+            d = acc.setdefault(name, {})
+            d.setdefault("entry", []).extend(rel(0)[m])
+            d.setdefault("exit", []).extend(exit_[m])
+            d.setdefault("run", []).extend(dur(5, 0)[m])
+            d.setdefault("plan", []).extend(dur(1, 0)[m])
+            d.setdefault("step_window", []).extend(dur(2, 1)[m])
+            st = m & ((segs & 1) != 0)
+            d.setdefault("step_loads", []).extend(dur(9, 1)[st])
+            d.setdefault("step_rotate", []).extend(dur(10, 9)[st])
+            d.setdefault("step_quantize_store", []).extend(dur(11, 10)[st])
+            d.setdefault("step_partials", []).extend(dur(2, 11)[st])
+            h = m & hist
+            d.setdefault("prologue", []).extend(dur(3, 2)[h])
+            d.setdefault("page_loop", []).extend(dur(4, 3)[h])
+            d.setdefault("wave_wait", []).extend(dur(8, 4)[h])
+            d.setdefault("wg_merge", []).extend(dur(5, 8)[h])
+            d.setdefault("history_pages", []).extend(pages[h])
+            d["count"] = d.get("count", 0) + int(m.sum())
+        ends.append({int(x): round(float(exit_[xcc == x].max()), 2) for x in np.unique(xcc)})
         mg = tab[SPLIT_ROWS:]
         mu = np.nonzero(mg[:, 0])[0]
         if mu.size:
             n_merge = max(n_merge, int(mu.max()) + 1)
-            me = (mg[mu, 0].astype(np.int64) - np.int64(t0)) * TICK_US
-            mx = (mg[mu, 3].astype(np.int64) - np.int64(t0)) * TICK_US
+            me = (mg[mu, 0].astype(np.int64) - t0) * TICK_US
+            mx = (mg[mu, 5].astype(np.int64) - t0) * TICK_US
             merge_spans.append((float(me.min()), float(mx.max())))
-            acc.setdefault("merge", {"entry": [], "exit": [], "run": []})
-            acc["merge"]["entry"] += list(me)
-            acc["merge"]["exit"] += list(mx)
-            acc["merge"]["run"] += list(mx - me)
+            d = acc.setdefault("merge", {})
+            d.setdefault("entry", []).extend(me)
+            d.setdefault("exit", []).extend(mx)
+            d.setdefault("run", []).extend(mx - me)
+            d["count"] = d.get("count", 0) + int(mu.size)
     out = {"launches": len(spans), "split_workgroups": n_split, "merge_workgroups": n_merge,
            "split_span_us": _pct(spans),
            "merge_entry_exit_us": [round(float(np.median([m[0] for m in merge_spans])), 2),
                                    round(float(np.median([m[1] for m in merge_spans])), 2)] if merge_spans else None,
-           "last_history_exit_per_xcd_us": ends[-1] if ends else None, "roles": {}}
+           "last_exit_per_xcd_us": ends[-1] if ends else None, "groups": {}}
     for name, d in acc.items():
-        out["roles"][name] = {k: _pct(v) for k, v in d.items()}
-        out["roles"][name]["workgroups_per_launch"] = len(d["entry"]) // max(1, len(spans))
+        cnt = d.pop("count")
+        out["groups"][name] = {k: _pct(v) for k, v in d.items()}
+        out["groups"][name]["workgroups_per_launch"] = cnt // max(1, len(spans))
     return out

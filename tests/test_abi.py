@@ -69,8 +69,10 @@ def test_sizes(lib):
     M = layout(mixed=True, int4_page_offset=60)
     assert brk.pool_bytes(M) == 60 * 8 * 1152 + 40 * 8 * 2176
     assert brk.page_bytes(layout(head_dim=64, num_q_heads=2, num_kv_heads=1), 2) == 640
-    # workspace grows with context and is 0 for invalid layouts
-    assert brk.decode_workspace_bytes(L, 1, 100_000) > brk.decode_workspace_bytes(L, 1, 1000) > 0
+    # the workspace holds a partial per work unit (a bounded number per kv-head, at least one per
+    # request) whatever the context; it is 0 for invalid layouts
+    assert brk.decode_workspace_bytes(L, 1, 100_000) == brk.decode_workspace_bytes(L, 1, 1000) > 0
+    assert brk.decode_workspace_bytes(L, 300, 1000) > brk.decode_workspace_bytes(L, 32, 1000)
     assert brk.decode_workspace_bytes(layout(head_dim=96), 1, 1000) == 0
 
 

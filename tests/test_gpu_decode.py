@@ -24,6 +24,8 @@ def small(base, **kw):
 DECODE = {
     "tiny-ref": lambda: synth.workload(1),
     "d128-gq4": lambda: small(2, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(1800, 1000)),
+    # 24 (request, kv-head) pairs: GQA 4 in 4-wavefront split workgroups (few pairs take 16)
+    "d128-gq4-b3": lambda: small(2, batch=3, num_q_heads=32, num_kv_heads=8, seq_lens=(1400, 700, 2000)),
     "d128-gq8": lambda: small(4, batch=2, num_q_heads=16, num_kv_heads=2, seq_lens=(1200, 2500)),
     "d128-gq1": lambda: small(2, batch=1, num_q_heads=2, num_kv_heads=2, seq_lens=(1500,)),
     "d128-gq2": lambda: small(2, batch=1, num_q_heads=4, num_kv_heads=2, seq_lens=(1100,)),
