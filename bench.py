@@ -62,6 +62,9 @@ def parse():
                     help="diagnostic mode: run N eager steps of the workload with liboscar_timeline.so and print "
                          "the per-workgroup phase percentiles instead of the benchmark line")
     ap.add_argument("--timeline-raw", default="", help="with --timeline: also save the raw tables (.npy)")
+    ap.add_argument("--only", default="", choices=["", "step", "bs32", "bs32_100k", "gqa8_ragged", "mixed", "prefill"],
+                    help="profiling mode: run only this measurement (plus --copy-probe-mib) and print its result "
+                         "instead of the benchmark line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
     return ap.parse_args()
@@ -639,6 +642,53 @@ def timeline_main(args):
     print(json.dumps(res), flush=True)
 
 
+def copy_probe(mib):
+    """A plain device copy of `mib` MiB (the reference that scales the HBM byte counters)."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return n
+
+
+def only_main(args):
+    """One measurement alone, for per-workload profiles (rocprofv3 runs of this process)."""
+    import torch
+    import synth
+    torch.manual_seed(0)
+    res = {"only": args.only}
+    if args.only == "step":
+        w = synth.workload(2)
+        est = args.batch * w.num_kv_heads * (args.context - 320) * 72
+        setup = Int2Setup(w, args.batch, args.context, args.copies or max(2, math.ceil(1.0e9 / est)),
+                          args.steps + args.warmup, fast_inputs=False)
+        ms, kern, mode = time_int2(setup, args.steps, args.warmup, args.eager)
+        res.update(workload=f"qwen3-8b-layer decode step, batch {args.batch}, context {args.context}",
+                   us_per_step=round(ms * 1e3, 2), kernel_ms={"split": round(float(kern[1]), 5),
+                                                              "merge": round(float(kern[2]), 5)}, launch=mode)
+    elif args.only == "bs32":
+        w32 = synth.workload(3)
+        est = 32 * 8 * (32_768 - 320) * 72
+        s32 = Int2Setup(w32, 32, 32_768, max(2, math.ceil(1.0e9 / est)), args.steps + args.warmup, fast_inputs=True)
+        ms, kern, mode = time_int2(s32, args.steps, args.warmup, args.eager)
+        res.update(workload="paged batch 32 x 32,768 tokens, demote in step", us_per_step=round(ms * 1e3, 2),
+                   kernel_ms={"split": round(float(kern[1]), 5), "merge": round(float(kern[2]), 5)}, launch=mode)
+    elif args.only == "bs32_100k":
+        args.no_bf16 = True
+        res.update(time_bs32_100k(args))
+    elif args.only == "gqa8_ragged":
+        res.update(time_decode_workload(synth.workload(4), args.steps, args.warmup))
+    elif args.only == "mixed":
+        res.update(time_decode_workload(synth.workload(5), args.steps, args.warmup))
+    elif args.only == "prefill":
+        res.update(time_prefill(synth.workload(2), args.batch, args.context))
+    if args.copy_probe_mib:
+        res["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -646,6 +696,9 @@ def main():
         sys.exit(2)
     if args.timeline:
         timeline_main(args)
+        return
+    if args.only:
+        print(json.dumps(only_main(args)), flush=True)
         return
     import torch
     import synth
@@ -743,12 +796,7 @@ def main():
         result["gqa8_ragged"] = time_decode_workload(synth.workload(4), args.steps, args.warmup)
         result["mixed_int2_int4"] = time_decode_workload(synth.workload(5), args.steps, args.warmup)
     if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        result["copy_probe_bytes"] = n
+        result["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(w, context)

@@ -514,7 +514,9 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
         if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
       }
   }
+  OSCAR_TL_SPLIT(12);
   __syncthreads();
+  OSCAR_TL_SPLIT(13);
   for (int idx = tid; idx < GQ * D; idx += NW * kWave) {
     const int hh = idx / D, ch = idx % D, nb = ch / 16;
     float mw[NW];
@@ -542,6 +544,7 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
     part_o[hh * D + ch] = empty ? 0.0f : (O * vscale + Z) / L;
     if (ch == 0) part_lse[hh] = empty ? kNegInf : M + log2f(L);
   }
+  OSCAR_TL_SPLIT(14);
 }
 
 // ------------------------------------------------------------------ page pipeline
@@ -903,7 +906,10 @@ struct QPage {
 
 // Raw buffer descriptor of one page-head (gfx9 family: base, stride 0, size in bytes, word 3
 // 0x00020000): the page's loads then take the same per-lane byte offsets on every page, and a
-// byte past the page-head would read as zero instead of touching the next one.
+// byte past the page-head would read as zero instead of touching the next one. A descriptor of
+// size 0 (prefetches past the range, page ids outside the pool) makes every load of the page an
+// out-of-range read: zeros, no memory access, so such a load completes as soon as the loads
+// issued before it have.
 // Cache policy of the history page loads: nt (streaming) where every load instruction of a wavefront
 // covers whole 128-byte lines: the codes at d <= 128 (an INT2 lane chunk of 8 or 16 bytes; an INT4
 // key or value part of 8 or 16 bytes, the parts of all lanes consecutive) and the metadata at GQA 4
@@ -914,17 +920,17 @@ template <int BITS, int D, int GQ>
 constexpr int kPageLoadPolicy = (D <= 128 && (GQ == 4 || GQ == 8)) ? 2 : 0;
 
 template <int BITS, int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head) {
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0, 4 * D * BITS + kMetaBytes,
-                                           0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head, bool live) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0,
+                                           live ? 4 * D * BITS + kMetaBytes : 0, 0x00020000);
 }
 
 template <int BITS, int D, int GQ>
-__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head, int lane) {
+__device__ __forceinline__ void load_qpage(QPage<BITS, D, GQ>& pr, uint64_t head, bool live, int lane) {
   constexpr int CW = QPage<BITS, D, GQ>::CW;
   constexpr int POL = kPageLoadPolicy<BITS, D, GQ>;
   const int g = lane / 16, c = lane % 16;
-  const __amdgpu_buffer_rsrc_t r = qpage_rsrc<BITS, D>(head);
+  const __amdgpu_buffer_rsrc_t r = qpage_rsrc<BITS, D>(head, live);
   if constexpr (BITS == 2 && CW == 1) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, POL);
     pr.kw[0] = v[0];
@@ -1327,8 +1333,8 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   st.init();
   if (dm.pool_pages > 0) {
     int cbase = wp0;
-    // Page-head address of a page (uniform): ids outside the pool or of the other width are invalid
-    // and read page-head 0 of the arena instead, as do the prefetches past the range.
+    // Page-head address of a page (uniform): ids outside the pool or of the other width are invalid;
+    // they and the prefetches past the range read zeros without touching memory.
     const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
     const int64_t head = qpage_head_bytes(D, BITS);
     const uint64_t region = (uint64_t)a.pool + (BITS == 2 ? 0 : (uint64_t)(off4 * qpage_head_bytes(D, 2) * dm.hkv));
@@ -1339,9 +1345,10 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
       const int id_nxt = __builtin_amdgcn_readlane(nxt, max(li - kIdChunk, 0));
       const int64_t id = li < kIdChunk ? id_cur : id_nxt;
       const bool valid = id >= first_id && id < (BITS == 2 ? off4 : dm.pool_pages);
+      const bool live = pg < wp1 && valid;
       const uint64_t ad = valid ? region + (uint64_t)(((id - first_id) * dm.hkv + kv) * head) : (uint64_t)a.pool;
-      load_qpage<BITS, D, GQ>(pr, ad, lane);
-      return pg < wp1 && valid;
+      load_qpage<BITS, D, GQ>(pr, ad, live, lane);
+      return live;
     };
     QPage<BITS, D, GQ> buf[NB];
     bool ok[NB];
@@ -1658,6 +1665,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
     merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, 0, true);
     for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, base, false);
   }
+  OSCAR_TL_MERGE(1);
   *reinterpret_cast<float4*>(&acc_h[grp][hl][4 * c4]) = ms_st.ah;
   *reinterpret_cast<float4*>(&acc_w[grp][hl][4 * c4]) = ms_st.aw;
   if (c4 == 0) {
@@ -1698,6 +1706,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
     }
   }
   __syncthreads();
+  OSCAR_TL_MERGE(3);
   // un-rotation: thread (j, part) forms part of out[h][j] = sum_i hsum[h][i] R_V[j][i] over
   // i = part, part + NP, ...; the parts are folded across the NP lanes of row j
   {

@@ -7,8 +7,9 @@
 // window segments done, 3 query operands ready, 4 page loop done (wavefront 0), 5 exit,
 // 6 segments (bit 0 step, 1 window, 2 INT2, 3 INT4) | history pages of the unit << 8,
 // 7 XCC_ID << 32 | HW_ID, 8 every wavefront past its page loop (last history segment), 9 step
-// segment loads done, 10 step rotation done, 11 step codes stored. Merge
-// kernel rows follow the split rows: 0 entry, 5 exit.
+// segment loads done, 10 step rotation done, 11 step codes stored, 12 workgroup merge: own state
+// in LDS, 13 past its barrier, 14 partial stored. Merge kernel rows follow the split rows:
+// 0 entry, 1 slots folded, 3 groups combined, 5 exit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,7 +19,7 @@ namespace oscar {
 
 constexpr int kTimelineSplitRows = 16384;
 constexpr int kTimelineMergeRows = 2048;
-constexpr int kTimelineCols = 12;
+constexpr int kTimelineCols = 16;
 
 #ifdef OSCAR_TIMELINE
 extern __device__ uint64_t g_timeline[kTimelineSplitRows + kTimelineMergeRows][kTimelineCols];

@@ -11,7 +11,7 @@ import numpy as np
 from . import _lib
 
 TIMELINE_LIB = os.path.join(_lib.HERE, "liboscar_timeline.so")
-SPLIT_ROWS, MERGE_ROWS, COLS = 16384, 2048, 12
+SPLIT_ROWS, MERGE_ROWS, COLS = 16384, 2048, 16
 TICK_US = 0.01           # s_memrealtime counts at 100 MHz
 
 
@@ -93,6 +93,10 @@ def summarize(tabs) -> dict:
             d.setdefault("page_loop", []).extend(dur(4, 3)[h])
             d.setdefault("wave_wait", []).extend(dur(8, 4)[h])
             d.setdefault("wg_merge", []).extend(dur(5, 8)[h])
+            d.setdefault("wg_state_to_lds", []).extend(dur(12, 8)[h])
+            d.setdefault("wg_barrier", []).extend(dur(13, 12)[h])
+            d.setdefault("wg_reduce_store", []).extend(dur(14, 13)[h])
+            d.setdefault("wg_to_exit", []).extend(dur(5, 14)[h])
             d.setdefault("history_pages", []).extend(pages[h])
             d["count"] = d.get("count", 0) + int(m.sum())
         ends.append({int(x): round(float(exit_[xcc == x].max()), 2) for x in np.unique(xcc)})
@@ -101,12 +105,17 @@ def summarize(tabs) -> dict:
         if mu.size:
             n_merge = max(n_merge, int(mu.max()) + 1)
             me = (mg[mu, 0].astype(np.int64) - t0) * TICK_US
+            mf = (mg[mu, 1].astype(np.int64) - t0) * TICK_US
+            mc = (mg[mu, 3].astype(np.int64) - t0) * TICK_US
             mx = (mg[mu, 5].astype(np.int64) - t0) * TICK_US
             merge_spans.append((float(me.min()), float(mx.max())))
             d = acc.setdefault("merge", {})
             d.setdefault("entry", []).extend(me)
             d.setdefault("exit", []).extend(mx)
             d.setdefault("run", []).extend(mx - me)
+            d.setdefault("fold", []).extend(mf - me)
+            d.setdefault("combine", []).extend(mc - mf)
+            d.setdefault("unrotate_store", []).extend(mx - mc)
             d["count"] = d.get("count", 0) + int(mu.size)
     out = {"launches": len(spans), "split_workgroups": n_split, "merge_workgroups": n_merge,
            "split_span_us": _pct(spans),

@@ -236,7 +236,7 @@ size_t oscar_decode_workspace_bytes(const oscar_layout_t* layout, int32_t batch,
  *   out        [batch][Hq][d] fp32
  *   softmax_scale 0 -> 1/sqrt(d)
  *   workspace  >= oscar_decode_workspace_bytes(); word 0 (uint32) is OR-ed with 1 when a page
- *              id outside [0, pool_pages) was skipped. Contents are scratch between calls; calls
+ *              id outside [0, pool_pages) was skipped (the caller clears it). Contents are scratch between calls; calls
  *              that overlap in time must not share a workspace.
  *   Page tables are read only at indices below pt_stride (longer histories are cut there).
  */
@@ -249,12 +249,11 @@ oscar_status_t oscar_decode_attn(const oscar_layout_t* layout, int32_t batch, in
                                  hipStream_t stream);
 
 /*
- * oscar_decode_attn with timing: identical work, plus hipEventRecord on `stream` of events[0..3]
- * (n_events >= 4, all created by the caller): before the query prologue kernel, before the split
- * kernel (BF16 window, INT2 and INT4 history pages in one launch), after it, and after the merge.
- * The prologue kernel runs only for decodes with many history workgroups (otherwise each history
- * workgroup rotates its own queries and events[0..1] bracket nothing). Intervals between
- * consecutive events time each kernel of the call.
+ * oscar_decode_attn with timing: identical work, plus events[0..3] (n_events >= 4, all created by
+ * the caller): events[0] recorded on `stream` before the split kernel (BF16 window, INT2 and INT4
+ * history pages in one launch), events[1] and events[2] stamped by the runtime at that kernel's
+ * start and end (hipExtLaunchKernel), events[3] recorded after the merge kernel. events[1..2] time
+ * the split kernel alone, events[2..3] the merge (with the gap between the launches).
  */
 oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                           const void* q, const int32_t* seq_len, const int32_t* n_int4,
@@ -268,13 +267,15 @@ oscar_status_t oscar_decode_attn_profiled(const oscar_layout_t* layout, int32_t 
  * One whole decode step (OSCAR overview page, method paragraph; study note, SGLang case): the
  * cache update of oscar_kv_demote (new_k/new_v appended, the oldest recent token demoted) and the
  * attention of oscar_decode_attn over the updated cache, in the same kernels (split and merge,
- * after the query prologue kernel when there are many history workgroups). The cache
- * after the call -- pool, window, seq_len_out, n_int4_out (both outputs required here, not
+ * one launch each). The cache after the call -- pool, window, seq_len_out, n_int4_out (both outputs required here, not
  * aliasing the inputs) -- is bit for bit what the two calls in sequence leave. The attention is
  * the same function of the updated cache; it reads the cache as it stands before the step and
  * takes the demoted token (same codes as the demote writes) and the new token as one-token
  * partials, so its output agrees with the two-call sequence to fp32 rounding, not bit for bit.
- * Arguments follow the two calls above; max_seq_len bounds the updated lengths (T + 1).
+ * Arguments follow the two calls above; max_seq_len bounds the updated lengths (T + 1). A request
+ * with no room for the new token (seq_len >= max_seq_len) is left as it is -- no demote, no
+ * append, seq_len_out = seq_len -- attends over its cache with its lengths cut to max_seq_len, and
+ * sets bit 1 of workspace word 0.
  */
 oscar_status_t oscar_decode_step(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
                                  const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
