@@ -9,12 +9,12 @@ from ._lib import LIB_PATH, Layout, lib, status_string
 from .ops import (make_layout, page_bytes, window_bytes, pool_bytes, decode_workspace_bytes,
                   bf16_decode_workspace_bytes, quantize_pack, quantize_pack_codebook, set_codebook, codebook_workspace_bytes,
                   codebook_fit, kv_prefill, kv_demote, decode_attn,
-                  decode_step, bf16_fill, bf16_decode_attn, allocate_bits, route_tokens, calib_query_cov,
+                  decode_step, decode_step_noalloc, bf16_fill, bf16_decode_attn, allocate_bits, route_tokens, calib_query_cov,
                   calib_value_cov, rotation_from_covariance)
 from .cache import CacheBuffers, allocate_cache
 
 __all__ = ["LIB_PATH", "Layout", "lib", "status_string", "make_layout", "page_bytes", "window_bytes",
            "pool_bytes", "decode_workspace_bytes", "bf16_decode_workspace_bytes", "quantize_pack",
-           "quantize_pack_codebook", "set_codebook", "codebook_workspace_bytes", "codebook_fit", "kv_prefill", "kv_demote", "decode_attn", "decode_step",
+           "quantize_pack_codebook", "set_codebook", "codebook_workspace_bytes", "codebook_fit", "kv_prefill", "kv_demote", "decode_attn", "decode_step", "decode_step_noalloc",
            "bf16_fill", "bf16_decode_attn", "allocate_bits", "route_tokens", "calib_query_cov", "calib_value_cov",
            "rotation_from_covariance", "CacheBuffers", "allocate_cache"]

@@ -50,6 +50,8 @@ _SIGS = {
                                     _P, _P, c_float, _P, c_size_t, _P, _P]),
     "oscar_decode_step_profiled": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              c_int32, _P, _P, _P, c_float, _P, c_size_t, _P, _P, c_int32, _P]),
+    "oscar_decode_step_noalloc": (c_int32, [_P, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            c_int32, _P, _P, _P, c_float, _P, _P]),
     "oscar_allocate_bits": (c_int32, [c_int32, _P, _P, _P, c_double, c_int32, _P, _P]),
     "oscar_route_tokens": (c_int32, [c_int32, c_int32, _P, _P, c_int32, _P, _P, _P]),
     "oscar_calib_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),

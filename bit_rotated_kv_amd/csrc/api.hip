@@ -3,6 +3,7 @@
 #include <math.h>
 #include <algorithm>
 #include <string.h>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -180,6 +181,38 @@ size_t page_bytes(const oscar_layout_t* L, int bits) {
   return (size_t)L->num_kv_heads * qpage_head_bytes(L->head_dim, bits);
 }
 
+}  // namespace
+
+// Workspace of oscar_decode_step_noalloc: one file-scope array per device (its code object's copy),
+// zero at load and never freed. Host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's name (which is a host-side stand-in, not a device address).
+constexpr size_t kStaticScratchBytes = OSCAR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+oscar_status_t scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return OSCAR_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return OSCAR_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return OSCAR_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -468,6 +501,29 @@ oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* L, int32_t batch
   return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
                    page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, softmax_scale, workspace,
                    workspace_bytes, out, events, stream);
+}
+
+oscar_status_t oscar_decode_step_noalloc(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len,
+                                         const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
+                                         const void* new_v, const uint8_t* demote_bits, const void* q,
+                                         const float* rot_k, const float* rot_v, void* pool,
+                                         const int32_t* page_table, const int32_t* page_table4, int32_t pt_stride,
+                                         void* window, int32_t* seq_len_out, int32_t* n_int4_out,
+                                         float softmax_scale, float* out, hipStream_t stream) {
+  oscar_status_t st = check_layout(L);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return OSCAR_ERR_INVALID_ARG;
+  // the device-independent bound of the plan, so acceptance does not depend on the device
+  if (oscar_decode_workspace_bytes(L, batch, max_seq_len) > kStaticScratchBytes) return OSCAR_ERR_WORKSPACE;
+  if (batch == 0) return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k,
+                                   rot_v, pool, page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out,
+                                   softmax_scale, nullptr, 0, out, nullptr, stream);
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != OSCAR_OK) return st;
+  return step_impl(L, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
+                   page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, softmax_scale, ws,
+                   kStaticScratchBytes, out, nullptr, stream);
 }
 
 oscar_status_t oscar_bf16_fill(const oscar_layout_t* L, int32_t batch, int32_t max_seq_len, const int32_t* seq_len,

@@ -255,8 +255,7 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
                 page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                 events: Optional[list] = None) -> torch.Tensor:
     """q [B, Hq, d] bf16 -> out [B, Hq, d] fp32. With ``events`` (4 torch.cuda.Event), calls the
-    timing variant, which records them around the kernels of the call (query prologue when
-    launched, split, merge)."""
+    timing variant, which records them around the kernels of the call (split, merge)."""
     _need(q, torch.bfloat16, "q")
     _need(seq_len, torch.int32, "seq_len")
     _need(window, torch.uint8, "window")
@@ -294,16 +293,9 @@ def decode_attn(layout: Layout, q: torch.Tensor, seq_len: torch.Tensor, window: 
     return out
 
 
-def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
-                rot_k: torch.Tensor, rot_v: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
-                window: torch.Tensor, seq_len_out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
-                out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
-                n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
-                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
-                events: Optional[list] = None) -> torch.Tensor:
-    """kv_demote's cache update and decode_attn over the updated cache, in one call (split and
-    merge, after the query prologue for large batches). With ``events`` (4 torch.cuda.Event), calls
-    the timing variant."""
+def _step_args(layout, seq_len, new_k, new_v, q, rot_k, rot_v, pool, page_table, window, seq_len_out, max_seq_len,
+               out, n_int4, n_int4_out, demote_bits, page_table4, softmax_scale):
+    """Checks the arguments of a decode step and returns (out, the C arguments before the workspace)."""
     _need(seq_len, torch.int32, "seq_len")
     _need(new_k, torch.bfloat16, "new_k")
     _need(new_v, torch.bfloat16, "new_v")
@@ -314,7 +306,6 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
     _need(page_table, torch.int32, "page_table")
     _need(window, torch.uint8, "window")
     _need(seq_len_out, torch.int32, "seq_len_out")
-    _need(workspace, torch.uint8, "workspace")
     for t, n in ((n_int4, "n_int4"), (n_int4_out, "n_int4_out"), (page_table4, "page_table4")):
         _need(t, torch.int32, n, optional=True)
     _need(demote_bits, torch.uint8, "demote_bits", optional=True)
@@ -334,7 +325,23 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
     _tables(B, page_table, page_table4)
     args = (_ref(layout), q.shape[0], max_seq_len, _p(seq_len), _p(n_int4), _p(new_k), _p(new_v), _p(demote_bits),
             _p(q), _p(rot_k), _p(rot_v), _p(pool), _p(page_table), _p(page_table4), page_table.shape[1], _p(window),
-            _p(seq_len_out), _p(n_int4_out), softmax_scale, _p(workspace), workspace.numel(), _p(out))
+            _p(seq_len_out), _p(n_int4_out), softmax_scale)
+    return out, args
+
+
+def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
+                rot_k: torch.Tensor, rot_v: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
+                window: torch.Tensor, seq_len_out: torch.Tensor, workspace: torch.Tensor, max_seq_len: int,
+                out: Optional[torch.Tensor] = None, n_int4: Optional[torch.Tensor] = None,
+                n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
+                page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                events: Optional[list] = None) -> torch.Tensor:
+    """kv_demote's cache update and decode_attn over the updated cache, in one call (split and
+    merge kernels). With ``events`` (4 torch.cuda.Event), calls the timing variant."""
+    _need(workspace, torch.uint8, "workspace")
+    out, args = _step_args(layout, seq_len, new_k, new_v, q, rot_k, rot_v, pool, page_table, window, seq_len_out,
+                           max_seq_len, out, n_int4, n_int4_out, demote_bits, page_table4, softmax_scale)
+    args = args + (_p(workspace), workspace.numel(), _p(out))
     if events is None:
         check(lib().oscar_decode_step(*args, _stream()), "oscar_decode_step")
         return out
@@ -344,6 +351,23 @@ def decode_step(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_
           "oscar_decode_step_profiled")
     return out
 
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_step_noalloc(layout: Layout, seq_len: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
+                        q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, pool: torch.Tensor,
+                        page_table: torch.Tensor, window: torch.Tensor, seq_len_out: torch.Tensor, max_seq_len: int,
+                        out: torch.Tensor, n_int4: Optional[torch.Tensor] = None,
+                        n_int4_out: Optional[torch.Tensor] = None, demote_bits: Optional[torch.Tensor] = None,
+                        page_table4: Optional[torch.Tensor] = None, softmax_scale: float = 0.0) -> torch.Tensor:
+    """decode_step without a workspace argument: the library's own per-device array of
+    NOALLOC_SCRATCH_BYTES serves as the workspace, and the call allocates nothing (``out`` is
+    required). Calls that overlap in time on one device race."""
+    out, args = _step_args(layout, seq_len, new_k, new_v, q, rot_k, rot_v, pool, page_table, window, seq_len_out,
+                           max_seq_len, out, n_int4, n_int4_out, demote_bits, page_table4, softmax_scale)
+    check(lib().oscar_decode_step_noalloc(*args, _p(out), _stream()), "oscar_decode_step_noalloc")
+    return out
 
 def bf16_fill(layout: Layout, seq_len: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pages: torch.Tensor,
               num_pages: int, page_table: torch.Tensor):

@@ -300,6 +300,33 @@ oscar_status_t oscar_decode_step_profiled(const oscar_layout_t* layout, int32_t 
                                           size_t workspace_bytes, float* out, hipEvent_t* events,
                                           int32_t n_events, hipStream_t stream);
 
+/* Bytes of the library-held workspace of oscar_decode_step_noalloc (per device). */
+#define OSCAR_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): oscar_decode_step with the same arguments and results
+ * but no workspace argument. Its workspace is a device array of OSCAR_NOALLOC_SCRATCH_BYTES held by
+ * the library on each device it runs on until the process ends; the call allocates nothing.
+ *   Rejected with OSCAR_ERR_WORKSPACE (before any device work) when
+ *   oscar_decode_workspace_bytes(layout, batch, max_seq_len) > OSCAR_NOALLOC_SCRATCH_BYTES (for
+ *   d = 128, 32 query and 8 kv heads: batch up to 256 at any length).
+ *   Every call on a device shares that device's array and leaves its contents behind; nothing in
+ *   it needs to start at zero. Calls that overlap in time on one device race (one stream, or
+ *   ordered streams, per device). The report word of the workspace (skipped page id, no room) is
+ *   not returned here; a request left without room still shows as seq_len_out = seq_len.
+ *   The first call on a device looks up the array's device address (hipGetSymbolAddress) with
+ *   that device current; OSCAR_ERR_LAUNCH if that fails.
+ */
+oscar_status_t oscar_decode_step_noalloc(const oscar_layout_t* layout, int32_t batch, int32_t max_seq_len,
+                                         const int32_t* seq_len, const int32_t* n_int4, const void* new_k,
+                                         const void* new_v, const uint8_t* demote_bits, const void* q,
+                                         const float* rot_k, const float* rot_v, void* pool,
+                                         const int32_t* page_table, const int32_t* page_table4,
+                                         int32_t pt_stride, void* window, int32_t* seq_len_out,
+                                         int32_t* n_int4_out, float softmax_scale, float* out,
+                                         hipStream_t stream);
+
 /*
  * In-house BF16 baseline: the full context of each request in BF16 pages (BF16 page-head
  * layout; page = Hkv page-heads, page ids index `pages`). Writes every position of k/v

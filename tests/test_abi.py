@@ -139,6 +139,26 @@ def test_step_argument_checks(lib):
               None, 0, None, None) == 0
 
 
+def test_noalloc_step_limits(lib):
+    """The no-allocation step accepts exactly the calls whose workspace bound fits its per-device
+    array (checked before any device work) and follows the step's argument checks."""
+    m = re.search(r"#define OSCAR_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == brk.ops.NOALLOC_SCRATCH_BYTES
+    lay = layout()
+    assert brk.decode_workspace_bytes(lay, 256, 1 << 20) <= brk.ops.NOALLOC_SCRATCH_BYTES
+    big = next(b for b in range(256, 1 << 16, 64)
+               if brk.decode_workspace_bytes(lay, b, 1000) > brk.ops.NOALLOC_SCRATCH_BYTES)
+    L = ctypes.byref(lay)
+    p = 1
+    st = lib.oscar_decode_step_noalloc
+    # (layout, batch, max_seq_len, seq_len, n_int4, new_k, new_v, demote_bits, q, rot_k, rot_v, pool,
+    #  page_table, page_table4, pt_stride, window, seq_len_out, n_int4_out, scale, out, stream)
+    assert st(L, big, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, 2, None, 0.0, p, None) == -3
+    assert st(L, -1, 1000, p, None, p, p, None, p, p, p, p, p, None, 100, p, 2, None, 0.0, p, None) == -1
+    assert st(L, 0, 1000, None, None, None, None, None, None, None, None, None, None, None, 100, None, 2, None, 0.0,
+              None, None) == 0
+
+
 def test_profiled_argument_checks(lib):
     """The timing variants need 4 caller-created events; nothing is enqueued otherwise."""
     L = ctypes.byref(layout())
