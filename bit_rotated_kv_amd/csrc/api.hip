@@ -17,7 +17,10 @@ namespace {
 constexpr int kMaxUnits = 2048;
 // Wide split workgroups (16 wavefronts) are used for GQA width 4 when this few (request, kv-head)
 // pairs would otherwise give each compute unit two or fewer 4-wavefront workgroups.
-constexpr int kWideMaxGroups = 16;
+#ifndef OSCAR_WIDE_MAX_GROUPS
+#define OSCAR_WIDE_MAX_GROUPS 16
+#endif
+constexpr int kWideMaxGroups = OSCAR_WIDE_MAX_GROUPS;
 // Plan costs: an INT2 history page costs 1, an INT4 page 2 (in the kernels); the step and the BF16
 // window are chains of latencies and cost about the pages their workgroup streams meanwhile
 // (per-workgroup timelines, one 100K-token request: the step's demote ~7 us, the window's 20 pages

@@ -485,7 +485,7 @@ __device__ __forceinline__ void softmax_page(WaveState<D, GQ>& st, const float (
 // read of an output is issued before the first is used.
 template <int D, int GQ, int VSH_BITS, bool REDIST = false, int NW = 4>
 __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8],
-                                float* part_o, float* part_lse, int nws = NW) {
+                                float* part_o, float* part_lse) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, h = lane % 16;
   float l_tot = st.l_part, z_tot = st.z_part;
   if constexpr (REDIST) {
@@ -500,20 +500,20 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
   l_tot += __shfl_xor(l_tot, 32, kWave);
   z_tot += __shfl_xor(z_tot, 16, kWave);
   z_tot += __shfl_xor(z_tot, 32, kWave);
-  if (g == 0 && h < GQ && wave < nws) {
+  // every wavefront writes its state (one that ran no page holds the empty state: m = -inf, sums
+  // 0), so the reduction below reads all NW entries without per-wavefront branches
+  if (g == 0 && h < GQ) {
     st_lds[wave][0][h] = st.m_run;
     st_lds[wave][1][h] = l_tot;
     st_lds[wave][2][h] = z_tot;
   }
-  if (wave < nws) {
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
+  for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
-      }
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
+    }
   OSCAR_TL_SPLIT(12);
   __syncthreads();
   OSCAR_TL_SPLIT(13);
@@ -523,7 +523,7 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      mw[w] = w < nws ? st_lds[w][0][hh] : kNegInf;
+      mw[w] = st_lds[w][0][hh];
       M = fmaxf(M, mw[w]);
     }
     float L = 0.0f, Z = 0.0f, O = 0.0f;
@@ -531,8 +531,8 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
     for (int w = 0; w < NW; ++w) {
       const bool live = mw[w] != kNegInf;
       const float aw = live ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.0f;
-      const float lw = w < nws ? st_lds[w][1][hh] : 0.0f, zw = w < nws ? st_lds[w][2][hh] : 0.0f;
-      const float ow = w < nws ? o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch] : 0.0f;
+      const float lw = st_lds[w][1][hh], zw = st_lds[w][2][hh];
+      const float ow = o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch];
       L = fmaf(aw, lw, L);
       Z = fmaf(aw, zw, Z);
       O = fmaf(aw, ow, O);
@@ -880,8 +880,8 @@ __device__ void window_seg(const DecodeArgs& a, int b, int kv, int w0, int ws, f
       cur = nxt;
     }
   }
-  // wavefronts past the unit's window pages hold no state
-  workgroup_merge<D, GQ, 16, false, NW>(st, o_lds, st_lds, po, pl, min(NW, (w1 - w0 + ws - 1) / ws));
+  // wavefronts past the unit's window pages hold the empty state
+  workgroup_merge<D, GQ, 16, false, NW>(st, o_lds, st_lds, po, pl);
 }
 
 // ------------------------------------------------------------------ INT2 / INT4 history pages
@@ -1409,9 +1409,8 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
   __syncthreads();
   OSCAR_TL_SPLIT(8);
-  // wavefronts past the segment's pages hold no state
-  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl,
-                                                              ppw > 0 ? min(NW, (p1 - p0 + ppw - 1) / ppw) : 1);
+  // wavefronts past the segment's pages hold the empty state
+  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl);
 }
 
 // LDS of the segments (one at a time per workgroup); 16-byte aligned for the vector reads of the
@@ -1649,7 +1648,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   // is done); its length is fetched now
   const bool ring = step_active(a, b) && h0 == 0 && tid < 2 * D;
   const int t_len = ring ? a.seq_len[b] : 0;
-  const int first = a.ws.req_units[2 * b], units = a.ws.req_units[2 * b + 1];
+  // one request owns every unit (no table read); otherwise the table the split wrote
+  const bool single = dm.batch == 1;
+  const int first = single ? 0 : a.ws.req_units[2 * b];
+  const int units = single ? a.ws.units_per_kv : a.ws.req_units[2 * b + 1];
   const int n = 3 * units + (a.step ? 2 : 0);
   // Slots are taken up to 12 at a time per thread: every load of a batch is issued (slots no segment
   // wrote are not read) before any is consumed, and the first batch's loads share one round trip
