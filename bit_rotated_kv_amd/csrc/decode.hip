@@ -1645,9 +1645,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   const int tid = threadIdx.x;
   const int hl = tid / TPH, r = tid % TPH, c4 = r % C4, grp = r / C4;
   // fused step: the new token's window slot is written at the end (every window read of the step
-  // is done); its length is fetched now
-  const bool ring = step_active(a, b) && h0 == 0 && tid < 2 * D;
-  const int t_len = ring ? a.seq_len[b] : 0;
+  // is done). Its length is fetched now as a vector load (an atomic load is never scalarised): it
+  // then shares the round trip of the partial loads instead of stalling the wavefront ahead of them.
+  const bool ring_wg = a.step && h0 == 0 && tid < 2 * D;
+  const int t_len = ring_wg ? __hip_atomic_load(a.seq_len + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
   // one request owns every unit (no table read); otherwise the table the split wrote
   const bool single = dm.batch == 1;
   const int first = single ? 0 : a.ws.req_units[2 * b];
@@ -1735,7 +1736,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
     }
   }
   OSCAR_TL_MERGE(5);
-  if (ring) {
+  if (ring_wg && t_len < dm.max_seq_len) {   // the step ran for this request (it had room)
     // the new token takes its window slot (the demoted token's ring slot, or position T), as the
     // demote kernel writes it
     int pgw, t;
