@@ -207,7 +207,7 @@ class Int2Setup:
 
 
 def time_int2(setup, steps, warmup, eager):
-    """Returns (ms per step, mean event intervals [launch gap, split, merge] in ms, launch mode).
+    """Returns (ms per step, median event intervals [launch gap, split, merge] in ms, launch mode).
 
     Step time: the K steps captured in one HIP graph and replayed (no host work inside the timed
     region). Kernel intervals: K more steps launched eagerly behind a GPU-side sleep, so every
@@ -246,6 +246,18 @@ def time_int2(setup, steps, warmup, eager):
         stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
+    setup.replay_spread_us = None
+    if mode == "graph":
+        # spread over further replays of the same K steps (replays repeat the same appends, so the
+        # caches stay in the same state)
+        per = []
+        for _ in range(9):
+            start.record()
+            g.replay()
+            stop.record()
+            torch.cuda.synchronize()
+            per.append(start.elapsed_time(stop) / steps)
+        setup.replay_spread_us = [round(float(x) * 1e3, 2) for x in np.percentile([ms] + per, [10, 50, 90])]
     base += steps
     # kernel intervals
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -261,7 +273,7 @@ def time_int2(setup, steps, warmup, eager):
     span = np.array([evs[i][0].elapsed_time(evs[i][3]) for i in range(steps)])
     # spread of the eagerly launched steps (first to last event of a step), microseconds
     setup.step_spread_us = [round(float(x) * 1e3, 2) for x in np.percentile(span, [10, 50, 90])]
-    return ms, k.mean(axis=0), mode
+    return ms, np.median(k, axis=0), mode
 
 
 # ---------------------------------------------------------------- Lloyd-Max codebook variant
@@ -444,7 +456,8 @@ def time_bs32_100k(args):
          "tokens_per_s": round(batch / (ms * 1e-3), 1), "split_GB_per_s": round(split, 1),
          "split_frac": round(split / HBM_PEAK_GBS, 4),
          "kernel_ms": {"split": round(float(k[1]), 5), "merge": round(float(k[2]), 5)},
-         "eager_step_us_p10_p50_p90": s.step_spread_us, "cache_copies": s.copies, "launch": mode}
+         "eager_step_us_p10_p50_p90": s.step_spread_us, "graph_step_us_p10_p50_p90": s.replay_spread_us,
+         "split_le_step": bool(float(k[1]) <= ms), "cache_copies": s.copies, "launch": mode}
     del s
     torch.cuda.empty_cache()
     if not args.no_bf16:
@@ -577,40 +590,109 @@ def traffic_from_profile():
 
 
 # ---------------------------------------------------------------- CPU oracle leg
-def cpu_baseline(w, context, kv_heads=8):
-    """The oracle's decode attention for `kv_heads` of the workload's KV heads (their query
-    groups) at full context, timed on the host; scaled to GB/s of the step's algorithmic bytes."""
+CPU_WORKERS_MAX = 16      # the host share of one GPU
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _cpu_step_worker(conn, wl, context, units, rk, rv):
+    """One worker process of the CPU baseline: builds the oracle caches of its (request, kv-head)
+    units at context - 1 tokens, then on each "go" runs one decode step per unit (append the new
+    token, which demotes position T - 256 into the INT2 history, then attend the unit's query
+    heads) and answers "done"."""
+    import threadpoolctl
+    threadpoolctl.threadpool_limits(1)          # BLAS threads = 1 per process
     import oracle
     import synth
-    import threadpoolctl
-    w1 = w
+    w = synth.workload(wl)
+    g = w.gqa
+    state = []
+    for b, kv in units:
+        K, V = synth.kv_slice(w, b, kv, context)
+        cache = oracle.OracleCache.from_prefix(K[None, :context - 1], V[None, :context - 1], rk[kv:kv + 1],
+                                               rv[kv:kv + 1], w.group_size)
+        q = synth.decode_query(w, b)[kv * g:(kv + 1) * g]
+        state.append((cache, q, K[None, context - 1].copy(), V[None, context - 1].copy()))
+        del K, V
+    conn.send("ready")
+    while conn.recv() == "go":
+        for cache, q, k, v in state:
+            cache.append(k, v)
+            oracle.decode_attention(cache, q)
+        conn.send("done")
+
+
+def cpu_baseline(wl=3, context=32_768, batch=32, steps=3):
+    """The oracle as it stands, timed on the host over one full decode step of the batch-32 x
+    32,768 workload: every (request, kv-head) unit demotes one token and attends its query heads.
+    Units run in min(os.cpu_count(), 16) worker processes with one BLAS thread each; the step's
+    wall time is the median of `steps` steps; GB/s counts the GPU step's algorithmic bytes."""
+    import multiprocessing as mp
+    import oracle
+    import synth
+    w = synth.workload(wl)
+    t_setup = time.perf_counter()
     rk, rv = [], []
-    for kv in range(kv_heads):
+    for kv in range(w.num_kv_heads):      # the rotations, as the oracle forms them (untimed)
         qc = synth.calibration_queries(w, kv)
         kc, vc = synth.calibration_context(w, kv)
         rk.append(oracle.rotation_fp32(oracle.compose_rotation(oracle.eigenbasis(oracle.query_covariance(qc)))))
         rv.append(oracle.rotation_fp32(oracle.compose_rotation(oracle.eigenbasis(
             oracle.score_weighted_value_covariance(qc[:, :1024], kc, vc, 1.0 / math.sqrt(w.head_dim))))))
-    rk, rv = np.stack(rk)[:kv_heads], np.stack(rv)[:kv_heads]
-    K = np.stack([synth.kv_slice(w1, 0, kv, context)[0] for kv in range(kv_heads)])
-    V = np.stack([synth.kv_slice(w1, 0, kv, context)[1] for kv in range(kv_heads)])
-    cache = oracle.OracleCache.from_prefix(K, V, rk, rv, w.group_size)      # untimed: the prefill
-    q = synth.decode_query(w, 0)[:kv_heads * w.gqa]
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] + [1])
-    times = []
-    while len(times) < 3 or (sum(times) < 12.0 and len(times) < 15):   # about 12 s of timed CPU work
-        t = time.perf_counter()
-        oracle.decode_attention(cache, q)
-        times.append(time.perf_counter() - t)
+    rk, rv = np.stack(rk), np.stack(rv)
+    units = [(b, kv) for b in range(batch) for kv in range(w.num_kv_heads)]
+    n = max(1, min(os.cpu_count() or 1, CPU_WORKERS_MAX, len(units)))
+    ctx = mp.get_context("spawn")
+    procs, conns = [], []
+    for i in range(n):
+        a, b_ = ctx.Pipe()
+        pr = ctx.Process(target=_cpu_step_worker, args=(b_, wl, context, units[i::n], rk, rv), daemon=True)
+        pr.start()
+        procs.append(pr)
+        conns.append(a)
+    try:
+        for c in conns:
+            if c.recv() != "ready":
+                raise RuntimeError("cpu baseline worker failed")
+        setup_s = time.perf_counter() - t_setup
+        times = []
+        for _ in range(steps):
+            t = time.perf_counter()
+            for c in conns:
+                c.send("go")
+            for c in conns:
+                if c.recv() != "done":
+                    raise RuntimeError("cpu baseline worker failed")
+            times.append(time.perf_counter() - t)
+        for c in conns:
+            c.send("stop")
+    finally:
+        for pr in procs:
+            pr.join(timeout=30)
+            if pr.is_alive():
+                pr.terminate()
     sec = float(np.median(times))
-    d = w.head_dim
-    nbytes = kv_heads * ((context - 320) * (2 * (d * 2 // 8) + 8) + 320 * 2 * d * 2)
-    return {"value": round(nbytes / sec / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle decode attention of {kv_heads} of {w.num_kv_heads} KV heads ({kv_heads * w.gqa} query "
-                      f"heads), full {context}-token context, median of {len(times)} runs of {sec:.2f} s; bytes counted as "
-                      f"the GPU metric's (INT2 history + BF16 window) for that share",
-            "seconds": round(sec, 3)}
+    d, hkv = w.head_dim, w.num_kv_heads
+    hist = context - 320
+    nbytes = (batch * hkv * hist * (2 * (d * 2 // 8) + 8) + batch * hkv * 320 * 2 * d * 2 +
+              batch * hkv * (2 * 2 * d * 2 + (2 * (d * 2 // 8) + 8)))
+    return {"value": round(nbytes / sec / 1e9, 6), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"one full decode step of the batch-{batch} x {context:,}-token workload ({len(units)} (request, "
+                      f"kv-head) units, each demoting one token into the INT2 history and attending its {w.gqa} query "
+                      f"heads), {n} worker processes with one BLAS thread each, median of {steps} steps; bytes counted "
+                      f"as the GPU step's (INT2 history + BF16 window + demote)",
+            "seconds_per_step": round(sec, 3), "step_times_s": [round(t, 3) for t in times],
+            "setup_s": round(setup_s, 1), "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 def timeline_main(args):
@@ -700,6 +782,12 @@ def main():
     if args.only:
         print(json.dumps(only_main(args)), flush=True)
         return
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched: the worker processes start from a process without a GPU context
+        log("timing the CPU oracle: one full batch-32 x 32,768 step, process-parallel")
+        cpu = cpu_baseline()
+        log(f"CPU oracle step {cpu['seconds_per_step']} s on {cpu['cores']} processes ({cpu['cpu_model']})")
     import torch
     import synth
     torch.manual_seed(0)
@@ -734,6 +822,8 @@ def main():
         "bytes_per_step": {"int2_history": int2, "bf16_window": bf16, "demote": demote, "total": step_bytes},
         "kernel_ms": {"split": round(split_ms, 5), "merge": round(float(kern[2]), 5)},
         "eager_step_us_p10_p50_p90": setup.step_spread_us,
+        "graph_step_us_p10_p50_p90": setup.replay_spread_us,
+        "split_le_step": bool(split_ms <= ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                      "kernel": "split_kernel<128,4,false,false> (BF16 window + INT2 history split-K + step workgroups, "
@@ -744,6 +834,8 @@ def main():
     del setup
     torch.cuda.empty_cache()
     log(f"INT2 step {ms * 1e3:.2f} us ({mode}); split {kern[1] * 1e3:.2f} us, merge {kern[2] * 1e3:.2f} us")
+    if split_ms > ms:
+        log("WARNING: the split kernel's event interval exceeds the graph-replayed step time")
     if not args.no_prefill:
         log("timing the prefill (matrix-core rotation + quantise)")
         result["prefill"] = time_prefill(w, batch, context)
@@ -776,7 +868,9 @@ def main():
                           "split_GB_per_s": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9, 1),
                           "split_frac": round((i2 + b2) / (float(k32[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel_ms": {"split": round(float(k32[1]), 5), "merge": round(float(k32[2]), 5)},
-                          "eager_step_us_p10_p50_p90": s32.step_spread_us}
+                          "eager_step_us_p10_p50_p90": s32.step_spread_us,
+                          "graph_step_us_p10_p50_p90": s32.replay_spread_us,
+                          "split_le_step": bool(float(k32[1]) <= ms32)}
         del s32
         torch.cuda.empty_cache()
         if not args.no_prefill:
@@ -797,9 +891,8 @@ def main():
         result["mixed_int2_int4"] = time_decode_workload(synth.workload(5), args.steps, args.warmup)
     if args.copy_probe_mib:
         result["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(w, context)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -11,7 +11,8 @@ import os
 from ctypes import c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboscar.so")
+# OSCAR_LIB names another build of the same library (the host sanitizer build for CPU tests)
+LIB_PATH = os.environ.get("OSCAR_LIB") or os.path.join(HERE, "liboscar.so")
 
 OSCAR_OK = 0
 STATUS = {0: "OSCAR_OK", -1: "OSCAR_ERR_INVALID_ARG", -2: "OSCAR_ERR_UNSUPPORTED", -3: "OSCAR_ERR_WORKSPACE",
