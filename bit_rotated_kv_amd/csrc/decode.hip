@@ -1280,13 +1280,16 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   }
 }
 
-// Page ids of a chunk of a wavefront's pages: lane i holds the id of page cb + i (i < kIdChunk), or
-// -1 at or past wp1. A page's address is formed from its id on the scalar unit when it is loaded.
+// Page indices of a chunk of a wavefront's pages, relative to the first page of the width's region:
+// lane i holds the index of page cb + i (i < kIdChunk), or -1 at or past wp1 and for ids outside
+// [first, lim) (another width's or outside the pool: skipped and flagged). Checked here, once per
+// lane and chunk, so a page's address is formed from its index on the scalar unit alone.
 constexpr int kIdChunk = 60;   // a multiple of both ring depths (4 and 6 pages)
 
-__device__ __forceinline__ int page_chunk(const int32_t* pt, int cb, int wp1, int lane) {
+__device__ __forceinline__ int page_chunk(const int32_t* pt, int cb, int wp1, int lane, int first, int lim) {
   const int idx = cb + lane;
-  return (lane < kIdChunk && idx < wp1) ? pt[idx] : -1;
+  const int id = (lane < kIdChunk && idx < wp1) ? pt[idx] : -1;
+  return (id >= first && id < lim) ? id - first : -1;
 }
 
 // History segment: pages [p0, p1) of width BITS of (b, kv), split into contiguous ranges of the NW
@@ -1319,8 +1322,12 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
 
   // Loads first, side by side: the page ids of this wavefront's first two chunks, the rows of R_K and
   // the queries of the group for the query prologue.
-  int cur = page_chunk(pt, wp0, wp1, lane);
-  int nxt = page_chunk(pt, wp0 + kIdChunk, wp1, lane);
+  // region of this width's page ids: INT2 ids [0, off4), INT4 ids [off4, pool_pages) (ids are 32-bit)
+  const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
+  const int id_first = BITS == 2 ? 0 : (int)min<int64_t>(off4, INT32_MAX);
+  const int id_lim = (int)min<int64_t>(BITS == 2 ? off4 : dm.pool_pages, INT32_MAX);
+  int cur = page_chunk(pt, wp0, wp1, lane, id_first, id_lim);
+  int nxt = page_chunk(pt, wp0 + kIdChunk, wp1, lane, id_first, id_lim);
   if (!PRE) rr.load(a.rot_k + (size_t)kv * D * D, tid);
   if (!PRE || !q_ready) qin.load(a.q + qbase * D, tid);
   const HistCounts hc = hist_counts(a, b);
@@ -1333,20 +1340,17 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   st.init();
   if (dm.pool_pages > 0) {
     int cbase = wp0;
-    // Page-head address of a page (uniform): ids outside the pool or of the other width are invalid;
-    // they and the prefetches past the range read zeros without touching memory.
-    const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
+    // Page-head address of a page (uniform): invalid ids and the prefetches past the range read
+    // zeros without touching memory.
     const int64_t head = qpage_head_bytes(D, BITS);
     const uint64_t region = (uint64_t)a.pool + (BITS == 2 ? 0 : (uint64_t)(off4 * qpage_head_bytes(D, 2) * dm.hkv));
-    const int64_t first_id = BITS == 2 ? 0 : off4;
     auto load = [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
       const int li = pg - cbase;
       const int id_cur = __builtin_amdgcn_readlane(cur, min(li, kWave - 1));
       const int id_nxt = __builtin_amdgcn_readlane(nxt, max(li - kIdChunk, 0));
-      const int64_t id = li < kIdChunk ? id_cur : id_nxt;
-      const bool valid = id >= first_id && id < (BITS == 2 ? off4 : dm.pool_pages);
-      const bool live = pg < wp1 && valid;
-      const uint64_t ad = valid ? region + (uint64_t)(((id - first_id) * dm.hkv + kv) * head) : (uint64_t)a.pool;
+      const int id = li < kIdChunk ? id_cur : id_nxt;
+      const bool live = pg < wp1 && id >= 0;
+      const uint64_t ad = region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head);
       load_qpage<BITS, D, GQ>(pr, ad, live, lane);
       return live;
     };
@@ -1372,7 +1376,7 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
       if (pg - cbase >= kIdChunk) {   // the next chunk of page ids becomes the current one
         cur = nxt;
         cbase += kIdChunk;
-        nxt = page_chunk(pt, cbase + kIdChunk, wp1, lane);
+        nxt = page_chunk(pt, cbase + kIdChunk, wp1, lane, id_first, id_lim);
       }
 #pragma unroll
       for (int k = 0; k < NB; k += 2) {
