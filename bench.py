@@ -67,6 +67,10 @@ def parse():
                          "instead of the benchmark line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling reference)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="write profiles/ summaries from rocprofv3 CSV output instead of benchmarking: "
+                         "'sq DIR' (SQ counter passes), 'traffic DIR' (FETCH_SIZE/WRITE_SIZE passes), "
+                         "'stats DIR' (kernel traces); DIR as the profiling commands below wrote it")
     return ap.parse_args()
 
 
@@ -595,6 +599,144 @@ def traffic_from_profile():
         return None
 
 
+# ---------------------------------------------------------------- profile summaries
+# The profiling runs behind profiles/ (each a process of its own; counters are collected per dispatch):
+#   SQ passes:      rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d DIR/sq_{w} -o run --
+#                   python3 -u bench.py --only {w} --steps 20 --warmup 5 --copies 6
+#   traffic passes: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR/fetch (DIR/write)
+#                   -o run -- python3 -u bench.py --only step --steps 50 --warmup 5 --copy-probe-mib 256
+#   kernel traces:  rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace_{w} -o run --
+#                   python3 -u bench.py --only {w} --steps 50 --warmup 5
+SQ_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT")
+PROFILE_WORKLOADS = ("step", "bs32", "gqa8_ragged", "prefill")
+SIMDS, SHADER_ENGINES, CLOCK_GHZ = 1024, 32, 2.4      # MI355X: 256 CUs x 4 SIMDs, 8 XCDs x 4 SEs
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _short_kernel(name):
+    for a, b in (("oscar::", ""), ("(anonymous namespace)::", ""), ("void ", "")):
+        name = name.replace(a, b)
+    return name.split("(")[0]
+
+
+def summarize_sq(d):
+    """Per-dispatch means of the SQ counters for every library kernel of each workload's pass, with
+    the issue fractions they imply."""
+    out = ["# rocprofv3 SQ counters of the decode split, merge and prefill kernels (per-dispatch means)",
+           f"# kernel sources sha256: {kernel_source_hash()}",
+           f"# command per workload w in {', '.join(PROFILE_WORKLOADS)}:",
+           f"#   rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d gpurun_out/pmc/sq_<w> -o run -- "
+           "python3 -u bench.py --only <w> --steps 20 --warmup 5 --copies 6",
+           "# derived (per dispatch): busy_us = SQ_BUSY_CYCLES / 32 shader engines / 2.4 GHz;",
+           "#   valu_issue = 4 * (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (1024 SIMDs * SQ_BUSY_CYCLES / 32) (a wave64",
+           "#   vector instruction occupies a SIMD for 4 cycles); mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 *",
+           "#   SQ_BUSY_CYCLES / 32); wait_inst = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; lds_conflict_per_cu_us =",
+           "#   SQ_LDS_BANK_CONFLICT / 256 CUs / 2.4 GHz. Counter runs serialise dispatches, so busy_us is the",
+           "#   profiled duration, not the benchmark's.", ""]
+    for w in PROFILE_WORKLOADS:
+        rows = [r for r in _csv_rows(os.path.join(d, f"sq_{w}"), "counter_collection.csv")
+                if "oscar" in r["Kernel_Name"]]
+        acc = {}
+        for r in rows:
+            key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        out.append(f"## workload: --only {w}")
+        for (k, grid, wg), cs in sorted(acc.items(), key=lambda kv: -np.mean(kv[1].get("SQ_BUSY_CYCLES", [0]))):
+            n = len(cs.get("SQ_BUSY_CYCLES", []))
+            if n < 3 or any(c not in cs for c in SQ_COUNTERS):
+                continue
+            m = {c: float(np.mean(v)) for c, v in cs.items()}
+            busy = m["SQ_BUSY_CYCLES"] / SHADER_ENGINES
+            valu = 4.0 * (m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / (SIMDS * busy)
+            mfma = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * busy)
+            out.append(f"{k} grid {grid} workgroup {wg}: {n} dispatches")
+            out.append("  " + "  ".join(f"{c}={m[c]:.4g}" for c in SQ_COUNTERS))
+            out.append(f"  busy_us={busy / CLOCK_GHZ / 1e3:.2f} valu_issue={valu:.3f} mfma_busy={mfma:.3f} "
+                       f"wait_inst={m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.3f} "
+                       f"lds_conflict_per_cu_us={m['SQ_LDS_BANK_CONFLICT'] / 256 / CLOCK_GHZ / 1e3:.2f} "
+                       f"valu_per_wave={(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_WAVES']:.0f} "
+                       f"mfma_per_wave={m['SQ_INSTS_MFMA'] / m['SQ_WAVES']:.1f}")
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
+def summarize_traffic(d):
+    """HBM bytes per bs1 split launch from FETCH_SIZE / WRITE_SIZE, scaled by the same counters' reading
+    of a plain 256 MiB device copy in the same run."""
+    def means(sub, name):
+        rows = [r for r in _csv_rows(os.path.join(d, sub), "counter_collection.csv") if r["Counter_Name"] == name]
+        split = [float(r["Counter_Value"]) for r in rows if "split_kernel" in r["Kernel_Name"]]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        return float(np.mean(split)), len(split), copy
+    fk, nf, cf = means("fetch", "FETCH_SIZE")
+    wk, nw, cw = means("write", "WRITE_SIZE")
+    copy_kib = 256 * 1024
+    ff, wf = copy_kib / cf, copy_kib / cw
+    traffic = (fk * ff + wk * wf) * 1024
+    alg = 58726400
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc/{d} -o run -- python3 -u bench.py --only step "
+           "--steps 50 --warmup 5 --copy-probe-mib 256")
+    lines = ["# rocprofv3 HBM counters of the split kernel at the qwen3-8b 100K-context bs1 step (INT2-only cache)",
+             f"# command (FETCH_SIZE pass): {cmd.format(c='FETCH_SIZE', d='fetch')}",
+             f"# command (WRITE_SIZE pass): {cmd.format(c='WRITE_SIZE', d='write')}",
+             "# per-dispatch counter means over the split launches of the run; the same run copies 256 MiB",
+             "# device-to-device once (--copy-probe-mib 256), whose counter reading gives the scale factor",
+             f"source_sha256: {kernel_source_hash()}",
+             f"split_dispatches_fetch: {nf}", f"split_dispatches_write: {nw}",
+             f"fetch_kib_per_dispatch: {fk:.3f}", f"write_kib_per_dispatch: {wk:.3f}",
+             f"copy_probe_kib: {copy_kib}", f"copy_fetch_kib: {cf:.3f}", f"copy_write_kib: {cw:.3f}",
+             f"fetch_factor: {ff:.5f}", f"write_factor: {wf:.5f}",
+             f"traffic_bytes_per_launch: {traffic:.0f}", f"algorithmic_bytes_per_launch: {alg}",
+             f"traffic_over_algorithmic: {traffic / alg:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_stats(d):
+    """Kernel-trace durations per (workload, kernel, grid)."""
+    import statistics
+    out = ["# rocprofv3 kernel trace durations (microseconds) of the library's kernels",
+           f"# kernel sources sha256: {kernel_source_hash()}",
+           f"# command per workload w in {', '.join(PROFILE_WORKLOADS)}:",
+           "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_<w> -o run -- "
+           "python3 -u bench.py --only <w> --steps 50 --warmup 5", ""]
+    for w in PROFILE_WORKLOADS:
+        rows = _csv_rows(os.path.join(d, f"trace_{w}"), "kernel_trace.csv")
+        groups = {}
+        for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+            if "oscar" not in r["Kernel_Name"]:
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+            groups.setdefault((_short_kernel(r["Kernel_Name"]), grid), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out.append(f"## workload: --only {w}")
+        out.append(f"{'kernel':<48} {'grid':>9} {'calls':>6} {'avg_us':>9} {'median':>9} {'min_us':>9} {'max_us':>9} "
+                   f"{'last50_avg':>10}")
+        for (k, g), v in sorted(groups.items(), key=lambda x: -sum(x[1])):
+            tail = v[-50:]
+            out.append(f"{k[:48]:<48} {g:>9} {len(v):>6} {sum(v) / len(v):>9.2f} {statistics.median(v):>9.2f} "
+                       f"{min(v):>9.2f} {max(v):>9.2f} {sum(tail) / len(tail):>10.2f}")
+        out.append("")
+    out.append("# last50_avg: the final 50 launches of the run, the eager steps whose HIP events give the bench's "
+               "kernel_ms (the earlier launches are graph replays)")
+    return "\n".join(out) + "\n"
+
+
+def summarize_main(args):
+    kind, d = args.summarize[0], args.summarize[1]
+    fn = {"sq": summarize_sq, "traffic": summarize_traffic, "stats": summarize_stats}[kind]
+    sys.stdout.write(fn(d))
+
+
 # ---------------------------------------------------------------- CPU oracle leg
 CPU_WORKERS_MAX = 16      # the host share of one GPU
 
@@ -784,6 +926,9 @@ def main():
         sys.exit(2)
     if args.timeline:
         timeline_main(args)
+        return
+    if args.summarize:
+        summarize_main(args)
         return
     if args.only:
         print(json.dumps(only_main(args)), flush=True)
