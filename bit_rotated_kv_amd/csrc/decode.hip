@@ -919,10 +919,13 @@ struct QPage {
 template <int BITS, int D, int GQ>
 constexpr int kPageLoadPolicy = (D <= 128 && (GQ == 4 || GQ == 8)) ? 2 : 0;
 
+// word 3 of a raw (untyped, unswizzled) buffer descriptor: loads at or past its size return zeros
+constexpr int kRawBufferFlags = 0x00020000;
+
 template <int BITS, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head, bool live) {
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0,
-                                           live ? 4 * D * BITS + kMetaBytes : 0, 0x00020000);
+                                           live ? 4 * D * BITS + kMetaBytes : 0, kRawBufferFlags);
 }
 
 template <int BITS, int D, int GQ>
@@ -1154,7 +1157,7 @@ __device__ __forceinline__ void page_logits(const QPage<BITS, D, GQ>& pr, float4
     xl = dpp_row_shr_into<4, 0x4>(xl, acc[2]);
     xl = dpp_row_shr_into<8, 0x8>(xl, acc[3]);
     lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh, xl, esc, uq);
-    lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;
+    if (lim < kPage) lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;   // a page with empty slots
   } else if constexpr (GQ == 8) {
     // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8; high parts from columns 0..7,
     // low parts from columns 8..15
@@ -1164,9 +1167,11 @@ __device__ __forceinline__ void page_logits(const QPage<BITS, D, GQ>& pr, float4
     const float l1 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[3]), __float_as_uint(acc[1])));
     lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0, l0, esc, uq);
     lg[1] = hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1, l1, esc, uq);
-    const int t0 = 4 * g + 2 * (c / 8);
-    lg[0] = t0 < lim ? lg[0] : kNegInf;
-    lg[1] = t0 + 1 < lim ? lg[1] : kNegInf;
+    if (lim < kPage) {   // a page with empty slots
+      const int t0 = 4 * g + 2 * (c / 8);
+      lg[0] = t0 < lim ? lg[0] : kNegInf;
+      lg[1] = t0 + 1 < lim ? lg[1] : kNegInf;
+    }
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1280,15 +1285,23 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   }
 }
 
-// Page indices of a chunk of a wavefront's pages, relative to the first page of the width's region:
-// lane i holds the index of page cb + i (i < kIdChunk), or -1 at or past wp1 and for ids outside
-// [first, lim) (another width's or outside the pool: skipped and flagged). Checked here, once per
-// lane and chunk, so a page's address is formed from its index on the scalar unit alone.
+// Page ids of a chunk of a wavefront's pages: lane i holds the id of page cb + i, or 0 at or past
+// wp1 (such pages are never loaded); a raw buffer load bounded at wp1 reads them, so no lane is
+// masked off and the loaded register needs no copy. Chunks start kIdChunk pages apart, so the last four lanes repeat the next chunk's first ids
+// and every prefetch of a trip finds its id in the current chunk; the next chunk is loaded a whole
+// chunk ahead and is only copied when it becomes current, so its load is not waited on early. page_index turns a page's id (read from its
+// lane onto the scalar unit) into its index relative to the first page of the width's region, -1 for
+// ids outside [first, lim) (another width's or outside the pool: skipped and flagged); the page's
+// address is then formed on the scalar unit.
 constexpr int kIdChunk = 60;   // a multiple of both ring depths (4 and 6 pages)
 
-__device__ __forceinline__ int page_chunk(const int32_t* pt, int cb, int wp1, int lane, int first, int lim) {
-  const int idx = cb + lane;
-  const int id = (lane < kIdChunk && idx < wp1) ? pt[idx] : -1;
+__device__ __forceinline__ int page_chunk(const int32_t* pt, int cb, int wp1, int lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(pt), (short)0, (int)(4 * max(wp1, 0)), kRawBufferFlags);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (cb + lane), 0, 0);
+}
+
+__device__ __forceinline__ int page_index(int id, int first, int lim) {
   return (id >= first && id < lim) ? id - first : -1;
 }
 
@@ -1311,6 +1324,8 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   // ahead do not fit the register bound of three workgroups per compute unit
   constexpr bool AHEAD = NB >= 6 && GQ < 8 && NW < 8;
   static_assert(NB % 2 == 0 && NB >= 4 && kIdChunk % NB == 0, "the ring holds whole page pairs");
+  // the furthest prefetch of a chunk's last trip reads lane kIdChunk + NB - 3 of the current chunk
+  static_assert(kIdChunk + NB - 3 < kWave, "every prefetch of a trip finds its id in the current chunk");
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, lane = tid % kWave, c = lane % 16;
   const int wave = uniform(tid / kWave);
@@ -1326,8 +1341,8 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   const int64_t off4 = dm.mixed ? dm.off4 : dm.pool_pages;
   const int id_first = BITS == 2 ? 0 : (int)min<int64_t>(off4, INT32_MAX);
   const int id_lim = (int)min<int64_t>(BITS == 2 ? off4 : dm.pool_pages, INT32_MAX);
-  int cur = page_chunk(pt, wp0, wp1, lane, id_first, id_lim);
-  int nxt = page_chunk(pt, wp0 + kIdChunk, wp1, lane, id_first, id_lim);
+  int cur = page_chunk(pt, wp0, wp1, lane);
+  int nxt = page_chunk(pt, wp0 + kIdChunk, wp1, lane);
   if (!PRE) rr.load(a.rot_k + (size_t)kv * D * D, tid);
   if (!PRE || !q_ready) qin.load(a.q + qbase * D, tid);
   const HistCounts hc = hist_counts(a, b);
@@ -1346,9 +1361,7 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
     const uint64_t region = (uint64_t)a.pool + (BITS == 2 ? 0 : (uint64_t)(off4 * qpage_head_bytes(D, 2) * dm.hkv));
     auto load = [&](QPage<BITS, D, GQ>& pr, int pg) -> bool {
       const int li = pg - cbase;
-      const int id_cur = __builtin_amdgcn_readlane(cur, min(li, kWave - 1));
-      const int id_nxt = __builtin_amdgcn_readlane(nxt, max(li - kIdChunk, 0));
-      const int id = li < kIdChunk ? id_cur : id_nxt;
+      const int id = page_index(__builtin_amdgcn_readlane(cur, min(li, kWave - 1)), id_first, id_lim);
       const bool live = pg < wp1 && id >= 0;
       const uint64_t ad = region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head);
       load_qpage<BITS, D, GQ>(pr, ad, live, lane);
@@ -1376,7 +1389,7 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
       if (pg - cbase >= kIdChunk) {   // the next chunk of page ids becomes the current one
         cur = nxt;
         cbase += kIdChunk;
-        nxt = page_chunk(pt, cbase + kIdChunk, wp1, lane, id_first, id_lim);
+        nxt = page_chunk(pt, cbase + kIdChunk, wp1, lane);
       }
 #pragma unroll
       for (int k = 0; k < NB; k += 2) {
