@@ -153,6 +153,16 @@ __device__ __forceinline__ float dpp_row_ror(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF,
                                                                false));
 }
+template <int N>
+__device__ __forceinline__ uint32_t dpp_row_ror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, true);   // every lane has a source
+}
+// DPP row shift left by N lanes (lane c reads lane c + N of its row; the last N lanes read 0).
+template <int N>
+__device__ __forceinline__ float dpp_row_shl_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x100 + N, 0xF, 0xF,
+                                                               true));
+}
 // Wave-uniform copy of a value (the compiler treats the result as scalar).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

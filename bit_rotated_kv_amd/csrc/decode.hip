@@ -1002,6 +1002,21 @@ __device__ __forceinline__ uint32_t split_f16(float w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two products p0*s0, p1*s1 split as split_f16 does, packed by part: `hi` holds the fp16 high
+// parts (token 0 in the low half), `lo` the fp16 of each product minus its high part. Each mixed
+// multiply-add writes its half in place (the compiler would build the halves apart and pack them).
+// The trailing s_nop gives a DPP read of either result the two wait states it needs after a vector
+// write (the compiler does not see the writes inside the statement).
+__device__ __forceinline__ void split_f16_pair(float p0, float s0, float p1, float s1, uint32_t& hi, uint32_t& lo) {
+  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(hi), "=&v"(lo)
+      : "v"(p0), "v"(s0), "v"(p1), "v"(s1));
+}
+
 // QK^T of one page: rows = the 16 token slots, columns = query operand columns (high parts of
 // the GQ heads in columns 0..GQ-1, low parts in GQ..2GQ-1, so one product covers both parts).
 // LUT: the codes become their codebook levels (two per byte permute) instead of subnormal slots.
@@ -1040,6 +1055,9 @@ __device__ __forceinline__ float4_t qk_page(const QPage<BITS, D, GQ>& pr, const 
 // nearly cancel only as far as the group's zero point exceeds the spread of its values).
 __device__ __forceinline__ float hist_logit(float s, float z, float xh, float xl, float esc, float u) {
   return fmaf(s, (xh + xl) * esc, z * u);
+}
+__device__ __forceinline__ float hist_logit_x(float s, float z, float x, float esc, float u) {
+  return fmaf(s, x * esc, z * u);
 }
 
 // B operand words of the PV product for value columns 16nb..16nb+15 of one page: the codes of the
@@ -1140,34 +1158,41 @@ constexpr int kPageLogits = GQ == 4 ? 1 : (GQ == 8 ? 2 : 4);
 
 // Logits of one page from its QK^T result `acc` (column c < GQ: high-part product of head c,
 // column GQ + c: low-part product). `lim` = tokens of the history from the page's first slot on:
-// slots at or past it get -inf.
+// slots at or past it get -inf. `lim` is uniform and below kPage only on the last page of a
+// range: the empty volatile asm keeps the masks behind a branch (the compiler would otherwise
+// compute and select them on every page).
 template <int BITS, int D, int GQ>
 __device__ __forceinline__ void page_logits(const QPage<BITS, D, GQ>& pr, float4_t acc, float uq, float esc, int lim,
                                             int lane, float (&lg)[kPageLogits<GQ>]) {
   const int g = lane / 16, c = lane % 16;
   if constexpr (GQ == 4) {
-    // lane (g, c) takes token 4g + c/4 of head c%4: high part from column c%4, low part from
-    // column 4 + c%4 of item c/4
-    float xh = acc[0];
-    xh = dpp_row_shr_into<4, 0x2>(xh, acc[1]);
-    xh = dpp_row_shr_into<8, 0x4>(xh, acc[2]);
-    xh = dpp_row_shr_into<12, 0x8>(xh, acc[3]);
-    float xl = acc[1];
-    xl = __uint_as_float(dpp_row_shl_into<4, 0x1>(__float_as_uint(xl), __float_as_uint(acc[0])));
-    xl = dpp_row_shr_into<4, 0x4>(xl, acc[2]);
-    xl = dpp_row_shr_into<8, 0x8>(xl, acc[3]);
-    lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), xh, xl, esc, uq);
-    if (lim < kPage) lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;   // a page with empty slots
+    // lane (g, c) takes token 4g + c/4 of head c%4. Lanes c < 4 first add the high part (own
+    // column) and the low part (column c + 4) of every row, then lane c passes row r on to lane
+    // 4r + c.
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = acc[r] + dpp_row_shl_f<4>(acc[r]);
+    float x = y[0];
+    x = dpp_row_shr_into<4, 0x2>(x, y[1]);
+    x = dpp_row_shr_into<8, 0x4>(x, y[2]);
+    x = dpp_row_shr_into<12, 0x8>(x, y[3]);
+    lg[0] = hist_logit_x(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), x, esc, uq);
+    if (lim < kPage) {
+      asm volatile("");
+      lg[0] = 4 * g + c / 4 < lim ? lg[0] : kNegInf;
+    }
   } else if constexpr (GQ == 8) {
-    // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8; high parts from columns 0..7,
-    // low parts from columns 8..15
-    const float h0 = dpp_row_shr_into<8, 0xC>(acc[0], acc[2]);
-    const float h1 = dpp_row_shr_into<8, 0xC>(acc[1], acc[3]);
-    const float l0 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[2]), __float_as_uint(acc[0])));
-    const float l1 = __uint_as_float(dpp_row_shl_into<8, 0x3>(__float_as_uint(acc[3]), __float_as_uint(acc[1])));
-    lg[0] = hist_logit(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), h0, l0, esc, uq);
-    lg[1] = hist_logit(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), h1, l1, esc, uq);
-    if (lim < kPage) {   // a page with empty slots
+    // lane (g, c): tokens 4g + 2(c/8) + {0, 1} of head c%8. Its own column holds one part of
+    // head c%8 (high for c < 8, low for c >= 8) and lane c^8 the other: each lane keeps the rows
+    // of its tokens and passes its partner the rows of the partner's tokens (x + y, added in
+    // either order, is the same sum).
+    const bool lo8 = c < 8;
+    const float x0 = (lo8 ? acc[0] : acc[2]) + dpp_row_ror<8>(lo8 ? acc[2] : acc[0]);
+    const float x1 = (lo8 ? acc[1] : acc[3]) + dpp_row_ror<8>(lo8 ? acc[3] : acc[1]);
+    lg[0] = hist_logit_x(lo_bf16(pr.mt[0]), hi_bf16(pr.mt[0]), x0, esc, uq);
+    lg[1] = hist_logit_x(lo_bf16(pr.mt[2]), hi_bf16(pr.mt[2]), x1, esc, uq);
+    if (lim < kPage) {
+      asm volatile("");
       const int t0 = 4 * g + 2 * (c / 8);
       lg[0] = t0 < lim ? lg[0] : kNegInf;
       lg[1] = t0 + 1 < lim ? lg[1] : kNegInf;
@@ -1177,7 +1202,11 @@ __device__ __forceinline__ void page_logits(const QPage<BITS, D, GQ>& pr, float4
     for (int r = 0; r < 4; ++r) {
       const float xl = __uint_as_float(dpp_row_shl<GQ>(__float_as_uint(acc[r])));
       lg[r] = hist_logit(lo_bf16(pr.mt[2 * r]), hi_bf16(pr.mt[2 * r]), acc[r], xl, esc, uq);
-      lg[r] = 4 * g + r < lim ? lg[r] : kNegInf;
+    }
+    if (lim < kPage) {
+      asm volatile("");
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lg[r] = 4 * g + r < lim ? lg[r] : kNegInf;
     }
   }
 }
@@ -1198,18 +1227,18 @@ __device__ __forceinline__ void page_operand(WaveState<D, GQ>& st, const QPage<B
     // +4, +8); rows 8..15 are zero (selector bytes 0x0C). Lanes 8..15 of y, u, v8 keep whatever
     // they hold: the selector zeroes those rows.
     const uint32_t P = split_f16(p[0] * lo_bf16(pr.mt[1]));
-    const uint32_t y = dpp_row_shr_into<4, 0x2>(dpp_row_shl_into<4, 0x1>(P, P), P);
-    const uint32_t u = dpp_row_shl_into<4, 0x2>(dpp_row_shl_into<12, 0x1>(P, P), P);
-    const uint32_t v8 = dpp_row_shl_into<8, 0x3>(P, P);
-    a01 = __builtin_amdgcn_perm(y, P, psel);
-    a23 = __builtin_amdgcn_perm(u, v8, psel);
+    // lane c takes tokens 4g + j from lanes 4j + c%4: P itself, and P rotated by 4, 8, 12 lanes
+    // (rotating right by 12 reads lane c + 4). Rows c < 4 pair (own, c+4) and (c+8, c+12); rows
+    // 4..7 pair (c-4, own) and (c+4, c+8).
+    const uint32_t r4 = dpp_row_ror_u<4>(P), r8 = dpp_row_ror_u<8>(P), r12 = dpp_row_ror_u<12>(P);
+    const bool b0 = c < 4;
+    a01 = __builtin_amdgcn_perm(b0 ? r12 : r4, P, psel);
+    a23 = __builtin_amdgcn_perm(b0 ? r4 : r12, r8, psel);
   } else if constexpr (GQ == 8) {
     st.l_part += p[0] + p[1];
     st.z_part = fmaf(p[0], hi_bf16(pr.mt[1]), fmaf(p[1], hi_bf16(pr.mt[3]), st.z_part));
-    const uint32_t q0 = split_f16(p[0] * lo_bf16(pr.mt[1]));
-    const uint32_t q1 = split_f16(p[1] * lo_bf16(pr.mt[3]));
-    const uint32_t P0 = pack_lo16(q0, q1);   // high parts of both tokens
-    const uint32_t L0 = pack_hi16(q0, q1);   // low parts of both tokens
+    uint32_t P0, L0;   // fp16 high parts of both tokens, and their low parts
+    split_f16_pair(p[0], lo_bf16(pr.mt[1]), p[1], lo_bf16(pr.mt[3]), P0, L0);
     // row c < 8: high parts of head c, tokens 4g, 4g+1 (own) and 4g+2, 4g+3 (lane c+8);
     // row c >= 8: low parts of head c-8, tokens 4g, 4g+1 (lane c-8) and 4g+2, 4g+3 (own)
     a01 = dpp_row_shr_into<8, 0xC>(P0, L0);
@@ -1346,7 +1375,7 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   if (!PRE) rr.load(a.rot_k + (size_t)kv * D * D, tid);
   if (!PRE || !q_ready) qin.load(a.q + qbase * D, tid);
   const HistCounts hc = hist_counts(a, b);
-  const int ntok = BITS == 2 ? hc.n2 : hc.n4;
+  const int ntok = uniform(BITS == 2 ? hc.n2 : hc.n4);   // so every page limit is a scalar
 
   // byte selector of the PV operand gather at GQA width 4 (lo/lo halves on lanes 0..3 of a row,
   // hi/hi halves on lanes 4..7, zero elsewhere)
