@@ -477,11 +477,13 @@ def time_bs32_100k(args):
     return r
 
 
-def time_decode_workload(w, steps, warmup):
+def time_decode_workload(w, steps, warmup, timeline_steps=0, timeline_raw=""):
     """Decode attention alone (no demote) over a whole workload batch at its own lengths: the
     ragged GQA-8 batch (workload 4) or the mixed INT2/INT4 batch (workload 5), whose token widths
     come from the library's class allocation and tag routing. K/V are GPU draws of the workload's
-    channel law; cache copies rotate so the Infinity Cache cannot serve repeats."""
+    channel law; cache copies rotate so the Infinity Cache cannot serve repeats. With
+    timeline_steps > 0 (diagnostic library loaded), records that many eager calls' per-workgroup
+    timelines instead and returns their summary."""
     import torch
     import bit_rotated_kv_amd as brk
     import synth
@@ -531,6 +533,20 @@ def time_decode_workload(w, steps, warmup):
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
+    if timeline_steps:
+        from bit_rotated_kv_amd import timeline
+        tabs = []
+        for i in range(timeline_steps):
+            timeline.clear()
+            call(warmup + i)
+            torch.cuda.synchronize()
+            tabs.append(timeline.read())
+        if timeline_raw:
+            np.save(timeline_raw, np.stack(tabs))
+        res = timeline.summarize(tabs)
+        res["workload"] = (f"{w.name}: batch {B}, lengths {min(lens)}..{tmax}, {hq}q/{hkv}kv heads, d {d}, "
+                           f"decode only, eager launches")
+        return res
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
@@ -850,6 +866,11 @@ def timeline_main(args):
     import synth
     from bit_rotated_kv_amd import timeline
     timeline.use_timeline_library()
+    if args.only in ("gqa8_ragged", "mixed"):
+        res = time_decode_workload(synth.workload(4 if args.only == "gqa8_ragged" else 5), 0, args.warmup,
+                                   timeline_steps=args.timeline, timeline_raw=args.timeline_raw)
+        print(json.dumps(res), flush=True)
+        return
     w = synth.workload(2 if args.batch == 1 else 3)
     batch, context = args.batch, args.context
     est = batch * w.num_kv_heads * (context - 320) * 72

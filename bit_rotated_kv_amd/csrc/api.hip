@@ -22,11 +22,25 @@ constexpr int kMaxUnits = 2048;
 #endif
 constexpr int kWideMaxGroups = OSCAR_WIDE_MAX_GROUPS;
 // Plan costs: an INT2 history page costs 1, an INT4 page 2 (in the kernels); the step and the BF16
-// window are chains of latencies and cost about the pages their workgroup streams meanwhile
-// (per-workgroup timelines, one 100K-token request: the step's demote ~7 us, the window's 20 pages
-// ~5 us; a 16-wavefront workgroup streams ~17 pages per us, a 4-wavefront one ~6).
-int step_cost(int nw) { return nw >= kSplitWavesWide ? 160 : 64; }
-int window_cost(int nw) { return nw >= kSplitWavesWide ? 80 : 96; }
+// window are chains of latencies and cost about the pages their workgroup streams meanwhile.
+// Per-workgroup timelines of one 100K-token request (16-wavefront workgroups streaming ~19 pages
+// per us): the window segment takes ~6 us and its unit then ends ~1 us after the history-only
+// units of its compute die, the step unit ~0.3 us after; a sweep of the two costs put the split's
+// end lowest at 200 (step) and 150 (window). 4-wavefront workgroups stream ~6-7 pages per us.
+#ifndef OSCAR_STEP_COST_WIDE
+#define OSCAR_STEP_COST_WIDE 200
+#endif
+#ifndef OSCAR_WIN_COST_WIDE
+#define OSCAR_WIN_COST_WIDE 150
+#endif
+#ifndef OSCAR_STEP_COST
+#define OSCAR_STEP_COST 64
+#endif
+#ifndef OSCAR_WIN_COST
+#define OSCAR_WIN_COST 96
+#endif
+int step_cost(int nw) { return nw >= kSplitWavesWide ? OSCAR_STEP_COST_WIDE : OSCAR_STEP_COST; }
+int window_cost(int nw) { return nw >= kSplitWavesWide ? OSCAR_WIN_COST_WIDE : OSCAR_WIN_COST; }
 
 // Smallest unit the plan aims for (cost of 16 INT2 pages): below it the per-workgroup overhead (query
 // prologue, workgroup merge, one more partial to merge) outweighs the spread.

@@ -5,15 +5,14 @@
 // INT4 pages) merged by log-sum-exp.
 //
 // Kernels of one decode call, in stream order:
-//   q_prologue   only when a decode has many history workgroups: the query operands of every
-//                (request, kv-head, code width), written once to the workspace
-//   split        one launch, homogeneous roles by workgroup index: BF16 window pages (sink +
-//                recent), INT2 history pages, INT4 history pages (mixed caches), and in a fused
-//                decode step one step workgroup per (request, kv-head); each workgroup = 4
-//                wavefronts and writes (o, lse) partials per query head. Without the prologue
-//                kernel, history workgroups form their own query operands: q' = (q . R_K) *
-//                scale * log2(e), split into fp16 high/low matrix-core operands scaled per
-//                channel for the code unpacking below.
+//   split        one launch, one workgroup per unit of a device-side work plan: a unit is a cost
+//                range of its request's sequence [step | INT2 pages | INT4 pages | BF16 window]
+//                and runs the segments that range holds (the fused step's demote and new-token
+//                partials, window pages, history pages of each width), writing (o, lse) partials
+//                per query head. Workgroups are 4 wavefronts, or 16 at small GQA-4 batches. Each
+//                history segment forms its query operands itself: q' = (q . R_K) * scale *
+//                log2(e), split into fp16 high/low matrix-core operands scaled per channel for the
+//                code unpacking below.
 //   merge        per (request, kv-head): LSE-merge the history partials (rotated basis), apply
 //                R_V^T, LSE-merge with the BF16 window partials, write the fp32 output; in a fused
 //                step it also writes the new token into its window slot.
@@ -35,8 +34,8 @@
 // c * 2^(p-24); the 2^(24-p) factor is folded into the query operand (keys) or applied once to the
 // accumulator (values). Query and softmax weights are split into high + low fp16 parts (~22
 // significant bits); the two parts sit in spare columns (QK^T) and spare rows (PV). Each
-// wavefront keeps a six-page load ring (three page pairs), with all its page ids fetched by one
-// vector load up front.
+// wavefront streams its contiguous page range through a load ring of page pairs (six pages, four
+// in 16-wavefront workgroups), its page ids fetched a chunk of 60 at a time.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
