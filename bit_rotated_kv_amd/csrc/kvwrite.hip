@@ -1,6 +1,8 @@
 // Cache writers: prefill (sink/recent windows and rotated+quantised history pages), the per-step
 // demote of the oldest recent token (OSCAR overview page, method paragraph; study note, SGLang
 // case), and the fill of the full-BF16 baseline cache.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "demote.hpp"
@@ -309,222 +311,255 @@ __device__ __forceinline__ uint32_t int2_code_estimate(float x, const QuantGrid&
   return (uint32_t)__builtin_amdgcn_fmed3f(r, 0.0f, 3.0f);
 }
 
+// Two 32-row tiles of x (row m of tile k at x + (32k + m) * stride; rows at or past nrows read as
+// zero) times the wavefront's slice of R: rotate_tile's products in rotate_tile's order for each
+// tile, the two tiles' chains interleaved so each hides the other's matrix-core latency.
+template <int D>
+__device__ __forceinline__ void rotate_tile_pair(const RotSlice<D>& rs, const uint16_t* x, int stride, int nrows,
+                                                 int lane, float16v_t& acc0, float16v_t& acc1) {
+  acc0 = float16v_t{};
+  acc1 = float16v_t{};
+#pragma unroll
+  for (int kk = 0; kk < RotSlice<D>::KS; ++kk) {
+    const bf16x8_t a0 = rotation_a(x, stride, nrows, kk, lane);
+    const bf16x8_t a1 = rotation_a(x + 32 * stride, stride, nrows - 32, kk, lane);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, rs.lo[kk], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, rs.lo[kk], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, rs.mid[kk], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, rs.mid[kk], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, rs.hi[kk], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, rs.hi[kk], acc1, 0, 0, 0);
+  }
+}
+
 // The history of an INT2-only cache (every token takes consecutive INT2 slots, so a chunk of 64
-// positions owns 4 whole pages). Same workgroups, rotation and code rule as prefill_hist_kernel, but
-// the codes never pass through LDS bytes: each quantising thread places its codes at their bit
-// positions in the page-head words they belong to and writes those partial words to LDS; the store
-// phase ORs the partials of a word and stores it whole.
-// Quantising thread (row qi, qq) takes channels 16c + 4qq + u (c < D/16, u < 4): its float4 reads of
-// the rotated row are then conflict-free (rows pitched 16 banks apart), and
-//  * key word (g, a) of the row's token holds channels 64a + 32k2 + 8g + j (k2 < 2, j < 8) at bit
-//    8k2 + 2(j/2) + 16(j%2): thread qq = 2(g%2) + j/4 holds 8 of them in its partial g/2 + 2a;
-//  * value word (column cv, a) of a 4-token group holds channels 64a + 16n4 + cv (n4 < 4) of the 4
-//    tokens 2m + hf at bit 2n4 + 8m + 16hf: thread qq = cv/4 of each row holds 4 in partial 4a + cv%4.
-// The rows' bf16 staging and the partial words share LDS (a barrier separates the last rotation read
-// from the first partial write).
+// positions owns 4 whole pages), with the rotation and code rule of prefill_hist_kernel. One
+// workgroup of 8 wavefronts per (run of `run` chunks, kv-head, request x {K, V}), one per compute
+// unit: wavefronts 0..3 rotate (matrix cores) and wavefronts 4..7 quantise and store, one chunk
+// apart, so the matrix cores and the vector units work at once. In iteration i the rotating
+// wavefronts stage chunk i+1's rows (loaded during iteration i-1) in LDS, issue chunk i+2's loads
+// and rotate chunk i; the quantising ones fetch chunk i's page ids and quantise and store chunk i-1.
+// Every LDS buffer passed between the two sides is double-buffered, so one workgroup barrier per
+// iteration orders them all.
+// Four quantising threads per row (token). Each assembles whole page-head words in registers and
+// stores them itself:
+//  * keys: key word (g, a) of a token holds channels 64a + 32k2 + 8g + j (k2 < 2, j < 8) at bit
+//    8k2 + 2(j/2) + 16(j%2), so thread qq = g takes those channels and stores words (g, 0..) whole;
+//  * values: value word (column cv, a) of a group of 4 tokens holds channels 64a + 16n4 + cv
+//    (n4 < 4) of tokens 2m + hf at bit 2n4 + 8m + 16hf, so thread qq takes channels 16c + 4qq + u
+//    and places its row's codes of columns 4qq + u; the four rows of a group sit 4 lanes apart in a
+//    DPP row, where two rotate-and-OR steps complete every word in every lane, and the lane of row r
+//    stores column 4qq + r.
+// The float4 reads of the rotated rows are conflict-free (rows pitched 16 banks apart).
 template <int D, bool CBK>
-__global__ __launch_bounds__(256, 2) void prefill_int2_kernel(CacheWriteArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_int2_kernel(CacheWriteArgs a, int run) {
   constexpr int CH = kPrefillChunk;
   constexpr int XS = D + 8;     // bf16 row pitch (16-byte pad)
   constexpr int RS = D + 16;    // fp32 row pitch: consecutive rows 16 banks apart
   constexpr int QC = D / 4;     // channels of a quantising thread
   constexpr int NC = D / 16;    // its float4 groups
   constexpr int SL = RotSlice<D>::SLICES;
-  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per thread
+  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per rotating thread
   constexpr int CB = D * 2 / 32;         // bytes of a lane's key (or value) part
   constexpr int NWL = CB / 4;            // its words
-  constexpr int NPK = 2 * NWL;           // key partial words per thread
-  constexpr int NPV = 4 * NWL;           // value partial words per thread
-  constexpr int PS = 9;                  // partial words per thread, padded (8 used at most)
-  union alignas(16) Stage {
-    uint16_t xs[CH][XS];
-    uint32_t part[CH * 4][PS];
-  };
-  __shared__ Stage stg;
-  __shared__ __attribute__((aligned(16))) float xr[CH][RS];
-  __shared__ uint32_t szs[CH];
-  constexpr int RUN_PAGES = kPrefillChunks * CH / kPage;
-  __shared__ int64_t page_s[RUN_PAGES];
+  constexpr int CP = CH / kPage;         // pages of a chunk
+  static_assert(NWL == 1 || NWL == 2, "d = 64 or 128");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][CH][XS];
+  __shared__ __attribute__((aligned(16))) float xr[2][CH][RS];
+  __shared__ int64_t pgs[2][CP];
   const Dims& dm = a.dm;
   const int kv = blockIdx.y, b = blockIdx.z / 2, sel = blockIdx.z % 2;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x;
+  const bool rot = tid < 256;                 // wavefronts 0..3 rotate
+  const int rt = tid % 256, wave = rt / kWave, lane = tid % kWave;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
   const int hist = T - dm.sink - dm.recent;
-  const int chunk0 = kPrefillChunks * blockIdx.x;
-  if (CH * chunk0 >= hist) return;
-  const int nchunks = min(kPrefillChunks, (hist - CH * chunk0 + CH - 1) / CH);
+  const int chunk0 = run * blockIdx.x;
+  if (CH * chunk0 >= hist) return;   // the whole workgroup
+  const int nchunks = min(run, (hist - CH * chunk0 + CH - 1) / CH);
   const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
-  RotSlice<D> rs;
-  if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
-  const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
-  const float clip = sel ? a.clip_v : a.clip_k;
   auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
     const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
 #pragma unroll
     for (int e = 0; e < XW; ++e) {
-      const int idx = tid + 256 * e, row = idx / (D / 8), c8 = idx % (D / 8);
+      const int idx = rt + 256 * e, row = idx / (D / 8), c8 = idx % (D / 8);
       w[e] = u32x4_t{0, 0, 0, 0};
       if (row < n) w[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(p0 + row) * D + 8 * c8);
     }
   };
-  u32x4_t xw[XW];
-  load_rows(chunk0, xw);
-  if (tid < RUN_PAGES) {
-    const int pi = CH * chunk0 / kPage + tid;
-    const int64_t page = pi < dm.pt_stride ? (int64_t)a.pt2[(size_t)b * dm.pt_stride + pi] : -1;
-    page_s[tid] = page_ok(page, 2, dm) ? page : -1;
-  }
-  const int qi = tid / 4, qq = tid % 4;
-  // bit offset of the thread's codes that depends on it alone: key words 4(qq%2) (j = 4(qq%2) + u);
-  // value words 8m + 16hf of the row's token within its group of 4
-  const int kbase = 4 * (qq % 2), vbase = 8 * ((qi % 4) / 2) + 16 * (qi % 2);
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int chunk = chunk0 + ci;
-    const int n = min(CH, hist - CH * chunk);
+  auto stage_rows = [&](int buf, const u32x4_t (&w)[XW]) {
 #pragma unroll
     for (int e = 0; e < XW; ++e) {
-      const int idx = tid + 256 * e;
-      *reinterpret_cast<u32x4_t*>(&stg.xs[idx / (D / 8)][8 * (idx % (D / 8))]) = xw[e];
+      const int idx = rt + 256 * e;
+      *reinterpret_cast<u32x4_t*>(&xs[buf][idx / (D / 8)][8 * (idx % (D / 8))]) = w[e];
     }
+  };
+  const int ct = tid - 256;            // quantising thread (tid >= 256)
+  auto fetch_pages = [&](int chunk, int buf) {   // page ids of a chunk (threads ct < CP)
+    const int pi = CP * chunk + ct;
+    const int64_t page = pi < dm.pt_stride ? (int64_t)a.pt2[(size_t)b * dm.pt_stride + pi] : -1;
+    pgs[buf][ct] = page_ok(page, 2, dm) ? page : -1;
+  };
+  if (rot) {   // rotating wavefronts
+    RotSlice<D> rs;
+    if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
+    u32x4_t xw[XW];
+    load_rows(chunk0, xw);
+    stage_rows(0, xw);
+    if (nchunks > 1) load_rows(chunk0 + 1, xw);
     __syncthreads();
-    if (ci + 1 < nchunks) load_rows(chunk + 1, xw);   // in flight during this chunk
-    if (wave < SL) {
+    for (int i = 0; i < nchunks + 1; ++i) {
+      if (i + 1 < nchunks) stage_rows((i + 1) % 2, xw);   // loaded during the previous iteration
+      if (i + 2 < nchunks) load_rows(chunk0 + i + 2, xw);
+      if (i < nchunks && wave < SL) {
+        const int n = min(CH, hist - CH * (chunk0 + i));
+        float16v_t acc0, acc1;
+        rotate_tile_pair<D>(rs, &xs[i % 2][0][0], XS, n, lane, acc0, acc1);
 #pragma unroll
-      for (int tile = 0; tile < CH / 32; ++tile) {
-        const float16v_t acc = rotate_tile<D>(rs, &stg.xs[32 * tile][0], XS, n - 32 * tile, lane);
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          xr[32 * tile + 8 * (j / 4) + 4 * (lane / 32) + j % 4][32 * wave + lane % 32] = acc[j];
+        for (int j = 0; j < 16; ++j) {
+          const int r = 8 * (j / 4) + 4 * (lane / 32) + j % 4, col = 32 * wave + lane % 32;
+          xr[i % 2][r][col] = acc0[j];
+          xr[i % 2][32 + r][col] = acc1[j];
+        }
       }
+      __syncthreads();
     }
+  } else {     // quantising wavefronts: as many barriers, in a loop of their own (so neither side's
+               // registers stay live in the other's)
+    const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
+    const float clip = sel ? a.clip_v : a.clip_k;
+    const int qi = ct / 4, qq = ct % 4;
+    const int r4 = qi % 4;                            // the row's token within its group of 4
+    const int vbase = 8 * (r4 / 2) + 16 * (r4 % 2);   // value words: bit 8m + 16hf of the row's token
     __syncthreads();
-    {
-      const bool live = qi < n;
-      float x[QC];
+    for (int i = 0; i < nchunks + 1; ++i) {
+      // chunk i's page ids, read by iteration i+1 (this one reads buffer (i-1) % 2)
+      if (i < nchunks && ct < CP) fetch_pages(chunk0 + i, i % 2);
+      if (i >= 1) {
+        // quantise and store chunk i-1 from the rotated rows of its buffer
+        const int chunk = chunk0 + i - 1, qb = (i - 1) % 2;
+        const int n = min(CH, hist - CH * chunk);
+        const bool live = qi < n;
+        // channel of the thread's value e = 4c + u: keys 64(c/4) + 32((c/2)%2) + 8qq + 4(c%2) + u,
+        // values 16c + 4qq + u
+        auto chan4 = [&](int c) { return sel == 0 ? 64 * (c / 4) + 32 * ((c / 2) % 2) + 8 * qq + 4 * (c % 2)
+                                                  : 16 * c + 4 * qq; };
+        float x[QC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(&xr[qi][16 * c + 4 * qq]);
-        x[4 * c] = v.x;
-        x[4 * c + 1] = v.y;
-        x[4 * c + 2] = v.z;
-        x[4 * c + 3] = v.w;
-      }
-      float mn = x[0], mx = x[0];
+        for (int c = 0; c < NC; ++c) {
+          const float4 v = *reinterpret_cast<const float4*>(&xr[qb][qi][chan4(c)]);
+          x[4 * c] = v.x;
+          x[4 * c + 1] = v.y;
+          x[4 * c + 2] = v.z;
+          x[4 * c + 3] = v.w;
+        }
+        float mn = x[0], mx = x[0];
 #pragma unroll
-      for (int e = 1; e < QC; ++e) {
-        mn = fminf(mn, x[e]);
-        mx = fmaxf(mx, x[e]);
-      }
-      mn = fminf(mn, dpp_f<0xB1>(mn));
-      mx = fmaxf(mx, dpp_f<0xB1>(mx));
-      mn = fminf(mn, dpp_f<0x4E>(mn));
-      mx = fmaxf(mx, dpp_f<0x4E>(mx));
-      const QuantGrid g = make_grid(mn, mx, clip, 3);
-      // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
-      // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone in
-      // x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny scale,
-      // a zero point far off the range) take int2_code_estimate.
-      bool short_row = false;
-      if (!CBK) {
+        for (int e = 1; e < QC; ++e) {
+          mn = fminf(mn, x[e]);
+          mx = fmaxf(mx, x[e]);
+        }
+        mn = fminf(mn, dpp_f<0xB1>(mn));
+        mx = fmaxf(mx, dpp_f<0xB1>(mx));
+        mn = fminf(mn, dpp_f<0x4E>(mn));
+        mx = fmaxf(mx, dpp_f<0x4E>(mx));
+        const QuantGrid g = make_grid(mn, mx, clip, 3);
+        // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
+        // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone
+        // in x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny
+        // scale, a zero point far off the range) take int2_code_estimate.
+        bool short_row = false;
+        if (!CBK) {
 #pragma clang fp contract(off)
-        const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
-        short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
-      }
-      uint32_t part[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) part[k] = 0;
-      uint32_t redo = 0;
-      // codes of the row segment under one rule for the whole thread (the branch is per row, so the
-      // loops stay straight-line; a wavefront skips a loop none of its lanes takes)
-      auto place = [&](int e, uint32_t code) {
-        const int c = e / 4, u = e % 4;
-        if (sel == 0)   // key: k2 = (c/2)%2, partial (c%2) + 2(c/4), bit 8k2 + 4(qq%2) + 2(u/2) + 16(u%2)
-          part[(c % 2) + 2 * (c / 4)] |= code << (kbase + 8 * ((c / 2) % 2) + 2 * (u / 2) + 16 * (u % 2));
-        else            // value: n4 = c%4, partial 4(c/4) + u, bit 2n4 + 8m + 16hf
-          part[4 * (c / 4) + u] |= code << (vbase + 2 * (c % 4));
-      };
-      if (CBK) {
-#pragma unroll
-        for (int e = 0; e < QC; ++e) {
-          bool r;
-          place(e, cb_code_fast(x[e], g, cb, r));
-          redo |= (uint32_t)r << e;
+          const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
+          short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
         }
-      } else if (short_row) {
+        // word and bit of value e: keys word c/4 (of key words (qq, 0..NWL-1)), bit
+        // 8((c/2)%2) + 4(c%2) + 2(u/2) + 16(u%2); values word 4(c/4) + u (column 4qq + u, word
+        // c/4), bit vbase + 2(c%4)
+        auto word_of = [&](int e) { return sel == 0 ? (e / 4) / 4 : 4 * ((e / 4) / 4) + e % 4; };
+        auto bit_of = [&](int e) {
+          const int c = e / 4, u = e % 4;
+          return sel == 0 ? 8 * ((c / 2) % 2) + 4 * (c % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * (c % 4);
+        };
+        uint32_t w[4 * NWL];
 #pragma unroll
-        for (int e = 0; e < QC; ++e) {
+        for (int k = 0; k < 4 * NWL; ++k) w[k] = 0;
+        uint32_t redo = 0;
+        if (CBK) {
+#pragma unroll
+          for (int e = 0; e < QC; ++e) {
+            bool r;
+            w[word_of(e)] |= cb_code_fast(x[e], g, cb, r) << bit_of(e);
+            redo |= (uint32_t)r << e;
+          }
+        } else if (short_row) {
+#pragma unroll
+          for (int e = 0; e < QC; ++e) {
 #pragma clang fp contract(off)
-          const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
-          const float rt = rintf(t);
-          redo |= (uint32_t)!(fabsf(t - rt) < 0.5f - 0x1p-14f) << e;
-          place(e, (uint32_t)rt);
-        }
-      } else {
+            const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
+            const float rt_ = rintf(t);
+            redo |= (uint32_t)!(fabsf(t - rt_) < 0.5f - 0x1p-14f) << e;
+            w[word_of(e)] |= (uint32_t)rt_ << bit_of(e);
+          }
+        } else {
 #pragma unroll
-        for (int e = 0; e < QC; ++e) {
-          bool r;
-          place(e, int2_code_estimate(x[e], g, r));
-          redo |= (uint32_t)r << e;
+          for (int e = 0; e < QC; ++e) {
+            bool r;
+            w[word_of(e)] |= int2_code_estimate(x[e], g, r) << bit_of(e);
+            redo |= (uint32_t)r << e;
+          }
         }
-      }
-      uint32_t* pw = stg.part[tid];
-      const int np = sel == 0 ? NPK : NPV;
-      if (live) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < np) pw[k] = part[k];
         // the rare codes the correctly rounded quotient decides
         while (redo) {
           const int e = __builtin_ctz(redo);
           redo &= redo - 1;
-          const float xv = xr[qi][16 * (e / 4) + 4 * qq + e % 4];
+          const float xv = xr[qb][qi][chan4(e / 4) + e % 4];
           const uint32_t code = CBK ? cb_code_exact(xv, g, cb) : quant_code_exact(xv, g, 3);
-          const int c = e / 4, u = e % 4;
-          const int k = sel == 0 ? (c % 2) + 2 * (c / 4) : 4 * (c / 4) + u;
-          const int sh = sel == 0 ? kbase + 8 * ((c / 2) % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * (c % 4);
-          pw[k] = (pw[k] & ~(3u << sh)) | (code << sh);
+          const int sh = bit_of(e);
+#pragma unroll
+          for (int k = 0; k < 4 * NWL; ++k)
+            if (k == word_of(e)) w[k] = (w[k] & ~(3u << sh)) | (code << sh);
         }
-        if (qq == 0) szs[qi] = g.s_bits | (g.z_bits << 16);
-      } else {
+        const int64_t page = pgs[qb][qi / kPage];
+        uint8_t* ph = page >= 0 ? page_head_mut(a.pool, page, kv, dm) : nullptr;
+        const int t = qi % kPage;
+        if (sel == 0) {
+          if (live && ph) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(ph + (size_t)(16 * qq + t) * 2 * CB);
+            if constexpr (NWL == 2) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+            } else {
+              dst[0] = w[0];
+            }
+          }
+        } else {
+          // rows past the history add nothing; the group's words are completed across its 4 rows
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < np) pw[k] = 0;   // rows past the history add nothing to value words
+          for (int k = 0; k < 4 * NWL; ++k) {
+            uint32_t v = live ? w[k] : 0u;
+            v |= dpp_row_ror_u<4>(v);
+            v |= dpp_row_ror_u<8>(v);
+            w[k] = v;
+          }
+          // the lane of row r stores column 4qq + r: words 4a + r (a < NWL)
+          const uint32_t v0 = r4 == 0 ? w[0] : (r4 == 1 ? w[1] : (r4 == 2 ? w[2] : w[3]));
+          if ((qi & ~3) < n && ph) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(ph + (size_t)(16 * (t / 4) + 4 * qq + r4) * 2 * CB + CB);
+            if constexpr (NWL == 2) {
+              const uint32_t v1 = r4 == 0 ? w[4] : (r4 == 1 ? w[5] : (r4 == 2 ? w[6] : w[7]));
+              *reinterpret_cast<uint2*>(dst) = make_uint2(v0, v1);
+            } else {
+              dst[0] = v0;
+            }
+          }
+        }
+        if (live && ph && qq == 0)
+          reinterpret_cast<uint32_t*>(ph + 4 * D * 2)[2 * t + sel] = g.s_bits | (g.z_bits << 16);
       }
+      __syncthreads();
     }
-    __syncthreads();
-    const int64_t* pgs = page_s + CH * ci / kPage;   // the chunk's pages
-    for (int i = tid; i < n; i += 256) {
-      const int64_t page = pgs[i / kPage];
-      if (page >= 0)
-        reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + 4 * D * 2)[2 * (i % kPage) + sel] = szs[i];
-    }
-    if (sel == 0) {
-      // key word (token i, g, a): partial g/2 + 2a of threads 2(g%2) and 2(g%2) + 1 of row i
-      for (int idx = tid; idx < n * 4 * NWL; idx += 256) {
-        const int i = idx / (4 * NWL), g = (idx / NWL) % 4, aw = idx % NWL;
-        const int64_t page = pgs[i / kPage];
-        if (page < 0) continue;
-        const int q0 = 2 * (g % 2), k = g / 2 + 2 * aw;
-        const uint32_t w = stg.part[4 * i + q0][k] | stg.part[4 * i + q0 + 1][k];
-        reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + (size_t)(16 * g + i % kPage) * 2 * CB)[aw] = w;
-      }
-    } else {
-      // value word (page j, group gg, column cv, a): partial 4a + cv%4 of thread cv/4 of its 4 rows
-      const int npg = (n + kPage - 1) / kPage;
-      for (int idx = tid; idx < npg * 64 * NWL; idx += 256) {
-        const int j = idx / (64 * NWL), r = idx % (64 * NWL);
-        const int gg = r / (16 * NWL), cv = (r / NWL) % 16, aw = r % NWL;
-        const int64_t page = pgs[j];
-        if (page < 0) continue;
-        const int i0 = kPage * j + 4 * gg, k = 4 * aw + cv % 4, q = cv / 4;
-        uint32_t w = 0;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) w |= stg.part[4 * (i0 + t4) + q][k];
-        reinterpret_cast<uint32_t*>(page_head_mut(a.pool, page, kv, dm) + (size_t)(16 * gg + cv) * 2 * CB + CB)[aw] = w;
-      }
-    }
-    __syncthreads();   // the staging rows of the next chunk overwrite the partial words
   }
 }
 
@@ -566,17 +601,32 @@ hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream) {
   if (hmax <= 0) return hipSuccess;
   const int runs = (hmax + kPrefillChunk * kPrefillChunks - 1) / (kPrefillChunk * kPrefillChunks);
   const dim3 grid(runs, dm.hkv, 2 * dm.batch);   // z: request x {K, V}
-  if (!dm.mixed) {   // INT2-only: whole pages per chunk, codes packed from registers
+  if (!dm.mixed) {
+    // INT2-only: one 8-wavefront workgroup per compute unit, each taking an equal run of chunks of
+    // its (request, kv-head, K or V) so that the launch fills the device in whole rounds
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    const int64_t hchunks = (hmax + kPrefillChunk - 1) / kPrefillChunk;
+    const int64_t groups = (int64_t)dm.hkv * 2 * dm.batch;
+    int64_t run = std::max<int64_t>(1, (hchunks * groups + cus - 1) / cus);
+    const int64_t per_group = (hchunks + run - 1) / run;
+    run = (hchunks + per_group - 1) / per_group;
+    const dim3 g2((unsigned)per_group, dm.hkv, 2 * dm.batch);
+    const int r = (int)run;
     if (a.codebook) {
       if (dm.d == 128)
-        hipLaunchKernelGGL((prefill_int2_kernel<128, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_int2_kernel<128, true>), g2, dim3(512), 0, stream, a, r);
       else
-        hipLaunchKernelGGL((prefill_int2_kernel<64, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_int2_kernel<64, true>), g2, dim3(512), 0, stream, a, r);
     } else {
       if (dm.d == 128)
-        hipLaunchKernelGGL((prefill_int2_kernel<128, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_int2_kernel<128, false>), g2, dim3(512), 0, stream, a, r);
       else
-        hipLaunchKernelGGL((prefill_int2_kernel<64, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_int2_kernel<64, false>), g2, dim3(512), 0, stream, a, r);
     }
   } else if (a.codebook) {
     if (dm.d == 128)
