@@ -163,6 +163,9 @@ __device__ __forceinline__ float dpp_row_shl_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x100 + N, 0xF, 0xF,
                                                                true));
 }
+// Word 3 of a raw (untyped, unswizzled) buffer descriptor: loads at or past its size return zeros
+// without touching memory.
+constexpr int kRawBufferFlags = 0x00020000;
 // Wave-uniform copy of a value (the compiler treats the result as scalar).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

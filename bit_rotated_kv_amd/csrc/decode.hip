@@ -918,9 +918,6 @@ struct QPage {
 template <int BITS, int D, int GQ>
 constexpr int kPageLoadPolicy = (D <= 128 && (GQ == 4 || GQ == 8)) ? 2 : 0;
 
-// word 3 of a raw (untyped, unswizzled) buffer descriptor: loads at or past its size return zeros
-constexpr int kRawBufferFlags = 0x00020000;
-
 template <int BITS, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t qpage_rsrc(uint64_t head, bool live) {
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(head), (short)0,

@@ -332,36 +332,41 @@ __device__ __forceinline__ void rotate_tile_pair(const RotSlice<D>& rs, const ui
   }
 }
 
+// Threads of the INT2 prefill: 4 rotating wavefronts, and 64 rows x 4 * (D / 64) quantising threads.
+template <int D>
+constexpr int kPrefillThreads = 256 + 64 * 4 * (D / 64);
+
 // The history of an INT2-only cache (every token takes consecutive INT2 slots, so a chunk of 64
 // positions owns 4 whole pages), with the rotation and code rule of prefill_hist_kernel. One
-// workgroup of 8 wavefronts per (run of `run` chunks, kv-head, request x {K, V}), one per compute
-// unit: wavefronts 0..3 rotate (matrix cores) and wavefronts 4..7 quantise and store, one chunk
-// apart, so the matrix cores and the vector units work at once. In iteration i the rotating
-// wavefronts stage chunk i+1's rows (loaded during iteration i-1) in LDS, issue chunk i+2's loads
-// and rotate chunk i; the quantising ones fetch chunk i's page ids and quantise and store chunk i-1.
-// Every LDS buffer passed between the two sides is double-buffered, so one workgroup barrier per
-// iteration orders them all.
-// Four quantising threads per row (token). Each assembles whole page-head words in registers and
-// stores them itself:
+// workgroup per compute unit and (run of `run` chunks, kv-head, request x {K, V}): wavefronts 0..3
+// rotate (matrix cores) and issue every load, the other wavefronts (8 at d = 128, two per SIMD; 4 at
+// d = 64) quantise and store, one chunk apart, so the matrix cores and the vector units work at
+// once. In iteration i the rotating wavefronts publish chunk i's page ids, stage chunk i+1's rows
+// (loaded during iteration i-1) in LDS, issue chunk i+2's row loads and chunk i+1's page-id loads,
+// and rotate chunk i; the quantising ones quantise and store chunk i-1. A load is thus never waited
+// on behind the stores (one counter covers both), and every LDS buffer passed between the sides is
+// double-buffered, so one workgroup barrier per iteration orders them all (each side runs its own
+// loop with as many barriers, so neither side's registers stay live in the other's).
+// A quantising thread (row, a, q), a < NWL = D/64 words per lane part, q < 4, takes 16 channels and
+// assembles whole page-head words in registers:
 //  * keys: key word (g, a) of a token holds channels 64a + 32k2 + 8g + j (k2 < 2, j < 8) at bit
-//    8k2 + 2(j/2) + 16(j%2), so thread qq = g takes those channels and stores words (g, 0..) whole;
+//    8k2 + 2(j/2) + 16(j%2): thread q takes word (q, a) and stores it;
 //  * values: value word (column cv, a) of a group of 4 tokens holds channels 64a + 16n4 + cv
-//    (n4 < 4) of tokens 2m + hf at bit 2n4 + 8m + 16hf, so thread qq takes channels 16c + 4qq + u
-//    and places its row's codes of columns 4qq + u; the four rows of a group sit 4 lanes apart in a
-//    DPP row, where two rotate-and-OR steps complete every word in every lane, and the lane of row r
-//    stores column 4qq + r.
-// The float4 reads of the rotated rows are conflict-free (rows pitched 16 banks apart).
+//    (n4 < 4) of tokens 2m + hf at bit 2n4 + 8m + 16hf: thread q places its row's codes of columns
+//    4q + u (u < 4) of word a; the 4 rows of a group are the 4 lanes of a quad, where two DPP swaps
+//    and ORs complete the words, and the lane of row r stores column 4q + r.
+// Lane l of a quantising wavefront: r = l % 4 (row within its group), q = (l / 4) % 4, s = l / 16
+// (a = s % NWL, row group s / NWL).
 template <int D, bool CBK>
-__global__ __launch_bounds__(512, 1) void prefill_int2_kernel(CacheWriteArgs a, int run) {
+__global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(CacheWriteArgs a, int run) {
   constexpr int CH = kPrefillChunk;
   constexpr int XS = D + 8;     // bf16 row pitch (16-byte pad)
   constexpr int RS = D + 16;    // fp32 row pitch: consecutive rows 16 banks apart
-  constexpr int QC = D / 4;     // channels of a quantising thread
-  constexpr int NC = D / 16;    // its float4 groups
   constexpr int SL = RotSlice<D>::SLICES;
-  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per rotating thread
   constexpr int CB = D * 2 / 32;         // bytes of a lane's key (or value) part
   constexpr int NWL = CB / 4;            // its words
+  constexpr int RPW = 16 / NWL;          // rows per quantising wavefront
+  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per rotating thread
   constexpr int CP = CH / kPage;         // pages of a chunk
   static_assert(NWL == 1 || NWL == 2, "d = 64 or 128");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][CH][XS];
@@ -369,197 +374,198 @@ __global__ __launch_bounds__(512, 1) void prefill_int2_kernel(CacheWriteArgs a, 
   __shared__ int64_t pgs[2][CP];
   const Dims& dm = a.dm;
   const int kv = blockIdx.y, b = blockIdx.z / 2, sel = blockIdx.z % 2;
-  const int tid = threadIdx.x;
-  const bool rot = tid < 256;                 // wavefronts 0..3 rotate
-  const int rt = tid % 256, wave = rt / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
   int T = a.seq_len[b];
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
   const int hist = T - dm.sink - dm.recent;
   const int chunk0 = run * blockIdx.x;
   if (CH * chunk0 >= hist) return;   // the whole workgroup
   const int nchunks = min(run, (hist - CH * chunk0 + CH - 1) / CH);
-  const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
-  auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
-    const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
+  if (tid < 256) {
+    // rotating wavefronts: they also issue every load of the kernel (rows, page ids) one iteration
+    // ahead, so no load waits behind the quantising wavefronts' stores
+    const int wave = tid / kWave;
+    const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
+    // a chunk's rows through a raw buffer descriptor over its n rows: the pieces of rows at or past n
+    // read as zeros, with no branch and no register cleared ahead of the load
+    auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
+      const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(src + (size_t)p0 * D), (short)0, n * D * 2, kRawBufferFlags);
 #pragma unroll
-    for (int e = 0; e < XW; ++e) {
-      const int idx = rt + 256 * e, row = idx / (D / 8), c8 = idx % (D / 8);
-      w[e] = u32x4_t{0, 0, 0, 0};
-      if (row < n) w[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(p0 + row) * D + 8 * c8);
-    }
-  };
-  auto stage_rows = [&](int buf, const u32x4_t (&w)[XW]) {
+      for (int e = 0; e < XW; ++e) w[e] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * e), 0, 0);
+    };
+    auto stage_rows = [&](int buf, const u32x4_t (&w)[XW]) {
 #pragma unroll
-    for (int e = 0; e < XW; ++e) {
-      const int idx = rt + 256 * e;
-      *reinterpret_cast<u32x4_t*>(&xs[buf][idx / (D / 8)][8 * (idx % (D / 8))]) = w[e];
-    }
-  };
-  const int ct = tid - 256;            // quantising thread (tid >= 256)
-  auto fetch_pages = [&](int chunk, int buf) {   // page ids of a chunk (threads ct < CP)
-    const int pi = CP * chunk + ct;
-    const int64_t page = pi < dm.pt_stride ? (int64_t)a.pt2[(size_t)b * dm.pt_stride + pi] : -1;
-    pgs[buf][ct] = page_ok(page, 2, dm) ? page : -1;
-  };
-  if (rot) {   // rotating wavefronts
+      for (int e = 0; e < XW; ++e) {
+        const int idx = tid + 256 * e;
+        *reinterpret_cast<u32x4_t*>(&xs[buf][idx / (D / 8)][8 * (idx % (D / 8))]) = w[e];
+      }
+    };
+    // page id of page tid % CP of a chunk through a raw buffer descriptor over the request's page
+    // table (a page past it reads as 0 and is dropped when published), kept as loaded until it is
+    // published an iteration later, so the load is not waited on at once
+    const __amdgpu_buffer_rsrc_t ptr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.pt2 + (size_t)b * dm.pt_stride), (short)0, 4 * dm.pt_stride, kRawBufferFlags);
+    auto load_page = [&](int chunk) -> int32_t {
+      return __builtin_amdgcn_raw_buffer_load_b32(ptr, 4 * (CP * chunk + tid % CP), 0, 0);
+    };
     RotSlice<D> rs;
     if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
     u32x4_t xw[XW];
     load_rows(chunk0, xw);
     stage_rows(0, xw);
+    int32_t pv = load_page(chunk0);
     if (nchunks > 1) load_rows(chunk0 + 1, xw);
     __syncthreads();
     for (int i = 0; i < nchunks + 1; ++i) {
-      if (i + 1 < nchunks) stage_rows((i + 1) % 2, xw);   // loaded during the previous iteration
-      if (i + 2 < nchunks) load_rows(chunk0 + i + 2, xw);
-      if (i < nchunks && wave < SL) {
-        const int n = min(CH, hist - CH * (chunk0 + i));
-        float16v_t acc0, acc1;
-        rotate_tile_pair<D>(rs, &xs[i % 2][0][0], XS, n, lane, acc0, acc1);
+      if (i < nchunks) {
+        // chunk i's page ids (read by the quantising wavefronts in iteration i+1)
+        if (tid < CP)
+          pgs[i % 2][tid] = CP * (chunk0 + i) + tid < dm.pt_stride && page_ok((int64_t)pv, 2, dm) ? (int64_t)pv : -1;
+        if (i + 1 < nchunks) {
+          stage_rows((i + 1) % 2, xw);   // loaded during the previous iteration
+          pv = load_page(chunk0 + i + 1);
+        }
+        if (i + 2 < nchunks) load_rows(chunk0 + i + 2, xw);
+        if (wave < SL) {
+          const int n = min(CH, hist - CH * (chunk0 + i));
+          float16v_t acc0, acc1;
+          rotate_tile_pair<D>(rs, &xs[i % 2][0][0], XS, n, lane, acc0, acc1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = 8 * (j / 4) + 4 * (lane / 32) + j % 4, col = 32 * wave + lane % 32;
-          xr[i % 2][r][col] = acc0[j];
-          xr[i % 2][32 + r][col] = acc1[j];
+          for (int j = 0; j < 16; ++j) {
+            const int r = 8 * (j / 4) + 4 * (lane / 32) + j % 4, col = 32 * wave + lane % 32;
+            xr[i % 2][r][col] = acc0[j];
+            xr[i % 2][32 + r][col] = acc1[j];
+          }
         }
       }
       __syncthreads();
     }
-  } else {     // quantising wavefronts: as many barriers, in a loop of their own (so neither side's
-               // registers stay live in the other's)
-    const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
-    const float clip = sel ? a.clip_v : a.clip_k;
-    const int qi = ct / 4, qq = ct % 4;
-    const int r4 = qi % 4;                            // the row's token within its group of 4
-    const int vbase = 8 * (r4 / 2) + 16 * (r4 % 2);   // value words: bit 8m + 16hf of the row's token
+    return;
+  }
+  // quantising wavefronts: stores only
+  const int ct = tid - 256;
+  const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
+  const float clip = sel ? a.clip_v : a.clip_k;
+  const int r4 = lane % 4, q = (lane / 4) % 4, s4 = lane / 16;
+  const int wa = s4 % NWL;                                   // word a of the thread
+  const int row = RPW * (ct / kWave) + 4 * (s4 / NWL) + r4;  // its row of the chunk
+  const int vbase = 8 * (r4 / 2) + 16 * (r4 % 2);            // value words: bit 8m + 16hf of the row's token
+  // channel of the thread's value e = 4c + u: keys 64a + 32(c/2) + 8q + 4(c%2) + u, values
+  // 64a + 16c + 4q + u
+  auto chan4 = [&](int c) { return sel == 0 ? 64 * wa + 32 * (c / 2) + 8 * q + 4 * (c % 2) : 64 * wa + 16 * c + 4 * q; };
+  // bit of value e in its word: keys 8(c/2) + 4(c%2) + 2(u/2) + 16(u%2) (one word), values
+  // vbase + 2c in word u (column 4q + u)
+  auto bit_of = [&](int e) {
+    const int c = e / 4, u = e % 4;
+    return sel == 0 ? 8 * (c / 2) + 4 * (c % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * c;
+  };
+  __syncthreads();
+  for (int i = 0; i < nchunks + 1; ++i) {
+    if (i >= 1) {
+      // quantise and store chunk i-1 from the rotated rows of its buffer
+      const int chunk = chunk0 + i - 1, qb = (i - 1) % 2;
+      const int n = min(CH, hist - CH * chunk);
+      const bool live = row < n;
+      float x[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(&xr[qb][row][chan4(c)]);
+        x[4 * c] = v.x;
+        x[4 * c + 1] = v.y;
+        x[4 * c + 2] = v.z;
+        x[4 * c + 3] = v.w;
+      }
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+      }
+      // the row's threads: lanes 4q + r4 of the DPP row (q < 4), and for two words the same lanes
+      // of the DPP row 16 lanes away
+      mn = fminf(mn, dpp_row_ror<4>(mn));
+      mx = fmaxf(mx, dpp_row_ror<4>(mx));
+      mn = fminf(mn, dpp_row_ror<8>(mn));
+      mx = fmaxf(mx, dpp_row_ror<8>(mx));
+      if constexpr (NWL == 2) {
+        mn = fminf(mn, __shfl_xor(mn, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      }
+      const QuantGrid g = make_grid(mn, mx, clip, 3);
+      // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
+      // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone
+      // in x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny
+      // scale, a zero point far off the range) take int2_code_estimate.
+      bool short_row = false;
+      if (!CBK) {
+#pragma clang fp contract(off)
+        const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
+        short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
+      }
+      uint32_t w[4];   // keys: w[0] only; values: column 4q + u in w[u]
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = 0;
+      auto word_of = [&](int e) { return sel == 0 ? 0 : e % 4; };
+      uint32_t redo = 0;
+      if (CBK) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          bool r;
+          w[word_of(e)] |= cb_code_fast(x[e], g, cb, r) << bit_of(e);
+          redo |= (uint32_t)r << e;
+        }
+      } else if (short_row) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+#pragma clang fp contract(off)
+          const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
+          const float rt_ = rintf(t);
+          redo |= (uint32_t)!(fabsf(t - rt_) < 0.5f - 0x1p-14f) << e;
+          w[word_of(e)] |= (uint32_t)rt_ << bit_of(e);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          bool r;
+          w[word_of(e)] |= int2_code_estimate(x[e], g, r) << bit_of(e);
+          redo |= (uint32_t)r << e;
+        }
+      }
+      // the rare codes the correctly rounded quotient decides
+      while (redo) {
+        const int e = __builtin_ctz(redo);
+        redo &= redo - 1;
+        const float xv = xr[qb][row][chan4(e / 4) + e % 4];
+        const uint32_t code = CBK ? cb_code_exact(xv, g, cb) : quant_code_exact(xv, g, 3);
+        const int sh = bit_of(e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k == word_of(e)) w[k] = (w[k] & ~(3u << sh)) | (code << sh);
+      }
+      const int64_t page = pgs[qb][row / kPage];
+      uint8_t* ph = page >= 0 ? page_head_mut(a.pool, page, kv, dm) : nullptr;
+      const int t = row % kPage;
+      if (sel == 0) {
+        if (live && ph) reinterpret_cast<uint32_t*>(ph + (size_t)(16 * q + t) * 2 * CB)[wa] = w[0];
+      } else {
+        // rows past the history add nothing; the quad's 4 rows complete the group's words
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t v = live ? w[k] : 0u;
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad swap 1,0,3,2
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // quad swap 2,3,0,1
+          w[k] = v;
+        }
+        const uint32_t v = r4 == 0 ? w[0] : (r4 == 1 ? w[1] : (r4 == 2 ? w[2] : w[3]));
+        if ((row & ~3) < n && ph)
+          reinterpret_cast<uint32_t*>(ph + (size_t)(16 * (t / 4) + 4 * q + r4) * 2 * CB + CB)[wa] = v;
+      }
+      if (live && ph && wa == 0 && q == 0)
+        reinterpret_cast<uint32_t*>(ph + 4 * D * 2)[2 * t + sel] = g.s_bits | (g.z_bits << 16);
+    }
     __syncthreads();
-    for (int i = 0; i < nchunks + 1; ++i) {
-      // chunk i's page ids, read by iteration i+1 (this one reads buffer (i-1) % 2)
-      if (i < nchunks && ct < CP) fetch_pages(chunk0 + i, i % 2);
-      if (i >= 1) {
-        // quantise and store chunk i-1 from the rotated rows of its buffer
-        const int chunk = chunk0 + i - 1, qb = (i - 1) % 2;
-        const int n = min(CH, hist - CH * chunk);
-        const bool live = qi < n;
-        // channel of the thread's value e = 4c + u: keys 64(c/4) + 32((c/2)%2) + 8qq + 4(c%2) + u,
-        // values 16c + 4qq + u
-        auto chan4 = [&](int c) { return sel == 0 ? 64 * (c / 4) + 32 * ((c / 2) % 2) + 8 * qq + 4 * (c % 2)
-                                                  : 16 * c + 4 * qq; };
-        float x[QC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float4 v = *reinterpret_cast<const float4*>(&xr[qb][qi][chan4(c)]);
-          x[4 * c] = v.x;
-          x[4 * c + 1] = v.y;
-          x[4 * c + 2] = v.z;
-          x[4 * c + 3] = v.w;
-        }
-        float mn = x[0], mx = x[0];
-#pragma unroll
-        for (int e = 1; e < QC; ++e) {
-          mn = fminf(mn, x[e]);
-          mx = fmaxf(mx, x[e]);
-        }
-        mn = fminf(mn, dpp_f<0xB1>(mn));
-        mx = fmaxf(mx, dpp_f<0xB1>(mx));
-        mn = fminf(mn, dpp_f<0x4E>(mn));
-        mx = fmaxf(mx, dpp_f<0x4E>(mx));
-        const QuantGrid g = make_grid(mn, mx, clip, 3);
-        // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
-        // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone
-        // in x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny
-        // scale, a zero point far off the range) take int2_code_estimate.
-        bool short_row = false;
-        if (!CBK) {
-#pragma clang fp contract(off)
-          const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
-          short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
-        }
-        // word and bit of value e: keys word c/4 (of key words (qq, 0..NWL-1)), bit
-        // 8((c/2)%2) + 4(c%2) + 2(u/2) + 16(u%2); values word 4(c/4) + u (column 4qq + u, word
-        // c/4), bit vbase + 2(c%4)
-        auto word_of = [&](int e) { return sel == 0 ? (e / 4) / 4 : 4 * ((e / 4) / 4) + e % 4; };
-        auto bit_of = [&](int e) {
-          const int c = e / 4, u = e % 4;
-          return sel == 0 ? 8 * ((c / 2) % 2) + 4 * (c % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * (c % 4);
-        };
-        uint32_t w[4 * NWL];
-#pragma unroll
-        for (int k = 0; k < 4 * NWL; ++k) w[k] = 0;
-        uint32_t redo = 0;
-        if (CBK) {
-#pragma unroll
-          for (int e = 0; e < QC; ++e) {
-            bool r;
-            w[word_of(e)] |= cb_code_fast(x[e], g, cb, r) << bit_of(e);
-            redo |= (uint32_t)r << e;
-          }
-        } else if (short_row) {
-#pragma unroll
-          for (int e = 0; e < QC; ++e) {
-#pragma clang fp contract(off)
-            const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
-            const float rt_ = rintf(t);
-            redo |= (uint32_t)!(fabsf(t - rt_) < 0.5f - 0x1p-14f) << e;
-            w[word_of(e)] |= (uint32_t)rt_ << bit_of(e);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < QC; ++e) {
-            bool r;
-            w[word_of(e)] |= int2_code_estimate(x[e], g, r) << bit_of(e);
-            redo |= (uint32_t)r << e;
-          }
-        }
-        // the rare codes the correctly rounded quotient decides
-        while (redo) {
-          const int e = __builtin_ctz(redo);
-          redo &= redo - 1;
-          const float xv = xr[qb][qi][chan4(e / 4) + e % 4];
-          const uint32_t code = CBK ? cb_code_exact(xv, g, cb) : quant_code_exact(xv, g, 3);
-          const int sh = bit_of(e);
-#pragma unroll
-          for (int k = 0; k < 4 * NWL; ++k)
-            if (k == word_of(e)) w[k] = (w[k] & ~(3u << sh)) | (code << sh);
-        }
-        const int64_t page = pgs[qb][qi / kPage];
-        uint8_t* ph = page >= 0 ? page_head_mut(a.pool, page, kv, dm) : nullptr;
-        const int t = qi % kPage;
-        if (sel == 0) {
-          if (live && ph) {
-            uint32_t* dst = reinterpret_cast<uint32_t*>(ph + (size_t)(16 * qq + t) * 2 * CB);
-            if constexpr (NWL == 2) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-            } else {
-              dst[0] = w[0];
-            }
-          }
-        } else {
-          // rows past the history add nothing; the group's words are completed across its 4 rows
-#pragma unroll
-          for (int k = 0; k < 4 * NWL; ++k) {
-            uint32_t v = live ? w[k] : 0u;
-            v |= dpp_row_ror_u<4>(v);
-            v |= dpp_row_ror_u<8>(v);
-            w[k] = v;
-          }
-          // the lane of row r stores column 4qq + r: words 4a + r (a < NWL)
-          const uint32_t v0 = r4 == 0 ? w[0] : (r4 == 1 ? w[1] : (r4 == 2 ? w[2] : w[3]));
-          if ((qi & ~3) < n && ph) {
-            uint32_t* dst = reinterpret_cast<uint32_t*>(ph + (size_t)(16 * (t / 4) + 4 * qq + r4) * 2 * CB + CB);
-            if constexpr (NWL == 2) {
-              const uint32_t v1 = r4 == 0 ? w[4] : (r4 == 1 ? w[5] : (r4 == 2 ? w[6] : w[7]));
-              *reinterpret_cast<uint2*>(dst) = make_uint2(v0, v1);
-            } else {
-              dst[0] = v0;
-            }
-          }
-        }
-        if (live && ph && qq == 0)
-          reinterpret_cast<uint32_t*>(ph + 4 * D * 2)[2 * t + sel] = g.s_bits | (g.z_bits << 16);
-      }
-      __syncthreads();
-    }
   }
 }
 
@@ -617,16 +623,17 @@ hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream) {
     run = (hchunks + per_group - 1) / per_group;
     const dim3 g2((unsigned)per_group, dm.hkv, 2 * dm.batch);
     const int r = (int)run;
+    const dim3 b128(kPrefillThreads<128>), b64(kPrefillThreads<64>);
     if (a.codebook) {
       if (dm.d == 128)
-        hipLaunchKernelGGL((prefill_int2_kernel<128, true>), g2, dim3(512), 0, stream, a, r);
+        hipLaunchKernelGGL((prefill_int2_kernel<128, true>), g2, b128, 0, stream, a, r);
       else
-        hipLaunchKernelGGL((prefill_int2_kernel<64, true>), g2, dim3(512), 0, stream, a, r);
+        hipLaunchKernelGGL((prefill_int2_kernel<64, true>), g2, b64, 0, stream, a, r);
     } else {
       if (dm.d == 128)
-        hipLaunchKernelGGL((prefill_int2_kernel<128, false>), g2, dim3(512), 0, stream, a, r);
+        hipLaunchKernelGGL((prefill_int2_kernel<128, false>), g2, b128, 0, stream, a, r);
       else
-        hipLaunchKernelGGL((prefill_int2_kernel<64, false>), g2, dim3(512), 0, stream, a, r);
+        hipLaunchKernelGGL((prefill_int2_kernel<64, false>), g2, b64, 0, stream, a, r);
     }
   } else if (a.codebook) {
     if (dm.d == 128)
