@@ -686,12 +686,17 @@ def summarize_sq(d):
     return "\n".join(out) + "\n"
 
 
+def _is_split(kernel_name: str) -> bool:
+    """The decode split kernels (the general split, and the one-request interleaved launch)."""
+    return "split_kernel" in kernel_name or "split_b1_kernel" in kernel_name
+
+
 def summarize_traffic(d):
     """HBM bytes per bs1 split launch from FETCH_SIZE / WRITE_SIZE, scaled by the same counters' reading
     of a plain 256 MiB device copy in the same run."""
     def means(sub, name):
         rows = [r for r in _csv_rows(os.path.join(d, sub), "counter_collection.csv") if r["Counter_Name"] == name]
-        split = [float(r["Counter_Value"]) for r in rows if "split_kernel" in r["Kernel_Name"]]
+        split = [float(r["Counter_Value"]) for r in rows if _is_split(r["Kernel_Name"])]
         copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
         return float(np.mean(split)), len(split), copy
     fk, nf, cf = means("fetch", "FETCH_SIZE")
@@ -998,8 +1003,8 @@ def main():
         "split_le_step": bool(split_ms <= ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "split_kernel<128,4,false,false> (BF16 window + INT2 history split-K + step workgroups, "
-                               "one launch)",
+                     "kernel": "split_b1_kernel<128,4,false,16> (one request: step and BF16 window on one "
+                               "workgroup per kv-head, INT2 history pages interleaved over the others; one launch)",
                      "bytes_per_launch": int2 + bf16},
         "setup_s": round(setup_s, 1),
     }

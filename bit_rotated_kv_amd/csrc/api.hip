@@ -45,6 +45,9 @@ int window_cost(int nw) { return nw >= kSplitWavesWide ? OSCAR_WIN_COST_WIDE : O
 // Smallest unit the plan aims for (cost of 16 INT2 pages): below it the per-workgroup overhead (query
 // prologue, workgroup merge, one more partial to merge) outweighs the spread.
 constexpr int kMinUnitCost = 16;
+// Interleaved one-request plan: its unit 0 runs the step and window (together ~7 us), so the
+// history units should stream at least this many pages each for it to pay off.
+constexpr int kInterleaveMinPages = 64;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -427,6 +430,12 @@ static oscar_status_t build_decode(const oscar_layout_t* L, int32_t batch, int32
   a.ws.nw = p.nw;
   a.ws.step_cost = p.step_cost;
   a.ws.win_cost = p.win_cost;
+  // One request in wide workgroups over an INT2-only cache: history pages interleaved over units
+  // 1 .. n-1 (no device-side plan, so page ids load before the length is read), when the history
+  // at max_seq_len gives those units at least kInterleaveMinPages pages each.
+  const int64_t hp_max = (std::max(0, hist_max) + kPage - 1) / kPage;
+  a.ws.interleave = batch == 1 && p.nw == kSplitWavesWide && !L->mixed && p.units_per_kv >= 2 &&
+                    hp_max >= (int64_t)kInterleaveMinPages * (p.units_per_kv - 1);
   a.step = step;
   *args = a;
   return OSCAR_OK;

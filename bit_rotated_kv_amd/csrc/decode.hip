@@ -1455,6 +1455,108 @@ __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, flo
   workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl);
 }
 
+// History segment of a one-request launch with interleaved pages (INT2-only cache, wide
+// workgroups): history page p belongs to history unit p mod nunits and, within it, to wavefront
+// (p / nunits) mod NW, so wavefront w of unit `unit` takes pages unit + nunits * (w + NW * r),
+// r = 0, 1, ... Which pages a wavefront may take does not depend on the request's length, so its
+// page ids, the rotation rows and the queries all load at once, before the length is known; the
+// length only bounds r. Units differ by at most one page, and so do the wavefronts of a unit.
+// LUT as in hist_seg.
+template <int D, int GQ, int NW, bool LUT = false>
+__device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, float* po, float* pl,
+                            float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8], HistQueryLds<D, GQ, NW>& qlds) {
+  constexpr int BITS = 2, NT = NW * kWave, NB = OSCAR_WIDE_RING;
+  static_assert(NB % 2 == 0 && NB >= 4 && kIdChunk % NB == 0, "the ring holds whole page pairs");
+  static_assert(kIdChunk + NB - 3 < kWave, "every prefetch of a trip finds its id in the current chunk");
+  const Dims& dm = a.dm;
+  const int tid = threadIdx.x, lane = tid % kWave, c = lane % 16;
+  const int wave = uniform(tid / kWave);
+  const int base = unit + nunits * wave, stride = nunits * NW;
+  // Page ids of list entries cb .. cb + 63 of this wavefront (lane i: entry cb + i); entries past the
+  // page table's row read as 0 and are never used (the length bounds the list below).
+  const __amdgpu_buffer_rsrc_t ptr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.pt2), (short)0, (int)(4 * max(dm.pt_stride, 0)), kRawBufferFlags);
+  auto chunk = [&](int cb) -> int {
+    const int64_t pg = (int64_t)base + (int64_t)stride * (cb + lane);
+    const int off = pg < dm.pt_stride ? (int)pg : dm.pt_stride;
+    return __builtin_amdgcn_raw_buffer_load_b32(ptr, 4 * off, 0, 0);
+  };
+  int cur = chunk(0);
+  int nxt = chunk(kIdChunk);
+  QRotRows<D, NT> rr;
+  QueryIn<D, GQ, NT> qin;
+  rr.load(a.rot_k + (size_t)kv * D * D, tid);
+  qin.load(a.q + (size_t)kv * GQ * D, tid);
+  const HistCounts hc = hist_counts(a, 0);
+  const int ntok = uniform(hc.n2);
+  const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
+  const int R = uniform(npages > base ? (npages - base + stride - 1) / stride : 0);   // this wavefront's pages
+  OSCAR_TL_SPLIT(1);
+  OSCAR_TL_SPLIT_VALUE(6, 4u | ((uint32_t)(R * NW) << 8));
+  OSCAR_TL_SPLIT(2);
+
+  const uint32_t psel = c < 4 ? 0x05040100u : (c < 8 ? 0x03020706u : 0x0C0C0C0Cu);
+  WaveState<D, GQ> st;
+  st.init();
+  if (dm.pool_pages > 0) {
+    int cbase = 0;
+    const int64_t head = qpage_head_bytes(D, BITS);
+    const int id_lim = (int)min<int64_t>(dm.pool_pages, INT32_MAX);
+    const uint64_t region = (uint64_t)a.pool;
+    auto load = [&](QPage<BITS, D, GQ>& pr, int r) -> bool {
+      const int li = r - cbase;
+      const int id = page_index(__builtin_amdgcn_readlane(cur, min(li, kWave - 1)), 0, id_lim);
+      const bool live = r < R && id >= 0;
+      const uint64_t ad = region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head);
+      load_qpage<BITS, D, GQ>(pr, ad, live, lane);
+      return live;
+    };
+    QPage<BITS, D, GQ> buf[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int k = 0; k < NB - 2; ++k) ok[k] = load(buf[k], k);
+    __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
+    half8_t bq[D / 32];
+    float uh, ul, esc;
+    hist_query_operands<BITS, D, GQ, NW, LUT>(rr, qin, qlds, a.scale_log2e, bq, uh, ul, esc);
+    OSCAR_TL_SPLIT(3);
+    const float uq = uh + ul;
+    const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
+    const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
+    for (int r = 0; r < R; r += NB) {
+      progress_priority(r, R);
+      if (r - cbase >= kIdChunk) {   // the next chunk of page ids becomes the current one
+        cur = nxt;
+        cbase += kIdChunk;
+        nxt = chunk(cbase + kIdChunk);
+      }
+#pragma unroll
+      for (int k = 0; k < NB; k += 2) {
+        ok[(k + NB - 2) % NB] = load(buf[(k + NB - 2) % NB], r + k + NB - 2);
+        ok[(k + NB - 1) % NB] = load(buf[(k + NB - 1) % NB], r + k + NB - 1);
+        if (r + k < R) {
+          const float4_t acc0 = qk_page<BITS, D, GQ, LUT>(buf[k], bq, cbk);
+          const float4_t acc1 = qk_page<BITS, D, GQ, LUT>(buf[k + 1], bq, cbk);
+          const int t0 = (base + stride * (r + k)) * kPage;   // first token of each page
+          const int t1 = t0 + stride * kPage;
+          if (ok[k] || ok[k + 1]) {
+            process_qpair<BITS, D, GQ, LUT>(st, buf[k], buf[k + 1], acc0, acc1, uq, esc, psel,
+                                            ok[k] ? ntok - t0 : 0, ok[k + 1] ? ntok - t1 : 0, lane, cbv);
+          }
+          if ((!ok[k] || (!ok[k + 1] && r + k + 1 < R)) && lane == 0) atomicOr(a.ws.flags, 1u);
+        }
+      }
+    }
+  } else if (lane == 0 && R > 0) {
+    atomicOr(a.ws.flags, 1u);
+  }
+  OSCAR_TL_SPLIT(4);
+  // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
+  __syncthreads();
+  OSCAR_TL_SPLIT(8);
+  workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl);
+}
+
 // LDS of the segments (one at a time per workgroup); 16-byte aligned for the vector reads of the
 // query operands
 template <int D, int GQ, int NW>
@@ -1531,6 +1633,43 @@ __global__ __launch_bounds__(NW * kWave, (kSplitMinBlocks<GQ, MIXED, NW>)) void 
         hist_seg<4, D, GQ, NW>(a, ru.b, kv, sg.p40, sg.p41, po + 2 * GQ * D, pl + 2 * GQ, scr.o, st_lds, scr.hist,
                                rr, qin, false);
     }
+  }
+  OSCAR_TL_SPLIT(5);
+}
+
+// The split launch of one request over an INT2-only cache in wide workgroups, with interleaved
+// history pages: unit 0 of each kv-head runs the step and the window; units 1 .. n-1 share the
+// history page by page (hist_seg_b1), so none of them waits for a work plan.
+template <int D, int GQ, bool CB, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void split_b1_kernel(DecodeArgs a, CacheWriteArgs cw) {
+  __shared__ float st_lds[NW][3][8];
+  __shared__ SplitScratch<D, GQ, NW> scr;
+  OSCAR_TL_SPLIT(0);
+#ifdef OSCAR_TIMELINE
+  OSCAR_TL_SPLIT_VALUE(7, timeline_placement());
+#endif
+  const int hkv = a.dm.hkv;
+  const int g = blockIdx.x, kv = g % hkv, tid = threadIdx.x, u = g / hkv;
+  float* po = a.ws.part_o + (size_t)g * 3 * GQ * D;
+  float* pl = a.ws.part_lse + (size_t)g * 3 * GQ;
+  if (u == 0) {
+    if (tid < 2 * GQ) pl[GQ + tid] = kNegInf;   // no history partials
+    if (kv == 0 && tid == 0) {
+      a.ws.req_units[0] = 0;
+      a.ws.req_units[1] = a.ws.units_per_kv;
+    }
+    OSCAR_TL_SPLIT(1);
+    OSCAR_TL_SPLIT_VALUE(6, (a.step ? 1u : 0u) | 2u);
+    if (a.step) {
+      step_seg<D, GQ, NW>(a, cw, 0, kv, scr.step);
+      __syncthreads();
+    }
+    window_seg<D, GQ, NW>(a, 0, kv, 0, 1, po, pl, scr.o, st_lds);
+    OSCAR_TL_SPLIT(2);
+  } else {
+    if (tid < 2 * GQ) pl[tid < GQ ? tid : GQ + tid] = kNegInf;   // no window or INT4 partials
+    hist_seg_b1<D, GQ, NW, CB>(a, kv, u - 1, a.ws.units_per_kv - 1, po + GQ * D, pl + GQ, scr.o, st_lds,
+                               scr.hist);
   }
   OSCAR_TL_SPLIT(5);
 }
@@ -1924,11 +2063,17 @@ static const void* split_symbol() {
   return reinterpret_cast<const void*>(&split_kernel<D, GQ, CB, MIXED, NW>);
 }
 
-// The split kernel instance of a launch (wide workgroups exist for GQA width 4 only).
+// The split kernel instance of a launch (wide workgroups exist for GQA width 4 only; `il`: the
+// interleaved one-request launch, INT2-only).
 template <int D, int GQ>
-static const void* split_function(bool cb, bool mixed, int nw) {
+static const void* split_function(bool cb, bool mixed, int nw, bool il = false) {
   if constexpr (GQ == 4) {
     if (nw == kSplitWavesWide) {
+      if (il) {
+        if (mixed) return nullptr;
+        return cb ? reinterpret_cast<const void*>(&split_b1_kernel<D, GQ, true, kSplitWavesWide>)
+                  : reinterpret_cast<const void*>(&split_b1_kernel<D, GQ, false, kSplitWavesWide>);
+      }
       if (mixed) return cb ? split_symbol<D, GQ, true, true, kSplitWavesWide>() : split_symbol<D, GQ, false, true, kSplitWavesWide>();
       return cb ? split_symbol<D, GQ, true, false, kSplitWavesWide>() : split_symbol<D, GQ, false, false, kSplitWavesWide>();
     }
@@ -1960,7 +2105,7 @@ int split_workgroups_per_cu(int d, int gq, bool cb, bool mixed, int nw) {
 template <int D, int GQ>
 static hipError_t launch_decode_t(const DecodeArgs& a, const CacheWriteArgs& cw, hipStream_t stream) {
   const Dims& dm = a.dm;
-  const void* f = split_function<D, GQ>(a.codebook != nullptr, dm.mixed != 0, a.ws.nw);
+  const void* f = split_function<D, GQ>(a.codebook != nullptr, dm.mixed != 0, a.ws.nw, a.ws.interleave != 0);
   if (!f) return hipErrorInvalidValue;
   // the timing variant records event 0, then brackets the split kernel with the dispatch's own
   // start and stop stamps (events 1 and 2), so its interval is the kernel's execution time

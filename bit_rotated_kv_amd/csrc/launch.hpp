@@ -38,6 +38,9 @@ struct DecodeWs {
   int nw;                  // wavefronts per split workgroup
   int step_cost;           // cost of the step segment (0 outside a fused step)
   int win_cost;            // cost of the BF16 window block
+  int interleave;          // one request, INT2-only, wide workgroups: unit 0 of each kv-head runs the
+                           // step and the window, units 1 .. units_per_kv-1 take the history pages
+                           // interleaved (page p: unit 1 + p mod (units_per_kv - 1))
 };
 
 // wavefronts of a split workgroup at large batch, and when a few (request, kv-head) pairs must fill
