@@ -210,6 +210,25 @@ class Int2Setup:
         return int2, bf16, demote
 
 
+def warm_graph(g, min_ms=60.0):
+    """Untimed replays of a captured graph until at least min_ms of GPU time has passed (at least
+    two; the first launch also uploads the graph). The device takes some tens of milliseconds of
+    sustained work to reach its steady speed: measured at batch 32, successive replays of a 20-step
+    graph ran 140, 162, 148, 135, 133, 129, ... 126 us per step, while a 200-step graph was steady
+    from its second replay."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done, n = 0.0, 0
+    while n < 2 or done < min_ms:
+        a.record()
+        for _ in range(4):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        done += a.elapsed_time(b)
+        n += 4
+
+
 def time_int2(setup, steps, warmup, eager):
     """Returns (ms per step, median event intervals [launch gap, split, merge] in ms, launch mode).
 
@@ -237,10 +256,9 @@ def time_int2(setup, steps, warmup, eager):
             setup.parity = parity0
     torch.cuda.synchronize()
     if mode == "graph":
-        # one untimed replay first: the graph's first launch also uploads it to the device (a one-off
+        # untimed replays first (the graph's first launch also uploads it to the device: a one-off
         # cost, not a step's); replays repeat the same appends, so the caches end in the same state
-        g.replay()
-        torch.cuda.synchronize()
+        warm_graph(g)
         start.record()
         g.replay()
         stop.record()
@@ -273,7 +291,14 @@ def time_int2(setup, steps, warmup, eager):
         for x in e:
             x.record()
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(1e8))
+    # the eager launches are queued behind about 60 ms of device work, so every one of them is queued
+    # before the device reaches it and the device runs at its steady speed: graph replays (which
+    # leave the caches as they found them), or a device-side sleep without a graph
+    if mode == "graph":
+        for _ in range(max(2, math.ceil(60.0 / max(ms * steps, 1e-3)))):
+            g.replay()
+    else:
+        torch.cuda._sleep(int(1e8))
     for i in range(steps):
         setup.step(base + i, events=evs[i])
     torch.cuda.synchronize()
@@ -343,6 +368,12 @@ def time_prefill(w, batch, context, reps=5):
     run()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    run()
+    b.record()
+    torch.cuda.synchronize()
+    for _ in range(max(1, math.ceil(60.0 / max(a.elapsed_time(b), 1e-3)))):   # ~60 ms of untimed prefills
+        run()
     a.record()
     for _ in range(reps):
         run()
@@ -436,8 +467,7 @@ def time_bf16(w, batch, context, steps, warmup, fast_inputs):
         for i in range(steps):
             step(i)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g.replay()                 # untimed: the first launch also uploads the graph
-    torch.cuda.synchronize()
+    warm_graph(g)
     a.record()
     g.replay()
     b.record()
@@ -552,8 +582,7 @@ def time_decode_workload(w, steps, warmup, timeline_steps=0, timeline_raw=""):
         for i in range(steps):
             call(i)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g.replay()                 # untimed: the first launch also uploads the graph
-    torch.cuda.synchronize()
+    warm_graph(g)
     a.record()
     g.replay()
     b.record()
@@ -564,7 +593,8 @@ def time_decode_workload(w, steps, warmup, timeline_steps=0, timeline_raw=""):
         for x in e:
             x.record()        # creates the event
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(1e8))
+    for _ in range(max(2, math.ceil(60.0 / max(ms * steps, 1e-3)))):   # queued behind ~60 ms of replays
+        g.replay()
     for i in range(steps):
         call(i, evs[i])
     torch.cuda.synchronize()

@@ -85,6 +85,28 @@ __device__ __forceinline__ uint32_t row_shr_or_zero(uint32_t v) {
   else return dpp_row_shr<N>(v);
 }
 
+// Sum / maximum over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or 16), every lane of
+// the group receiving it: quad swaps, then the half-row and row mirrors (DPP, no LDS traffic).
+// Every lane of the wavefront must be active.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
+  if constexpr (N >= 2) v += dpp_f<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_f<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_f<0x141>(v);
+  if constexpr (N >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 // ------------------------------------------------------------------ split bookkeeping
 struct HistCounts {
   int T, hist, n2, n4;
@@ -516,6 +538,46 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
   OSCAR_TL_SPLIT(12);
   __syncthreads();
   OSCAR_TL_SPLIT(13);
+  // With at least twice as many threads as outputs, SPLIT adjacent lanes share an output, each
+  // folding every SPLIT-th wavefront; their maxima and sums are combined across the lanes (DPP).
+  constexpr int SPLIT = NW * kWave >= 2 * GQ * D ? NW * kWave / (GQ * D) : 1;
+  if constexpr (SPLIT >= 2) {
+    static_assert(NW % SPLIT == 0 && SPLIT <= 16 && (SPLIT & (SPLIT - 1)) == 0, "lane groups of the merge");
+    constexpr int WPS = NW / SPLIT;
+    const int idx = tid / SPLIT, s = tid % SPLIT;
+    const int hh = idx / D, ch = idx % D, nb = ch / 16;
+    float mw[WPS];
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < WPS; ++i) {
+      mw[i] = st_lds[s + SPLIT * i][0][hh];
+      M = fmaxf(M, mw[i]);
+    }
+    M = lanes_max<SPLIT>(M);
+    float L = 0.0f, Z = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int i = 0; i < WPS; ++i) {
+      const int w = s + SPLIT * i;
+      const bool live = mw[i] != kNegInf;
+      const float aw = live ? __builtin_amdgcn_exp2f(mw[i] - M) : 0.0f;
+      L = fmaf(aw, st_lds[w][1][hh], L);
+      Z = fmaf(aw, st_lds[w][2][hh], Z);
+      O = fmaf(aw, o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch], O);
+    }
+    L = lanes_sum<SPLIT>(L);
+    Z = lanes_sum<SPLIT>(Z);
+    O = lanes_sum<SPLIT>(O);
+    float vscale = 1.0f;
+    if (VSH_BITS == 2) vscale = ldexpf(1.0f, 24 - 2 * (nb % 4));
+    if (VSH_BITS == 4) vscale = ldexpf(1.0f, 24 - 4 * (nb % 2));
+    const bool empty = (M == kNegInf) || !(L > 0.0f);
+    if (s == 0) {
+      part_o[hh * D + ch] = empty ? 0.0f : (O * vscale + Z) / L;
+      if (ch == 0) part_lse[hh] = empty ? kNegInf : M + log2f(L);
+    }
+    OSCAR_TL_SPLIT(14);
+    return;
+  }
   for (int idx = tid; idx < GQ * D; idx += NW * kWave) {
     const int hh = idx / D, ch = idx % D, nb = ch / 16;
     float mw[NW];
@@ -1513,13 +1575,22 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
     };
     QPage<BITS, D, GQ> buf[NB];
     bool ok[NB];
+    // The first pages load before the length is known (they only need their ids): a page past the
+    // history is read and then masked. The rest of the ring goes by the length.
 #pragma unroll
-    for (int k = 0; k < NB - 2; ++k) ok[k] = load(buf[k], k);
+    for (int k = 0; k < NB - 2; ++k) {
+      const int id = page_index(__builtin_amdgcn_readlane(cur, k), 0, id_lim);
+      load_qpage<BITS, D, GQ>(buf[k], region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head), id >= 0,
+                              lane);
+      ok[k] = id >= 0;
+    }
     __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
     half8_t bq[D / 32];
     float uh, ul, esc;
     hist_query_operands<BITS, D, GQ, NW, LUT>(rr, qin, qlds, a.scale_log2e, bq, uh, ul, esc);
     OSCAR_TL_SPLIT(3);
+#pragma unroll
+    for (int k = 0; k < NB - 2; ++k) ok[k] = ok[k] && k < R;
     const float uq = uh + ul;
     const Codebook cbk = load_codebook(LUT ? a.codebook : nullptr, kv, 0);
     const Codebook cbv = load_codebook(LUT ? a.codebook : nullptr, kv, 1);
@@ -1694,7 +1765,7 @@ struct MergeState {
 struct MergeCtx {
   int first, units; // the request's units
   int kv, bk;
-  int n;           // slots: 3 per unit (window, INT2, INT4), then 2 step slots in a fused step
+  int n;           // slots: 3 per unit (window, INT2, INT4; one per unit in the interleaved launch), then 2 step slots in a fused step
   const float* rv; // R_V of the kv-head [D][D]
   float* rv_s;     // LDS copy of R_V, padded rows
   int grp, hh, c4, tid;   // hh: query head within the kv group
@@ -1705,7 +1776,9 @@ struct MergeCtx {
 template <int D, int GQ>
 __device__ __forceinline__ void merge_slot(const DecodeArgs& a, const MergeCtx& c, int i, size_t& lse_at,
                                            size_t& o_at, bool& window, bool& step) {
-  const int nu = 3 * c.units;
+  // interleaved one-request launch: unit 0 holds only the window partial, the others only INT2
+  const bool il = a.ws.interleave != 0;
+  const int nu = il ? c.units : 3 * c.units;
   step = i >= nu;
   if (step) {
     const size_t s = (size_t)c.bk * 2 + (i - nu);
@@ -1714,7 +1787,7 @@ __device__ __forceinline__ void merge_slot(const DecodeArgs& a, const MergeCtx& 
     window = i - nu == 1;
     return;
   }
-  const int j = i / 3, kind = i - 3 * j;
+  const int j = il ? i : i / 3, kind = il ? (i == 0 ? 0 : 1) : i - 3 * j;
   window = kind == 0;
   const size_t slot = ((size_t)a.dm.hkv * (c.first + j) + c.kv) * 3 + kind;
   lse_at = slot * GQ + c.hh;
@@ -1779,28 +1852,6 @@ __device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, 
   }
 }
 
-// Sum / maximum over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or 16), every lane of
-// the group receiving it: quad swaps, then the half-row and row mirrors (DPP, no LDS traffic).
-// Every lane of the wavefront must be active.
-template <int N>
-__device__ __forceinline__ float lanes_sum(float v) {
-  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
-  if constexpr (N >= 2) v += dpp_f<0xB1>(v);
-  if constexpr (N >= 4) v += dpp_f<0x4E>(v);
-  if constexpr (N >= 8) v += dpp_f<0x141>(v);
-  if constexpr (N >= 16) v += dpp_f<0x140>(v);
-  return v;
-}
-template <int N>
-__device__ __forceinline__ float lanes_max(float v) {
-  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "lane group of 1..16");
-  if constexpr (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
-  if constexpr (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
-  if constexpr (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
-  if constexpr (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
-  return v;
-}
-
 template <int D, int GQ, int HW>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, CacheWriteArgs cw) {
   constexpr int NT = kMergeThreads;
@@ -1834,7 +1885,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   const bool single = dm.batch == 1;
   const int first = single ? 0 : a.ws.req_units[2 * b];
   const int units = single ? a.ws.units_per_kv : a.ws.req_units[2 * b + 1];
-  const int n = 3 * units + (a.step ? 2 : 0);
+  const int n = (a.ws.interleave ? units : 3 * units) + (a.step ? 2 : 0);
   // Slots are taken up to 12 at a time per thread: every load of a batch is issued (slots no segment
   // wrote are not read) before any is consumed, and the first batch's loads share one round trip
   // with the R_V staging.
