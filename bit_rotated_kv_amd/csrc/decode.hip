@@ -386,7 +386,9 @@ __device__ void query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<
       if (lane < CG) *reinterpret_cast<float4*>(&L.ps[wave][h][4 * cg]) = acc;
     }
   }
+  OSCAR_TL_SPLIT(11);
   __syncthreads();
+  OSCAR_TL_SPLIT(15);
   constexpr int NC = D / kWave;  // channels per lane in the head pass
   for (int h = wave; h < GQ; h += NW) {
     float v[NC];
@@ -1584,6 +1586,7 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
                               lane);
       ok[k] = id >= 0;
     }
+    OSCAR_TL_SPLIT(9);
     __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
     half8_t bq[D / 32];
     float uh, ul, esc;
@@ -1616,6 +1619,7 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
           }
           if ((!ok[k] || (!ok[k + 1] && r + k + 1 < R)) && lane == 0) atomicOr(a.ws.flags, 1u);
         }
+        if (r == 0 && k == 0) OSCAR_TL_SPLIT(10);
       }
     }
   } else if (lane == 0 && R > 0) {

@@ -15,8 +15,12 @@
  * General contract
  *  - Every pointer argument named *_host is host memory; every other pointer is device memory
  *    on the current HIP device. The caller allocates and owns every buffer. The library never
- *    allocates device memory, never synchronises the stream and keeps no global state.
- *  - All work is enqueued asynchronously on `stream` (0 = the default stream).
+ *    allocates device memory and keeps no global state (oscar_decode_step_noalloc aside: its
+ *    workspace is a fixed array of the library on each device).
+ *  - All work is enqueued asynchronously on `stream` (0 = the default stream), and no call
+ *    synchronises the stream, with two offline exceptions documented at their declarations:
+ *    oscar_codebook_fit (waits for `stream` each iteration) and oscar_rotation_from_covariance
+ *    (host computation, no device work).
  *  - Arguments are validated on the host (scalars, null pointers, sizes); on a validation error
  *    nothing is enqueued and a negative status is returned. Device-resident values (lengths,
  *    page ids) are not read by the host: lengths above max_seq_len are clamped, and page ids
