@@ -8,7 +8,9 @@
 // 6 segments (bit 0 step, 1 window, 2 INT2, 3 INT4) | history pages of the unit << 8,
 // 7 XCC_ID << 32 | HW_ID, 8 every wavefront past its page loop (last history segment), 9 step
 // segment loads done, 10 step rotation done, 11 step codes stored, 12 workgroup merge: own state
-// in LDS, 13 past its barrier, 14 partial stored. Merge kernel rows follow the split rows:
+// in LDS, 13 past its barrier, 14 partial stored. History units of the interleaved one-request
+// launch reuse 9 (first page loads issued), 10 (first page pair done), 11 (query products formed)
+// and 15 (past the query prologue's first barrier). Merge kernel rows follow the split rows:
 // 0 entry, 1 slots folded, 3 groups combined, 5 exit.
 #pragma once
 
