@@ -62,6 +62,10 @@ def parse():
                     help="diagnostic mode: run N eager steps of the workload with liboscar_timeline.so and print "
                          "the per-workgroup phase percentiles instead of the benchmark line")
     ap.add_argument("--timeline-raw", default="", help="with --timeline: also save the raw tables (.npy)")
+    ap.add_argument("--timeline-run", type=int, default=3, metavar="K",
+                    help="with --timeline: each recorded table is the last of K steps launched back to back, so the "
+                         "recorded split follows the previous step's merge as in a decode loop (K = 1: a step "
+                         "launched on an idle device)")
     ap.add_argument("--only", default="", choices=["", "step", "bs32", "bs32_100k", "gqa8_ragged", "mixed", "prefill"],
                     help="profiling mode: run only this measurement (plus --copy-probe-mib) and print its result "
                          "instead of the benchmark line")
@@ -610,7 +614,7 @@ def time_decode_workload(w, steps, warmup, timeline_steps=0, timeline_raw=""):
 
 
 # ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_qwen3_8b_100k_bs1_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_b1_kernel_qwen3_8b_100k_bs1_traffic.txt")
 
 
 SPLIT_SOURCES = ("api.hip", "common.hpp", "decode.hip", "demote.hpp", "launch.hpp")
@@ -911,20 +915,25 @@ def timeline_main(args):
     est = batch * w.num_kv_heads * (context - 320) * 72
     copies = args.copies or max(2, math.ceil(1.0e9 / est))
     log(f"timeline: batch {batch}, context {context}, {copies} copies, {args.timeline} steps")
-    setup = Int2Setup(w, batch, context, copies, args.warmup + args.timeline, fast_inputs=batch > 1)
+    setup = Int2Setup(w, batch, context, copies, args.warmup + args.timeline * max(1, args.timeline_run),
+                      fast_inputs=batch > 1)
     for i in range(args.warmup):
         setup.step(i)
     torch.cuda.synchronize()
     tabs = []
+    n = args.warmup
     for i in range(args.timeline):
         timeline.clear()
-        setup.step(args.warmup + i)
+        for _ in range(max(1, args.timeline_run)):
+            setup.step(n)
+            n += 1
         torch.cuda.synchronize()
         tabs.append(timeline.read())
     if args.timeline_raw:
         np.save(args.timeline_raw, np.stack(tabs))
     res = timeline.summarize(tabs)
-    res["workload"] = f"{w.name}: batch {batch}, context {context}, fused decode step, eager launches"
+    res["workload"] = (f"{w.name}: batch {batch}, context {context}, fused decode step, eager launches, each table the "
+                       f"last of {max(1, args.timeline_run)} steps launched back to back")
     print(json.dumps(res), flush=True)
 
 

@@ -98,6 +98,15 @@ def summarize(tabs) -> dict:
             d.setdefault("wg_reduce_store", []).extend(dur(14, 13)[h])
             d.setdefault("wg_to_exit", []).extend(dur(5, 14)[h])
             d.setdefault("history_pages", []).extend(pages[h])
+            # history units of the interleaved one-request launch (column 9 set): the prologue in parts
+            il = h & (col(9) != 0) & ((segs & 3) == 0)
+            if il.any():
+                d.setdefault("il_ids_and_first_loads", []).extend(dur(9, 0)[il])
+                d.setdefault("il_query_products", []).extend(dur(11, 9)[il])
+                d.setdefault("il_query_barrier", []).extend(dur(15, 11)[il])
+                d.setdefault("il_query_head_pass", []).extend(dur(3, 15)[il])
+                d.setdefault("il_first_pair", []).extend(dur(10, 3)[il])
+                d.setdefault("il_loop_rest", []).extend(dur(4, 10)[il])
             d["count"] = d.get("count", 0) + int(m.sum())
         ends.append({int(x): round(float(exit_[xcc == x].max()), 2) for x in np.unique(xcc)})
         mg = tab[SPLIT_ROWS:]
