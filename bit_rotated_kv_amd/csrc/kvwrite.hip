@@ -2,6 +2,7 @@
 // demote of the oldest recent token (OSCAR overview page, method paragraph; study note, SGLang
 // case), and the fill of the full-BF16 baseline cache.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -446,127 +447,134 @@ __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(Cac
   }
   // quantising wavefronts: stores only
   const int ct = tid - 256;
-  const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, sel);
-  const float clip = sel ? a.clip_v : a.clip_k;
-  const int r4 = lane % 4, q = (lane / 4) % 4, s4 = lane / 16;
-  const int wa = s4 % NWL;                                   // word a of the thread
-  const int row = RPW * (ct / kWave) + 4 * (s4 / NWL) + r4;  // its row of the chunk
-  const int vbase = 8 * (r4 / 2) + 16 * (r4 % 2);            // value words: bit 8m + 16hf of the row's token
-  // channel of the thread's value e = 4c + u: keys 64a + 32(c/2) + 8q + 4(c%2) + u, values
-  // 64a + 16c + 4q + u
-  auto chan4 = [&](int c) { return sel == 0 ? 64 * wa + 32 * (c / 2) + 8 * q + 4 * (c % 2) : 64 * wa + 16 * c + 4 * q; };
-  // bit of value e in its word: keys 8(c/2) + 4(c%2) + 2(u/2) + 16(u%2) (one word), values
-  // vbase + 2c in word u (column 4q + u)
-  auto bit_of = [&](int e) {
-    const int c = e / 4, u = e % 4;
-    return sel == 0 ? 8 * (c / 2) + 4 * (c % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * c;
-  };
-  __syncthreads();
-  for (int i = 0; i < nchunks + 1; ++i) {
-    if (i >= 1) {
-      // quantise and store chunk i-1 from the rotated rows of its buffer
-      const int chunk = chunk0 + i - 1, qb = (i - 1) % 2;
-      const int n = min(CH, hist - CH * chunk);
-      const bool live = row < n;
-      float x[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(&xr[qb][row][chan4(c)]);
-        x[4 * c] = v.x;
-        x[4 * c + 1] = v.y;
-        x[4 * c + 2] = v.z;
-        x[4 * c + 3] = v.w;
-      }
-      float mn = x[0], mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) {
-        mn = fminf(mn, x[e]);
-        mx = fmaxf(mx, x[e]);
-      }
-      // the row's threads: lanes 4q + r4 of the DPP row (q < 4), and for two words the same lanes
-      // of the DPP row 16 lanes away
-      mn = fminf(mn, dpp_row_ror<4>(mn));
-      mx = fmaxf(mx, dpp_row_ror<4>(mx));
-      mn = fminf(mn, dpp_row_ror<8>(mn));
-      mx = fmaxf(mx, dpp_row_ror<8>(mx));
-      if constexpr (NWL == 2) {
-        mn = fminf(mn, __shfl_xor(mn, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      }
-      const QuantGrid g = make_grid(mn, mx, clip, 3);
-      // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
-      // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone
-      // in x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny
-      // scale, a zero point far off the range) take int2_code_estimate.
-      bool short_row = false;
-      if (!CBK) {
-#pragma clang fp contract(off)
-        const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
-        short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
-      }
-      uint32_t w[4];   // keys: w[0] only; values: column 4q + u in w[u]
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = 0;
-      auto word_of = [&](int e) { return sel == 0 ? 0 : e % 4; };
-      uint32_t redo = 0;
-      if (CBK) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          bool r;
-          w[word_of(e)] |= cb_code_fast(x[e], g, cb, r) << bit_of(e);
-          redo |= (uint32_t)r << e;
-        }
-      } else if (short_row) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-#pragma clang fp contract(off)
-          const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
-          const float rt_ = rintf(t);
-          redo |= (uint32_t)!(fabsf(t - rt_) < 0.5f - 0x1p-14f) << e;
-          w[word_of(e)] |= (uint32_t)rt_ << bit_of(e);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          bool r;
-          w[word_of(e)] |= int2_code_estimate(x[e], g, r) << bit_of(e);
-          redo |= (uint32_t)r << e;
-        }
-      }
-      // the rare codes the correctly rounded quotient decides
-      while (redo) {
-        const int e = __builtin_ctz(redo);
-        redo &= redo - 1;
-        const float xv = xr[qb][row][chan4(e / 4) + e % 4];
-        const uint32_t code = CBK ? cb_code_exact(xv, g, cb) : quant_code_exact(xv, g, 3);
-        const int sh = bit_of(e);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k == word_of(e)) w[k] = (w[k] & ~(3u << sh)) | (code << sh);
-      }
-      const int64_t page = pgs[qb][row / kPage];
-      uint8_t* ph = page >= 0 ? page_head_mut(a.pool, page, kv, dm) : nullptr;
-      const int t = row % kPage;
-      if (sel == 0) {
-        if (live && ph) reinterpret_cast<uint32_t*>(ph + (size_t)(16 * q + t) * 2 * CB)[wa] = w[0];
-      } else {
-        // rows past the history add nothing; the quad's 4 rows complete the group's words
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t v = live ? w[k] : 0u;
-          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad swap 1,0,3,2
-          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // quad swap 2,3,0,1
-          w[k] = v;
-        }
-        const uint32_t v = r4 == 0 ? w[0] : (r4 == 1 ? w[1] : (r4 == 2 ? w[2] : w[3]));
-        if ((row & ~3) < n && ph)
-          reinterpret_cast<uint32_t*>(ph + (size_t)(16 * (t / 4) + 4 * q + r4) * 2 * CB + CB)[wa] = v;
-      }
-      if (live && ph && wa == 0 && q == 0)
-        reinterpret_cast<uint32_t*>(ph + 4 * D * 2)[2 * t + sel] = g.s_bits | (g.z_bits << 16);
-    }
+  // the K and V workgroups run separately instantiated quantiser loops (SELV = 0: keys, 1: values),
+  // so the channel map, the bit positions and the word choice are compile-time constants
+  auto quantise = [&](auto selc) {
+    constexpr int SELV = decltype(selc)::value;
+    const Codebook cb = load_codebook(CBK ? a.codebook : nullptr, kv, SELV);
+    const float clip = SELV ? a.clip_v : a.clip_k;
+    const int r4 = lane % 4, q = (lane / 4) % 4, s4 = lane / 16;
+    const int wa = s4 % NWL;                                   // word a of the thread
+    const int row = RPW * (ct / kWave) + 4 * (s4 / NWL) + r4;  // its row of the chunk
+    const int vbase = 8 * (r4 / 2) + 16 * (r4 % 2);            // value words: bit 8m + 16hf of the row's token
+    // channel of the thread's value e = 4c + u: keys 64a + 32(c/2) + 8q + 4(c%2) + u, values
+    // 64a + 16c + 4q + u
+    auto chan4 = [&](int c) { return SELV == 0 ? 64 * wa + 32 * (c / 2) + 8 * q + 4 * (c % 2) : 64 * wa + 16 * c + 4 * q; };
+    // bit of value e in its word: keys 8(c/2) + 4(c%2) + 2(u/2) + 16(u%2) (one word), values
+    // vbase + 2c in word u (column 4q + u)
+    auto bit_of = [&](int e) {
+      const int c = e / 4, u = e % 4;
+      return SELV == 0 ? 8 * (c / 2) + 4 * (c % 2) + 2 * (u / 2) + 16 * (u % 2) : vbase + 2 * c;
+    };
     __syncthreads();
-  }
+    for (int i = 0; i < nchunks + 1; ++i) {
+      if (i >= 1) {
+        // quantise and store chunk i-1 from the rotated rows of its buffer
+        const int chunk = chunk0 + i - 1, qb = (i - 1) % 2;
+        const int n = min(CH, hist - CH * chunk);
+        const bool live = row < n;
+        float x[16];
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 v = *reinterpret_cast<const float4*>(&xr[qb][row][chan4(c)]);
+          x[4 * c] = v.x;
+          x[4 * c + 1] = v.y;
+          x[4 * c + 2] = v.z;
+          x[4 * c + 3] = v.w;
+        }
+        float mn = x[0], mx = x[0];
+  #pragma unroll
+        for (int e = 1; e < 16; ++e) {
+          mn = fminf(mn, x[e]);
+          mx = fmaxf(mx, x[e]);
+        }
+        // the row's threads: lanes 4q + r4 of the DPP row (q < 4), and for two words the same lanes
+        // of the DPP row 16 lanes away
+        mn = fminf(mn, dpp_row_ror<4>(mn));
+        mx = fmaxf(mx, dpp_row_ror<4>(mx));
+        mn = fminf(mn, dpp_row_ror<8>(mn));
+        mx = fmaxf(mx, dpp_row_ror<8>(mx));
+        if constexpr (NWL == 2) {
+          mn = fminf(mn, __shfl_xor(mn, 16, kWave));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        }
+        const QuantGrid g = make_grid(mn, mx, clip, 3);
+        // A row whose whole estimate range [t(lo), t(hi)] lies in (-0.5, 3.5) (so |t| < 32 and the
+        // rounded estimate needs no clamp) takes the short form of the uniform rule; t is monotone
+        // in x, so the bound holds for every clamped value of the row. Other rows (a zero or tiny
+        // scale, a zero point far off the range) take int2_code_estimate.
+        bool short_row = false;
+        if (!CBK) {
+  #pragma clang fp contract(off)
+          const float tlo = (g.lo - g.z) * g.rs, thi = (g.hi - g.z) * g.rs;
+          short_row = g.s > 0.0f && tlo > -0.5f && thi < 3.5f;
+        }
+        uint32_t w[4];   // keys: w[0] only; values: column 4q + u in w[u]
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = 0;
+        auto word_of = [&](int e) { return SELV == 0 ? 0 : e % 4; };
+        uint32_t redo = 0;
+        if (CBK) {
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            bool r;
+            w[word_of(e)] |= cb_code_fast(x[e], g, cb, r) << bit_of(e);
+            redo |= (uint32_t)r << e;
+          }
+        } else if (short_row) {
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+  #pragma clang fp contract(off)
+            const float t = (__builtin_amdgcn_fmed3f(x[e], g.lo, g.hi) - g.z) * g.rs;
+            const float rt_ = rintf(t);
+            redo |= (uint32_t)!(fabsf(t - rt_) < 0.5f - 0x1p-14f) << e;
+            w[word_of(e)] |= (uint32_t)rt_ << bit_of(e);
+          }
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            bool r;
+            w[word_of(e)] |= int2_code_estimate(x[e], g, r) << bit_of(e);
+            redo |= (uint32_t)r << e;
+          }
+        }
+        // the rare codes the correctly rounded quotient decides
+        while (redo) {
+          const int e = __builtin_ctz(redo);
+          redo &= redo - 1;
+          const float xv = xr[qb][row][chan4(e / 4) + e % 4];
+          const uint32_t code = CBK ? cb_code_exact(xv, g, cb) : quant_code_exact(xv, g, 3);
+          const int sh = bit_of(e);
+  #pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (k == word_of(e)) w[k] = (w[k] & ~(3u << sh)) | (code << sh);
+        }
+        const int64_t page = pgs[qb][row / kPage];
+        uint8_t* ph = page >= 0 ? page_head_mut(a.pool, page, kv, dm) : nullptr;
+        const int t = row % kPage;
+        if (SELV == 0) {
+          if (live && ph) reinterpret_cast<uint32_t*>(ph + (size_t)(16 * q + t) * 2 * CB)[wa] = w[0];
+        } else {
+          // rows past the history add nothing; the quad's 4 rows complete the group's words
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t v = live ? w[k] : 0u;
+            v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad swap 1,0,3,2
+            v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // quad swap 2,3,0,1
+            w[k] = v;
+          }
+          const uint32_t v = r4 == 0 ? w[0] : (r4 == 1 ? w[1] : (r4 == 2 ? w[2] : w[3]));
+          if ((row & ~3) < n && ph)
+            reinterpret_cast<uint32_t*>(ph + (size_t)(16 * (t / 4) + 4 * q + r4) * 2 * CB + CB)[wa] = v;
+        }
+        if (live && ph && wa == 0 && q == 0)
+          reinterpret_cast<uint32_t*>(ph + 4 * D * 2)[2 * t + SELV] = g.s_bits | (g.z_bits << 16);
+      }
+      __syncthreads();
+    }
+  };
+  if (sel == 0) quantise(std::integral_constant<int, 0>{});
+  else quantise(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------ demote (one decode step)
