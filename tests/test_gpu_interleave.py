@@ -159,3 +159,20 @@ def test_interleaved_step_equals_demote_then_decode(t0):
     ref = oracle.decode_attention(p.caches[0], p.q[0])[None]
     worst, mab = G.check_close(out_b.cpu().numpy().astype(np.float64), ref, tag=f"interleaved step t0={t0}")
     print(f"t0={t0}: worst rel-L2 {worst:.2e} max-abs {mab:.2e}")
+
+
+def test_interleaved_decode_reuses_a_dirty_workspace():
+    """A workspace holding garbage (report word aside), reused call after call, gives the
+    fresh-workspace result every time in the interleaved launch."""
+    p = P.make_problem(_workload(5_000), with_oracle=False)
+    cb, rk, rv, _, _ = _cache(p, oracle_written=False)
+    ref, _ = _decode(p, cb, rk, rv)
+    q = G.bf16_tensor(oracle.bf16_bits(p.q))
+    for fill in (0x5A, 0x00, 0xFF):
+        ws = torch.full((brk.decode_workspace_bytes(cb.layout, 1, TMAX),), fill, dtype=torch.uint8, device="cuda")
+        ws[:4] = 0
+        for _ in range(3):
+            out = brk.decode_attn(cb.layout, q, cb.seq_len, cb.window, cb.pool, cb.page_table, rk, rv, ws, TMAX)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().astype(np.float64), ref), f"fill {fill:#x}"
+        assert int(ws[:4].view(torch.int32).item()) == 0
