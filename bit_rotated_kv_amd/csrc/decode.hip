@@ -530,13 +530,40 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
     st_lds[wave][1][h] = l_tot;
     st_lds[wave][2][h] = z_tot;
   }
+  // FOLD (GQA 4 and 8): the high and low rows of a head are added in registers before the state
+  // goes to LDS. At GQA 4 they are 16 lanes apart (rows c and c + 4: lane groups 0 and 1), at GQA 8
+  // 32 lanes apart (rows c and c + 8: lane groups 0-1 and 2-3); one lane-swap instruction takes the
+  // accumulators of two adjacent 16-column blocks nb = 2k, 2k+1 at once, and their sums land side by
+  // side, so every write covers 32 consecutive columns of one head. Other widths store both rows.
+  constexpr bool FOLD = (GQ == 4 || GQ == 8) && D % 32 == 0;
+  if constexpr (FOLD) {
 #pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb)
+    for (int k = 0; k < D / 32; ++k)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t a0 = __float_as_uint(st.o[2 * k][r]), a1 = __float_as_uint(st.o[2 * k + 1][r]);
+        float sum;
+        if constexpr (GQ == 4) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
+          // lanes 0-15: block 2k, rows r and r + 4; lanes 16-31: block 2k + 1
+          sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          if (lane < 32) o_lds[wave][r][32 * k + lane] = sum;
+        } else {
+          const auto sw = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
+          // lanes 0-31: block 2k, rows 4g + r (g < 2) and their low rows; lanes 32-63: block 2k + 1
+          sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          o_lds[wave][4 * (g % 2) + r][32 * k + 16 * (g / 2) + h] = sum;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row < 2 * GQ) o_lds[wave][row][16 * nb + h] = st.o[nb][r];
+      }
+  }
   OSCAR_TL_SPLIT(12);
   __syncthreads();
   OSCAR_TL_SPLIT(13);
@@ -564,7 +591,7 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
       const float aw = live ? __builtin_amdgcn_exp2f(mw[i] - M) : 0.0f;
       L = fmaf(aw, st_lds[w][1][hh], L);
       Z = fmaf(aw, st_lds[w][2][hh], Z);
-      O = fmaf(aw, o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch], O);
+      O = fmaf(aw, FOLD ? o_lds[w][hh][ch] : o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch], O);
     }
     L = lanes_sum<SPLIT>(L);
     Z = lanes_sum<SPLIT>(Z);
@@ -595,7 +622,7 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
       const bool live = mw[w] != kNegInf;
       const float aw = live ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.0f;
       const float lw = st_lds[w][1][hh], zw = st_lds[w][2][hh];
-      const float ow = o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch];
+      const float ow = FOLD ? o_lds[w][hh][ch] : o_lds[w][hh][ch] + o_lds[w][GQ + hh][ch];
       L = fmaf(aw, lw, L);
       Z = fmaf(aw, zw, Z);
       O = fmaf(aw, ow, O);
