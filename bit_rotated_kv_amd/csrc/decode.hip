@@ -1798,7 +1798,6 @@ struct MergeCtx {
   int kv, bk;
   int n;           // slots: 3 per unit (window, INT2, INT4; one per unit in the interleaved launch), then 2 step slots in a fused step
   const float* rv; // R_V of the kv-head [D][D]
-  float* rv_s;     // LDS copy of R_V, padded rows
   int grp, hh, c4, tid;   // hh: query head within the kv group
 };
 
@@ -1825,11 +1824,10 @@ __device__ __forceinline__ void merge_slot(const DecodeArgs& a, const MergeCtx& 
   o_at = (slot * GQ + c.hh) * D;
 }
 
-// Folds slots base + grp + k*NG (k < MS) into the thread's state; with `stage`, also copies R_V
-// into LDS between issuing the slot loads and consuming them.
-template <int D, int GQ, int MS, int NG, int RS, int NT>
-__device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, const MergeCtx& c, int base,
-                                           bool stage) {
+// Folds slots base + grp + k*NG (k < MS) into the thread's state: every load is issued before any
+// is consumed.
+template <int D, int GQ, int MS, int NG>
+__device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, const MergeCtx& c, int base) {
   float lv[MS];
   float4 vv[MS];
   bool use[MS], win[MS];
@@ -1846,19 +1844,6 @@ __device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, 
     const float* po = step ? a.ws.step_o : a.ws.part_o;
     lv[k] = live ? pl[la] : kNegInf;
     vv[k] = live ? *reinterpret_cast<const float4*>(po + oa + 4 * c.c4) : float4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  if (stage) {
-    const float4* rv4 = reinterpret_cast<const float4*>(c.rv);
-#pragma unroll
-    for (int k = 0; k < D * D / 4 / NT; ++k) {
-      const int e = c.tid + k * NT;           // float4 index
-      const float4 r4 = rv4[e];
-      float* dst = c.rv_s + ((4 * e) / D) * RS + (4 * e) % D;
-      dst[0] = r4.x;
-      dst[1] = r4.y;
-      dst[2] = r4.z;
-      dst[3] = r4.w;
-    }
   }
 #pragma unroll
   for (int k = 0; k < MS; ++k) {
@@ -1892,11 +1877,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   constexpr int SUB = NT / (HW * D);  // combine: threads per output column (adjacent lanes)
   constexpr int GPS = NG / SUB;       // slot groups per combine thread (4)
   constexpr int NP = NT / D;          // un-rotation: threads per R_V row (adjacent lanes)
-  constexpr int RP = D / NP;
-  constexpr int RS = D + NP;          // padded LDS row of R_V: the NP parts of a row walk distinct banks
+  constexpr int RP = D / NP;          // contiguous entries of the row per thread
   constexpr int AS = D + 4;           // padded LDS row of a group's sums
-  static_assert(GPS * SUB == NG && NP * RP == D && SUB <= 16 && NP <= 16, "merge thread layout");
-  __shared__ float rv_s[D * RS];
+  static_assert(GPS * SUB == NG && NP * RP == D && SUB <= 16 && NP <= 16 && RP % 4 == 0, "merge thread layout");
   __shared__ __attribute__((aligned(16))) float acc_h[NG][HW][AS];
   __shared__ __attribute__((aligned(16))) float acc_w[NG][HW][AS];
   __shared__ float m_s[NG][HW], w_s[NG][HW];
@@ -1921,15 +1904,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   // wrote are not read) before any is consumed, and the first batch's loads share one round trip
   // with the R_V staging.
   MergeState ms_st{kNegInf, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  const MergeCtx mc{first, units, kv, bk, n, a.rot_v + (size_t)kv * D * D, rv_s, grp, h0 + hl, c4, tid};
+  const MergeCtx mc{first, units, kv, bk, n, a.rot_v + (size_t)kv * D * D, grp, h0 + hl, c4, tid};
+  // the thread's RP contiguous entries of its R_V row for the un-rotation, loaded with the first
+  // batch of partials (one round trip; R_V is read straight into registers, not staged in LDS)
+  const int uj = tid / NP, upart = tid % NP;
+  float4 rvr[RP / 4];
+#pragma unroll
+  for (int e = 0; e < RP / 4; ++e)
+    rvr[e] = *reinterpret_cast<const float4*>(mc.rv + (size_t)uj * D + RP * upart + 4 * e);
   const int per_thread = (n + NG - 1) / NG;   // uniform
   if (per_thread <= 4) {
-    merge_fold<D, GQ, 4, NG, RS, NT>(a, ms_st, mc, 0, true);
+    merge_fold<D, GQ, 4, NG>(a, ms_st, mc, 0);
   } else if (per_thread <= 12) {
-    merge_fold<D, GQ, 12, NG, RS, NT>(a, ms_st, mc, 0, true);
+    merge_fold<D, GQ, 12, NG>(a, ms_st, mc, 0);
   } else {
-    merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, 0, true);
-    for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG, RS, NT>(a, ms_st, mc, base, false);
+    merge_fold<D, GQ, 8, NG>(a, ms_st, mc, 0);
+    for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG>(a, ms_st, mc, base);
   }
   OSCAR_TL_MERGE(1);
   *reinterpret_cast<float4*>(&acc_h[grp][hl][4 * c4]) = ms_st.ah;
@@ -1974,18 +1964,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   __syncthreads();
   OSCAR_TL_MERGE(3);
   // un-rotation: thread (j, part) forms part of out[h][j] = sum_i hsum[h][i] R_V[j][i] over
-  // i = part, part + NP, ...; the parts are folded across the NP lanes of row j
+  // i = RP part .. RP part + RP - 1 (its registers); the parts are folded across the NP lanes of row j
   {
-    const int j = tid / NP, part = tid % NP;
-    const float* rrow = rv_s + j * RS + part;
+    const int j = uj, part = upart;
     float acc[HW];
 #pragma unroll
     for (int h2 = 0; h2 < HW; ++h2) acc[h2] = 0.0f;
 #pragma unroll
     for (int k = 0; k < RP; ++k) {
-      const float rji = rrow[NP * k];
+      const float4& r4 = rvr[k / 4];
+      const float rji = (k % 4 == 0) ? r4.x : ((k % 4 == 1) ? r4.y : ((k % 4 == 2) ? r4.z : r4.w));
 #pragma unroll
-      for (int h2 = 0; h2 < HW; ++h2) acc[h2] = fmaf(hsum[h2][part + NP * k], rji, acc[h2]);
+      for (int h2 = 0; h2 < HW; ++h2) acc[h2] = fmaf(hsum[h2][RP * part + k], rji, acc[h2]);
     }
 #pragma unroll
     for (int h2 = 0; h2 < HW; ++h2) acc[h2] = lanes_sum<NP>(acc[h2]);
