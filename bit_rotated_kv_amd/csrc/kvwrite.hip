@@ -28,8 +28,11 @@ __device__ inline int window_position(int j, int t, int T, int sink, int recent)
 
 // ------------------------------------------------------------------ prefill: window + counts
 // One workgroup per (window page, kv-head, request); the first page's workgroup of kv-head 0 also
-// counts the request's INT4 history tokens.
+// counts the request's INT4 history tokens. Every element of the thread is loaded before any is
+// stored: the page could alias the inputs as far as the compiler knows, so a loop of load-store
+// pairs would wait out one memory round trip per element.
 __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
+  constexpr int kItems = kPage * 128 / 256;   // elements per thread at the largest head_dim
   const Dims& dm = a.dm;
   const int j = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = dm.d;
@@ -38,11 +41,21 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
   const int64_t pb = bf16_page_head_bytes(d);
   uint16_t* pg = reinterpret_cast<uint16_t*>(a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + j) * pb);
   const size_t src = ((size_t)b * dm.hkv + kv) * dm.max_seq_len;
-  for (int idx = tid; idx < kPage * d; idx += 256) {
-    const int t = idx / d, ch = idx % d;
-    const int p = window_position(j, t, T, dm.sink, dm.recent);
-    pg[bf16_key_index(d, t, ch)] = p >= 0 ? a.k[(src + p) * d + ch] : (uint16_t)0;
-    pg[bf16_value_index(d, t, ch)] = p >= 0 ? a.v[(src + p) * d + ch] : (uint16_t)0;
+  uint16_t kx[kItems], vx[kItems];
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int idx = tid + 256 * i, t = idx / d, ch = idx % d;
+    const int p = idx < kPage * d ? window_position(j, t, T, dm.sink, dm.recent) : -1;
+    kx[i] = p >= 0 ? a.k[(src + p) * d + ch] : (uint16_t)0;
+    vx[i] = p >= 0 ? a.v[(src + p) * d + ch] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int idx = tid + 256 * i, t = idx / d, ch = idx % d;
+    if (idx < kPage * d) {
+      pg[bf16_key_index(d, t, ch)] = kx[i];
+      pg[bf16_value_index(d, t, ch)] = vx[i];
+    }
   }
   if (j == 0 && kv == 0 && a.n_int4_out) {
     __shared__ int red[256];
