@@ -46,7 +46,9 @@ def _compile(src: str, timeline: bool = False) -> str:
 
 def _link(objs, lib: str):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: a symbol left undefined (such as a kernel whose host stub the compiler dropped)
+    # fails the link instead of the first load
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

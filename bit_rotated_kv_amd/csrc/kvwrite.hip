@@ -325,18 +325,35 @@ __device__ __forceinline__ uint32_t int2_code_estimate(float x, const QuantGrid&
   return (uint32_t)__builtin_amdgcn_fmed3f(r, 0.0f, 3.0f);
 }
 
-// Two 32-row tiles of x (row m of tile k at x + (32k + m) * stride; rows at or past nrows read as
-// zero) times the wavefront's slice of R: rotate_tile's products in rotate_tile's order for each
-// tile, the two tiles' chains interleaved so each hides the other's matrix-core latency.
+// Rows of a chunk in LDS without padding: 16-byte piece c of row r sits at slot c ^ swz(r) of the
+// row, so the 16 lanes of a 256-byte LDS pass that read one piece of 16 consecutive rows (the A
+// operand below) hit 16 different slots. At d = 128 a row is one pass wide (swz = r mod 16); at
+// d = 64 two rows share a pass (swz = (r / 2) mod 8).
 template <int D>
-__device__ __forceinline__ void rotate_tile_pair(const RotSlice<D>& rs, const uint16_t* x, int stride, int nrows,
-                                                 int lane, float16v_t& acc0, float16v_t& acc1) {
+__device__ __forceinline__ int piece_swizzle(int r) {
+  return D == 128 ? r % 16 : (r / 2) % 8;
+}
+
+// A operand (rows row0..row0+31, k-step kk) of the 32x32x16 product from the swizzled rows.
+template <int D>
+__device__ __forceinline__ bf16x8_t swizzled_rotation_a(const uint16_t* x, int row0, int kk, int lane) {
+  const int m = row0 + lane % 32, c = 2 * kk + lane / 32;
+  return __builtin_bit_cast(bf16x8_t,
+                            *reinterpret_cast<const u32x4_t*>(x + m * D + 8 * (c ^ piece_swizzle<D>(m))));
+}
+
+// Both 32-row tiles of a chunk (swizzled rows; rows past the chunk's history are zeros there) times
+// the wavefront's slice of R: rotate_tile's products in rotate_tile's order for each tile, the two
+// tiles' chains interleaved so each hides the other's matrix-core latency.
+template <int D>
+__device__ __forceinline__ void rotate_swizzled_pair(const RotSlice<D>& rs, const uint16_t* x, int lane,
+                                                     float16v_t& acc0, float16v_t& acc1) {
   acc0 = float16v_t{};
   acc1 = float16v_t{};
 #pragma unroll
   for (int kk = 0; kk < RotSlice<D>::KS; ++kk) {
-    const bf16x8_t a0 = rotation_a(x, stride, nrows, kk, lane);
-    const bf16x8_t a1 = rotation_a(x + 32 * stride, stride, nrows - 32, kk, lane);
+    const bf16x8_t a0 = swizzled_rotation_a<D>(x, 0, kk, lane);
+    const bf16x8_t a1 = swizzled_rotation_a<D>(x, 32, kk, lane);
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, rs.lo[kk], acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, rs.lo[kk], acc1, 0, 0, 0);
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, rs.mid[kk], acc0, 0, 0, 0);
@@ -345,6 +362,24 @@ __device__ __forceinline__ void rotate_tile_pair(const RotSlice<D>& rs, const ui
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, rs.hi[kk], acc1, 0, 0, 0);
   }
 }
+
+// 16 bytes per lane from a raw buffer (byte offset voff of the lane) straight into LDS: lane L
+// writes bytes 16L..16L+15 from `lds`, which must be the same for the whole wavefront.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector memory operations of the wavefront are outstanding (loads into LDS
+// included), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier after the wavefront's LDS operations. The compiler's own barrier would also
+// wait for every row load still streaming into LDS, which is what the loads run ahead to avoid.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Threads of the INT2 prefill: 4 rotating wavefronts, and 64 rows x 4 * (D / 64) quantising threads.
 template <int D>
@@ -355,12 +390,13 @@ constexpr int kPrefillThreads = 256 + 64 * 4 * (D / 64);
 // workgroup per compute unit and (run of `run` chunks, kv-head, request x {K, V}): wavefronts 0..3
 // rotate (matrix cores) and issue every load, the other wavefronts (8 at d = 128, two per SIMD; 4 at
 // d = 64) quantise and store, one chunk apart, so the matrix cores and the vector units work at
-// once. In iteration i the rotating wavefronts publish chunk i's page ids, stage chunk i+1's rows
-// (loaded during iteration i-1) in LDS, issue chunk i+2's row loads and chunk i+1's page-id loads,
-// and rotate chunk i; the quantising ones quantise and store chunk i-1. A load is thus never waited
-// on behind the stores (one counter covers both), and every LDS buffer passed between the sides is
-// double-buffered, so one workgroup barrier per iteration orders them all (each side runs its own
-// loop with as many barriers, so neither side's registers stay live in the other's).
+// once. In iteration i the rotating wavefronts publish chunk i's page ids, issue chunk i+1's
+// page-id loads and chunk i+2's row loads (straight into the third of three LDS row buffers), and
+// rotate chunk i; the quantising ones quantise and store chunk i-1. A load is thus never waited on
+// behind the stores (one counter covers both), a chunk's rows have two iterations to arrive, and
+// the rotated rows and page ids passed between the sides are double-buffered, so one workgroup
+// barrier per iteration orders them all (each side runs its own loop with as many barriers, so
+// neither side's registers stay live in the other's).
 // A quantising thread (row, a, q), a < NWL = D/64 words per lane part, q < 4, takes 16 channels and
 // assembles whole page-head words in registers:
 //  * keys: key word (g, a) of a token holds channels 64a + 32k2 + 8g + j (k2 < 2, j < 8) at bit
@@ -374,16 +410,19 @@ constexpr int kPrefillThreads = 256 + 64 * 4 * (D / 64);
 template <int D, bool CBK>
 __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(CacheWriteArgs a, int run) {
   constexpr int CH = kPrefillChunk;
-  constexpr int XS = D + 8;     // bf16 row pitch (16-byte pad)
   constexpr int RS = D + 16;    // fp32 row pitch: consecutive rows 16 banks apart
   constexpr int SL = RotSlice<D>::SLICES;
   constexpr int CB = D * 2 / 32;         // bytes of a lane's key (or value) part
   constexpr int NWL = CB / 4;            // its words
   constexpr int RPW = 16 / NWL;          // rows per quantising wavefront
-  constexpr int XW = CH * D / 8 / 256;   // 16-byte row pieces per rotating thread
-  constexpr int CP = CH / kPage;         // pages of a chunk
+  constexpr int XW = CH * D * 2 / 1024 / 4;   // 1 KB row blocks of a chunk per rotating wavefront
+  constexpr int CP = CH / kPage;              // pages of a chunk
   static_assert(NWL == 1 || NWL == 2, "d = 64 or 128");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][CH][XS];
+  // three row buffers as separate arrays: the compiler then sees that reading one does not wait
+  // for the loads still streaming into another
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[CH * D];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[CH * D];
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[CH * D];
   __shared__ __attribute__((aligned(16))) float xr[2][CH][RS];
   __shared__ int64_t pgs[2][CP];
   const Dims& dm = a.dm;
@@ -396,25 +435,31 @@ __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(Cac
   if (CH * chunk0 >= hist) return;   // the whole workgroup
   const int nchunks = min(run, (hist - CH * chunk0 + CH - 1) / CH);
   if (tid < 256) {
-    // rotating wavefronts: they also issue every load of the kernel (rows, page ids) one iteration
-    // ahead, so no load waits behind the quantising wavefronts' stores
-    const int wave = tid / kWave;
+    // rotating wavefronts: they also issue every load of the kernel (rows, page ids) ahead of its
+    // use, so no load waits behind the quantising wavefronts' stores
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * D;
-    // a chunk's rows through a raw buffer descriptor over its n rows: the pieces of rows at or past n
-    // read as zeros, with no branch and no register cleared ahead of the load
-    auto load_rows = [&](int chunk, u32x4_t (&w)[XW]) {
-      const int p0 = dm.sink + CH * chunk, n = min(CH, hist - CH * chunk);
+    // a chunk's rows into row buffer `buf`, through a raw buffer descriptor over its n rows (pieces
+    // of rows at or past n arrive as zeros; a chunk past the history has n = 0 and reads nothing).
+    // Each load writes one 1 KB block of the buffer, lane L its 16-byte slot L; the global piece it
+    // fetches is the one the swizzle puts in that slot.
+    int goff[XW];
+#pragma unroll
+    for (int e = 0; e < XW; ++e) {
+      const int slot = 64 * (XW * wave + e) + lane;
+      const int row = slot / (D / 8), c = (slot % (D / 8)) ^ piece_swizzle<D>(row);
+      goff[e] = 16 * (row * (D / 8) + c);
+    }
+    auto load_rows = [&](int chunk, uint16_t* buf) {
+      const int p0 = dm.sink + CH * chunk;
+      // uniform by construction; said so, or the compiler may place it in a vector register and
+      // loop over the "distinct" descriptors
+      const int n = __builtin_amdgcn_readfirstlane(max(0, min(CH, hist - CH * chunk)));
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(src + (size_t)p0 * D), (short)0, n * D * 2, kRawBufferFlags);
 #pragma unroll
-      for (int e = 0; e < XW; ++e) w[e] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * e), 0, 0);
-    };
-    auto stage_rows = [&](int buf, const u32x4_t (&w)[XW]) {
-#pragma unroll
-      for (int e = 0; e < XW; ++e) {
-        const int idx = tid + 256 * e;
-        *reinterpret_cast<u32x4_t*>(&xs[buf][idx / (D / 8)][8 * (idx % (D / 8))]) = w[e];
-      }
+      for (int e = 0; e < XW; ++e)
+        buffer_load_lds16(r, buf + 512 * (XW * wave + e), goff[e]);
     };
     // page id of page tid % CP of a chunk through a raw buffer descriptor over the request's page
     // table (a page past it reads as 0 and is dropped when published), kept as loaded until it is
@@ -426,36 +471,41 @@ __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(Cac
     };
     RotSlice<D> rs;
     if (wave < SL) rs.load((sel ? a.rot_v : a.rot_k) + (size_t)kv * D * D, wave, lane);
-    u32x4_t xw[XW];
-    load_rows(chunk0, xw);
-    stage_rows(0, xw);
+    // Every iteration issues the same loads (past the run: an empty row range, a page id that is
+    // not published), so the count of loads in flight is the same on every path.
     int32_t pv = load_page(chunk0);
-    if (nchunks > 1) load_rows(chunk0 + 1, xw);
-    __syncthreads();
-    for (int i = 0; i < nchunks + 1; ++i) {
-      if (i < nchunks) {
-        // chunk i's page ids (read by the quantising wavefronts in iteration i+1)
-        if (tid < CP)
-          pgs[i % 2][tid] = CP * (chunk0 + i) + tid < dm.pt_stride && page_ok((int64_t)pv, 2, dm) ? (int64_t)pv : -1;
-        if (i + 1 < nchunks) {
-          stage_rows((i + 1) % 2, xw);   // loaded during the previous iteration
-          pv = load_page(chunk0 + i + 1);
-        }
-        if (i + 2 < nchunks) load_rows(chunk0 + i + 2, xw);
-        if (wave < SL) {
-          const int n = min(CH, hist - CH * (chunk0 + i));
-          float16v_t acc0, acc1;
-          rotate_tile_pair<D>(rs, &xs[i % 2][0][0], XS, n, lane, acc0, acc1);
+    load_rows(chunk0, xs0);
+    load_rows(chunk0 + 1, xs1);
+    wait_vmem<XW>();   // everything but chunk 1's rows
+    lds_barrier();
+    // iteration i on row buffers cur (chunk i) and ahead (chunk i+2); the loop steps through the
+    // three buffers in turn, so each access names its buffer
+    auto iteration = [&](int i, const uint16_t* cur, uint16_t* ahead) {
+      if (i > nchunks) return;
+      // chunk i's page ids (read by the quantising wavefronts in iteration i+1)
+      if (tid < CP && i < nchunks)
+        pgs[i % 2][tid] = CP * (chunk0 + i) + tid < dm.pt_stride && page_ok((int64_t)pv, 2, dm) ? (int64_t)pv : -1;
+      pv = load_page(chunk0 + i + 1);
+      load_rows(chunk0 + i + 2, ahead);
+      if (i < nchunks && wave < SL) {
+        float16v_t acc0, acc1;
+        rotate_swizzled_pair<D>(rs, cur, lane, acc0, acc1);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int r = 8 * (j / 4) + 4 * (lane / 32) + j % 4, col = 32 * wave + lane % 32;
-            xr[i % 2][r][col] = acc0[j];
-            xr[i % 2][32 + r][col] = acc1[j];
-          }
+        for (int j = 0; j < 16; ++j) {
+          const int r = 8 * (j / 4) + 4 * (lane / 32) + j % 4, col = 32 * wave + lane % 32;
+          xr[i % 2][r][col] = acc0[j];
+          xr[i % 2][32 + r][col] = acc1[j];
         }
       }
-      __syncthreads();
+      wait_vmem<XW>();   // chunk i+1's rows and page ids have arrived (chunk i+2's may still stream in)
+      lds_barrier();
+    };
+    for (int i = 0; i < nchunks + 1; i += 3) {
+      iteration(i, xs0, xs2);
+      iteration(i + 1, xs1, xs0);
+      iteration(i + 2, xs2, xs1);
     }
+    wait_vmem<0>();   // no load may still write this workgroup's LDS once its wavefronts end
     return;
   }
   // quantising wavefronts: stores only
