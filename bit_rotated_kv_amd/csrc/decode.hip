@@ -1653,9 +1653,9 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
     atomicOr(a.ws.flags, 1u);
   }
   OSCAR_TL_SPLIT(4);
-  // the merge buffers share LDS with the query prologue: every wavefront is past its prologue
-  __syncthreads();
   OSCAR_TL_SPLIT(8);
+  // o_lds and st_lds are not shared with the query prologue's LDS: the state goes out at once, and
+  // the merge's own barrier waits for the other wavefronts
   workgroup_merge<D, GQ, LUT ? 0 : BITS, Redist<GQ>::on, NW>(st, o_lds, st_lds, po, pl);
 }
 
@@ -1671,6 +1671,17 @@ union alignas(16) SplitScratch {
 // Workgroups of a split launch that a compute unit should hold: three at GQA 8 in an INT2-only
 // cache (the register count is then bounded to fit), one of the wide workgroups, else what the
 // resources give.
+// LDS of the one-request launch: the merge buffer has its own space, so a wavefront writes its
+// state as soon as its pages are done, while others still read the query prologue's LDS.
+template <int D, int GQ, int NW>
+struct alignas(16) SplitB1Scratch {
+  union alignas(16) Seg {
+    HistQueryLds<D, GQ, NW> hist;
+    StepLds<D, GQ> step;
+  } seg;
+  float o[NW][2 * GQ][D];   // workgroup merge of the history or window segment
+};
+
 template <int GQ, bool MIXED, int NW>
 constexpr int kSplitMinBlocks = NW >= 16 ? 1 : (NW >= 8 ? 2 : ((GQ == 8 && !MIXED) ? 3 : 1));
 
@@ -1745,7 +1756,7 @@ __global__ __launch_bounds__(NW * kWave, (kSplitMinBlocks<GQ, MIXED, NW>)) void 
 template <int D, int GQ, bool CB, int NW>
 __global__ __launch_bounds__(NW * kWave, 1) void split_b1_kernel(DecodeArgs a, CacheWriteArgs cw) {
   __shared__ float st_lds[NW][3][8];
-  __shared__ SplitScratch<D, GQ, NW> scr;
+  __shared__ SplitB1Scratch<D, GQ, NW> scr;
   OSCAR_TL_SPLIT(0);
 #ifdef OSCAR_TIMELINE
   OSCAR_TL_SPLIT_VALUE(7, timeline_placement());
@@ -1763,7 +1774,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void split_b1_kernel(DecodeArgs a, C
     OSCAR_TL_SPLIT(1);
     OSCAR_TL_SPLIT_VALUE(6, (a.step ? 1u : 0u) | 2u);
     if (a.step) {
-      step_seg<D, GQ, NW>(a, cw, 0, kv, scr.step);
+      step_seg<D, GQ, NW>(a, cw, 0, kv, scr.seg.step);
       __syncthreads();
     }
     window_seg<D, GQ, NW>(a, 0, kv, 0, 1, po, pl, scr.o, st_lds);
@@ -1771,7 +1782,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void split_b1_kernel(DecodeArgs a, C
   } else {
     if (tid < 2 * GQ) pl[tid < GQ ? tid : GQ + tid] = kNegInf;   // no window or INT4 partials
     hist_seg_b1<D, GQ, NW, CB>(a, kv, u - 1, a.ws.units_per_kv - 1, po + GQ * D, pl + GQ, scr.o, st_lds,
-                               scr.hist);
+                               scr.seg.hist);
   }
   OSCAR_TL_SPLIT(5);
 }
