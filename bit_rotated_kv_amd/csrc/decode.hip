@@ -338,9 +338,14 @@ __device__ __forceinline__ float sum_adjacent_tree(float (&x)[N]) {
 // parts of head c-GQ for GQ <= c < 2GQ.
 // LUT: the key operand holds codebook levels (normal fp16 values, no bit-position factor), so
 // every channel takes p = 0 and the products carry 2^(24-E) instead of 2^-E.
-template <int BITS, int D, int GQ, int NW, bool LUT = false>
+// A callable run by every wavefront between its query products and the prologue's first barrier.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int BITS, int D, int GQ, int NW, bool LUT = false, typename Hook = NoHook>
 __device__ void query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<D, GQ, NW * kWave>& qin,
-                               HistQueryLds<D, GQ, NW>& L, float scale_log2e) {
+                               HistQueryLds<D, GQ, NW>& L, float scale_log2e, Hook&& hook = Hook{}) {
   constexpr int NT = NW * kWave;
   constexpr int CG = QRotRows<D, NT>::CG, QR = QRotRows<D, NT>::QR;
   using QI = QueryIn<D, GQ, NT>;
@@ -387,6 +392,7 @@ __device__ void query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<
     }
   }
   OSCAR_TL_SPLIT(11);
+  hook();
   __syncthreads();
   OSCAR_TL_SPLIT(15);
   constexpr int NC = D / kWave;  // channels per lane in the head pass
@@ -440,12 +446,12 @@ __device__ void query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<
 
 // The operands of query_operands as registers: lane (g, c) gets operand column c and the constants
 // of head c % GQ.
-template <int BITS, int D, int GQ, int NW, bool LUT = false>
+template <int BITS, int D, int GQ, int NW, bool LUT = false, typename Hook = NoHook>
 __device__ void hist_query_operands(const QRotRows<D, NW * kWave>& rr, const QueryIn<D, GQ, NW * kWave>& qin,
                                     HistQueryLds<D, GQ, NW>& L, float scale_log2e, half8_t (&bq)[D / 32], float& uh,
-                                    float& ul, float& esc) {
+                                    float& ul, float& esc, Hook&& hook = Hook{}) {
   const int lane = threadIdx.x % kWave, g = lane / 16, c = lane % 16;
-  query_operands<BITS, D, GQ, NW, LUT>(rr, qin, L, scale_log2e);
+  query_operands<BITS, D, GQ, NW, LUT>(rr, qin, L, scale_log2e, hook);
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const u32x4_t z = {0, 0, 0, 0};
@@ -1605,19 +1611,22 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
     QPage<BITS, D, GQ> buf[NB];
     bool ok[NB];
     // The first pages load before the length is known (they only need their ids): a page past the
-    // history is read and then masked. The rest of the ring goes by the length.
-#pragma unroll
-    for (int k = 0; k < NB - 2; ++k) {
-      const int id = page_index(__builtin_amdgcn_readlane(cur, k), 0, id_lim);
-      load_qpage<BITS, D, GQ>(buf[k], region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head), id >= 0,
-                              lane);
-      ok[k] = id >= 0;
-    }
-    OSCAR_TL_SPLIT(9);
-    __builtin_amdgcn_sched_barrier(0);  // every prefetch is issued before the query prologue waits
+    // history is read and then masked. They are requested once the wavefront's query products are
+    // done, i.e. once its rotation rows have arrived: requested at entry, their traffic delayed the
+    // rotation rows, which every wavefront waits for at the prologue's barrier. The rest of the
+    // ring goes by the length.
     half8_t bq[D / 32];
     float uh, ul, esc;
-    hist_query_operands<BITS, D, GQ, NW, LUT>(rr, qin, qlds, a.scale_log2e, bq, uh, ul, esc);
+    hist_query_operands<BITS, D, GQ, NW, LUT>(rr, qin, qlds, a.scale_log2e, bq, uh, ul, esc, [&]() {
+#pragma unroll
+      for (int k = 0; k < NB - 2; ++k) {
+        const int id = page_index(__builtin_amdgcn_readlane(cur, k), 0, id_lim);
+        load_qpage<BITS, D, GQ>(buf[k], region + (uint64_t)(((int64_t)max(id, 0) * dm.hkv + kv) * head), id >= 0,
+                                lane);
+        ok[k] = id >= 0;
+      }
+      OSCAR_TL_SPLIT(9);
+    });
     OSCAR_TL_SPLIT(3);
 #pragma unroll
     for (int k = 0; k < NB - 2; ++k) ok[k] = ok[k] && k < R;

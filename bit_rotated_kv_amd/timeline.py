@@ -101,9 +101,10 @@ def summarize(tabs) -> dict:
             # history units of the interleaved one-request launch (column 9 set): the prologue in parts
             il = h & (col(9) != 0) & ((segs & 3) == 0)
             if il.any():
-                d.setdefault("il_ids_and_first_loads", []).extend(dur(9, 0)[il])
-                d.setdefault("il_query_products", []).extend(dur(11, 9)[il])
-                d.setdefault("il_query_barrier", []).extend(dur(15, 11)[il])
+                # the first page loads go out after the wavefront's query products (11, then 9)
+                d.setdefault("il_query_products", []).extend(dur(11, 0)[il])
+                d.setdefault("il_first_loads", []).extend(dur(9, 11)[il])
+                d.setdefault("il_query_barrier", []).extend(dur(15, 9)[il])
                 d.setdefault("il_query_head_pass", []).extend(dur(3, 15)[il])
                 d.setdefault("il_first_pair", []).extend(dur(10, 3)[il])
                 d.setdefault("il_loop_rest", []).extend(dur(4, 10)[il])
