@@ -1845,9 +1845,10 @@ __device__ __forceinline__ void merge_slot(const DecodeArgs& a, const MergeCtx& 
 }
 
 // Folds slots base + grp + k*NG (k < MS) into the thread's state: every load is issued before any
-// is consumed.
-template <int D, int GQ, int MS, int NG>
-__device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, const MergeCtx& c, int base) {
+// is consumed; `hook` runs between the two.
+template <int D, int GQ, int MS, int NG, typename Hook = NoHook>
+__device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, const MergeCtx& c, int base,
+                                           Hook&& hook = Hook{}) {
   float lv[MS];
   float4 vv[MS];
   bool use[MS], win[MS];
@@ -1865,6 +1866,7 @@ __device__ __forceinline__ void merge_fold(const DecodeArgs& a, MergeState& st, 
     lv[k] = live ? pl[la] : kNegInf;
     vv[k] = live ? *reinterpret_cast<const float4*>(po + oa + 4 * c.c4) : float4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  hook();   // loads that are needed later go out behind this batch's
 #pragma unroll
   for (int k = 0; k < MS; ++k) {
     // slots past the last and empty partials (lse = -inf: no such segment, or no token) weigh 0
@@ -1925,20 +1927,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, Cach
   // with the R_V staging.
   MergeState ms_st{kNegInf, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   const MergeCtx mc{first, units, kv, bk, n, a.rot_v + (size_t)kv * D * D, grp, h0 + hl, c4, tid};
-  // the thread's RP contiguous entries of its R_V row for the un-rotation, loaded with the first
-  // batch of partials (one round trip; R_V is read straight into registers, not staged in LDS)
+  // the thread's RP contiguous entries of its R_V row for the un-rotation, requested right behind
+  // the first batch of partials (so the fold waits for the partials only; R_V is read straight into
+  // registers, not staged in LDS)
   const int uj = tid / NP, upart = tid % NP;
   float4 rvr[RP / 4];
+  auto load_rv = [&]() {
 #pragma unroll
-  for (int e = 0; e < RP / 4; ++e)
-    rvr[e] = *reinterpret_cast<const float4*>(mc.rv + (size_t)uj * D + RP * upart + 4 * e);
+    for (int e = 0; e < RP / 4; ++e)
+      rvr[e] = *reinterpret_cast<const float4*>(mc.rv + (size_t)uj * D + RP * upart + 4 * e);
+  };
   const int per_thread = (n + NG - 1) / NG;   // uniform
   if (per_thread <= 4) {
-    merge_fold<D, GQ, 4, NG>(a, ms_st, mc, 0);
+    merge_fold<D, GQ, 4, NG>(a, ms_st, mc, 0, load_rv);
   } else if (per_thread <= 12) {
-    merge_fold<D, GQ, 12, NG>(a, ms_st, mc, 0);
+    merge_fold<D, GQ, 12, NG>(a, ms_st, mc, 0, load_rv);
   } else {
-    merge_fold<D, GQ, 8, NG>(a, ms_st, mc, 0);
+    merge_fold<D, GQ, 8, NG>(a, ms_st, mc, 0, load_rv);
     for (int base = 8 * NG; base < n; base += 8 * NG) merge_fold<D, GQ, 8, NG>(a, ms_st, mc, base);
   }
   OSCAR_TL_MERGE(1);
