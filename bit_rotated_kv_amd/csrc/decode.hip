@@ -1578,12 +1578,15 @@ __device__ void hist_seg_b1(const DecodeArgs& a, int kv, int unit, int nunits, f
     const int off = pg < dm.pt_stride ? (int)pg : dm.pt_stride;
     return __builtin_amdgcn_raw_buffer_load_b32(ptr, 4 * off, 0, 0);
   };
-  int cur = chunk(0);
-  int nxt = chunk(kIdChunk);
+  // the rotation rows and the queries first: the query products wait for them, and a wait on a
+  // load waits for every load issued before it (the page ids come from the page table in HBM,
+  // while the rotation rows are mostly in L2)
   QRotRows<D, NT> rr;
   QueryIn<D, GQ, NT> qin;
   rr.load(a.rot_k + (size_t)kv * D * D, tid);
   qin.load(a.q + (size_t)kv * GQ * D, tid);
+  int cur = chunk(0);
+  int nxt = chunk(kIdChunk);
   const HistCounts hc = hist_counts(a, 0);
   const int ntok = uniform(hc.n2);
   const int npages = min((ntok + kPage - 1) / kPage, dm.pt_stride);
