@@ -107,6 +107,17 @@ __device__ __forceinline__ float lanes_max(float v) {
   return v;
 }
 
+// v plus the value of the lane 16 apart (lane l and l ^ 16), and the same 32 lanes apart: a lane
+// swap of v with itself puts each lane's own value and its partner's in the two results.
+__device__ __forceinline__ float rows_sum16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float rows_sum32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ------------------------------------------------------------------ split bookkeeping
 struct HistCounts {
   int T, hist, n2, n4;
@@ -517,18 +528,31 @@ __device__ void workgroup_merge(const WaveState<D, GQ>& st, float (*o_lds)[2 * G
                                 float* part_o, float* part_lse) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16, h = lane % 16;
   float l_tot = st.l_part, z_tot = st.z_part;
+  // All on the vector units (no LDS round trip): row rotations, then lane swaps across rows.
   if constexpr (REDIST) {
-    // lanes c, c+GQ, ... of a row share a head: fold them first
-#pragma unroll
-    for (int o = GQ; o < 16; o <<= 1) {
-      l_tot += __shfl_xor(l_tot, o, kWave);
-      z_tot += __shfl_xor(z_tot, o, kWave);
+    // lanes c, c+GQ, ... of a row share a head: fold them first (a row rotated by 8, then by 4, ...
+    // down to GQ, sums the lanes of c's residue class mod GQ)
+    if constexpr (GQ <= 8) {
+      l_tot += dpp_row_ror<8>(l_tot);
+      z_tot += dpp_row_ror<8>(z_tot);
+    }
+    if constexpr (GQ <= 4) {
+      l_tot += dpp_row_ror<4>(l_tot);
+      z_tot += dpp_row_ror<4>(z_tot);
+    }
+    if constexpr (GQ <= 2) {
+      l_tot += dpp_row_ror<2>(l_tot);
+      z_tot += dpp_row_ror<2>(z_tot);
+    }
+    if constexpr (GQ <= 1) {
+      l_tot += dpp_row_ror<1>(l_tot);
+      z_tot += dpp_row_ror<1>(z_tot);
     }
   }
-  l_tot += __shfl_xor(l_tot, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
-  z_tot += __shfl_xor(z_tot, 16, kWave);
-  z_tot += __shfl_xor(z_tot, 32, kWave);
+  l_tot = rows_sum16(l_tot);
+  l_tot = rows_sum32(l_tot);
+  z_tot = rows_sum16(z_tot);
+  z_tot = rows_sum32(z_tot);
   // every wavefront writes its state (one that ran no page holds the empty state: m = -inf, sums
   // 0), so the reduction below reads all NW entries without per-wavefront branches
   if (g == 0 && h < GQ) {
