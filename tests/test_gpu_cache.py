@@ -20,6 +20,8 @@ CASES = {
                                                cal_tokens=1500, cal_ctx=512),
     "d128-mixed": lambda: synth.workload(5, batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=(1500, 900),
                                          cal_tokens=1500, cal_ctx=512),
+    # INT2-only at d 64 with histories 580 and 13 (a last chunk of 4 rows, a request shorter than a chunk)
+    "d64-int2-ragged": lambda: synth.workload(1, batch=2, num_q_heads=4, num_kv_heads=2, seq_lens=(900, 333)),
     "d64-mixed": lambda: synth.workload(5, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, group_size=64,
                                         seq_lens=(1300, 800), cal_tokens=1500, cal_ctx=512),
 }
