@@ -1459,6 +1459,7 @@ template <int BITS, int D, int GQ, int NW, bool LUT = false, bool PRE = false>
 __device__ void hist_seg(const DecodeArgs& a, int b, int kv, int p0, int p1, float* po, float* pl,
                          float (*o_lds)[2 * GQ][D], float (*st_lds)[3][8], HistQueryLds<D, GQ, NW>& qlds,
                          QRotRows<D, NW * kWave>& rr, QueryIn<D, GQ, NW * kWave>& qin, bool q_ready) {
+  constexpr int NT = NW * kWave;
   // Load ring of NB page buffers, taken as NB/2 page pairs (compile-time indices). With six pages
   // (below GQA 8) the QK^T products run one pair ahead: the matrix cores work on pair k+1 while the vector units
   // run the softmax of pair k, and the loads of pair k+2 are in flight. Wide workgroups (four
