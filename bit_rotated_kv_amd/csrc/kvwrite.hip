@@ -73,6 +73,33 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(CacheWriteArgs a) {
   }
 }
 
+// The window's K (sel 0) or V (sel 1) halves of pages j = x, x + nx, ... of one (request, kv-head),
+// copied by NT threads (thread t of them): the INT2-only prefill spreads the window over the
+// workgroups of its own launch. Every element a thread copies is loaded before any is stored.
+template <int NT>
+__device__ void window_slice(const CacheWriteArgs& a, int b, int kv, int sel, int T, int x, int nx, int t) {
+  constexpr int kItems = (kPage * 128 + NT - 1) / NT;   // elements per thread and page, at most
+  const Dims& dm = a.dm;
+  const int d = dm.d;
+  const int64_t pb = bf16_page_head_bytes(d);
+  const uint16_t* src = (sel ? a.v : a.k) + ((size_t)b * dm.hkv + kv) * dm.max_seq_len * d;
+  for (int j = x; j < dm.wpages; j += nx) {
+    uint16_t* pg = reinterpret_cast<uint16_t*>(a.window + ((size_t)(b * dm.hkv + kv) * dm.wpages + j) * pb);
+    uint16_t e[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int idx = t + NT * i, tk = idx / d, ch = idx % d;
+      const int p = idx < kPage * d ? window_position(j, tk, T, dm.sink, dm.recent) : -1;
+      e[i] = p >= 0 ? src[(size_t)p * d + ch] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int idx = t + NT * i, tk = idx / d, ch = idx % d;
+      if (idx < kPage * d) pg[sel ? bf16_value_index(d, tk, ch) : bf16_key_index(d, tk, ch)] = e[i];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ prefill: history pages
 // One workgroup per (run of kPrefillChunks 64-position chunks of the history, kv-head, request x
 // {K, V}). Wavefront w holds the 32-column slice w of R (three bf16 parts) in registers for the
@@ -432,7 +459,13 @@ __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(Cac
   T = T < 0 ? 0 : (T > dm.max_seq_len ? dm.max_seq_len : T);
   const int hist = T - dm.sink - dm.recent;
   const int chunk0 = run * blockIdx.x;
-  if (CH * chunk0 >= hist) return;   // the whole workgroup
+  // the window of this (request, kv-head, K or V) is shared among the launch's runs (the cache has
+  // no INT4 tokens: its count is 0)
+  if (a.n_int4_out && blockIdx.x == 0 && kv == 0 && sel == 0 && tid == 0) a.n_int4_out[b] = 0;
+  if (CH * chunk0 >= hist) {   // no history chunk for the workgroup: only its window pages
+    window_slice<kPrefillThreads<D>>(a, b, kv, sel, T, blockIdx.x, gridDim.x, tid);
+    return;
+  }
   const int nchunks = min(run, (hist - CH * chunk0 + CH - 1) / CH);
   if (tid < 256) {
     // rotating wavefronts: they also issue every load of the kernel (rows, page ids) ahead of its
@@ -508,8 +541,10 @@ __global__ __launch_bounds__(kPrefillThreads<D>, 1) void prefill_int2_kernel(Cac
     wait_vmem<0>();   // no load may still write this workgroup's LDS once its wavefronts end
     return;
   }
-  // quantising wavefronts: stores only
+  // quantising wavefronts: stores only (the window pages of the workgroup first, while the rotating
+  // wavefronts load the rotation and the first chunks)
   const int ct = tid - 256;
+  window_slice<kPrefillThreads<D> - 256>(a, b, kv, sel, T, blockIdx.x, gridDim.x, ct);
   // the K and V workgroups run separately instantiated quantiser loops (SELV = 0: keys, 1: values),
   // so the channel map, the bit positions and the word choice are compile-time constants
   auto quantise = [&](auto selc) {
@@ -671,10 +706,13 @@ __global__ __launch_bounds__(256) void bf16_fill_kernel(Bf16Args a) {
 hipError_t launch_prefill(const CacheWriteArgs& a, hipStream_t stream) {
   const Dims& dm = a.dm;
   if (dm.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_window_kernel, dim3(dm.wpages, dm.hkv, dm.batch), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int hmax = dm.max_seq_len - dm.sink - dm.recent;
+  // an INT2-only cache with history positions has its window copied by the history launch
+  if (dm.mixed || hmax <= 0) {
+    hipLaunchKernelGGL(prefill_window_kernel, dim3(dm.wpages, dm.hkv, dm.batch), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (hmax <= 0) return hipSuccess;
   const int runs = (hmax + kPrefillChunk * kPrefillChunks - 1) / (kPrefillChunk * kPrefillChunks);
   const dim3 grid(runs, dm.hkv, 2 * dm.batch);   // z: request x {K, V}
